@@ -1,0 +1,128 @@
+"""Single-query decode attention over the packed cache (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What is computed, per sequence b and query head h (KV head kh = h // G with
+G = Hq / Hkv, contiguous groups):
+
+* the query is rotated once: qr = Pi q (all dequantized keys live in the
+  rotated domain, and Pi is orthogonal, so <q, Pi^T khat> = <qr, khat>);
+* compressed token t (cache row t - sink) has score
+      s_t = scale * n_t * ( <qr, c[idx_t]> + QJL_t ),
+      QJL_t = sqrt(pi/2)/m * gamma_t * <S qr, z_t>   (only with a QJL stage)
+  (noze.it "TurboQuant-MLX: ...", section "Il metodo TurboQuant, in breve":
+  codebook scores plus the 1-bit sketch correction that makes the inner
+  product estimate unbiased);
+* sink tokens t < sink are kept raw and scored s_t = scale * <q, k_t>
+  (GitHub issue "Greetings from TurboQuant-MLX...", item 1: the first ~128
+  tokens stay uncompressed);
+* w = softmax(s) over all tokens of the sequence (sink and compressed jointly);
+* out = Pi^T sum_{t compressed, w_t >= eps} w_t n^V_t c_V[idx^V_t]
+        + sum_{t sink} w_t v_t,
+  where tokens below the threshold eps are dropped without renormalising
+  (same issue, item 3: V dequantization is skipped for attention weight
+  below 1e-6; eps = 0 disables the rule).
+
+Readings: scale = 1/sqrt(d); q and out are float; the weight compared with eps
+is the final normalised softmax weight.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .quantize import Spec, dequantize_rotated, rotation_of, sketch_of
+
+
+def attend_rotated(q: np.ndarray, qr: np.ndarray, khat: np.ndarray, k_norm: np.ndarray,
+                   vhat: np.ndarray, v_norm: np.ndarray, pi_v: np.ndarray, *,
+                   qjl_dots: np.ndarray | None = None, sink_k: np.ndarray | None = None,
+                   sink_v: np.ndarray | None = None, scale: float, v_skip: float = 0.0):
+    """Softmax attention with keys/values given as unit vectors in the rotated domain.
+
+    khat/vhat [T, d] rotated unit-norm vectors (centroids for the cache, or the
+    exact rotated vectors in the identity tests); qjl_dots [T] the optional
+    sketch correction already in inner-product units.  Returns (out, w, keep).
+    """
+    dots = khat @ qr
+    if qjl_dots is not None:
+        dots = dots + qjl_dots
+    s_comp = scale * np.asarray(k_norm, np.float64) * dots
+    n_sink = 0 if sink_k is None else sink_k.shape[0]
+    s_sink = scale * (np.asarray(sink_k, np.float64) @ q) if n_sink else np.zeros(0)
+    s = np.concatenate((s_sink, s_comp))
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    w_sink, w_comp = w[:n_sink], w[n_sink:]
+    keep = w_comp >= v_skip if v_skip > 0 else np.ones(w_comp.shape, dtype=bool)
+    acc_rot = (w_comp[keep] * np.asarray(v_norm, np.float64)[keep]) @ vhat[keep]
+    out = pi_v.T @ acc_rot
+    if n_sink:
+        out = out + w_sink @ np.asarray(sink_v, np.float64)
+    return out, w, keep
+
+
+def attend_one(q: np.ndarray, kspec: Spec, k_idx: np.ndarray, k_norm: np.ndarray,
+               vspec: Spec, v_idx: np.ndarray, v_norm: np.ndarray, *,
+               k_bits: np.ndarray | None = None, k_gamma: np.ndarray | None = None,
+               sink_k: np.ndarray | None = None, sink_v: np.ndarray | None = None,
+               scale: float | None = None, v_skip: float = 0.0,
+               pi_k: np.ndarray | None = None, pi_v: np.ndarray | None = None,
+               s_mat: np.ndarray | None = None, return_weights: bool = False):
+    """Attention output for one query head over one KV stream (float64).
+
+    q [d]; k_idx/v_idx [T, d] codes of the compressed tokens; norms [T];
+    k_bits [T, m] bool and k_gamma [T] for QJL; sink_k/sink_v [S, d] raw.
+    """
+    d = kspec.d
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    q = np.asarray(q, dtype=np.float64)
+    pi_k = rotation_of(kspec) if pi_k is None else pi_k
+    pi_v = rotation_of(vspec) if pi_v is None else pi_v
+    qr = pi_k @ q
+    khat = dequantize_rotated(np.asarray(k_idx), kspec)
+    vhat = dequantize_rotated(np.asarray(v_idx), vspec)
+    qjl = None
+    if kspec.qjl_m:
+        s_mat = sketch_of(kspec) if s_mat is None else s_mat
+        m = kspec.qjl_m
+        u = s_mat @ qr
+        z = np.where(np.asarray(k_bits, dtype=bool), 1.0, -1.0)
+        qjl = np.sqrt(np.pi / 2.0) / m * np.asarray(k_gamma, np.float64) * (z @ u)
+    out, w, keep = attend_rotated(q, qr, khat, k_norm, vhat, v_norm, pi_v, qjl_dots=qjl,
+                                  sink_k=sink_k, sink_v=sink_v, scale=scale, v_skip=v_skip)
+    if return_weights:
+        return out, w, keep
+    return out
+
+
+def attend(q: np.ndarray, kspec: Spec, vspec: Spec, seq_lens, k_idx, k_norm, v_idx, v_norm,
+           *, k_bits=None, k_gamma=None, sink_k=None, sink_v=None, sink: int = 0,
+           scale: float | None = None, v_skip: float = 0.0) -> np.ndarray:
+    """Batched decode attention.
+
+    q [B, Hq, d]; seq_lens [B] (sink included); per (b, kh) the compressed
+    arrays are indexed ``k_idx[b][kh]`` -> [L_b - sink, d] (lists or arrays);
+    sink_k/sink_v [B][Hkv] -> [sink, d].  Returns out [B, Hq, d] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv = len(k_idx[0])
+    G = Hq // Hkv
+    pi_k, pi_v = rotation_of(kspec), rotation_of(vspec)
+    s_mat = sketch_of(kspec) if kspec.qjl_m else None
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        ns = min(sink, L)
+        nc = L - ns
+        for h in range(Hq):
+            kh = h // G
+            out[b, h] = attend_one(
+                q[b, h], kspec, k_idx[b][kh][:nc], k_norm[b][kh][:nc],
+                vspec, v_idx[b][kh][:nc], v_norm[b][kh][:nc],
+                k_bits=None if k_bits is None else k_bits[b][kh][:nc],
+                k_gamma=None if k_gamma is None else k_gamma[b][kh][:nc],
+                sink_k=None if not ns else sink_k[b][kh][:ns],
+                sink_v=None if not ns else sink_v[b][kh][:ns],
+                scale=scale, v_skip=v_skip, pi_k=pi_k, pi_v=pi_v, s_mat=s_mat)
+    return out

@@ -1,0 +1,128 @@
+"""Pins of the oracle's decode attention (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attend as at
+from oracle import quantize as qz
+from oracle.rotation import sketch
+
+
+def sdpa(q, K, V, scale):
+    s = scale * (K @ q)
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    return w @ V, w
+
+
+def _data(T=300, seed=0, d=128):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(d), rng.standard_normal((T, d)), rng.standard_normal((T, d))
+
+
+def test_identity_dequantize_then_textbook_sdpa():
+    # Attending in the rotated domain equals textbook SDPA over explicitly
+    # dequantized keys/values Khat = n Pi^T c[idx] (Pi orthogonal).
+    q, K, V = _data()
+    ks, vs = qz.Spec(bits_lo=4, bits_hi=4), qz.Spec(bits_lo=3, bits_hi=3)
+    qk, qv = qz.quantize(K, ks), qz.quantize(V, vs)
+    out = at.attend_one(q, ks, qk.idx, qk.norms, vs, qv.idx, qv.norms)
+    pi = qz.rotation_of(ks)
+    Kh = qk.norms.astype(np.float64)[:, None] * (qz.dequantize_rotated(qk.idx, ks) @ pi)
+    Vh = qv.norms.astype(np.float64)[:, None] * (qz.dequantize_rotated(qv.idx, vs) @ pi)
+    ref, _ = sdpa(q, Kh, Vh, 1 / math.sqrt(128))
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_identity_exact_rotation_gives_plain_attention():
+    # Feeding the exact rotated unit vectors instead of centroids recovers
+    # softmax(q K^T / sqrt(d)) V on the original data.
+    q, K, V = _data(seed=1)
+    spec = qz.Spec()
+    pi = qz.rotation_of(spec)
+    nk, nv = np.linalg.norm(K, axis=1), np.linalg.norm(V, axis=1)
+    yk, yv = (K @ pi.T) / nk[:, None], (V @ pi.T) / nv[:, None]
+    out, _, _ = at.attend_rotated(q, pi @ q, yk, nk, yv, nv, pi, scale=1 / math.sqrt(128))
+    ref, _ = sdpa(q, K, V, 1 / math.sqrt(128))
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_sink_tokens_join_the_softmax_raw():
+    q, K, V = _data(T=200, seed=2)
+    ks = vs = qz.Spec(bits_lo=4, bits_hi=4)
+    n_sink = 16
+    qk, qv = qz.quantize(K[n_sink:], ks), qz.quantize(V[n_sink:], vs)
+    out = at.attend_one(q, ks, qk.idx, qk.norms, vs, qv.idx, qv.norms,
+                        sink_k=K[:n_sink], sink_v=V[:n_sink])
+    pi = qz.rotation_of(ks)
+    Kh = np.concatenate([K[:n_sink], qk.norms.astype(np.float64)[:, None] * (qz.dequantize_rotated(qk.idx, ks) @ pi)])
+    Vh = np.concatenate([V[:n_sink], qv.norms.astype(np.float64)[:, None] * (qz.dequantize_rotated(qv.idx, vs) @ pi)])
+    ref, _ = sdpa(q, Kh, Vh, 1 / math.sqrt(128))
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_v_skip_bound_and_no_renormalisation():
+    q, K, V = _data(T=2000, seed=3)
+    q = q * 6.0                                     # peaked scores so the rule fires
+    ks = vs = qz.Spec(bits_lo=4, bits_hi=4)
+    qk, qv = qz.quantize(K, ks), qz.quantize(V, vs)
+    o0, w, _ = at.attend_one(q, ks, qk.idx, qk.norms, vs, qv.idx, qv.norms, return_weights=True)
+    oe, _, keep = at.attend_one(q, ks, qk.idx, qk.norms, vs, qv.idx, qv.norms, v_skip=1e-6,
+                                return_weights=True)
+    skipped = ~keep
+    assert skipped.sum() > 10 and np.all(w[skipped] < 1e-6) and np.all(w[keep] >= 1e-6)
+    vhat_norm = qv.norms.astype(np.float64)      # ||n c[idx]|| <= n since ||c[idx]|| < 1
+    bound = np.sum(w[skipped] * vhat_norm[skipped])
+    assert 0 < np.linalg.norm(oe - o0) <= bound
+    # dropping is not renormalised: out_eps = out_0 - sum_skipped w_t vhat_t exactly
+    pi = qz.rotation_of(vs)
+    vh = qv.norms.astype(np.float64)[:, None] * (qz.dequantize_rotated(qv.idx, vs) @ pi)
+    assert np.max(np.abs((o0 - w[skipped] @ vh[skipped]) - oe)) < 1e-13
+
+
+def test_gqa_head_mapping():
+    rng = np.random.default_rng(4)
+    B, Hq, Hkv, T = 2, 8, 2, 64
+    ks = vs = qz.Spec(bits_lo=3, bits_hi=3)
+    q = rng.standard_normal((B, Hq, 128))
+    kidx, knorm, vidx, vnorm = [], [], [], []
+    for b in range(B):
+        kb, vb = [], []
+        for h in range(Hkv):
+            kb.append(qz.quantize(rng.standard_normal((T, 128)), ks))
+            vb.append(qz.quantize(rng.standard_normal((T, 128)), vs))
+        kidx.append([x.idx for x in kb]); knorm.append([x.norms for x in kb])
+        vidx.append([x.idx for x in vb]); vnorm.append([x.norms for x in vb])
+    lens = [T, T - 7]
+    out = at.attend(q, ks, vs, lens, kidx, knorm, vidx, vnorm)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // (Hq // Hkv)
+            L = lens[b]
+            ref = at.attend_one(q[b, h], ks, kidx[b][kh][:L], knorm[b][kh][:L],
+                                vs, vidx[b][kh][:L], vnorm[b][kh][:L])
+            assert np.array_equal(out[b, h], ref)
+
+
+def test_qjl_scores_unbiased_over_seeds():
+    # The sketch-corrected score n(<qr, c[idx]> + estimate) averages to the exact
+    # <q, k> over QJL seeds (the rotation, hence the residual, stays fixed).
+    rng = np.random.default_rng(9)
+    qv, k = rng.standard_normal(128), rng.standard_normal(128)
+    exact = qv @ k
+    vals, plain = [], []
+    for s in range(1500):
+        spec = qz.Spec(bits_lo=2, bits_hi=2, qjl_m=128, qjl_seed=500 + s)
+        S = sketch(spec.qjl_seed, 128, 128)
+        qq = qz.quantize(k[None, :], spec, s_mat=S)
+        pi = qz.rotation_of(spec)
+        qr = pi @ qv
+        base = qz.dequantize_rotated(qq.idx, spec)[0] @ qr
+        corr = qz.qjl_inner_estimate(qr, S, qq.qjl_bits[0], qq.rnorms[0])
+        n = float(qq.norms64[0])
+        vals.append(n * (base + corr))
+        plain.append(n * base)
+    vals = np.array(vals)
+    se = vals.std() / math.sqrt(len(vals))
+    assert abs(vals.mean() - exact) < 4 * se
