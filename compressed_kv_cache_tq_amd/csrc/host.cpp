@@ -1,0 +1,470 @@
+// Host half of libtq.so: seeded rotation and sketch, Lloyd-Max codebook,
+// device tables, argument validation and the C ABI entry points.
+//
+// Method: noze.it, "TurboQuant-MLX: quantizzare pesi e KV cache per LLM
+// open-weight su Mac", sections "Il metodo TurboQuant, in breve" (random
+// rotation, per-coordinate optimal scalar quantizer, 1-bit JL sketch of the
+// residual) and "Cosa aggiunge turboquant-mlx" (Lloyd-Max codebook).
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tq_status fail(tq_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+// ---------------------------------------------------------------------------
+// Random streams.  SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): the state
+// advances by 0x9E3779B97F4A7C15 and each output is the 64-bit finalizer of
+// the new state.  Uniform doubles use the top 53 bits; Gaussians use
+// Box-Muller on consecutive pairs, r = sqrt(-2 ln(1-u_a)) times cos then sin
+// of 2 pi u_b, filled in order.
+
+struct SplitMix64 {
+  uint64_t state;
+  uint64_t next() {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+};
+
+double unit_double(uint64_t z) { return static_cast<double>(z >> 11) * 0x1.0p-53; }
+
+void gaussian_fill(uint64_t seed, double* out, size_t n) {
+  SplitMix64 g{seed};
+  for (size_t i = 0; i < n; i += 2) {
+    const double ua = unit_double(g.next());
+    const double ub = unit_double(g.next());
+    const double r = std::sqrt(-2.0 * std::log(1.0 - ua));
+    const double ang = 2.0 * M_PI * ub;
+    out[i] = r * std::cos(ang);
+    if (i + 1 < n) out[i + 1] = r * std::sin(ang);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Haar rotation: Householder QR of the seeded Gaussian matrix A (row-major),
+// A = Q R, then pi = Q diag(sign R_kk) so that the triangular factor has a
+// positive diagonal (Mezzadri 2007), which makes pi unique.
+
+void rotation_build(int d, uint64_t seed, double* pi) {
+  std::vector<double> a(static_cast<size_t>(d) * d);
+  gaussian_fill(seed, a.data(), a.size());
+  std::vector<double> vs(static_cast<size_t>(d) * d, 0.0);  // Householder vectors, row k = v_k
+  std::vector<double> vn(d, 0.0);                           // |v_k|^2 (0: identity reflector)
+  std::vector<double> rdiag(d, 0.0);
+  for (int k = 0; k < d; ++k) {
+    double nrm2 = 0.0;
+    for (int i = k; i < d; ++i) nrm2 += a[i * d + k] * a[i * d + k];
+    const double nrm = std::sqrt(nrm2);
+    if (nrm == 0.0) { rdiag[k] = 0.0; continue; }
+    const double alpha = a[k * d + k] > 0 ? -nrm : nrm;  // R_kk after the reflection
+    double* v = &vs[static_cast<size_t>(k) * d];
+    for (int i = k; i < d; ++i) v[i] = a[i * d + k];
+    v[k] -= alpha;
+    double v2 = 0.0;
+    for (int i = k; i < d; ++i) v2 += v[i] * v[i];
+    vn[k] = v2;
+    if (v2 == 0.0) { rdiag[k] = alpha; continue; }
+    for (int j = k; j < d; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += v[i] * a[i * d + j];
+      const double f = 2.0 * dot / v2;
+      for (int i = k; i < d; ++i) a[i * d + j] -= f * v[i];
+    }
+    rdiag[k] = a[k * d + k];
+  }
+  // Q = H_0 H_1 ... H_{d-1}, accumulated by applying the reflectors to I from the left
+  // in reverse order.
+  std::vector<double> q(static_cast<size_t>(d) * d, 0.0);
+  for (int i = 0; i < d; ++i) q[i * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    if (vn[k] == 0.0) continue;
+    const double* v = &vs[static_cast<size_t>(k) * d];
+    for (int j = 0; j < d; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += v[i] * q[i * d + j];
+      const double f = 2.0 * dot / vn[k];
+      for (int i = k; i < d; ++i) q[i * d + j] -= f * v[i];
+    }
+  }
+  for (int i = 0; i < d; ++i)
+    for (int k = 0; k < d; ++k) pi[i * d + k] = q[i * d + k] * (rdiag[k] < 0 ? -1.0 : 1.0);
+}
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max codebook for the law of one coordinate X of a uniform unit vector
+// in R^d: density K_d (1-x^2)^((d-3)/2) on [-1, 1], i.e. (1+X)/2 ~
+// Beta(a, a) with a = (d-1)/2.  Cell masses use the regularised incomplete
+// beta function (continued fraction, DLMF 8.17.22, evaluated with the
+// modified Lentz method); first moments have the closed form
+// K_d/(d-1) [(1-lo^2)^((d-1)/2) - (1-hi^2)^((d-1)/2)].
+
+double beta_cf(double a, double b, double x) {
+  const double tiny = 1e-300;
+  double c = 1.0, dd = 1.0 - (a + b) * x / (a + 1.0);
+  if (std::fabs(dd) < tiny) dd = tiny;
+  dd = 1.0 / dd;
+  double h = dd;
+  for (int m = 1; m <= 100000; ++m) {
+    const double m2 = 2.0 * m;
+    double num = m * (b - m) * x / ((a + m2 - 1.0) * (a + m2));
+    dd = 1.0 + num * dd;
+    if (std::fabs(dd) < tiny) dd = tiny;
+    c = 1.0 + num / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    dd = 1.0 / dd;
+    h *= dd * c;
+    num = -(a + m) * (a + b + m) * x / ((a + m2) * (a + m2 + 1.0));
+    dd = 1.0 + num * dd;
+    if (std::fabs(dd) < tiny) dd = tiny;
+    c = 1.0 + num / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    dd = 1.0 / dd;
+    const double step = dd * c;
+    h *= step;
+    if (std::fabs(step - 1.0) < 1e-16) break;
+  }
+  return h;
+}
+
+// Regularised incomplete beta I_x(a, b).
+double ibeta(double a, double b, double x) {
+  if (x <= 0.0) return 0.0;
+  if (x >= 1.0) return 1.0;
+  const double lfront = std::lgamma(a + b) - std::lgamma(a) - std::lgamma(b) + a * std::log(x) +
+                         b * std::log1p(-x);
+  const double front = std::exp(lfront);
+  if (x < (a + 1.0) / (a + b + 2.0)) return front * beta_cf(a, b, x) / a;
+  return 1.0 - front * beta_cf(b, a, 1.0 - x) / b;
+}
+
+struct CoordLaw {
+  int d;
+  double a;       // (d-1)/2
+  double kd;      // normaliser K_d
+  explicit CoordLaw(int d_) : d(d_), a(0.5 * (d_ - 1)) {
+    kd = std::exp(std::lgamma(0.5 * d_) - std::lgamma(0.5 * (d_ - 1))) / std::sqrt(M_PI);
+  }
+  double upper_tail(double x) const {  // P(X > x)
+    if (x <= -1.0) return 1.0;
+    if (x >= 1.0) return 0.0;
+    return ibeta(a, a, 0.5 * (1.0 - x));
+  }
+  double mass(double lo, double hi) const { return upper_tail(lo) - upper_tail(hi); }
+  double moment(double lo, double hi) const {
+    const double p = 0.5 * (d - 1);
+    auto g = [p](double x) { const double t = 1.0 - x * x; return t <= 0.0 ? 0.0 : std::pow(t, p); };
+    return kd / (d - 1) * (g(lo) - g(hi));
+  }
+};
+
+void codebook_build(int d, int bits, double* cen, double* bnd) {
+  const CoordLaw law(d);
+  const int L = 1 << bits;
+  std::vector<double> c(L), t(L - 1), e(L + 1);
+  // Start: conditional means of L equal-mass cells (quantiles by bisection).
+  for (int j = 1; j < L; ++j) {
+    const double target = 1.0 - static_cast<double>(j) / L;  // upper-tail mass above the edge
+    double lo = -1.0, hi = 1.0;
+    for (int it = 0; it < 200; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      if (law.upper_tail(mid) > target) lo = mid; else hi = mid;
+    }
+    e[j] = 0.5 * (lo + hi);
+  }
+  e[0] = -1.0;
+  e[L] = 1.0;
+  for (int j = 0; j < L; ++j) c[j] = law.moment(e[j], e[j + 1]) / law.mass(e[j], e[j + 1]);
+  double best = INFINITY;
+  int stall = 0;
+  for (int it = 0; it < 200000; ++it) {
+    for (int j = 1; j < L; ++j) e[j] = 0.5 * (c[j - 1] + c[j]);
+    std::vector<double> cn(L);
+    for (int j = 0; j < L; ++j) cn[j] = law.moment(e[j], e[j + 1]) / law.mass(e[j], e[j + 1]);
+    double step = 0.0;
+    for (int j = 0; j < L; ++j) {
+      const double sym = 0.5 * (cn[j] - cn[L - 1 - j]);  // the law is symmetric about 0
+      step = std::fmax(step, std::fabs(sym - c[j]));
+      c[j] = sym;
+    }
+    if (step < 1e-15) break;
+    if (step < best) { best = step; stall = 0; }
+    else if (++stall > 50 && step < 1e-13) break;
+  }
+  for (int j = 0; j < L - 1; ++j) t[j] = 0.5 * (c[j] + c[j + 1]);
+  if (L % 2 == 0) t[L / 2 - 1] = 0.0;
+  std::memcpy(cen, c.data(), sizeof(double) * L);
+  std::memcpy(bnd, t.data(), sizeof(double) * (L - 1));
+}
+
+// ---------------------------------------------------------------------------
+// IEEE binary16 from a double, round to nearest even, in one rounding step.
+uint16_t to_half(double v) {
+  const uint16_t sign = std::signbit(v) ? 0x8000u : 0u;
+  const double a = std::fabs(v);
+  if (std::isnan(v)) return 0x7E00u;
+  if (a >= 65520.0) return sign | 0x7C00u;
+  if (a < 0x1.0p-14) {  // subnormal range: multiples of 2^-24
+    const double m = std::nearbyint(a * 0x1.0p24);
+    return sign | static_cast<uint16_t>(m);  // m == 1024 encodes the smallest normal
+  }
+  int e;
+  std::frexp(a, &e);  // a = f 2^e, f in [0.5, 1)
+  int ex = e - 1;     // a = 1.m 2^ex
+  double m = std::nearbyint(std::ldexp(a, 10 - ex));  // in [1024, 2048]
+  if (m >= 2048.0) { m = 1024.0; ++ex; }
+  if (ex > 15) return sign | 0x7C00u;
+  return sign | static_cast<uint16_t>(((ex + 15) << 10) | (static_cast<int>(m) - 1024));
+}
+
+double from_half(uint16_t h) {
+  const int ex = (h >> 10) & 0x1F, man = h & 0x3FF;
+  double v = ex == 0 ? std::ldexp(man, -24) : std::ldexp(1024 + man, ex - 25);
+  return (h & 0x8000u) ? -v : v;
+}
+
+// ---------------------------------------------------------------------------
+tq_status check_spec(const tq_spec* s, tq::Spec* out) {
+  if (!s) return fail(TQ_E_ARG, "spec is NULL");
+  if (s->d != TQ_DIM) return fail(TQ_E_UNSUPPORTED, "d must be 128");
+  auto okb = [](int b) { return b >= 2 && b <= 4; };
+  if (!okb(s->bits_lo)) return fail(TQ_E_UNSUPPORTED, "bits_lo must be 2, 3 or 4");
+  if (s->split != 64 && s->split != 128) return fail(TQ_E_UNSUPPORTED, "split must be 64 or 128");
+  const int bhi = s->split == 128 ? s->bits_lo : s->bits_hi;
+  if (!okb(bhi)) return fail(TQ_E_UNSUPPORTED, "bits_hi must be 2, 3 or 4");
+  const int bl = s->bits_lo;
+  const bool combo_ok = (bl == bhi) || (bl == 4 && bhi == 3) || (bl == 3 && bhi == 2);
+  if (!combo_ok) return fail(TQ_E_UNSUPPORTED, "mixed widths supported: 4/3 and 3/2 (split 64)");
+  if (s->layout != TQ_LAYOUT_RECORD && s->layout != TQ_LAYOUT_TILED)
+    return fail(TQ_E_ARG, "layout must be TQ_LAYOUT_RECORD or TQ_LAYOUT_TILED");
+  if (s->qjl_m != 0 && s->qjl_m != TQ_QJL_M) return fail(TQ_E_UNSUPPORTED, "qjl_m must be 0 or 128");
+  if (s->qjl_m && s->layout != TQ_LAYOUT_RECORD)
+    return fail(TQ_E_UNSUPPORTED, "the QJL sketch needs the record layout");
+  if (out) {
+    out->bits_lo = bl;
+    out->bits_hi = bhi;
+    out->qjl_m = s->qjl_m;
+    out->layout = s->layout;
+    out->code_bytes = 8 * (bl + bhi);
+  }
+  return TQ_OK;
+}
+
+tq_status check_tables(const void* tables, const tq::Spec& sp, const char* what) {
+  if (!tables) return fail(TQ_E_ARG, std::string(what) + " tables pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(tables) % 256)
+    return fail(TQ_E_ARG, std::string(what) + " tables must be 256-byte aligned");
+  (void)sp;
+  return TQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+tq_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return TQ_OK;
+  return fail(TQ_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tq_format_version(void) { return TQ_FORMAT_VERSION; }
+
+const char* tq_last_error(void) { return g_err.c_str(); }
+
+tq_status tq_codebook_build(int32_t d, int32_t bits, double* centroids, double* boundaries) {
+  if (d < 3 || d > 65536) return fail(TQ_E_ARG, "d must be in [3, 65536]");
+  if (bits < 1 || bits > 8) return fail(TQ_E_ARG, "bits must be in [1, 8]");
+  if (!centroids || !boundaries) return fail(TQ_E_ARG, "output pointer is NULL");
+  try {
+    codebook_build(d, bits, centroids, boundaries);
+  } catch (const std::bad_alloc&) {
+    return fail(TQ_E_ARG, "out of host memory");
+  }
+  return TQ_OK;
+}
+
+tq_status tq_rotation_build(int32_t d, uint64_t seed, double* pi) {
+  if (d < 1 || d > 1024) return fail(TQ_E_ARG, "d must be in [1, 1024]");
+  if (!pi) return fail(TQ_E_ARG, "output pointer is NULL");
+  try {
+    rotation_build(d, seed, pi);
+  } catch (const std::bad_alloc&) {
+    return fail(TQ_E_ARG, "out of host memory");
+  }
+  return TQ_OK;
+}
+
+tq_status tq_sketch_build(int32_t m, int32_t d, uint64_t seed, double* s) {
+  if (m < 1 || m > 1024 || d < 1 || d > 1024) return fail(TQ_E_ARG, "m and d must be in [1, 1024]");
+  if (!s) return fail(TQ_E_ARG, "output pointer is NULL");
+  gaussian_fill(seed, s, static_cast<size_t>(m) * d);
+  return TQ_OK;
+}
+
+size_t tq_tables_bytes(void) { return sizeof(tq::Tables); }
+
+tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
+  tq::Spec sp;
+  if (tq_status st = check_spec(spec, &sp); st != TQ_OK) return st;
+  if (!host_buf) return fail(TQ_E_ARG, "host_buf is NULL");
+  if (bytes < sizeof(tq::Tables)) return fail(TQ_E_ARG, "host_buf smaller than tq_tables_bytes()");
+  if (!aligned(host_buf, 16)) return fail(TQ_E_ARG, "host_buf must be 16-byte aligned");
+  try {
+    std::vector<unsigned char> raw(sizeof(tq::Tables) + 256, 0);
+    auto* t = reinterpret_cast<tq::Tables*>((reinterpret_cast<uintptr_t>(raw.data()) + 255) &
+                                            ~static_cast<uintptr_t>(255));
+    t->magic = tq::TABLES_MAGIC;
+    t->version = TQ_FORMAT_VERSION;
+    t->bits[0] = sp.bits_lo;
+    t->bits[1] = sp.bits_hi;
+    t->split = sp.bits_lo == sp.bits_hi ? 128u : 64u;
+    t->qjl_m = sp.qjl_m;
+    t->layout = sp.layout;
+    for (int h = 0; h < 2; ++h) {
+      const int b = t->bits[h], L = 1 << b;
+      std::vector<double> c(L), bd(L - 1);
+      codebook_build(tq::D, b, c.data(), bd.data());
+      for (int j = 0; j < 16; ++j) {
+        t->bnd[h][j] = j < L - 1 ? static_cast<float>(bd[j]) : INFINITY;
+        t->cen[h][j] = j < L ? static_cast<float>(c[j]) : 0.0f;
+        t->cen16[h][j] = j < L ? to_half(c[j]) : 0;
+      }
+    }
+    std::vector<double> m(tq::D * tq::D);
+    rotation_build(tq::D, spec->rot_seed, m.data());
+    for (int i = 0; i < tq::D * tq::D; ++i) {
+      t->pi[i] = static_cast<float>(m[i]);
+      const double v = m[i] * tq::PI_SCALE;
+      const uint16_t hi = to_half(v);
+      t->pi_hi[i] = hi;
+      t->pi_lo[i] = to_half(v - from_half(hi));
+    }
+    if (sp.qjl_m) {
+      gaussian_fill(spec->qjl_seed, m.data(), static_cast<size_t>(tq::QJL_M) * tq::D);
+      for (int i = 0; i < tq::QJL_M * tq::D; ++i) {
+        t->s[i] = static_cast<float>(m[i]);
+        const uint16_t hi = to_half(m[i]);
+        t->s_hi[i] = hi;
+        t->s_lo[i] = to_half(m[i] - from_half(hi));
+      }
+    }
+    std::memcpy(host_buf, t, sizeof(tq::Tables));
+  } catch (const std::bad_alloc&) {
+    return fail(TQ_E_ARG, "out of host memory");
+  }
+  return TQ_OK;
+}
+
+size_t tq_code_bytes(const tq_spec* spec) {
+  tq::Spec sp;
+  if (check_spec(spec, &sp) != TQ_OK) return 0;
+  return static_cast<size_t>(sp.code_bytes);
+}
+
+size_t tq_cache_code_bytes(const tq_spec* spec, int64_t cap) {
+  tq::Spec sp;
+  if (check_spec(spec, &sp) != TQ_OK || cap < 0) return 0;
+  int64_t pos = cap;
+  if (sp.layout == TQ_LAYOUT_TILED) pos = (cap + tq::TILE - 1) / tq::TILE * tq::TILE;
+  return static_cast<size_t>(pos) * sp.code_bytes;
+}
+
+tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
+                         int64_t n_streams, int64_t n_tok, int64_t x_stream_stride,
+                         int64_t x_row_stride, int64_t tok0, const tq_cache* cache, void* stream) {
+  tq::Spec sp;
+  if (tq_status st = check_spec(spec, &sp); st != TQ_OK) return st;
+  if (tq_status st = check_tables(tables, sp, "quantize"); st != TQ_OK) return st;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_E_ARG, "dtype must be TQ_F32 or TQ_BF16");
+  if (!cache) return fail(TQ_E_ARG, "cache is NULL");
+  if (n_streams < 0 || n_tok < 0 || tok0 < 0) return fail(TQ_E_ARG, "negative size or offset");
+  if (cache->cap < 0 || tok0 + n_tok > cache->cap) return fail(TQ_E_ARG, "tok0 + n_tok exceeds cache cap");
+  if (sp.layout == TQ_LAYOUT_TILED && cache->cap % tq::TILE)
+    return fail(TQ_E_ARG, "tiled cache cap must be a multiple of 32");
+  if (n_streams == 0 || n_tok == 0) return TQ_OK;
+  const size_t es = dtype == TQ_F32 ? 4 : 2;
+  if (!x || !cache->codes || !cache->norms) return fail(TQ_E_ARG, "x, codes and norms must be non-NULL");
+  if (!aligned(x, 16)) return fail(TQ_E_ARG, "x must be 16-byte aligned");
+  if ((x_row_stride * static_cast<int64_t>(es)) % 16 || (x_stream_stride * static_cast<int64_t>(es)) % 16)
+    return fail(TQ_E_ARG, "x strides must be multiples of 16 bytes");
+  if (x_row_stride < tq::D && n_tok > 1) return fail(TQ_E_ARG, "x_row_stride smaller than d");
+  if (!aligned(cache->codes, 16) || !aligned(cache->norms, 4))
+    return fail(TQ_E_ARG, "codes must be 16-byte and norms 4-byte aligned");
+  if (sp.qjl_m) {
+    if (!cache->qjl_signs || !cache->qjl_rnorms) return fail(TQ_E_ARG, "QJL arrays must be non-NULL");
+    if (!aligned(cache->qjl_signs, 16) || !aligned(cache->qjl_rnorms, 4))
+      return fail(TQ_E_ARG, "qjl_signs must be 16-byte and qjl_rnorms 4-byte aligned");
+  }
+  const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x,
+                                           n_streams, n_tok, x_stream_stride, x_row_stride, tok0,
+                                           *cache, static_cast<hipStream_t>(stream));
+  return hip_status(e, "tq_quantize_kv launch");
+}
+
+size_t tq_attend_workspace_bytes(const tq_attn* attn) {
+  if (!attn || attn->batch < 0 || attn->hq <= 0 || attn->hkv <= 0 || attn->max_len < 0) return 0;
+  return tq::plan_attend(*attn).ws_bytes;
+}
+
+tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cache* kc,
+                           const tq_spec* vs, const void* vtables, const tq_cache* vc,
+                           const tq_attn* attn, const float* q, const uint16_t* sink_k,
+                           const uint16_t* sink_v, const int32_t* seq_lens, float* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  tq::Spec ksp, vsp;
+  if (tq_status st = check_spec(ks, &ksp); st != TQ_OK) return st;
+  if (tq_status st = check_spec(vs, &vsp); st != TQ_OK) return st;
+  if (ksp.layout != TQ_LAYOUT_RECORD) return fail(TQ_E_UNSUPPORTED, "keys must use the record layout");
+  if (vsp.layout != TQ_LAYOUT_TILED) return fail(TQ_E_UNSUPPORTED, "values must use the tiled layout");
+  if (vsp.qjl_m) return fail(TQ_E_UNSUPPORTED, "values carry no QJL sketch");
+  if (tq_status st = check_tables(ktables, ksp, "key"); st != TQ_OK) return st;
+  if (tq_status st = check_tables(vtables, vsp, "value"); st != TQ_OK) return st;
+  if (!attn || !kc || !vc) return fail(TQ_E_ARG, "attn, kc and vc must be non-NULL");
+  const tq_attn& a = *attn;
+  if (a.batch < 0 || a.hq <= 0 || a.hkv <= 0) return fail(TQ_E_ARG, "batch, hq, hkv out of range");
+  if (a.hq % a.hkv) return fail(TQ_E_ARG, "hq must be a multiple of hkv");
+  if (a.hq / a.hkv > 16) return fail(TQ_E_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (a.sink < 0 || a.max_len < 0) return fail(TQ_E_ARG, "negative sink or max_len");
+  if (!(a.v_skip >= 0.0f) || !(a.v_skip < 1.0f)) return fail(TQ_E_ARG, "v_skip must be in [0, 1)");
+  if (!std::isfinite(a.scale)) return fail(TQ_E_ARG, "scale must be finite");
+  if (a.batch == 0) return TQ_OK;
+  if (vc->cap % tq::TILE) return fail(TQ_E_ARG, "value cache cap must be a multiple of 32");
+  if (a.max_len - a.sink > std::min(kc->cap, vc->cap))
+    return fail(TQ_E_ARG, "max_len - sink exceeds the cache capacity");
+  if (!q || !out || !seq_lens) return fail(TQ_E_ARG, "q, out and seq_lens must be non-NULL");
+  if (!kc->codes || !kc->norms || !vc->codes || !vc->norms) return fail(TQ_E_ARG, "cache arrays are NULL");
+  if (ksp.qjl_m && (!kc->qjl_signs || !kc->qjl_rnorms)) return fail(TQ_E_ARG, "key QJL arrays are NULL");
+  if (a.sink > 0 && (!sink_k || !sink_v)) return fail(TQ_E_ARG, "sink_k and sink_v are required when sink > 0");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(kc->codes, 16) || !aligned(vc->codes, 16) ||
+      !aligned(kc->norms, 16) || !aligned(vc->norms, 16) || !aligned(seq_lens, 4))
+    return fail(TQ_E_ARG, "q, out, codes and norms must be 16-byte aligned");
+  if (a.sink > 0 && (!aligned(sink_k, 16) || !aligned(sink_v, 16)))
+    return fail(TQ_E_ARG, "sink arrays must be 16-byte aligned");
+  if (ksp.qjl_m && (!aligned(kc->qjl_signs, 16) || !aligned(kc->qjl_rnorms, 16)))
+    return fail(TQ_E_ARG, "QJL arrays must be 16-byte aligned");
+  const tq::AttendPlan plan = tq::plan_attend(a);
+  if (!workspace || ws_bytes < plan.ws_bytes) return fail(TQ_E_WORKSPACE, "workspace too small");
+  if (!aligned(workspace, 16)) return fail(TQ_E_ARG, "workspace must be 16-byte aligned");
+  const hipError_t e = tq::launch_attend(ksp, static_cast<const tq::Tables*>(ktables), *kc, vsp,
+                                         static_cast<const tq::Tables*>(vtables), *vc, a, plan, q,
+                                         sink_k, sink_v, seq_lens, out, workspace,
+                                         static_cast<hipStream_t>(stream));
+  return hip_status(e, "tq_attend_decode launch");
+}
+
+}  // extern "C"

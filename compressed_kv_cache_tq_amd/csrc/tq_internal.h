@@ -1,0 +1,81 @@
+// Internal declarations shared by the host half (host.cpp) and the HIP
+// kernels (quantize.hip, attend.hip) of libtq.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int D = TQ_DIM;
+constexpr int TILE = TQ_TILE_TOKENS;
+constexpr int QJL_M = TQ_QJL_M;
+constexpr uint32_t TABLES_MAGIC = 0x31515454u;  // "TTQ1"
+
+// Device tables of one tq_spec, built on the host by tq_tables_build.
+//
+// Half index 0 is the codebook of rotated coordinates [0, split), 1 of
+// [split, d) (both the same codebook for a uniform width).  Boundaries are
+// ascending and padded with +inf; centroids ascending, padded with 0.
+//
+// The rotation is stored row-major (y = pi x) in fp32 and, for the MFMA
+// contraction, as an fp16 pair pi_hi + pi_lo = 256 * pi (hi = fp16 of
+// 256*pi, lo = fp16 of the remainder), which keeps about 22 significant bits.
+// The sketch S (qjl_m x d, row-major) is stored the same way without the 256
+// factor.  All arrays start on 256-byte boundaries.
+struct alignas(256) Tables {
+  uint32_t magic;
+  uint32_t version;
+  uint32_t bits[2];
+  uint32_t split;
+  uint32_t qjl_m;
+  uint32_t layout;
+  uint32_t pad0;
+  float bnd[2][16];
+  float cen[2][16];
+  uint16_t cen16[2][16];
+  uint8_t pad1[512 - 32 - 128 - 128 - 64];
+  float pi[D * D];
+  uint16_t pi_hi[D * D];
+  uint16_t pi_lo[D * D];
+  float s[D * D];
+  uint16_t s_hi[D * D];
+  uint16_t s_lo[D * D];
+};
+
+constexpr float PI_SCALE = 256.0f;
+
+// Validated, normalised view of a tq_spec.
+struct Spec {
+  int bits_lo;
+  int bits_hi;   // == bits_lo for a uniform width
+  int qjl_m;
+  int layout;
+  int code_bytes;  // per token
+};
+
+hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x,
+                           int64_t n_streams, int64_t n_tok, int64_t x_stream_stride,
+                           int64_t x_row_stride, int64_t tok0, const tq_cache& cache,
+                           hipStream_t stream);
+
+struct AttendPlan {
+  int n_split;       // splits of the compressed token range per (b, kv head)
+  int64_t chunk;     // tokens per split (multiple of TILE)
+  size_t ws_bytes;   // workspace needed
+};
+
+AttendPlan plan_attend(const tq_attn& a);
+
+hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
+                         const Spec& vs, const Tables* vtab, const tq_cache& vc,
+                         const tq_attn& a, const AttendPlan& plan, const float* q,
+                         const uint16_t* sink_k, const uint16_t* sink_v,
+                         const int32_t* seq_lens, float* out, void* workspace,
+                         hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,278 @@
+"""Thin ctypes binding of libtq.so (include/tq.h).
+
+Argument marshalling only: every step of quantization and decode attention
+runs in the library's HIP kernels; PyTorch provides device memory and the
+current stream.  The functions keep the C names without the ``tq_`` prefix.
+Loading fails loudly when libtq.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+D = 128
+TILE = 32
+QJL_M = 128
+F32, BF16 = 0, 1
+LAYOUT_RECORD, LAYOUT_TILED = 0, 1
+STATUS = {0: "TQ_OK", -1: "TQ_E_ARG", -2: "TQ_E_UNSUPPORTED", -3: "TQ_E_WORKSPACE", -4: "TQ_E_HIP"}
+
+EXPORTS = [
+    "tq_format_version", "tq_last_error", "tq_codebook_build", "tq_rotation_build", "tq_sketch_build",
+    "tq_tables_bytes", "tq_tables_build", "tq_code_bytes", "tq_cache_code_bytes", "tq_quantize_kv",
+    "tq_attend_workspace_bytes", "tq_attend_decode",
+]
+
+
+class TqSpec(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("bits_lo", ctypes.c_int32), ("bits_hi", ctypes.c_int32),
+                ("split", ctypes.c_int32), ("qjl_m", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("rot_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64)]
+
+
+class TqCache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("qjl_signs", ctypes.c_void_p),
+                ("qjl_rnorms", ctypes.c_void_p), ("cap", ctypes.c_int64)]
+
+
+class TqAttn(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("sink", ctypes.c_int32), ("scale", ctypes.c_float), ("v_skip", ctypes.c_float),
+                ("max_len", ctypes.c_int64)]
+
+
+class TqError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtq.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m compressed_kv_cache_tq_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+    sig = {
+        "tq_format_version": (I32, []),
+        "tq_last_error": (ctypes.c_char_p, []),
+        "tq_codebook_build": (I32, [I32, I32, P, P]),
+        "tq_rotation_build": (I32, [I32, U64, P]),
+        "tq_sketch_build": (I32, [I32, I32, U64, P]),
+        "tq_tables_bytes": (SZ, []),
+        "tq_tables_build": (I32, [ctypes.POINTER(TqSpec), P, SZ]),
+        "tq_code_bytes": (SZ, [ctypes.POINTER(TqSpec)]),
+        "tq_cache_code_bytes": (SZ, [ctypes.POINTER(TqSpec), I64]),
+        "tq_quantize_kv": (I32, [ctypes.POINTER(TqSpec), P, I32, P, I64, I64, I64, I64, I64,
+                                 ctypes.POINTER(TqCache), P]),
+        "tq_attend_workspace_bytes": (SZ, [ctypes.POINTER(TqAttn)]),
+        "tq_attend_decode": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache), ctypes.POINTER(TqSpec), P,
+                                   ctypes.POINTER(TqCache), ctypes.POINTER(TqAttn), P, P, P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(st: int, where: str) -> None:
+    if st != 0:
+        raise TqError(st, where, lib().tq_last_error().decode())
+
+
+def last_error() -> str:
+    return lib().tq_last_error().decode()
+
+
+def format_version() -> int:
+    return lib().tq_format_version()
+
+
+@dataclass(frozen=True)
+class Spec:
+    """Quantizer of one tensor (mirrors tq_spec)."""
+    bits_lo: int
+    bits_hi: int | None = None
+    split: int = D
+    qjl_m: int = 0
+    layout: int = LAYOUT_RECORD
+    rot_seed: int = 0
+    qjl_seed: int = 1
+
+    def c(self) -> TqSpec:
+        return TqSpec(D, self.bits_lo, self.bits_lo if self.bits_hi is None else self.bits_hi, self.split,
+                      self.qjl_m, self.layout, self.rot_seed, self.qjl_seed)
+
+    @property
+    def widths(self) -> np.ndarray:
+        w = np.full(D, self.bits_lo if self.split == D or self.bits_hi is None else self.bits_hi, dtype=np.int64)
+        w[: self.split] = self.bits_lo
+        return w
+
+
+# ---- host-only builders ------------------------------------------------------
+
+def codebook_build(d: int, bits: int):
+    c = np.zeros(1 << bits)
+    t = np.zeros((1 << bits) - 1)
+    _check(lib().tq_codebook_build(d, bits, c.ctypes.data, t.ctypes.data), "tq_codebook_build")
+    return c, t
+
+
+def rotation_build(d: int, seed: int) -> np.ndarray:
+    m = np.zeros((d, d))
+    _check(lib().tq_rotation_build(d, seed, m.ctypes.data), "tq_rotation_build")
+    return m
+
+
+def sketch_build(m: int, d: int, seed: int) -> np.ndarray:
+    s = np.zeros((m, d))
+    _check(lib().tq_sketch_build(m, d, seed, s.ctypes.data), "tq_sketch_build")
+    return s
+
+
+def tables_bytes() -> int:
+    return int(lib().tq_tables_bytes())
+
+
+def tables_build(spec: Spec) -> np.ndarray:
+    """Host tables (uint8) for ``spec``."""
+    n = tables_bytes()
+    raw = np.zeros(n + 256, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 256
+    buf = raw[off: off + n]
+    cs = spec.c()
+    _check(lib().tq_tables_build(ctypes.byref(cs), buf.ctypes.data, n), "tq_tables_build")
+    return buf.copy()
+
+
+def code_bytes(spec: Spec) -> int:
+    cs = spec.c()
+    return int(lib().tq_code_bytes(ctypes.byref(cs)))
+
+
+def cache_code_bytes(spec: Spec, cap: int) -> int:
+    cs = spec.c()
+    return int(lib().tq_cache_code_bytes(ctypes.byref(cs), cap))
+
+
+def attend_workspace_bytes(batch: int, hq: int, hkv: int, sink: int, max_len: int) -> int:
+    a = TqAttn(batch, hq, hkv, sink, 0.0, 0.0, max_len)
+    return int(lib().tq_attend_workspace_bytes(ctypes.byref(a)))
+
+
+# ---- device-side wrappers (torch for memory and stream) ----------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def device_tables(spec: Spec, device="cuda"):
+    """Device copy of the tables (256-byte aligned torch uint8 tensor)."""
+    torch = _torch()
+    host = torch.from_numpy(tables_build(spec))
+    dev = torch.empty(host.numel() + 256, dtype=torch.uint8, device=device)
+    off = (-dev.data_ptr()) % 256
+    view = dev[off: off + host.numel()]
+    view.copy_(host)
+    return view
+
+
+@dataclass
+class Cache:
+    """Packed cache of one tensor for n_streams streams of cap positions (torch tensors)."""
+    spec: Spec
+    cap: int
+    codes: object
+    norms: object
+    qjl_signs: object = None
+    qjl_rnorms: object = None
+
+    def c(self) -> TqCache:
+        return TqCache(_ptr(self.codes), _ptr(self.norms), _ptr(self.qjl_signs), _ptr(self.qjl_rnorms), self.cap)
+
+    def streams(self, start: int, count: int) -> "Cache":
+        """View of streams [start, start + count)."""
+        nb = cache_code_bytes(self.spec, self.cap)
+        cut = lambda t, per: None if t is None else t[start * per: (start + count) * per]
+        m8 = self.spec.qjl_m // 8
+        return Cache(self.spec, self.cap, cut(self.codes, nb), cut(self.norms, self.cap),
+                     cut(self.qjl_signs, self.cap * m8), cut(self.qjl_rnorms, self.cap))
+
+
+def alloc_cache(spec: Spec, n_streams: int, cap: int, device="cuda", fill: int | None = None) -> Cache:
+    torch = _torch()
+    if spec.layout == LAYOUT_TILED:
+        cap = -(-cap // TILE) * TILE
+    nb = cache_code_bytes(spec, cap)
+    codes = torch.empty(max(n_streams * nb, 16), dtype=torch.uint8, device=device)
+    if fill is not None:
+        codes.fill_(fill)
+    norms = torch.zeros(max(n_streams * cap, 4), dtype=torch.float32, device=device)
+    signs = rn = None
+    if spec.qjl_m:
+        signs = torch.zeros(max(n_streams * cap * spec.qjl_m // 8, 16), dtype=torch.uint8, device=device)
+        rn = torch.zeros(max(n_streams * cap, 4), dtype=torch.float32, device=device)
+    return Cache(spec, cap, codes, norms, signs, rn)
+
+
+def quantize_kv(spec: Spec, tables, x, cache: Cache, tok0: int = 0, n_streams: int | None = None,
+                n_tok: int | None = None, stream: int | None = None) -> None:
+    """Quantize x ([n_streams, n_tok, d] view, float32 or bfloat16, rows 16-byte aligned)."""
+    torch = _torch()
+    if x.dtype == torch.float32:
+        dt = F32
+    elif x.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    if x.dim() == 2:
+        x = x.unsqueeze(0)
+    if x.dim() != 3 or x.shape[-1] != D or x.stride(-1) != 1:
+        raise ValueError("x must be [n_streams, n_tok, 128] with contiguous rows")
+    ns = x.shape[0] if n_streams is None else n_streams
+    nt = x.shape[1] if n_tok is None else n_tok
+    cs, cc = spec.c(), cache.c()
+    st = _stream(x.device) if stream is None else stream
+    _check(lib().tq_quantize_kv(ctypes.byref(cs), tables.data_ptr(), dt, x.data_ptr(), ns, nt, x.stride(0),
+                                x.stride(1), tok0, ctypes.byref(cc), st), "tq_quantize_kv")
+
+
+def attend_decode(kspec: Spec, ktables, kcache: Cache, vspec: Spec, vtables, vcache: Cache, q, seq_lens, out,
+                  workspace, *, hkv: int, sink: int = 0, sink_k=None, sink_v=None, scale: float | None = None,
+                  v_skip: float = 0.0, max_len: int | None = None, stream: int | None = None) -> None:
+    """One decode step: q [B, Hq, d] fp32, seq_lens int32 [B] (device), out [B, Hq, d] fp32."""
+    B, Hq, _ = q.shape
+    if max_len is None:
+        max_len = sink + min(kcache.cap, vcache.cap)
+    a = TqAttn(B, Hq, hkv, sink, (1.0 / np.sqrt(D)) if scale is None else scale, v_skip, max_len)
+    ks, vs, kc, vc = kspec.c(), vspec.c(), kcache.c(), vcache.c()
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().tq_attend_decode(ctypes.byref(ks), ktables.data_ptr(), ctypes.byref(kc), ctypes.byref(vs),
+                                  vtables.data_ptr(), ctypes.byref(vc), ctypes.byref(a), q.data_ptr(),
+                                  _ptr(sink_k), _ptr(sink_v), seq_lens.data_ptr(), out.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), st),
+           "tq_attend_decode")

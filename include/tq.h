@@ -1,0 +1,209 @@
+/*
+ * tq.h - TurboQuant packed KV cache for AMD MI355X (gfx950): C ABI of libtq.so.
+ *
+ * The method (noze.it, "TurboQuant-MLX: quantizzare pesi e KV cache per LLM
+ * open-weight su Mac", section "Il metodo TurboQuant, in breve"): every key or
+ * value head vector keeps its norm, is rotated by a seeded random orthogonal
+ * matrix, and each rotated coordinate is quantized on its own with a b-bit
+ * Lloyd-Max codebook built for the post-rotation coordinate law (section
+ * "Cosa aggiunge turboquant-mlx").  An optional second stage stores a 1-bit
+ * quantized Johnson-Lindenstrauss sketch of the residual plus the residual
+ * norm, which makes the inner-product estimate unbiased.  It is online and
+ * data-oblivious: no calibration input exists in this interface.
+ *
+ * Decode attention reads the packed cache directly: the query is rotated
+ * once, scores come from codebook lookups (plus the sketch correction), the
+ * values are accumulated in the rotated domain and one inverse rotation is
+ * applied per query head.  The first `sink` tokens of every sequence may be
+ * kept raw in bf16 (GitHub issue "Greetings from TurboQuant-MLX & Some
+ * Insights to Share!", item 1), and value tokens whose attention weight is
+ * below a threshold may be dropped (same issue, item 3).
+ *
+ * Conventions for every entry point
+ *  - Ownership: the caller owns every host and device buffer, including the
+ *    device copy of the tables and the attention workspace.  The library
+ *    allocates no device memory and keeps no state except a thread-local
+ *    error string.
+ *  - Errors: arguments are validated on the host before any launch.  A
+ *    failed check returns a negative tq_status, launches nothing and sets
+ *    tq_last_error().  A failed launch returns TQ_E_HIP with the HIP error
+ *    text.
+ *  - Data: kernels never fail on data.  Non-finite inputs give unspecified
+ *    codes and outputs; vectors whose squared norm overflows fp32 likewise.
+ *  - Streams: `stream` is a hipStream_t (NULL = default stream).  Every
+ *    device call is asynchronous on that stream; the library never
+ *    synchronizes.
+ *  - Device pointers must be 16-byte aligned unless stated otherwise.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_FORMAT_VERSION 1   /* bit layouts described at tq_cache below */
+#define TQ_DIM 128            /* head dimension d supported by the kernels */
+#define TQ_TILE_TOKENS 32     /* tokens per tile of the tiled layout */
+#define TQ_QJL_M 128          /* rows m of the QJL sketch when enabled */
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_E_ARG = -1,          /* invalid argument (shape, pointer, alignment, range) */
+  TQ_E_UNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+  TQ_E_WORKSPACE = -3,    /* workspace smaller than tq_attend_workspace_bytes */
+  TQ_E_HIP = -4           /* a HIP launch failed; see tq_last_error() */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+typedef enum {
+  TQ_LAYOUT_RECORD = 0,   /* one packed record per token (keys) */
+  TQ_LAYOUT_TILED = 1     /* 32-token tiles, coordinate-major sub-blocks (values) */
+} tq_layout;
+
+/* Quantizer of one tensor (the keys or the values of a cache).
+ * Rotated coordinates [0, split) use bits_lo bits, [split, d) use bits_hi
+ * (noze.it page, section "Il metodo TurboQuant, in breve": 3.5 and 2.5 bits
+ * per channel; 3.5 bits = split 64 with 4 and 3 bits).  split == d means a
+ * uniform width and bits_hi is then ignored. */
+typedef struct {
+  int32_t d;          /* must be TQ_DIM */
+  int32_t bits_lo;    /* 2, 3 or 4 */
+  int32_t bits_hi;    /* 2, 3 or 4 (ignored when split == d) */
+  int32_t split;      /* 64 or 128 */
+  int32_t qjl_m;      /* 0 (no sketch) or TQ_QJL_M; only with TQ_LAYOUT_RECORD */
+  int32_t layout;     /* tq_layout */
+  uint64_t rot_seed;  /* seed of the rotation (SplitMix64 stream) */
+  uint64_t qjl_seed;  /* seed of the sketch matrix S */
+} tq_spec;
+
+/* One tensor of a packed cache, for n_streams = batch * kv_heads streams of
+ * `cap` token positions each (stream s = b * kv_heads + h).
+ *
+ * codes   RECORD: stream s, position p at byte (s*cap + p) * tq_code_bytes(spec).
+ *         The record is a little-endian LSB-first bit stream: coordinate i's
+ *         index occupies stream bits [o_i, o_i + b_i), o_i = sum_{k<i} b_k,
+ *         stream bit j = bit (j mod 8) of byte j/8.
+ *         TILED: stream s at byte s * tq_cache_code_bytes(spec, cap); tile
+ *         T = p / 32 at T * 32 * tq_code_bytes(spec) within the stream.  A
+ *         tile has 4 token groups (tokens 8g..8g+7) x 16 coordinate groups
+ *         (coordinates 8q..8q+7); sub-block (g, q) holds 8 coordinates x 8
+ *         tokens in 8*b_q bytes at g*G + sum_{q'<q} 8*b_q' (G = sum_q 8*b_q),
+ *         and (coordinate 8q+r, token 8g+s) occupies its bits
+ *         [(8r+s)*b_q, (8r+s)*b_q + b_q).  cap must be a multiple of 32.
+ * norms   fp32 [n_streams][cap]: Euclidean norm of the stored input vector.
+ * qjl_signs  [n_streams][cap][qjl_m/8] bytes, bit j set iff (S r)_j >= 0
+ *         (r = rotated unit vector minus its centroids); NULL if qjl_m == 0.
+ * qjl_rnorms fp32 [n_streams][cap]: ||r||; NULL if qjl_m == 0.
+ * Codes/norms are 4-byte aligned at least; codes must be 16-byte aligned. */
+typedef struct {
+  uint8_t* codes;
+  float* norms;
+  uint8_t* qjl_signs;
+  float* qjl_rnorms;
+  int64_t cap;
+} tq_cache;
+
+/* Decode-attention problem.  Query head h reads KV head h / (hq / hkv). */
+typedef struct {
+  int32_t batch;    /* B */
+  int32_t hq;       /* query heads per sequence */
+  int32_t hkv;      /* KV heads per sequence; hq % hkv == 0, hq/hkv <= 16 */
+  int32_t sink;     /* leading tokens kept raw bf16 (0 = none) */
+  float scale;      /* softmax scale, normally 1/sqrt(d) */
+  float v_skip;     /* drop value tokens with weight below this (0 = off) */
+  int64_t max_len;  /* host-side upper bound of seq_lens (sizes the split grid) */
+} tq_attn;
+
+/* Version of the bit layouts produced and read by this library. */
+int32_t tq_format_version(void);
+
+/* Thread-local text describing the last non-OK status of this thread. */
+const char* tq_last_error(void);
+
+/* Host only.  Lloyd-Max codebook for one coordinate of a uniformly random
+ * unit vector in R^d, whose density is proportional to (1-x^2)^((d-3)/2)
+ * (noze.it page, sections "Il metodo TurboQuant, in breve" and "Cosa
+ * aggiunge turboquant-mlx").  Writes 2^bits centroids ascending and 2^bits-1
+ * boundaries (midpoints of consecutive centroids).  3 <= d <= 65536,
+ * 1 <= bits <= 8.  Deterministic. */
+tq_status tq_codebook_build(int32_t d, int32_t bits, double* centroids, double* boundaries);
+
+/* Host only.  The seeded rotation Pi (d x d, row-major, y = Pi x): the Q
+ * factor of a SplitMix64/Box-Muller Gaussian matrix, with column signs chosen
+ * so that R has a positive diagonal (Haar measure).  1 <= d <= 1024. */
+tq_status tq_rotation_build(int32_t d, uint64_t seed, double* pi);
+
+/* Host only.  The QJL sketch S (m x d, row-major), i.i.d. N(0,1) from the
+ * same generator seeded with `seed`.  1 <= m, d <= 1024. */
+tq_status tq_sketch_build(int32_t m, int32_t d, uint64_t seed, double* s);
+
+/* Size in bytes of the device tables of one tq_spec (same for every spec). */
+size_t tq_tables_bytes(void);
+
+/* Host only.  Fills `host_buf` (tq_tables_bytes() bytes, 16-byte aligned)
+ * with everything the kernels need for `spec`: codebooks, rotation and
+ * sketch in fp32 and as fp16 high/low splits.  The caller copies it to
+ * device memory once and passes that copy as `tables` below. */
+tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes);
+
+/* Bytes of one token's packed codes: d * (average bits) / 8. */
+size_t tq_code_bytes(const tq_spec* spec);
+
+/* Bytes of the code array of one stream holding `cap` positions. */
+size_t tq_cache_code_bytes(const tq_spec* spec, int64_t cap);
+
+/* Quantize n_tok vectors of each of n_streams streams into cache positions
+ * [tok0, tok0 + n_tok) (noze.it page, section "Il metodo TurboQuant, in
+ * breve": norm, random rotation, per-coordinate Lloyd-Max quantization, and
+ * the optional 1-bit sketch of the residual).
+ *   tables  device copy of tq_tables_build(spec)
+ *   dtype   TQ_F32 or TQ_BF16 elements of x
+ *   x       device; vector (s, i) starts at element s*x_stream_stride +
+ *           i*x_row_stride and holds d contiguous elements; 16-byte aligned
+ *           rows
+ *   cache   device arrays (tq_cache); positions outside the written range,
+ *           including the other tokens of partially written tiles, keep
+ *           their previous contents.
+ * Requires tok0 >= 0, tok0 + n_tok <= cache->cap.  n_streams or n_tok may be
+ * 0 (nothing is launched). */
+tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
+                         int64_t n_streams, int64_t n_tok, int64_t x_stream_stride,
+                         int64_t x_row_stride, int64_t tok0, const tq_cache* cache,
+                         void* stream);
+
+/* Workspace bytes tq_attend_decode needs for this problem. */
+size_t tq_attend_workspace_bytes(const tq_attn* attn);
+
+/* One decode step of attention read directly from the packed cache.
+ *   ks/ktables/kc  keys: TQ_LAYOUT_RECORD, optional QJL sketch
+ *   vs/vtables/vc  values: TQ_LAYOUT_TILED, no QJL
+ *   q        device fp32 [batch][hq][d]
+ *   sink_k/sink_v  device bf16 [batch][hkv][sink][d] (NULL iff sink == 0)
+ *   seq_lens device int32 [batch]: tokens of each sequence including the
+ *            sink; compressed token t >= sink lives at cache position t-sink.
+ *            Each value must lie in [0, sink + min(kc->cap, vc->cap)] and
+ *            not exceed max_len.  A sequence of length 0 gives zeros.
+ *   out      device fp32 [batch][hq][d]
+ *   workspace device, >= tq_attend_workspace_bytes(attn) bytes
+ * scores: s_t = scale * n_t * (<Pi q, c[idx_t]> + sqrt(pi/2)/m * gamma_t *
+ * <S Pi q, z_t>) for compressed tokens, scale * <q, k_t> for sink tokens;
+ * out = Pi_V^T sum_t w_t n^V_t c_V[idx^V_t] + sum_sink w_t v_t with w the
+ * softmax over all tokens.  With v_skip > 0 a compressed token's value is
+ * dropped (not renormalised) when exp(s_t - m) < v_skip for the running
+ * maximum m of its split, which implies its final weight is below v_skip. */
+tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cache* kc,
+                           const tq_spec* vs, const void* vtables, const tq_cache* vc,
+                           const tq_attn* attn, const float* q, const uint16_t* sink_k,
+                           const uint16_t* sink_v, const int32_t* seq_lens, float* out,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

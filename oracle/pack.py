@@ -69,11 +69,11 @@ def pack_records(idx: np.ndarray, widths: np.ndarray) -> np.ndarray:
 def unpack_records(rec: np.ndarray, widths: np.ndarray) -> np.ndarray:
     """records [n, nbytes] -> idx [n, d] int64 (record layout)."""
     widths = np.asarray(widths, dtype=np.int64)
-    bits = _bytes_to_bits(rec).astype(np.int64)
+    bits = _bytes_to_bits(rec)
     idx = np.zeros(bits.shape[:-1] + (len(widths),), dtype=np.int64)
     for i, pos in enumerate(_stream_positions(widths)):
         for k, p in enumerate(pos):
-            idx[..., i] |= bits[..., p] << k
+            idx[..., i] |= bits[..., p].astype(np.int64) << k
     return idx
 
 
@@ -150,7 +150,7 @@ def pack_tiled(idx: np.ndarray, widths: np.ndarray, tok0: int = 0,
 def unpack_tiled(buf: np.ndarray, widths: np.ndarray, n_tok: int, tok0: int = 0) -> np.ndarray:
     """Read codes of tokens tok0 .. tok0+n_tok-1 from a tiled buffer -> [n_tok, d]."""
     base, widths = _tile_bit_index(widths)
-    bits = _bytes_to_bits(np.asarray(buf, dtype=np.uint8)).astype(np.int64)
+    bits = _bytes_to_bits(np.asarray(buf, dtype=np.uint8))
     tile_bits = TILE_TOKENS * int(widths.sum())
     pos = tok0 + np.arange(n_tok)
     tile, t = np.divmod(pos, TILE_TOKENS)
@@ -158,6 +158,6 @@ def unpack_tiled(buf: np.ndarray, widths: np.ndarray, n_tok: int, tok0: int = 0)
     idx = np.zeros((n_tok, len(widths)), dtype=np.int64)
     for k in range(int(widths.max())):
         has = widths > k
-        val = bits[np.where(has[None, :], start + k, 0)]
+        val = bits[np.where(has[None, :], start + k, 0)].astype(np.int64)
         idx |= np.where(has[None, :], val, 0) << k
     return idx

@@ -1,0 +1,162 @@
+"""libtq.so on the CPU: it loads, exports every symbol tq.h declares, its host
+builders agree with the oracle, and bad arguments fail before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from compressed_kv_cache_tq_amd import tq
+from oracle import codebook as ocb
+from oracle import rotation as orot
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tq.LIB_PATH), reason="libtq.so not built")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    names = header_functions()
+    assert names == sorted(tq.EXPORTS)
+    lib = tq.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert tq.format_version() == 1
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [3, 128])
+def test_codebook_matches_oracle(d, bits):
+    c, t = tq.codebook_build(d, bits)
+    cb = ocb.lloyd_max(d, bits)
+    assert np.max(np.abs(c - cb.centroids)) <= 1e-12
+    assert np.max(np.abs(t - cb.boundaries)) <= 1e-12
+
+
+@pytest.mark.parametrize("seed", [0, 7, 12345])
+def test_rotation_matches_oracle(seed):
+    pi = tq.rotation_build(128, seed)
+    assert np.max(np.abs(pi - orot.rotation(seed, 128))) <= 1e-12
+
+
+def test_sketch_matches_oracle():
+    s = tq.sketch_build(128, 128, 1)
+    assert np.max(np.abs(s - orot.sketch(1, 128, 128))) <= 1e-13
+
+
+def _tables_view(spec):
+    buf = tq.tables_build(spec)
+    hdr = buf[:32].view(np.uint32)
+    off = 512
+    pi = buf[off: off + 65536].view(np.float32).reshape(128, 128)
+    off += 65536
+    pi_hi = buf[off: off + 32768].view(np.float16).reshape(128, 128)
+    off += 32768
+    pi_lo = buf[off: off + 32768].view(np.float16).reshape(128, 128)
+    off += 32768
+    s = buf[off: off + 65536].view(np.float32).reshape(128, 128)
+    off += 65536
+    s_hi = buf[off: off + 32768].view(np.float16).reshape(128, 128)
+    off += 32768
+    s_lo = buf[off: off + 32768].view(np.float16).reshape(128, 128)
+    bnd = buf[32: 32 + 128].view(np.float32).reshape(2, 16)
+    cen = buf[160: 160 + 128].view(np.float32).reshape(2, 16)
+    cen16 = buf[288: 288 + 64].view(np.float16).reshape(2, 16)
+    return hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16
+
+
+def test_tables_content():
+    spec = tq.Spec(4, 3, split=64, qjl_m=128)
+    hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16 = _tables_view(spec)
+    assert tq.tables_bytes() == 512 + 4 * 65536
+    assert hdr[0] == 0x31515454 and hdr[1] == 1 and hdr[2] == 4 and hdr[3] == 3
+    ref = orot.rotation(0, 128)
+    assert np.array_equal(pi, ref.astype(np.float32))
+    two = pi_hi.astype(np.float64) + pi_lo.astype(np.float64)
+    assert np.max(np.abs(two - 256 * ref)) <= 256 * 2.0 ** -22
+    assert np.array_equal(pi_hi, (256 * ref).astype(np.float16))
+    sref = orot.sketch(1, 128, 128)
+    assert np.array_equal(s, sref.astype(np.float32))
+    assert np.max(np.abs(s_hi.astype(np.float64) + s_lo.astype(np.float64) - sref)) <= np.abs(sref).max() * 2.0 ** -21
+    for h, b in ((0, 4), (1, 3)):
+        cb = ocb.lloyd_max(128, b)
+        L = 1 << b
+        assert np.array_equal(bnd[h, : L - 1], cb.boundaries.astype(np.float32))
+        assert np.all(np.isinf(bnd[h, L - 1:]))
+        assert np.array_equal(cen[h, :L], cb.centroids.astype(np.float32))
+        assert np.array_equal(cen16[h, :L], cb.centroids.astype(np.float16))
+
+
+def test_code_bytes():
+    assert tq.code_bytes(tq.Spec(4)) == 64
+    assert tq.code_bytes(tq.Spec(3)) == 48
+    assert tq.code_bytes(tq.Spec(2)) == 32
+    assert tq.code_bytes(tq.Spec(4, 3, split=64)) == 56
+    assert tq.cache_code_bytes(tq.Spec(3, layout=tq.LAYOUT_TILED), 33) == 64 * 48
+
+
+@pytest.mark.parametrize("bad", [
+    dict(bits_lo=5), dict(bits_lo=1), dict(split=32), dict(qjl_m=64),
+    dict(qjl_m=128, layout=1), dict(bits_lo=2, bits_hi=4, split=64), dict(layout=7),
+])
+def test_bad_specs_rejected(bad):
+    kw = dict(bits_lo=4, bits_hi=None, split=128, qjl_m=0, layout=0)
+    kw.update(bad)
+    spec = tq.Spec(**kw)
+    buf = np.zeros(tq.tables_bytes(), dtype=np.uint8)
+    cs = spec.c()
+    st = tq.lib().tq_tables_build(ctypes.byref(cs), buf.ctypes.data, buf.size)
+    assert st in (-1, -2)
+    assert tq.last_error()
+
+
+def test_quantize_argument_errors_without_launch():
+    L = tq.lib()
+    spec = tq.Spec(4).c()
+    cache = tq.TqCache(0x1000, 0x2000, None, None, 64)
+    fake_tab = ctypes.c_void_p(0x10000)
+    # NULL x
+    assert L.tq_quantize_kv(ctypes.byref(spec), fake_tab, 1, None, 1, 8, 0, 128, 0, ctypes.byref(cache), None) == -1
+    # misaligned x
+    assert L.tq_quantize_kv(ctypes.byref(spec), fake_tab, 1, 0x1002, 1, 8, 0, 128, 0, ctypes.byref(cache), None) == -1
+    # beyond capacity
+    assert L.tq_quantize_kv(ctypes.byref(spec), fake_tab, 1, 0x1000, 1, 65, 0, 128, 0, ctypes.byref(cache), None) == -1
+    # bad dtype
+    assert L.tq_quantize_kv(ctypes.byref(spec), fake_tab, 5, 0x1000, 1, 8, 0, 128, 0, ctypes.byref(cache), None) == -1
+    # nothing to do: OK without touching the device
+    assert L.tq_quantize_kv(ctypes.byref(spec), fake_tab, 1, 0x1000, 0, 8, 0, 128, 0, ctypes.byref(cache), None) == 0
+    # tiled layout needs cap % 32 == 0
+    ts = tq.Spec(3, layout=1).c()
+    c2 = tq.TqCache(0x1000, 0x2000, None, None, 40)
+    assert L.tq_quantize_kv(ctypes.byref(ts), fake_tab, 1, 0x1000, 1, 8, 0, 128, 0, ctypes.byref(c2), None) == -1
+
+
+def test_attend_argument_errors_without_launch():
+    L = tq.lib()
+    ks, vs = tq.Spec(4).c(), tq.Spec(3, layout=1).c()
+    kc = tq.TqCache(0x1000, 0x2000, None, None, 64)
+    vc = tq.TqCache(0x3000, 0x4000, None, None, 64)
+    tab = ctypes.c_void_p(0x10000)
+
+    def call(a, ks_=ks, vs_=vs, ws=1 << 20, q=0x5000, kc_=kc):
+        return L.tq_attend_decode(ctypes.byref(ks_), tab, ctypes.byref(kc_), ctypes.byref(vs_), tab,
+                                  ctypes.byref(vc), ctypes.byref(a), q, None, None, 0x6000, 0x7000,
+                                  0x8000, ws, None)
+
+    assert call(tq.TqAttn(1, 6, 4, 0, 0.1, 0.0, 64)) == -1            # hq % hkv
+    assert call(tq.TqAttn(1, 64, 2, 0, 0.1, 0.0, 64)) == -2           # G > 16
+    assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 65)) == -1            # max_len > cap
+    assert call(tq.TqAttn(1, 8, 2, 4, 0.1, 0.0, 64)) == -1            # sink without buffers
+    assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), ws=16) == -3     # workspace
+    assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), q=None) == -1
+    assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), ks_=vs, vs_=ks) == -2  # layouts swapped
+    assert call(tq.TqAttn(0, 8, 2, 0, 0.1, 0.0, 64)) == 0             # empty batch: nothing launched
+    ws = tq.attend_workspace_bytes(2, 32, 8, 0, 32768)
+    assert ws >= 2 * 32 * (2 * 128 + 4) * 4
