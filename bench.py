@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant packed-KV hot path on one MI355X.
+
+One step = one pass of the whole path over the GQA decode workload (batch 1,
+32 query heads / 8 KV heads, d = 128, context 32768, bf16 K/V with 4 outlier
+key channels per head, K 4-bit records, V 3-bit tiles):
+  quantize all K vectors, quantize all V vectors, one decode-attention step.
+Inputs are resident in HBM before timing.  Four copies of the inputs and of
+the packed cache rotate between steps, and a step attends over a cache copy
+written three steps earlier, so reads are not served from the 256 MB
+Infinity Cache.  Timing uses HIP events on the launch stream.
+
+Prints one JSON line.  `value` is the decode-attention throughput in GB/s of
+algorithmic bytes (packed K and V records, norms, q and out).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "packed-KV decode-attention GB/s (% HBM peak) + quantize Mvec/s at d=128"
+WORKLOAD = "gqa_decode"
+COPIES = 4
+KERNEL_SOURCES = ["compressed_kv_cache_tq_amd/csrc/quantize.hip", "compressed_kv_cache_tq_amd/csrc/attend.hip"]
+
+
+def source_hash(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(name: str):
+    """Per-dispatch HBM bytes measured with rocprofv3 --pmc for a kernel, or None
+    if the summary is missing or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = kv.get("source")
+    if not src or kv.get("source_sha256_16") != source_hash(src):
+        return None
+    return float(kv["hbm_bytes_per_dispatch"])
+
+
+def cpu_baseline(inp, run_codes, wl, kspec, vspec):
+    """The float64 oracle on the host: decode attention over the GPU's packed
+    cache (all heads) plus quantization of a 16384-vector sample."""
+    from oracle import attend as oat
+    from oracle import pack as opk
+    from oracle import quantize as oqz
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    ks = oqz.Spec(bits_lo=kspec.bits_lo, bits_hi=kspec.bits_lo, split=128)
+    vs = oqz.Spec(bits_lo=vspec.bits_lo, bits_hi=vspec.bits_lo, split=128)
+    kraw, kn, vraw, vn = run_codes
+    T = wl.ctx
+    t0 = time.perf_counter()
+    pi = oqz.rotation_of(ks)
+    G = wl.hq // wl.hkv
+    for h in range(wl.hkv):
+        kidx = opk.unpack_records(kraw[h], kspec.widths)
+        vidx = opk.unpack_tiled(vraw[h], vspec.widths, T)
+        khat = oqz.dequantize_rotated(kidx, ks)
+        vhat = oqz.dequantize_rotated(vidx, vs)
+        for g in range(G):
+            qq = inp.q[0, h * G + g].astype(np.float64)
+            oat.attend_rotated(qq, pi @ qq, khat, kn[h], vhat, vn[h], pi, scale=1 / np.sqrt(128))
+    t_dec = time.perf_counter() - t0
+    dec_bytes = wl.hkv * T * (kspec_bytes(kspec) + 4 + kspec_bytes(vspec) + 4) + 2 * wl.hq * 128 * 4
+    n_q = 16384
+    xs = inp.k[0][0][:n_q].astype(np.float64)
+    t1 = time.perf_counter()
+    qq = oqz.quantize(xs, ks)
+    opk.pack_records(qq.idx[:2048], kspec.widths)  # packing cost on a slice, scaled below
+    t_q = time.perf_counter() - t1
+    return {
+        "value": round(dec_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"decode: full step (8 KV heads x {T} tokens, 32 q heads) on the GPU's packed cache; "
+                  f"quantize: {n_q} K vectors",
+        "decode_seconds": round(t_dec, 3),
+        "quantize_Mvec_s": round(n_q / t_q / 1e6, 5),
+    }
+
+
+def kspec_bytes(spec) -> int:
+    from compressed_kv_cache_tq_amd import tq
+    return tq.code_bytes(spec)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); every box here has a single "
+              f"MI355X and this path is not sharded across GPUs.", file=sys.stderr)
+        return 2
+    import torch
+    from compressed_kv_cache_tq_amd import tq, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = workloads.WORKLOADS[WORKLOAD]
+    inp = workloads.generate(WORKLOAD)
+    B, Hkv, Hq, T = wl.batch, wl.hkv, wl.hq, wl.ctx
+    kspec = tq.Spec(wl.k.bits_lo, layout=tq.LAYOUT_RECORD)
+    vspec = tq.Spec(wl.v.bits_lo, layout=tq.LAYOUT_TILED)
+    ktab, vtab = tq.device_tables(kspec), tq.device_tables(vspec)
+    xk_host = np.stack(inp.k_bf16).reshape(B * Hkv, T, 128)
+    xv_host = np.stack(inp.v_bf16).reshape(B * Hkv, T, 128)
+    xk = [torch.from_numpy(xk_host.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(COPIES)]
+    xv = [torch.from_numpy(xv_host.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(COPIES)]
+    kc = [tq.alloc_cache(kspec, B * Hkv, T) for _ in range(COPIES)]
+    vc = [tq.alloc_cache(vspec, B * Hkv, T) for _ in range(COPIES)]
+    q = torch.from_numpy(inp.q).cuda()
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(tq.attend_workspace_bytes(B, Hq, Hkv, 0, T) // 4 + 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s, a = i % COPIES, (i + 1) % COPIES
+        if ev is not None:
+            ev[0].record(stream)
+        tq.quantize_kv(kspec, ktab, xk[s], kc[s])
+        if ev is not None:
+            ev[1].record(stream)
+        tq.quantize_kv(vspec, vtab, xv[s], vc[s])
+        if ev is not None:
+            ev[2].record(stream)
+        tq.attend_decode(kspec, ktab, kc[a], vspec, vtab, vc[a], q, lens, out, ws, hkv=Hkv, max_len=T)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(max(args.warmup, COPIES)):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    qk_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    qv_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    at_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    n_vec = B * Hkv * T
+    kcb, vcb = tq.code_bytes(kspec), tq.code_bytes(vspec)
+    dec_bytes = n_vec * (kcb + 4 + vcb + 4) + 2 * B * Hq * 128 * 4
+    qk_bytes = n_vec * (128 * 2 + kcb + 4)
+    qv_bytes = n_vec * (128 * 2 + vcb + 4)
+    dec_s = at_ms.mean() / 1e3
+    quant_s = (qk_ms.mean() + qv_ms.mean()) / 1e3
+    dec_gbs = dec_bytes / dec_s / 1e9
+    quant_mvec = 2 * n_vec / quant_s / 1e6
+    quant_gbs = (qk_bytes + qv_bytes) / quant_s / 1e9
+
+    # dominant kernel of the step (largest device time): one of the two quantize launches
+    if qk_ms.mean() >= qv_ms.mean():
+        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_k", qk_ms.mean(), qk_bytes, "quantize_kernel<4,4,bf16,record>"
+    else:
+        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms.mean(), qv_bytes, "quantize_kernel<3,3,bf16,tiled>"
+    dom_gbs = dom_bytes / (dom_ms / 1e3) / 1e9
+    traffic = read_traffic(dom_name)
+    roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom_kernel,
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2)}
+    att_traffic = read_traffic("attend")
+    roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
+                       "kernel": "prep + split_kernel<4,4,3,3> + combine (one decode step)",
+                       "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms.mean() * 1e3, 2)}
+    res = {
+        "metric": METRIC, "value": round(dec_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "d": 128, "context": T,
+                   "kv_dtype": "bf16", "k_bits": wl.k.bits_lo, "v_bits": wl.v.bits_lo, "qjl": False,
+                   "structure": "4 key channels per head x10"},
+        "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
+        "decode_us": round(at_ms.mean() * 1e3, 2),
+        "quantize_Mvec_s": round(quant_mvec, 1), "quantize_GB_s": round(quant_gbs, 2),
+        "quantize_pct_hbm_peak": round(100 * quant_gbs / HBM_PEAK_GBS, 2),
+        "quantize_us": {"k": round(qk_ms.mean() * 1e3, 2), "v": round(qv_ms.mean() * 1e3, 2)},
+        "roofline": roofline, "roofline_attend": roofline_attend,
+    }
+    if not args.no_cpu_baseline:
+        a = (args.warmup + args.steps) % COPIES
+        nb_k, nb_v = tq.cache_code_bytes(kspec, T), tq.cache_code_bytes(vspec, T)
+        kraw = [kc[a].codes[h * nb_k:(h + 1) * nb_k].cpu().numpy().reshape(T, kcb) for h in range(Hkv)]
+        vraw = [vc[a].codes[h * nb_v:(h + 1) * nb_v].cpu().numpy() for h in range(Hkv)]
+        kn = [kc[a].norms[h * T:(h + 1) * T].cpu().numpy() for h in range(Hkv)]
+        vn = [vc[a].norms[h * T:(h + 1) * T].cpu().numpy() for h in range(Hkv)]
+        res["cpu_baseline"] = cpu_baseline(inp, (kraw, kn, vraw, vn), wl, kspec, vspec)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

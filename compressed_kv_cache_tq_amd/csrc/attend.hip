@@ -7,14 +7,15 @@
 // to Share!": item 1 (the first ~128 tokens stay uncompressed) and item 3
 // (value dequantization is skipped when the attention weight is below 1e-6).
 //
-// Three launches on one stream:
-//  prep    q~ = Pi_K q (times scale*log2 e) and u = S q~, per query head,
-//          stored with a power-of-two scale so they split into fp16 hi + lo;
-//  split   one workgroup (4 waves) per (split, kv head, sequence); each wave
-//          streams 32-token tiles: K records -> LUT dequantization in
-//          registers -> scores on MFMA for all query heads of the group ->
-//          online softmax -> V tiles (token-major sub-blocks) -> P V on MFMA
-//          in the rotated domain; the 4 waves merge in LDS and write one
+// Two launches on one stream:
+//  split   one workgroup (4 waves) per (split, kv head, sequence).  It first
+//          rotates the group's queries, q~ = Pi_K q (times scale*log2 e), and
+//          u = S q~, with a power-of-two scale so they split into fp16 hi +
+//          lo.  Each wave then streams 32-token tiles, prefetching the next
+//          tile into registers: K records -> LUT dequantization in registers
+//          -> scores on MFMA for all query heads of the group -> online
+//          softmax -> V tiles (coordinate-major sub-blocks) -> P V on MFMA in
+//          the rotated domain.  The 4 waves merge in LDS and write one
 //          partial (m, l, acc[128]) per query head;
 //  combine per query head: log-sum-exp merge of the splits and the raw bf16
 //          sink tokens, one inverse rotation Pi_V^T, normalisation.
@@ -32,6 +33,7 @@ constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
 constexpr int PART = 132;  // floats per partial: m, l, 2 pad, acc[128]
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float QJL_C = 1.2533141373155003f / QJL_M;  // sqrt(pi/2) / m
 
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -59,80 +61,108 @@ __device__ __forceinline__ half8 dequant8(const uint32_t* w, int k, const uint32
   return as_half8(lut[v & M], lut[(v >> (2 * B)) & M], lut[(v >> (4 * B)) & M], lut[(v >> (6 * B)) & M]);
 }
 
-// ---------------------------------------------------------------------------
-// prep: one block of 128 threads per (b, query head).
-__global__ __launch_bounds__(128) void prep_kernel(const Tables* __restrict__ ktab, const float* __restrict__ q,
-                                                   float* __restrict__ qs, float* __restrict__ qexp,
-                                                   float scale, int qjl) {
-  __shared__ float qv[D];
-  __shared__ float qr[D];
-  __shared__ float red[4];
-  const int bh = blockIdx.x, i = threadIdx.x;
-  qv[i] = q[static_cast<int64_t>(bh) * D + i];
-  __syncthreads();
-  float acc = 0.0f;
-  for (int j = 0; j < D; ++j) acc = fmaf(ktab->pi[i * D + j], qv[j], acc);
-  acc *= scale * LOG2E;
-  qr[i] = acc;
-  // power-of-two scale so that max |value| lands in [2^13, 2^14)
-  auto pow2_scale = [&](float v, int slot) {
-    float m = fabsf(v);
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((i & 63) == 0) red[i >> 6] = m;
-    __syncthreads();
-    const float mx = fmaxf(red[0], red[1]);
-    __syncthreads();
-    int ex = 0;
-    if (mx > 0.0f) frexpf(mx, &ex);
-    const int sh = 14 - ex;
-    if (i == 0) qexp[static_cast<int64_t>(bh) * 4 + slot] = ldexpf(1.0f, -sh);
-    return sh;
-  };
-  const int sq = pow2_scale(acc, 0);
-  qs[static_cast<int64_t>(bh) * 2 * D + i] = ldexpf(acc, sq);
-  if (qjl) {
-    __syncthreads();
-    float u = 0.0f;
-    for (int j = 0; j < D; ++j) u = fmaf(ktab->s[i * D + j], qr[j], u);
-    const int su = pow2_scale(u, 1);
-    qs[static_cast<int64_t>(bh) * 2 * D + D + i] = ldexpf(u, su);
+// Registers of one 32-token tile for one lane (prefetched one tile ahead).
+struct TileRegs {
+  uint32_t kw[2][4];  // K record chunk of token slots mu(0, n), mu(1, n)
+  uint32_t vw[8];     // V sub-block (token group j, coordinate group n)
+  float4 kn[2];       // K norms of tokens 8j .. 8j+7
+  float4 vn[2];       // V norms of tokens 8j .. 8j+7
+  uint32_t zw[2];     // QJL sign dword j of token slots mu(0, n), mu(1, n)
+  float4 rn[2];       // QJL residual norms of tokens 8j .. 8j+7
+};
+
+template <int KLO, int KHI, int VLO, int VHI, bool QJL>
+__device__ __forceinline__ void load_tile(TileRegs& r, int64_t t0, int n, int j, const uint8_t* kbase,
+                                          const uint8_t* vbase, const float* knb, const float* vnb,
+                                          const uint32_t* zb, const float* rnb) {
+  constexpr int KBYTES = 8 * (KLO + KHI);
+  constexpr int VBYTES = 8 * (VLO + VHI);
+  constexpr int VG = 64 * (VLO + VHI);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int64_t tok = t0 + 8 * (n >> 2) + 4 * mb + (n & 3);
+    const uint8_t* rec = kbase + tok * KBYTES;
+    if (j < 2) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + 4 * KLO * j);
+#pragma unroll
+      for (int w = 0; w < KLO; ++w) r.kw[mb][w] = p[w];
+    } else {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + 8 * KLO + 4 * KHI * (j - 2));
+#pragma unroll
+      for (int w = 0; w < KHI; ++w) r.kw[mb][w] = p[w];
+    }
+    if constexpr (QJL) r.zw[mb] = zb[tok * (QJL_M / 32) + j];
+  }
+  const uint8_t* tile = vbase + (t0 / TILE) * (TILE * VBYTES) + j * VG;
+  if (n < 8) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(tile + 8 * VLO * n);
+#pragma unroll
+    for (int w = 0; w < 2 * VLO; ++w) r.vw[w] = p[w];
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(tile + 64 * VLO + 8 * VHI * (n - 8));
+#pragma unroll
+    for (int w = 0; w < 2 * VHI; ++w) r.vw[w] = p[w];
+  }
+  const int64_t tb = t0 + 8 * j;
+  r.kn[0] = *reinterpret_cast<const float4*>(knb + tb);
+  r.kn[1] = *reinterpret_cast<const float4*>(knb + tb + 4);
+  r.vn[0] = *reinterpret_cast<const float4*>(vnb + tb);
+  r.vn[1] = *reinterpret_cast<const float4*>(vnb + tb + 4);
+  if constexpr (QJL) {
+    r.rn[0] = *reinterpret_cast<const float4*>(rnb + tb);
+    r.rn[1] = *reinterpret_cast<const float4*>(rnb + tb + 4);
   }
 }
 
-// Load this lane's q~ (or u) fragment for k-steps 0..3: head n (0 if n >= G),
-// coordinates 32j + 8ks + e, split into fp16 hi + lo.
-__device__ __forceinline__ void load_qfrag(const float* qsrc, bool ok, int j, half8 (&hi)[4], half8 (&lo)[4]) {
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = ok ? qsrc[32 * j + 8 * ks + e] : 0.0f;
-      const _Float16 h = static_cast<_Float16>(v);
-      hi[ks][e] = h;
-      lo[ks][e] = static_cast<_Float16>(v - static_cast<float>(h));
-    }
+__device__ __forceinline__ float f4get(const float4 (&v)[2], int e) {
+  const float4 x = v[e >> 2];
+  const int k = e & 3;
+  return k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
 }
 
+// Split kernel: one workgroup per (split, kv head, sequence).
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-__global__ __launch_bounds__(THREADS) void split_kernel(
+__global__ __launch_bounds__(THREADS, 2) void split_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
     const uint8_t* __restrict__ ksigns, const float* __restrict__ krn, int64_t kcap,
     const Tables* __restrict__ vtab, const uint8_t* __restrict__ vcodes, const float* __restrict__ vnorms,
-    int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ qs,
-    const float* __restrict__ qexp, float* __restrict__ parts, int hq, int hkv, int sink, int n_split,
-    int64_t chunk, float v_skip) {
+    int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q, float* __restrict__ parts,
+    int hq, int hkv, int sink, int n_split, int64_t chunk, float qscale, float v_skip) {
   constexpr int KBYTES = 8 * (KLO + KHI);
   constexpr int VBYTES = 8 * (VLO + VHI);
-  constexpr int VG = 64 * (VLO + VHI);  // bytes of one 8-token group of a V tile
   __shared__ uint32_t lutk[2][256];
   __shared__ uint32_t lutv[2][256];
   __shared__ uint32_t lutz[4];
+  __shared__ float qraw[16][D];
+  __shared__ float qrot[16][D];
+  __shared__ float urot[QJL ? 16 : 1][D];
+  __shared__ float qexp[16][2];
   __shared__ float mrg_m[WAVES][16];
   __shared__ float mrg_l[WAVES][16];
   __shared__ float mrg_acc[WAVES][16][D];
 
   const int split = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int G = hq / hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
+  const int64_t L = seq_lens[b];
+  const int64_t comp = L > sink ? L - sink : 0;
+  const int64_t t_begin = static_cast<int64_t>(split) * chunk;
+  const int64_t t_end = t_begin + chunk < comp ? t_begin + chunk : comp;
+
+  const uint8_t* kbase = kcodes + stream * kcap * KBYTES;
+  const uint8_t* vbase = vcodes + stream * vcap * VBYTES;
+  const float* knb = knorms + stream * kcap;
+  const float* vnb = vnorms + stream * vcap;
+  const uint32_t* zb = QJL ? reinterpret_cast<const uint32_t*>(ksigns) + stream * kcap * (QJL_M / 32) : nullptr;
+  const float* rnb = QJL ? krn + stream * kcap : nullptr;
+
+  // First tile's loads go out before the query preparation below.
+  TileRegs cur;
+  int64_t t0 = t_begin + 32 * wave;
+  if (t0 < t_end) load_tile<KLO, KHI, VLO, VHI, QJL>(cur, t0, n, j, kbase, vbase, knb, vnb, zb, rnb);
+
   // LUTs: entry e of width B = centroid(e & mask) | centroid(e >> B) << 16 (fp16 bits)
   for (int e = threadIdx.x; e < 256; e += THREADS) {
 #pragma unroll
@@ -148,27 +178,100 @@ __global__ __launch_bounds__(THREADS) void split_kernel(
     }
     if (e < 4) lutz[e] = ((e & 1) ? 0x3C00u : 0xBC00u) | (((e >> 1) & 1) ? 0x3C000000u : 0xBC000000u);
   }
+  // ---- query preparation: qrot = Pi_K q * scale * log2(e); urot = S qrot.
+  const float* qg = q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += THREADS) qraw[idx / D][idx % D] = qg[idx];
+  __syncthreads();
+  // thread (i, hf): output coordinate i, inputs [64 hf, 64 hf + 64), all heads.
+  // The thread's 64 matrix entries are loaded at once (one round trip), then
+  // reused for every head.
+  {
+    const int i = threadIdx.x & (D - 1), hf = threadIdx.x >> 7;
+    float w[64];
+#pragma unroll
+    for (int k = 0; k < 64; ++k) w[k] = ktab->pit[(64 * hf + k) * D + i];
+    for (int g = 0; g < G; ++g) {
+      const float4* qv4 = reinterpret_cast<const float4*>(&qraw[g][64 * hf]);
+      float a = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float4 x = qv4[k];
+        a = fmaf(w[4 * k], x.x, a);
+        a = fmaf(w[4 * k + 1], x.y, a);
+        a = fmaf(w[4 * k + 2], x.z, a);
+        a = fmaf(w[4 * k + 3], x.w, a);
+      }
+      if (hf) qrot[g][i] = a;
+      __syncthreads();
+      if (!hf) qrot[g][i] = (qrot[g][i] + a) * qscale;
+      __syncthreads();
+    }
+    if constexpr (QJL) {
+#pragma unroll
+      for (int k = 0; k < 64; ++k) w[k] = ktab->sit[(64 * hf + k) * D + i];
+      for (int g = 0; g < G; ++g) {
+        const float4* qv4 = reinterpret_cast<const float4*>(&qrot[g][64 * hf]);
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float4 x = qv4[k];
+          a = fmaf(w[4 * k], x.x, a);
+          a = fmaf(w[4 * k + 1], x.y, a);
+          a = fmaf(w[4 * k + 2], x.z, a);
+          a = fmaf(w[4 * k + 3], x.w, a);
+        }
+        if (hf) urot[g][i] = a;
+        __syncthreads();
+        if (!hf) urot[g][i] += a;
+        __syncthreads();
+      }
+    }
+  }
+  // power-of-two scale per head so |value| * 2^sh < 2^14: fp16 hi + lo keeps ~22 bits
+  for (int g = wave; g < G; g += WAVES) {
+#pragma unroll
+    for (int which = 0; which < (QJL ? 2 : 1); ++which) {
+      const float* v = which ? urot[QJL ? g : 0] : qrot[g];
+      float m = fmaxf(fabsf(v[lane]), fabsf(v[lane + 64]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      int ex = 0;
+      if (m > 0.0f) frexpf(m, &ex);
+      if (lane == 0) qexp[g][which] = static_cast<float>(14 - ex);
+    }
+  }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, j = lane >> 4;
-  const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
-  const int64_t L = seq_lens[b];
-  const int64_t comp = L > sink ? L - sink : 0;
-  const int64_t t_begin = static_cast<int64_t>(split) * chunk;
-  const int64_t t_end = t_begin + chunk < comp ? t_begin + chunk : comp;
-
-  // query fragments (B operand of the score MFMA): column n = query head
-  const int64_t qh_idx = static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + n;
+  // query fragments (B operand of the score MFMA): column n = query head n
   const bool head_ok = n < G;
   half8 qh[4], ql[4], uh[QJL ? 4 : 1], ul[QJL ? 4 : 1];
-  const float* qsrc = qs + (head_ok ? qh_idx : 0) * 2 * D;
-  load_qfrag(qsrc, head_ok, j, qh, ql);
-  float qinv = head_ok ? qexp[qh_idx * 4 + 0] : 0.0f;
-  float uinv = 0.0f;
-  if constexpr (QJL) {
-    load_qfrag(qsrc + D, head_ok, j, uh, ul);
-    uinv = head_ok ? qexp[qh_idx * 4 + 1] * (1.2533141373155003f / QJL_M) : 0.0f;  // sqrt(pi/2)/m
+  float qinv = 0.0f, uinv = 0.0f;
+  {
+    const int g = head_ok ? n : 0;
+    const int sq = static_cast<int>(qexp[g][0]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = head_ok ? ldexpf(qrot[g][32 * j + 8 * ks + e], sq) : 0.0f;
+        const _Float16 hv = static_cast<_Float16>(v);
+        qh[ks][e] = hv;
+        ql[ks][e] = static_cast<_Float16>(v - static_cast<float>(hv));
+      }
+    qinv = head_ok ? ldexpf(1.0f, -sq) : 0.0f;
+    if constexpr (QJL) {
+      const int su = static_cast<int>(qexp[g][1]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = head_ok ? ldexpf(urot[g][32 * j + 8 * ks + e], su) : 0.0f;
+          const _Float16 hv = static_cast<_Float16>(v);
+          uh[ks][e] = hv;
+          ul[ks][e] = static_cast<_Float16>(v - static_cast<float>(hv));
+        }
+      uinv = head_ok ? ldexpf(QJL_C, -su) : 0.0f;
+    }
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -176,63 +279,11 @@ __global__ __launch_bounds__(THREADS) void split_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f32x4{};
 
-  const uint8_t* kbase = kcodes + stream * kcap * KBYTES;
-  const uint8_t* vbase = vcodes + stream * vcap * VBYTES;
-  const float* knb = knorms + stream * kcap;
-  const float* vnb = vnorms + stream * vcap;
-
-  for (int64_t t0 = t_begin + 32 * wave; t0 < t_end; t0 += 32 * WAVES) {
-    // ---- K: lane (rho = n, j) loads chunk j of the record of token slot
-    // mu(mb, rho) = 8(rho/4) + 4mb + rho%4 for M-blocks mb = 0, 1.
-    uint32_t kw[2][4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int slot = 8 * (n >> 2) + 4 * mb + (n & 3);
-      const int64_t tok = t0 + slot;
-      const uint8_t* rec = kbase + (tok < t_end ? tok : t0) * KBYTES;
-      if (j < 2) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + 4 * KLO * j);
-#pragma unroll
-        for (int w = 0; w < KLO; ++w) kw[mb][w] = p[w];
-      } else {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(rec + 8 * KLO + 4 * KHI * (j - 2));
-#pragma unroll
-        for (int w = 0; w < KHI; ++w) kw[mb][w] = p[w];
-      }
-    }
-    uint32_t zw[2];
-    if constexpr (QJL) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int slot = 8 * (n >> 2) + 4 * mb + (n & 3);
-        const int64_t tok = t0 + slot;
-        zw[mb] = reinterpret_cast<const uint32_t*>(ksigns + ((stream * kcap) + (tok < t_end ? tok : t0)) * (QJL_M / 8))[j];
-      }
-    }
-    // ---- V: lane (n, j) loads sub-block (g = j, q = n) of the tile.
-    uint32_t vw[8];
-    {
-      const uint8_t* tile = vbase + (t0 / TILE) * (TILE * VBYTES) + j * VG;
-      if (n < 8) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(tile + 8 * VLO * n);
-#pragma unroll
-        for (int w = 0; w < 2 * VLO; ++w) vw[w] = p[w];
-      } else {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(tile + 64 * VLO + 8 * VHI * (n - 8));
-#pragma unroll
-        for (int w = 0; w < 2 * VHI; ++w) vw[w] = p[w];
-      }
-    }
-    // norms of tokens 8j + e (score layout: lane (head n, j) holds tokens 8j + 4mb + i)
-    float kn[8], vn[8], rn[8];
+  for (; t0 < t_end; t0 += 32 * WAVES) {
+    TileRegs nxt;
+    const int64_t t1 = t0 + 32 * WAVES;
+    if (t1 < t_end) load_tile<KLO, KHI, VLO, VHI, QJL>(nxt, t1, n, j, kbase, vbase, knb, vnb, zb, rnb);
     const int64_t tb = t0 + 8 * j;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool ok = tb + e < t_end;
-      kn[e] = ok ? knb[tb + e] : 0.0f;
-      vn[e] = ok ? vnb[tb + e] : 0.0f;
-      if constexpr (QJL) rn[e] = ok ? krn[stream * kcap + tb + e] : 0.0f;
-    }
 
     // ---- scores on MFMA: A = dequantized K (16 tokens x 32 coords), B = q~
     f32x4 sk[2], sz[2];
@@ -243,13 +294,13 @@ __global__ __launch_bounds__(THREADS) void split_kernel(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         half8 a;
-        if constexpr (KLO == KHI) a = dequant8<KLO>(kw[mb], ks, lutk[0]);
-        else a = j < 2 ? dequant8<KLO>(kw[mb], ks, lutk[0]) : dequant8<KHI>(kw[mb], ks, lutk[1]);
+        if constexpr (KLO == KHI) a = dequant8<KLO>(cur.kw[mb], ks, lutk[0]);
+        else a = j < 2 ? dequant8<KLO>(cur.kw[mb], ks, lutk[0]) : dequant8<KHI>(cur.kw[mb], ks, lutk[1]);
         sk[mb] = mfma16(a, qh[ks], sk[mb]);
         sk[mb] = mfma16(a, ql[ks], sk[mb]);
         if constexpr (QJL) {
-          const uint32_t zb = (zw[mb] >> (8 * ks)) & 0xFFu;
-          const half8 z = as_half8(lutz[zb & 3], lutz[(zb >> 2) & 3], lutz[(zb >> 4) & 3], lutz[zb >> 6]);
+          const uint32_t zv = (cur.zw[mb] >> (8 * ks)) & 0xFFu;
+          const half8 z = as_half8(lutz[zv & 3], lutz[(zv >> 2) & 3], lutz[(zv >> 4) & 3], lutz[zv >> 6]);
           sz[mb] = mfma16(z, uh[ks], sz[mb]);
           sz[mb] = mfma16(z, ul[ks], sz[mb]);
         }
@@ -263,8 +314,8 @@ __global__ __launch_bounds__(THREADS) void split_kernel(
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * mb + i;
         float dot = sk[mb][i] * qinv;
-        if constexpr (QJL) dot = fmaf(rn[e] * sz[mb][i], uinv, dot);
-        s[e] = tb + e < t_end ? kn[e] * dot : -INFINITY;
+        if constexpr (QJL) dot = fmaf(f4get(cur.rn, e) * sz[mb][i], uinv, dot);
+        s[e] = tb + e < t_end ? f4get(cur.kn, e) * dot : -INFINITY;
         tmax = fmaxf(tmax, s[e]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -282,17 +333,21 @@ __global__ __launch_bounds__(THREADS) void split_kernel(
       if (p1 < v_skip) p1 = 0.0f;
       psum += p0 + p1;
       any |= (p0 > 0.0f) | (p1 > 0.0f);
-      const _Float16 h0 = static_cast<_Float16>(p0 * vn[e]), h1 = static_cast<_Float16>(p1 * vn[e + 1]);
+      const float v0 = tb + e < t_end ? f4get(cur.vn, e) : 0.0f;
+      const float v1 = tb + e + 1 < t_end ? f4get(cur.vn, e + 1) : 0.0f;
+      const _Float16 h0 = static_cast<_Float16>(p0 * v0), h1 = static_cast<_Float16>(p1 * v1);
       pw[e >> 1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
                    (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
     }
     l_run = l_run * alpha + psum;
-    // rescale the accumulator rows (query heads 4j + i) by their alpha
+    // rescale the accumulator rows (query heads 4j + i) only when a maximum moved
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, 4 * j + i);
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * j + i);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k][i] *= ai;
+        for (int k = 0; k < 8; ++k) acc[k][i] *= ai;
+      }
     }
     // skip the value work of a tile whose weights all fell below v_skip
     if (__any(any && head_ok)) {
@@ -300,21 +355,21 @@ __global__ __launch_bounds__(THREADS) void split_kernel(
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         half8 bv;
-        if constexpr (VLO == VHI) bv = dequant8<VLO>(vw, nb, lutv[0]);
-        else bv = n < 8 ? dequant8<VLO>(vw, nb, lutv[0]) : dequant8<VHI>(vw, nb, lutv[1]);
+        if constexpr (VLO == VHI) bv = dequant8<VLO>(cur.vw, nb, lutv[0]);
+        else bv = n < 8 ? dequant8<VLO>(cur.vw, nb, lutv[0]) : dequant8<VHI>(cur.vw, nb, lutv[1]);
         acc[nb] = mfma16(pa, bv, acc[nb]);
       }
     }
+    cur = nxt;
   }
 
-  // ---- merge the 4 waves.  l: sum over the 4 token lanes of a head.
+  // ---- merge the 4 waves; l: sum over the 4 token lanes of a head.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (lane < 16) {
     mrg_m[wave][lane] = m_run;
     mrg_l[wave][lane] = l_run;
   }
-  // acc[nb][i]: query head 4j + i, coordinate 8n + nb
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -344,84 +399,123 @@ __global__ __launch_bounds__(THREADS) void split_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// combine: one block of 128 threads per (b, query head).
-__global__ __launch_bounds__(128) void combine_kernel(const Tables* __restrict__ vtab, const float* __restrict__ q,
-                                                      const uint16_t* __restrict__ sink_k,
-                                                      const uint16_t* __restrict__ sink_v,
-                                                      const int32_t* __restrict__ seq_lens,
-                                                      const float* __restrict__ parts, float* __restrict__ out,
-                                                      int hq, int hkv, int sink, int n_split, float scale) {
+// combine: one block of 512 threads per (b, query head): log-sum-exp merge of
+// the split partials and the raw sink tokens, one inverse rotation.  Thread
+// (i, hf) handles coordinate i and a quarter hf of every reduction, so each
+// thread has few, independent loads in flight.
+constexpr int CT = 512;
+
+__global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ vtab, const float* __restrict__ q,
+                                                     const uint16_t* __restrict__ sink_k,
+                                                     const uint16_t* __restrict__ sink_v,
+                                                     const int32_t* __restrict__ seq_lens,
+                                                     const float* __restrict__ parts, float* __restrict__ out,
+                                                     int hq, int hkv, int sink, int n_split, float qscale) {
   extern __shared__ float sm[];
-  float* orot = sm;            // [D]
-  float* qv = sm + D;          // [D]
-  float* ssc = sm + 2 * D;     // [sink] sink scores, then weights
-  __shared__ float red[2];
-  const int bh = blockIdx.x, i = threadIdx.x;
+  float* fs = sm;                 // [n_split] split maxima, then weights
+  float* ls = fs + n_split;       // [n_split] split sums
+  float* ssc = ls + n_split;      // [sink] sink scores, then weights
+  __shared__ float qv[D];
+  __shared__ float orot[4][D];
+  __shared__ float obuf[4][D];
+  __shared__ float red[16];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = bh / hq, h = bh % hq, kh = h / (hq / hkv);
   const int64_t L = seq_lens[b];
   const int ns = static_cast<int>(L < sink ? L : sink);
   const float* pp = parts + static_cast<int64_t>(bh) * n_split * PART;
-  qv[i] = q[static_cast<int64_t>(bh) * D + i] * (scale * LOG2E);
-  // global maximum over splits and sink scores
-  float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp)
-    if (pp[sp * PART + 1] > 0.0f) M = fmaxf(M, pp[sp * PART]);
+  if (tid < D) qv[tid] = q[static_cast<int64_t>(bh) * D + tid] * qscale;
+  float mloc = -INFINITY;
+  for (int sp = tid; sp < n_split; sp += CT) {
+    const float m = pp[sp * PART], l = pp[sp * PART + 1];
+    fs[sp] = m;
+    ls[sp] = l;
+    if (l > 0.0f) mloc = fmaxf(mloc, m);
+  }
   __syncthreads();
   const uint16_t* sk = sink_k + (static_cast<int64_t>(b) * hkv + kh) * sink * D;
   const uint16_t* sv = sink_v + (static_cast<int64_t>(b) * hkv + kh) * sink * D;
-  float smax = -INFINITY;
-  for (int t = i; t < ns; t += 128) {
+  for (int t = tid; t < ns; t += CT) {
+    const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(t) * D);
     float dot = 0.0f;
-    for (int c = 0; c < D; ++c) dot = fmaf(__uint_as_float(static_cast<uint32_t>(sk[t * D + c]) << 16), qv[c], dot);
-    ssc[t] = dot;
-    smax = fmaxf(smax, dot);
-  }
-  for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, __shfl_xor(smax, o));
-  if ((i & 63) == 0) red[i >> 6] = smax;
-  __syncthreads();
-  M = fmaxf(M, fmaxf(red[0], red[1]));
-  // merged rotated accumulator and total weight
-  float a = 0.0f, l = 0.0f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float lp = pp[sp * PART + 1];
-      if (lp > 0.0f) {
-        const float f = exp2f(pp[sp * PART] - M);
-        a = fmaf(f, pp[sp * PART + 4 + i], a);
-        l = fmaf(f, lp, l);
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const uint4 w = row[c];
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        dot = fmaf(__uint_as_float(u[k] << 16), qv[8 * c + 2 * k], dot);
+        dot = fmaf(__uint_as_float(u[k] & 0xFFFF0000u), qv[8 * c + 2 * k + 1], dot);
       }
     }
+    ssc[t] = dot;
+    mloc = fmaxf(mloc, dot);
   }
-  orot[i] = a;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+  if (lane == 0) red[wave] = mloc;
   __syncthreads();
-  for (int t = i; t < ns; t += 128) ssc[t] = exp2f(ssc[t] - M);
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < CT / 64; ++w) M = fmaxf(M, red[w]);
+  float lloc = 0.0f;
+  for (int sp = tid; sp < n_split; sp += CT) {
+    const float f = (ls[sp] > 0.0f && M != -INFINITY) ? exp2f(fs[sp] - M) : 0.0f;
+    fs[sp] = f;
+    lloc = fmaf(f, ls[sp], lloc);
+  }
+  for (int t = tid; t < ns; t += CT) {
+    const float w = exp2f(ssc[t] - M);
+    ssc[t] = w;
+    lloc += w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
   __syncthreads();
-  for (int t = 0; t < ns; ++t) l += ssc[t];
-  // one inverse rotation: out_i = sum_c Pi[c][i] orot[c]
+  if (lane == 0) red[8 + wave] = lloc;
+  const int i = tid & (D - 1), hf = tid >> 7;
+  float a = 0.0f;
+#pragma unroll 4
+  for (int sp = hf; sp < n_split; sp += 4) a = fmaf(fs[sp], pp[sp * PART + 4 + i], a);
+  orot[hf][i] = a;
+  __syncthreads();
+  float Lsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < CT / 64; ++w) Lsum += red[8 + w];
+  // one inverse rotation: out_i = sum_c Pi[c][i] orot[c] (+ raw sink values)
   float o = 0.0f;
-  for (int c = 0; c < D; ++c) o = fmaf(vtab->pi[c * D + i], orot[c], o);
-  for (int t = 0; t < ns; ++t) o = fmaf(ssc[t], __uint_as_float(static_cast<uint32_t>(sv[t * D + i]) << 16), o);
-  out[static_cast<int64_t>(bh) * D + i] = l > 0.0f ? o / l : 0.0f;
+#pragma unroll
+  for (int cc = 32 * hf; cc < 32 * hf + 32; ++cc)
+    o = fmaf(vtab->pi[cc * D + i], orot[0][cc] + orot[1][cc] + orot[2][cc] + orot[3][cc], o);
+  for (int t = hf; t < ns; t += 4)
+    o = fmaf(ssc[t], __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + i]) << 16), o);
+  obuf[hf][i] = o;
+  __syncthreads();
+  if (tid < D) {
+    const float v = obuf[0][tid] + obuf[1][tid] + obuf[2][tid] + obuf[3][tid];
+    out[static_cast<int64_t>(bh) * D + tid] = Lsum > 0.0f ? v / Lsum : 0.0f;
+  }
 }
 
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
-                        const tq_attn& a, const AttendPlan& plan, const int32_t* seq_lens, const float* qs,
-                        const float* qexp, float* parts, hipStream_t st) {
+                        const tq_attn& a, const AttendPlan& plan, const int32_t* seq_lens, const float* q,
+                        float* parts, hipStream_t st) {
   hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_split, a.hkv, a.batch), dim3(THREADS), 0,
                      st, ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms,
-                     vc.cap, seq_lens, qs, qexp, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.v_skip);
+                     vc.cap, seq_lens, q, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.scale * LOG2E,
+                     a.v_skip);
   return hipGetLastError();
 }
 
 template <int KLO, int KHI>
 hipError_t dispatch_v(int vkey, bool qjl, const Tables* ktab, const tq_cache& kc, const Tables* vtab,
                       const tq_cache& vc, const tq_attn& a, const AttendPlan& plan, const int32_t* sl,
-                      const float* qs, const float* qe, float* parts, hipStream_t st) {
-#define TQ_V(VL, VH)                                                                                        \
-  case VL * 10 + VH:                                                                                        \
-    return qjl ? launch_split<KLO, KHI, VL, VH, true>(ktab, kc, vtab, vc, a, plan, sl, qs, qe, parts, st)  \
-               : launch_split<KLO, KHI, VL, VH, false>(ktab, kc, vtab, vc, a, plan, sl, qs, qe, parts, st);
+                      const float* q, float* parts, hipStream_t st) {
+#define TQ_V(VL, VH)                                                                                  \
+  case VL * 10 + VH:                                                                                  \
+    return qjl ? launch_split<KLO, KHI, VL, VH, true>(ktab, kc, vtab, vc, a, plan, sl, q, parts, st)  \
+               : launch_split<KLO, KHI, VL, VH, false>(ktab, kc, vtab, vc, a, plan, sl, q, parts, st);
   switch (vkey) {
     TQ_V(2, 2)
     TQ_V(3, 3)
@@ -452,7 +546,7 @@ AttendPlan plan_attend(const tq_attn& a) {
   p.n_split = static_cast<int>(ns);
   p.chunk = chunk_tiles * TILE;
   const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
-  p.ws_bytes = static_cast<size_t>(heads) * (2 * D + 4 + static_cast<int64_t>(p.n_split) * PART) * sizeof(float);
+  p.ws_bytes = static_cast<size_t>(heads) * static_cast<int64_t>(p.n_split) * PART * sizeof(float);
   return p;
 }
 
@@ -461,27 +555,22 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                          void* workspace, hipStream_t st) {
   const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
-  float* qs = static_cast<float*>(workspace);
-  float* qexp = qs + heads * 2 * D;
-  float* parts = qexp + heads * 4;
-  hipLaunchKernelGGL(prep_kernel, dim3(static_cast<unsigned>(heads)), dim3(128), 0, st, ktab, q, qs, qexp, a.scale,
-                     ks.qjl_m ? 1 : 0);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  float* parts = static_cast<float*>(workspace);
   const int vkey = vs.bits_lo * 10 + vs.bits_hi;
   const bool qjl = ks.qjl_m != 0;
   hipError_t e;
   switch (ks.bits_lo * 10 + ks.bits_hi) {
-    case 22: e = dispatch_v<2, 2>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, qs, qexp, parts, st); break;
-    case 33: e = dispatch_v<3, 3>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, qs, qexp, parts, st); break;
-    case 44: e = dispatch_v<4, 4>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, qs, qexp, parts, st); break;
-    case 43: e = dispatch_v<4, 3>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, qs, qexp, parts, st); break;
-    case 32: e = dispatch_v<3, 2>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, qs, qexp, parts, st); break;
+    case 22: e = dispatch_v<2, 2>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, q, parts, st); break;
+    case 33: e = dispatch_v<3, 3>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, q, parts, st); break;
+    case 44: e = dispatch_v<4, 4>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, q, parts, st); break;
+    case 43: e = dispatch_v<4, 3>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, q, parts, st); break;
+    case 32: e = dispatch_v<3, 2>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, q, parts, st); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const size_t smem = (2 * D + static_cast<size_t>(a.sink)) * sizeof(float);
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(heads)), dim3(128), smem, st, vtab, q, sink_k, sink_v,
-                     seq_lens, parts, out, a.hq, a.hkv, a.sink, plan.n_split, a.scale);
+  const size_t smem = (2 * static_cast<size_t>(plan.n_split) + static_cast<size_t>(a.sink)) * sizeof(float);
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(heads)), dim3(CT), smem, st, vtab, q, sink_k, sink_v,
+                     seq_lens, parts, out, a.hq, a.hkv, a.sink, plan.n_split, a.scale * LOG2E);
   return hipGetLastError();
 }
 

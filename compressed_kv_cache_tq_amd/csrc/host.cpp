@@ -347,6 +347,8 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
     }
     std::vector<double> m(tq::D * tq::D);
     rotation_build(tq::D, spec->rot_seed, m.data());
+    for (int i = 0; i < tq::D; ++i)
+      for (int k = 0; k < tq::D; ++k) t->pit[k * tq::D + i] = static_cast<float>(m[i * tq::D + k]);
     for (int i = 0; i < tq::D * tq::D; ++i) {
       t->pi[i] = static_cast<float>(m[i]);
       const double v = m[i] * tq::PI_SCALE;
@@ -356,6 +358,8 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
     }
     if (sp.qjl_m) {
       gaussian_fill(spec->qjl_seed, m.data(), static_cast<size_t>(tq::QJL_M) * tq::D);
+      for (int i = 0; i < tq::QJL_M; ++i)
+        for (int k = 0; k < tq::D; ++k) t->sit[k * tq::QJL_M + i] = static_cast<float>(m[i * tq::D + k]);
       for (int i = 0; i < tq::QJL_M * tq::D; ++i) {
         t->s[i] = static_cast<float>(m[i]);
         const uint16_t hi = to_half(m[i]);
@@ -443,7 +447,7 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
   if (!(a.v_skip >= 0.0f) || !(a.v_skip < 1.0f)) return fail(TQ_E_ARG, "v_skip must be in [0, 1)");
   if (!std::isfinite(a.scale)) return fail(TQ_E_ARG, "scale must be finite");
   if (a.batch == 0) return TQ_OK;
-  if (vc->cap % tq::TILE) return fail(TQ_E_ARG, "value cache cap must be a multiple of 32");
+  if (vc->cap % tq::TILE || kc->cap % tq::TILE) return fail(TQ_E_ARG, "cache caps must be multiples of 32");
   if (a.max_len - a.sink > std::min(kc->cap, vc->cap))
     return fail(TQ_E_ARG, "max_len - sink exceeds the cache capacity");
   if (!q || !out || !seq_lens) return fail(TQ_E_ARG, "q, out and seq_lens must be non-NULL");

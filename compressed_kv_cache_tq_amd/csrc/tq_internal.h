@@ -26,7 +26,9 @@ constexpr uint32_t TABLES_MAGIC = 0x31515454u;  // "TTQ1"
 // contraction, as an fp16 pair pi_hi + pi_lo = 256 * pi (hi = fp16 of
 // 256*pi, lo = fp16 of the remainder), which keeps about 22 significant bits.
 // The sketch S (qjl_m x d, row-major) is stored the same way without the 256
-// factor.  All arrays start on 256-byte boundaries.
+// factor.  pit / sit are the transposes in fp32 (coalesced matrix-vector
+// products with one output per thread).  All arrays start on 256-byte
+// boundaries.
 struct alignas(256) Tables {
   uint32_t magic;
   uint32_t version;
@@ -45,6 +47,8 @@ struct alignas(256) Tables {
   float s[D * D];
   uint16_t s_hi[D * D];
   uint16_t s_lo[D * D];
+  float pit[D * D];
+  float sit[D * D];
 };
 
 constexpr float PI_SCALE = 256.0f;

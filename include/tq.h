@@ -184,12 +184,16 @@ size_t tq_attend_workspace_bytes(const tq_attn* attn);
  *   vs/vtables/vc  values: TQ_LAYOUT_TILED, no QJL
  *   q        device fp32 [batch][hq][d]
  *   sink_k/sink_v  device bf16 [batch][hkv][sink][d] (NULL iff sink == 0)
+ *   kc->cap and vc->cap must be multiples of 32.
  *   seq_lens device int32 [batch]: tokens of each sequence including the
  *            sink; compressed token t >= sink lives at cache position t-sink.
  *            Each value must lie in [0, sink + min(kc->cap, vc->cap)] and
  *            not exceed max_len.  A sequence of length 0 gives zeros.
  *   out      device fp32 [batch][hq][d]
- *   workspace device, >= tq_attend_workspace_bytes(attn) bytes
+ *   workspace device, >= tq_attend_workspace_bytes(attn) bytes; no state is
+ *            kept in it between calls
+ * Value norms must stay below 2^15 (the weighted values pass through fp16
+ * on the way into the matrix cores).
  * scores: s_t = scale * n_t * (<Pi q, c[idx_t]> + sqrt(pi/2)/m * gamma_t *
  * <S Pi q, z_t>) for compressed tokens, scale * <q, k_t> for sink tokens;
  * out = Pi_V^T sum_t w_t n^V_t c_V[idx^V_t] + sum_sink w_t v_t with w the
