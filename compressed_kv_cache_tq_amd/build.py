@@ -27,7 +27,7 @@ def hipcc() -> str:
 
 def common_flags() -> list[str]:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         "-I", os.path.join(ROOT, "include"),
         # keep the compiler from emitting packed fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -230,6 +230,32 @@ uint16_t to_half(double v) {
   return sign | static_cast<uint16_t>(((ex + 15) << 10) | (static_cast<int>(m) - 1024));
 }
 
+// bfloat16 from a double, round to nearest even (one rounding step; finite
+// values below the overflow threshold).
+uint16_t to_bf16(double v) {
+  if (v == 0.0) return std::signbit(v) ? 0x8000u : 0u;
+  const uint16_t sign = std::signbit(v) ? 0x8000u : 0u;
+  const double a = std::fabs(v);
+  int e;
+  std::frexp(a, &e);   // a = f 2^e, f in [0.5, 1)
+  int ex = e - 1;      // a = 1.m 2^ex
+  if (ex < -126) {     // subnormal: multiples of 2^-133
+    const double m = std::nearbyint(std::ldexp(a, 133));
+    return sign | static_cast<uint16_t>(m);
+  }
+  double m = std::nearbyint(std::ldexp(a, 7 - ex));  // in [128, 256]
+  if (m >= 256.0) { m = 128.0; ++ex; }
+  if (ex > 127) return sign | 0x7F80u;
+  return sign | static_cast<uint16_t>(((ex + 127) << 7) | (static_cast<int>(m) - 128));
+}
+
+double from_bf16(uint16_t b) {
+  const uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
 double from_half(uint16_t h) {
   const int ex = (h >> 10) & 0x1F, man = h & 0x3FF;
   double v = ex == 0 ? std::ldexp(man, -24) : std::ldexp(1024 + man, ex - 25);
@@ -349,6 +375,14 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
     rotation_build(tq::D, spec->rot_seed, m.data());
     for (int i = 0; i < tq::D; ++i)
       for (int k = 0; k < tq::D; ++k) t->pit[k * tq::D + i] = static_cast<float>(m[i * tq::D + k]);
+    for (int i = 0; i < tq::D * tq::D; ++i) {
+      const uint16_t b0 = to_bf16(m[i]);
+      const uint16_t b1 = to_bf16(m[i] - from_bf16(b0));
+      const uint16_t b2 = to_bf16(m[i] - from_bf16(b0) - from_bf16(b1));
+      t->pi_b16[0][i] = b0;
+      t->pi_b16[1][i] = b1;
+      t->pi_b16[2][i] = b2;
+    }
     for (int i = 0; i < tq::D * tq::D; ++i) {
       t->pi[i] = static_cast<float>(m[i]);
       const double v = m[i] * tq::PI_SCALE;

@@ -27,8 +27,9 @@ constexpr uint32_t TABLES_MAGIC = 0x31515454u;  // "TTQ1"
 // 256*pi, lo = fp16 of the remainder), which keeps about 22 significant bits.
 // The sketch S (qjl_m x d, row-major) is stored the same way without the 256
 // factor.  pit / sit are the transposes in fp32 (coalesced matrix-vector
-// products with one output per thread).  All arrays start on 256-byte
-// boundaries.
+// products with one output per thread).  pi_b16 splits pi itself into three
+// bf16 parts (hi, mid, lo) for the bf16 MFMA path.  All arrays start on
+// 256-byte boundaries.
 struct alignas(256) Tables {
   uint32_t magic;
   uint32_t version;
@@ -49,6 +50,7 @@ struct alignas(256) Tables {
   uint16_t s_lo[D * D];
   float pit[D * D];
   float sit[D * D];
+  uint16_t pi_b16[3][D * D];  // bf16 split of pi: hi + mid + lo keeps ~24 bits
 };
 
 constexpr float PI_SCALE = 256.0f;

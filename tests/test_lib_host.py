@@ -71,6 +71,11 @@ def _tables_view(spec):
     off += 65536
     sit = buf[off: off + 65536].view(np.float32).reshape(128, 128)
     assert np.array_equal(pit, pi.T) and np.array_equal(sit, s.T)
+    off += 65536
+    b16 = buf[off: off + 3 * 32768].view(np.uint16).reshape(3, 128, 128)
+    parts = (b16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = orot.rotation(0, 128)
+    assert np.max(np.abs(parts.sum(0) - ref)) <= 2.0 ** -24 * np.abs(ref).max()
     bnd = buf[32: 32 + 128].view(np.float32).reshape(2, 16)
     cen = buf[160: 160 + 128].view(np.float32).reshape(2, 16)
     cen16 = buf[288: 288 + 64].view(np.float16).reshape(2, 16)
@@ -80,7 +85,7 @@ def _tables_view(spec):
 def test_tables_content():
     spec = tq.Spec(4, 3, split=64, qjl_m=128)
     hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16 = _tables_view(spec)
-    assert tq.tables_bytes() == 512 + 6 * 65536
+    assert tq.tables_bytes() == 512 + 6 * 65536 + 3 * 32768
     assert hdr[0] == 0x31515454 and hdr[1] == 1 and hdr[2] == 4 and hdr[3] == 3
     ref = orot.rotation(0, 128)
     assert np.array_equal(pi, ref.astype(np.float32))
