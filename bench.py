@@ -56,9 +56,88 @@ def read_traffic(name: str):
     return float(kv["hbm_bytes_per_dispatch"])
 
 
+CALIB_BYTES = 512 << 20
+# Kernels of one bench step, by the name rocprofv3 reports, and the traffic
+# file each one's counters go to.
+STEP_KERNELS = {
+    "quantize_k": ["quantize_kernel<4, 4, 0, false, false>"],
+    "quantize_v": ["quantize_kernel<3, 3, 0, true, false>"],
+    "attend": ["prep_kernel", "split_kernel<4, 4, 3, 3, false>", "combine_kernel"],
+}
+STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0], "attend": KERNEL_SOURCES[1]}
+
+
+def _pmc_per_dispatch(run_dir: str, counter: str):
+    """{dispatch_id: (kernel_name, counter value summed over instances)} of a rocprofv3 run."""
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(run_dir, "**", "*.db"), recursive=True)
+    if len(dbs) != 1:
+        raise SystemExit(f"expected one rocprofv3 database under {run_dir}, found {len(dbs)}")
+    con = sqlite3.connect(dbs[0])
+    per = {}
+    for did, name, cname, v in con.execute(
+            "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+        if cname != counter:
+            continue
+        n, tot = per.get(did, (name, 0.0))
+        per[did] = (n, tot + float(v))
+    if not per:
+        raise SystemExit(f"no {counter} values in {dbs[0]}")
+    return per
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, command: str = "") -> int:
+    """HBM bytes per dispatch of each bench kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by the factor that maps the same counter of the
+    calibration copy onto its known CALIB_BYTES read and written."""
+    out = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _pmc_per_dispatch(run_dir, counter)
+        calib = [v for _, (n, v) in sorted(per.items()) if "neg_kernel" in n][-5:]
+        if len(calib) < 5:
+            raise SystemExit(f"{run_dir}: the calibration kernel (--copy-calibration) is missing")
+        factor = CALIB_BYTES / (1024.0 * float(np.median(calib)))
+        for key, names in STEP_KERNELS.items():
+            tot, raw = 0.0, 0.0
+            for kname in names:
+                vals = [v for n, v in per.values() if kname in n.replace("(anonymous namespace)::", "")]
+                if not vals:
+                    raise SystemExit(f"{run_dir}: no dispatch of {kname}")
+                tot += float(np.mean(vals)) * 1024.0 * factor
+                raw += float(np.mean(vals))
+            out.setdefault(key, {})[counter] = (tot, factor, raw, float(np.median(calib)))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for key, d in out.items():
+        fetch, ff, fraw, fcal = d["FETCH_SIZE"]
+        write, fw, wraw, wcal = d["WRITE_SIZE"]
+        src = STEP_SOURCES[key]
+        path = os.path.join(ROOT, "profiles", f"traffic_{key}.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic per dispatch of {', '.join(STEP_KERNELS[key])} (gqa_decode bench step),\n")
+            f.write("# from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by the factor that maps\n")
+            f.write(f"# the counter of a {CALIB_BYTES >> 20} MiB fp32 streaming kernel onto its known bytes.\n")
+            if command:
+                f.write(f"# command: {command}\n")
+            f.write(f"source = {src}\n")
+            f.write(f"source_sha256_16 = {source_hash(src)}\n")
+            f.write(f"fetch_size_kib_raw = {fraw:.1f}\n")
+            f.write(f"write_size_kib_raw = {wraw:.1f}\n")
+            f.write(f"calibration_fetch_kib_raw = {fcal:.1f}\n")
+            f.write(f"calibration_write_kib_raw = {wcal:.1f}\n")
+            f.write(f"fetch_factor = {ff:.4f}\n")
+            f.write(f"write_factor = {fw:.4f}\n")
+            f.write(f"fetch_bytes_per_dispatch = {fetch:.0f}\n")
+            f.write(f"write_bytes_per_dispatch = {write:.0f}\n")
+            f.write(f"hbm_bytes_per_dispatch = {fetch + write:.0f}\n")
+        print(open(path).read())
+    return 0
+
+
 def cpu_baseline(inp, run_codes, wl, kspec, vspec):
     """The float64 oracle on the host: decode attention over the GPU's packed
-    cache (all heads) plus quantization of a 16384-vector sample."""
+    cache (all heads, median of 3 runs) plus quantize + pack of one KV head's
+    keys (32768 vectors)."""
     from oracle import attend as oat
     from oracle import pack as opk
     from oracle import quantize as oqz
@@ -71,31 +150,34 @@ def cpu_baseline(inp, run_codes, wl, kspec, vspec):
     vs = oqz.Spec(bits_lo=vspec.bits_lo, bits_hi=vspec.bits_lo, split=128)
     kraw, kn, vraw, vn = run_codes
     T = wl.ctx
-    t0 = time.perf_counter()
-    pi = oqz.rotation_of(ks)
     G = wl.hq // wl.hkv
-    for h in range(wl.hkv):
-        kidx = opk.unpack_records(kraw[h], kspec.widths)
-        vidx = opk.unpack_tiled(vraw[h], vspec.widths, T)
-        khat = oqz.dequantize_rotated(kidx, ks)
-        vhat = oqz.dequantize_rotated(vidx, vs)
-        for g in range(G):
-            qq = inp.q[0, h * G + g].astype(np.float64)
-            oat.attend_rotated(qq, pi @ qq, khat, kn[h], vhat, vn[h], pi, scale=1 / np.sqrt(128))
-    t_dec = time.perf_counter() - t0
+    pi = oqz.rotation_of(ks)
+
+    def decode_once():
+        t0 = time.perf_counter()
+        for h in range(wl.hkv):
+            kidx = opk.unpack_records(kraw[h], kspec.widths)
+            vidx = opk.unpack_tiled(vraw[h], vspec.widths, T)
+            khat = oqz.dequantize_rotated(kidx, ks)
+            vhat = oqz.dequantize_rotated(vidx, vs)
+            for g in range(G):
+                qq = inp.q[0, h * G + g].astype(np.float64)
+                oat.attend_rotated(qq, pi @ qq, khat, kn[h], vhat, vn[h], pi, scale=1 / np.sqrt(128))
+        return time.perf_counter() - t0
+
+    t_dec = float(np.median([decode_once() for _ in range(3)]))
     dec_bytes = wl.hkv * T * (kspec_bytes(kspec) + 4 + kspec_bytes(vspec) + 4) + 2 * wl.hq * 128 * 4
-    n_q = 16384
-    xs = inp.k[0][0][:n_q].astype(np.float64)
+    xs = inp.k[0][0].astype(np.float64)
     t1 = time.perf_counter()
     qq = oqz.quantize(xs, ks)
-    opk.pack_records(qq.idx[:2048], kspec.widths)  # packing cost on a slice, scaled below
+    opk.pack_records(qq.idx, kspec.widths)
     t_q = time.perf_counter() - t1
     return {
         "value": round(dec_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"decode: full step (8 KV heads x {T} tokens, 32 q heads) on the GPU's packed cache; "
-                  f"quantize: {n_q} K vectors",
+        "sample": f"decode: full step (8 KV heads x {T} tokens, 32 q heads) on the GPU's packed cache, "
+                  f"median of 3; quantize: the {len(xs)} key vectors of KV head 0",
         "decode_seconds": round(t_dec, 3),
-        "quantize_Mvec_s": round(n_q / t_q / 1e6, 5),
+        "quantize_Mvec_s": round(len(xs) / t_q / 1e6, 5),
     }
 
 
@@ -110,7 +192,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 512 MiB fp32 streaming kernel (out = -in) 5 times; "
+                         "its byte counts calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, with --copy-calibration) into profiles/traffic_*.txt")
+    ap.add_argument("--command", default="", help="command line recorded by --traffic-summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary, command=args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); every box here has a single "
               f"MI355X and this path is not sharded across GPUs.", file=sys.stderr)
@@ -208,6 +299,13 @@ def main() -> int:
         "quantize_us": {"k": round(qk_ms.mean() * 1e3, 2), "v": round(qv_ms.mean() * 1e3, 2)},
         "roofline": roofline, "roofline_attend": roofline_attend,
     }
+    if args.copy_calibration:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         a = (args.warmup + args.steps) % COPIES
         nb_k, nb_v = tq.cache_code_bytes(kspec, T), tq.cache_code_bytes(vspec, T)
