@@ -62,7 +62,7 @@ CALIB_BYTES = 512 << 20
 STEP_KERNELS = {
     "quantize_k": ["quantize_kernel<4, 4, 0, false, false>"],
     "quantize_v": ["quantize_kernel<3, 3, 0, true, false>"],
-    "attend": ["prep_kernel", "split_kernel<4, 4, 3, 3, false>", "combine_kernel"],
+    "attend": ["attend_kernel<4, 4, 3, 3, false>"],
 }
 STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0], "attend": KERNEL_SOURCES[1]}
 
@@ -225,7 +225,7 @@ def main() -> int:
     q = torch.from_numpy(inp.q).cuda()
     lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
-    ws = torch.empty(tq.attend_workspace_bytes(B, Hq, Hkv, 0, T) // 4 + 4, dtype=torch.float32, device="cuda")
+    ws = tq.alloc_attend_workspace(B, Hq, Hkv, 0, T)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -283,7 +283,7 @@ def main() -> int:
     att_traffic = read_traffic("attend")
     roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
-                       "kernel": "prep + split_kernel<4,4,3,3> + combine (one decode step)",
+                       "kernel": "attend_kernel<4,4,3,3> (one fused decode step)",
                        "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms.mean() * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(dec_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -7,19 +7,21 @@
 // to Share!": item 1 (the first ~128 tokens stay uncompressed) and item 3
 // (value dequantization is skipped when the attention weight is below 1e-6).
 //
-// Three launches on one stream:
-//  prep    one workgroup per (sequence, query head): q~ = Pi_K q (times
-//          scale*log2 e) and u = S q~, scaled by a power of two and split
-//          into fp16 hi + lo, written in exactly the register layout the
-//          split kernel's MFMA reads;
-//  split   one workgroup (8 waves) per (split, kv head, sequence).  Each wave
-//          streams 32-token tiles with two tiles prefetched into registers:
-//          K records -> LUT dequantization -> scores on MFMA for all query
-//          heads of the group -> online softmax -> V tiles (coordinate-major
-//          sub-blocks) -> P V on MFMA in the rotated domain.  The waves merge
-//          in LDS and write one partial (m, l, acc[128]) per query head;
-//  combine per query head: log-sum-exp merge of the splits and the raw bf16
-//          sink tokens, one inverse rotation Pi_V^T, normalisation.
+// One launch, one workgroup of 8 waves per (split, kv head, sequence):
+//  prologue  the workgroup rotates the query heads of its group, q~ = Pi_K q
+//            (times scale * log2 e), and u = S q~, then scales each head by a
+//            power of two and splits it into fp16 hi + lo, straight into the
+//            register layout of the score MFMA's A operand;
+//  stream    each wave streams 32-token tiles with one or two tiles
+//            prefetched into registers: K records -> LUT dequantization ->
+//            scores on MFMA for all query heads of the group -> online
+//            softmax -> V tiles (coordinate-major sub-blocks) -> P V on MFMA
+//            in the rotated domain.  The waves merge in LDS and write one
+//            partial (m, l, acc[128]) per query head;
+//  combine   the last workgroup of a (sequence, kv head) to finish, found with
+//            a counter in the workspace that it resets to zero, merges the
+//            partials and the raw bf16 sink tokens (log-sum-exp), applies one
+//            inverse rotation Pi_V^T per query head and normalises.
 //
 // Codebook LUTs: entry e of width B maps two codes to their two fp16
 // centroids.  The centroids depend only on (d, B), so one LUT per width
@@ -39,12 +41,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int SW = 8;          // waves per split workgroup
 constexpr int ST = 64 * SW;    // threads per split workgroup
 constexpr int PART = 132;      // floats per partial: m, l, 2 pad, acc[128]
+constexpr int GMAX = 16;       // query heads per kv head
+constexpr int MAX_SINK = 512;  // raw sink tokens per sequence
+constexpr int MAX_SPLIT = 512; // splits per (sequence, kv head)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float QJL_C = 1.2533141373155003f / QJL_M;  // sqrt(pi/2) / m
-// prep output per kv stream: q fragments [4 ks][hi, lo][64 lanes] uint4,
-// u fragments likewise, then qinv[16], uinv[16]
-constexpr int PREP_FRAG = 4 * 2 * 64 * 16;
-constexpr int PREP_BYTES = 2 * PREP_FRAG + 128;
 
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -78,6 +79,15 @@ struct LutPlan {
   static constexpr int off() { return B == 4 ? off4 : B == 3 ? off3 : off2; }
 };
 
+// Stores and loads of the split partials, coherent across the XCDs' L2s
+// without a whole-cache write-back.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
 }
@@ -97,94 +107,6 @@ __device__ __forceinline__ half8 dequant8(const uint32_t* w, int k, const uint8_
     for (int p = 0; p < 4; ++p) a[p] = (((v >> (2 * B * p)) & M) << 8) | lane4;
   }
   return as_half8(lds_u32(lut, a[0]), lds_u32(lut, a[1]), lds_u32(lut, a[2]), lds_u32(lut, a[3]));
-}
-
-// ---------------------------------------------------------------------------
-// prep: one block of 256 threads per (sequence, query head).  Thread (i, hf)
-// produces rotated coordinate i from inputs [64 hf, 64 hf + 64); every load
-// it needs (its slice of the transposed rotation and sketch, the query) is
-// issued before any arithmetic.
-__global__ __launch_bounds__(256) void prep_kernel(const Tables* __restrict__ ktab, const float* __restrict__ q,
-                                                   uint8_t* __restrict__ prep, int hq, int hkv, float qscale,
-                                                   int qjl) {
-  __shared__ float qraw[D];
-  __shared__ float part[2][D];
-  __shared__ float qrot[D];
-  __shared__ float urot[D];
-  __shared__ int shx[2];
-  const int bh = blockIdx.x, b = bh / hq, h = bh % hq, G = hq / hkv, kh = h / G, n = h % G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = tid & (D - 1), hf = tid >> 7;
-  float w[64], ws[64];
-#pragma unroll
-  for (int k = 0; k < 64; ++k) w[k] = ktab->pit[(64 * hf + k) * D + i];
-  if (qjl) {
-#pragma unroll
-    for (int k = 0; k < 64; ++k) ws[k] = ktab->sit[(64 * hf + k) * D + i];
-  }
-  if (tid < D) qraw[tid] = q[static_cast<int64_t>(bh) * D + tid];
-  __syncthreads();
-  auto dot64 = [&](const float (&m)[64], const float* src) {
-    const float4* v4 = reinterpret_cast<const float4*>(src + 64 * hf);
-    float a = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float4 x = v4[k];
-      a = fmaf(m[4 * k], x.x, a);
-      a = fmaf(m[4 * k + 1], x.y, a);
-      a = fmaf(m[4 * k + 2], x.z, a);
-      a = fmaf(m[4 * k + 3], x.w, a);
-    }
-    return a;
-  };
-  part[hf][i] = dot64(w, qraw);
-  __syncthreads();
-  if (tid < D) qrot[tid] = (part[0][tid] + part[1][tid]) * qscale;
-  __syncthreads();
-  if (qjl) {
-    part[hf][i] = dot64(ws, qrot);
-    __syncthreads();
-    if (tid < D) urot[tid] = part[0][tid] + part[1][tid];
-    __syncthreads();
-  }
-  // power-of-two scale so that |value| * 2^sh < 2^14 (wave 0: q~, wave 1: u)
-  if (wave < (qjl ? 2 : 1)) {
-    const float* v = wave ? urot : qrot;
-    float m = fmaxf(fabsf(v[lane]), fabsf(v[lane + 64]));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    int ex = 0;
-    if (m > 0.0f) frexpf(m, &ex);
-    if (lane == 0) shx[wave] = 14 - ex;
-  }
-  __syncthreads();
-  // fragments of lanes l with l & 15 == n: (ks, hilo, j) -> lane l = 16 j + n,
-  // coordinates 32 j + 8 ks + e
-  uint8_t* dst = prep + (static_cast<int64_t>(b) * hkv + kh) * PREP_BYTES;
-  if (tid < (qjl ? 64 : 32)) {
-    const int which = tid >> 5, c = tid & 31, ks = c >> 3, hl = (c >> 2) & 1, j = c & 3;
-    const float* v = which ? urot : qrot;
-    const int sh = shx[which];
-    uint32_t wv[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      _Float16 hv[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float x = ldexpf(v[32 * j + 8 * ks + e + u], sh);
-        const _Float16 hi = static_cast<_Float16>(x);
-        hv[u] = hl ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
-      }
-      wv[e >> 1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[0])) |
-                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[1])) << 16);
-    }
-    reinterpret_cast<uint4*>(dst + which * PREP_FRAG)[(ks * 2 + hl) * 64 + 16 * j + n] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
-  if (tid == 64) {
-    float* inv = reinterpret_cast<float*>(dst + 2 * PREP_FRAG);
-    inv[n] = ldexpf(1.0f, -shx[0]);
-    inv[16 + n] = qjl ? ldexpf(QJL_C, -shx[1]) : 0.0f;
-  }
 }
 
 // Registers of one 32-token tile for one lane (prefetched one tile ahead).
@@ -246,25 +168,35 @@ __device__ __forceinline__ float f4get(const float4 (&v)[2], int e) {
   return k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
 }
 
-// Split kernel: one workgroup of 8 waves per (split, kv head, sequence).
+// The fused kernel: one workgroup of 8 waves per (split, kv head, sequence).
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-__global__ __launch_bounds__(ST, 1) void split_kernel(
+__global__ __launch_bounds__(ST, 1) void attend_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
     const uint8_t* __restrict__ ksigns, const float* __restrict__ krn, int64_t kcap,
     const Tables* __restrict__ vtab, const uint8_t* __restrict__ vcodes, const float* __restrict__ vnorms,
-    int64_t vcap, const int32_t* __restrict__ seq_lens, const uint8_t* __restrict__ prep,
-    float* __restrict__ parts, int hq, int hkv, int sink, int n_split, int64_t chunk, float v_skip) {
+    int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q,
+    const uint16_t* __restrict__ sink_k, const uint16_t* __restrict__ sink_v, float* __restrict__ parts,
+    uint32_t* __restrict__ counters, float* __restrict__ out, int hq, int hkv, int sink, int n_split,
+    int64_t chunk, float v_skip, float qscale) {
   using LP = LutPlan<KLO, KHI, VLO, VHI>;
   constexpr int KBYTES = 8 * (KLO + KHI);
   constexpr int VBYTES = 8 * (VLO + VHI);
+  // LDS: [LUTs | query prologue] while streaming, then reused by the wave
+  // merge and by the combine.
+  constexpr int PRO_OFF = (LP::bytes + 255) / 256 * 256;
+  constexpr int PRO = (GMAX * D + 4 * GMAX * D + GMAX * D + (QJL ? GMAX * D : 0) + 2 * GMAX) * 4;
   constexpr int MRG = SW * 16 * (D + 2) * 4;
-  constexpr int SMEM = LP::bytes > MRG ? LP::bytes : MRG;
+  constexpr int CMB = (2 * GMAX * MAX_SPLIT + GMAX * MAX_SINK + 2 * GMAX * D + GMAX * 4 * D + GMAX) * 4;
+  constexpr int SMEM = (PRO_OFF + PRO > MRG ? PRO_OFF + PRO : MRG) > CMB ? (PRO_OFF + PRO > MRG ? PRO_OFF + PRO : MRG)
+                                                                          : CMB;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ uint32_t lutz[4];
+  __shared__ int last_flag;
 
   const int split = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int G = hq / hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
   const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
   const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
@@ -281,33 +213,24 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   const uint32_t* zb = QJL ? reinterpret_cast<const uint32_t*>(ksigns) + stream * kcap * (QJL_M / 32) : nullptr;
   const float* rnb = QJL ? krn + stream * kcap : nullptr;
 
-  // First tile's loads go out before the LUT build.
+  // First tile's loads go out before anything else.
   TileRegs cur;
   uint32_t t0 = t_begin + 32 * wave;
   if (t0 < t_end) load_tile<KLO, KHI, VLO, VHI, QJL>(cur, t0, n, j, kbase, vbase, knb, vnb, zb, rnb);
 
-  // query fragments from the prep kernel
-  const uint8_t* pq = prep + stream * PREP_BYTES;
-  half8 qh[4], ql[4], uh[QJL ? 4 : 1], ul[QJL ? 4 : 1];
+  // ---- prologue: rotate the group's queries.  Thread (pi_i, kq) forms the
+  // partial dot of rotated coordinate pi_i over inputs [32 kq, 32 kq + 32).
+  float* qraw = reinterpret_cast<float*>(smem + PRO_OFF);  // [GMAX][D]
+  float* ppart = qraw + GMAX * D;                            // [4][GMAX][D]
+  float* qrot = ppart + 4 * GMAX * D;                        // [GMAX][D]
+  float* urot = qrot + GMAX * D;                             // [GMAX][D] (QJL)
+  int* shx = reinterpret_cast<int*>(urot + (QJL ? GMAX * D : 0));  // [2][GMAX]
+  const float* qg = q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D;
+  if (tid < G * (D / 4)) reinterpret_cast<float4*>(qraw)[tid] = reinterpret_cast<const float4*>(qg)[tid];
+  const int pi_i = tid & (D - 1), kq = tid >> 7;
+  float w[32];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    qh[ks] = __builtin_bit_cast(half8, reinterpret_cast<const uint4*>(pq)[(ks * 2 + 0) * 64 + lane]);
-    ql[ks] = __builtin_bit_cast(half8, reinterpret_cast<const uint4*>(pq)[(ks * 2 + 1) * 64 + lane]);
-    if constexpr (QJL) {
-      uh[ks] = __builtin_bit_cast(half8, reinterpret_cast<const uint4*>(pq + PREP_FRAG)[(ks * 2 + 0) * 64 + lane]);
-      ul[ks] = __builtin_bit_cast(half8, reinterpret_cast<const uint4*>(pq + PREP_FRAG)[(ks * 2 + 1) * 64 + lane]);
-    }
-  }
-  const bool head_ok = n < G;
-  if (!head_ok) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      qh[ks] = ql[ks] = half8{};
-      if constexpr (QJL) uh[ks] = ul[ks] = half8{};
-    }
-  }
-  const float qinv = head_ok ? reinterpret_cast<const float*>(pq + 2 * PREP_FRAG)[n] : 0.0f;
-  const float uinv = (QJL && head_ok) ? reinterpret_cast<const float*>(pq + 2 * PREP_FRAG)[16 + n] : 0.0f;
+  for (int k = 0; k < 32; ++k) w[k] = ktab->pit[(32 * kq + k) * D + pi_i];
 
   // replicated pair LUTs: entry e of width B at off_B + e*256 + replica*4
   auto build_lut = [&](auto bw) {
@@ -330,6 +253,84 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   if (threadIdx.x < 4)
     lutz[threadIdx.x] = ((threadIdx.x & 1) ? 0x3C00u : 0xBC00u) | (((threadIdx.x >> 1) & 1) ? 0x3C000000u : 0xBC000000u);
   __syncthreads();
+
+  auto partial_dots = [&](const float (&m)[32], const float* src) {
+    for (int g = 0; g < G; ++g) {
+      const float4* v4 = reinterpret_cast<const float4*>(src + g * D + 32 * kq);
+      float a = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 x = v4[k];
+        a = fmaf(m[4 * k], x.x, a);
+        a = fmaf(m[4 * k + 1], x.y, a);
+        a = fmaf(m[4 * k + 2], x.z, a);
+        a = fmaf(m[4 * k + 3], x.w, a);
+      }
+      ppart[(kq * GMAX + g) * D + pi_i] = a;
+    }
+  };
+  auto reduce_parts = [&](float* dst, float scale) {
+    for (int idx = tid; idx < G * D; idx += ST) {
+      const int g = idx >> 7, i = idx & (D - 1);
+      dst[idx] = (ppart[(0 * GMAX + g) * D + i] + ppart[(1 * GMAX + g) * D + i] + ppart[(2 * GMAX + g) * D + i] +
+                  ppart[(3 * GMAX + g) * D + i]) * scale;
+    }
+  };
+  partial_dots(w, qraw);
+  __syncthreads();
+  reduce_parts(qrot, qscale);
+  if constexpr (QJL) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) w[k] = ktab->sit[(32 * kq + k) * D + pi_i];
+    __syncthreads();
+    partial_dots(w, qrot);
+    __syncthreads();
+    reduce_parts(urot, 1.0f);
+  }
+  __syncthreads();
+  // power-of-two scale per head so that |value| * 2^sh < 2^14
+  for (int g = wave; g < G; g += SW) {
+#pragma unroll
+    for (int which = 0; which < (QJL ? 2 : 1); ++which) {
+      const float* v = (which ? urot : qrot) + g * D;
+      float mx = fmaxf(fabsf(v[lane]), fabsf(v[lane + 64]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      int ex = 0;
+      if (mx > 0.0f) frexpf(mx, &ex);
+      if (lane == 0) shx[which * GMAX + g] = 14 - ex;
+    }
+  }
+  __syncthreads();
+  // A-operand fragments: lane (n, j) holds coordinates 32 j + 8 ks + e of
+  // query head n of the group, as fp16 hi and lo parts
+  const bool head_ok = n < G;
+  half8 qh[4], ql[4], uh[QJL ? 4 : 1], ul[QJL ? 4 : 1];
+  auto fragments = [&](const float* v, int sh, half8 (&hi)[4], half8 (&lo)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float4* src = reinterpret_cast<const float4*>(v + n * D + 32 * j + 8 * ks);
+      const float4 x0 = src[0], x1 = src[1];
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = ldexpf(xs[e], sh);
+        const _Float16 h = static_cast<_Float16>(x);
+        hi[ks][e] = head_ok ? h : static_cast<_Float16>(0.0f);
+        lo[ks][e] = head_ok ? static_cast<_Float16>(x - static_cast<float>(h)) : static_cast<_Float16>(0.0f);
+      }
+    }
+  };
+  const int shq = head_ok ? shx[n] : 0;
+  fragments(qrot, shq, qh, ql);
+  const float qinv = head_ok ? ldexpf(1.0f, -shq) : 0.0f;
+  float uinv = 0.0f;
+  if constexpr (QJL) {
+    const int shu = head_ok ? shx[GMAX + n] : 0;
+    fragments(urot, shu, uh, ul);
+    uinv = head_ok ? ldexpf(QJL_C, -shu) : 0.0f;
+  }
+
   const uint8_t* lut_klo = smem + LP::template off<KLO>();
   const uint8_t* lut_khi = smem + LP::template off<KHI>();
   const uint8_t* lut_vlo = smem + LP::template off<VLO>();
@@ -488,170 +489,221 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       }
     }
     float* part = parts + ((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * n_split + split) * PART;
-    part[4 + c] = a;
+    store_agent(part + 4 + c, a);
     if (c == 0) {
-      part[0] = M;
-      part[1] = l;
+      store_agent(part, M);
+      store_agent(part + 1, l);
     }
   }
-}
 
-// ---------------------------------------------------------------------------
-// combine: one block of 512 threads per (b, query head): log-sum-exp merge of
-// the split partials and the raw sink tokens, one inverse rotation.  Thread
-// (i, hf) handles coordinate i and a quarter hf of every reduction; its
-// loads of the rotation column and of the first partials go out first.
-constexpr int CT = 512;
+  // ---- completion: the last workgroup of this (sequence, kv head) combines.
+  // The partials went out as agent-coherent stores (through to the memory
+  // side, visible to every XCD); each wave waits for its own before the
+  // barrier, so the counter increment follows all of them.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counters + stream, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = prev == static_cast<uint32_t>(n_split - 1);
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  if (tid == 0) __hip_atomic_store(counters + stream, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-__global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ vtab, const float* __restrict__ q,
-                                                     const uint16_t* __restrict__ sink_k,
-                                                     const uint16_t* __restrict__ sink_v,
-                                                     const int32_t* __restrict__ seq_lens,
-                                                     const float* __restrict__ parts, float* __restrict__ out,
-                                                     int hq, int hkv, int sink, int n_split, float qscale) {
-  extern __shared__ float sm[];
-  float* fs = sm;                 // [n_split] split maxima, then weights
-  float* ls = fs + n_split;       // [n_split] split sums
-  float* ssc = ls + n_split;      // [sink] sink scores, then weights
-  __shared__ float qv[D];
-  __shared__ float orot[4][D];
-  __shared__ float obuf[4][D];
-  __shared__ float red[16];
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = bh / hq, h = bh % hq, kh = h / (hq / hkv);
-  const int i = tid & (D - 1), hf = tid >> 7;
-  const int64_t L = seq_lens[b];
-  const int ns = static_cast<int>(L < sink ? L : sink);
-  const float* pp = parts + static_cast<int64_t>(bh) * n_split * PART;
-  // independent loads first: rotation column slice and the first partials
+  // Combine (one workgroup per group, run once: the code is kept compact).
+  // fw[g][s]: maximum of split s for head g, then its weight; lsp[g][s]: its
+  // sum; ssc[g][t]: sink scores, then weights; qv[g][]: scaled raw queries;
+  // rsum[g][]: rotated-domain sums; obuf[g][hf][]: output quarters.
+  const int ns_sink = static_cast<int>(L < sink ? L : sink);
+  float* fw = reinterpret_cast<float*>(smem);     // [GMAX][MAX_SPLIT]
+  float* lsp = fw + GMAX * MAX_SPLIT;             // [GMAX][MAX_SPLIT]
+  float* ssc = lsp + GMAX * MAX_SPLIT;            // [GMAX][MAX_SINK]
+  float* qv = ssc + GMAX * MAX_SINK;              // [GMAX][D]
+  float* rsum = qv + GMAX * D;                    // [GMAX][D]
+  float* obuf = rsum + GMAX * D;                  // [GMAX][4][D]
+  float* Lh = obuf + GMAX * 4 * D;                // [GMAX]
+  const int64_t head0 = static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G;
+  const float* pp = parts + head0 * n_split * PART;
+  // requested first: coordinate (tid & 127) of the first 32 splits of head
+  // (tid >> 7), the item this thread accumulates (one per thread for G <= 4)
+  constexpr int PV = 32;
+  float pv[PV];
+  const int g0 = tid >> 7, i0 = tid & (D - 1);
+  if (g0 < G) {
+#pragma unroll
+    for (int u = 0; u < PV; ++u)
+      pv[u] = u < n_split ? load_agent(pp + (static_cast<int64_t>(g0) * n_split + u) * PART + 4 + i0) : 0.0f;
+  }
+  if (ns_sink > 0)
+    for (int idx = tid; idx < G * D; idx += ST) qv[idx] = qg[idx] * qscale;
+  __syncthreads();
+  const uint16_t* sk = sink_k + stream * static_cast<int64_t>(sink) * D;
+  const uint16_t* sv = sink_v + stream * static_cast<int64_t>(sink) * D;
+  // one wave per head: maximum over splits and sink scores, then weights
+  for (int g = wave; g < G; g += SW) {
+    const float* pg = pp + static_cast<int64_t>(g) * n_split * PART;
+    float mx = -INFINITY;
+    for (int sp = lane; sp < n_split; sp += 64) {
+      const float m = load_agent(pg + sp * PART), l = load_agent(pg + sp * PART + 1);
+      const float mv = l > 0.0f ? m : -INFINITY;
+      fw[g * MAX_SPLIT + sp] = mv;
+      lsp[g * MAX_SPLIT + sp] = l;
+      mx = fmaxf(mx, mv);
+    }
+    for (int t = lane; t < ns_sink; t += 64) {
+      const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(t) * D);
+      const float* qr = qv + g * D;
+      float dot = 0.0f;
+      for (int c = 0; c < D / 8; ++c) {
+        const uint4 wv = row[c];
+        dot = fmaf(__uint_as_float(wv.x << 16), qr[8 * c], dot);
+        dot = fmaf(__uint_as_float(wv.x & 0xFFFF0000u), qr[8 * c + 1], dot);
+        dot = fmaf(__uint_as_float(wv.y << 16), qr[8 * c + 2], dot);
+        dot = fmaf(__uint_as_float(wv.y & 0xFFFF0000u), qr[8 * c + 3], dot);
+        dot = fmaf(__uint_as_float(wv.z << 16), qr[8 * c + 4], dot);
+        dot = fmaf(__uint_as_float(wv.z & 0xFFFF0000u), qr[8 * c + 5], dot);
+        dot = fmaf(__uint_as_float(wv.w << 16), qr[8 * c + 6], dot);
+        dot = fmaf(__uint_as_float(wv.w & 0xFFFF0000u), qr[8 * c + 7], dot);
+      }
+      ssc[g * MAX_SINK + t] = dot;
+      mx = fmaxf(mx, dot);
+    }
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float lsum = 0.0f;
+    for (int sp = lane; sp < n_split; sp += 64) {
+      const float mv = fw[g * MAX_SPLIT + sp];
+      const float f = mv == -INFINITY ? 0.0f : exp2f(mv - mx);
+      fw[g * MAX_SPLIT + sp] = f;
+      lsum = fmaf(f, lsp[g * MAX_SPLIT + sp], lsum);
+    }
+    for (int t = lane; t < ns_sink; t += 64) {
+      const float wt = exp2f(ssc[g * MAX_SINK + t] - mx);
+      ssc[g * MAX_SINK + t] = wt;
+      lsum += wt;
+    }
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) Lh[g] = lsum;
+  }
+  __syncthreads();
+  // rotated-domain sums: item (g, i) = sum_s w_s acc_s[i]
+  for (int idx = tid; idx < G * D; idx += ST) {
+    const int g = idx >> 7, i = idx & (D - 1);
+    const float* src = pp + static_cast<int64_t>(g) * n_split * PART + 4 + i;
+    const float* wg = fw + g * MAX_SPLIT;
+    float a = 0.0f;
+    int s0 = 0;
+    if (idx == tid) {  // first item: its first 32 splits are in pv already
+#pragma unroll
+      for (int u = 0; u < PV; ++u)
+        if (u < n_split) a = fmaf(wg[u], pv[u], a);
+      s0 = PV;
+    }
+#pragma unroll 16
+    for (int sp = s0; sp < n_split; ++sp) a = fmaf(wg[sp], load_agent(src + static_cast<int64_t>(sp) * PART), a);
+    rsum[idx] = a;
+  }
+  __syncthreads();
+  // one inverse rotation per head (+ raw sink values): thread (ci, hf) takes
+  // rotated coordinates [32 hf, 32 hf + 32) and sink tokens hf, hf + 4, ...
+  const int ci = tid & (D - 1), hf = tid >> 7;
   float pic[32];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) pic[k] = vtab->pi[(32 * hf + k) * D + i];
-  constexpr int PF = 8;
-  float pa[PF];
+  for (int k = 0; k < 32; ++k) pic[k] = vtab->pi[(32 * hf + k) * D + ci];
+  for (int g = 0; g < G; ++g) {
+    const float4* r4 = reinterpret_cast<const float4*>(rsum + g * D + 32 * hf);
+    float o = 0.0f;
 #pragma unroll
-  for (int k = 0; k < PF; ++k) {
-    const int sp = hf + 4 * k;
-    pa[k] = sp < n_split ? pp[sp * PART + 4 + i] : 0.0f;
-  }
-  if (tid < D) qv[tid] = q[static_cast<int64_t>(bh) * D + tid] * qscale;
-  float mloc = -INFINITY;
-  for (int sp = tid; sp < n_split; sp += CT) {
-    const float m = pp[sp * PART], l = pp[sp * PART + 1];
-    fs[sp] = m;
-    ls[sp] = l;
-    if (l > 0.0f) mloc = fmaxf(mloc, m);
-  }
-  __syncthreads();
-  const uint16_t* sk = sink_k + (static_cast<int64_t>(b) * hkv + kh) * sink * D;
-  const uint16_t* sv = sink_v + (static_cast<int64_t>(b) * hkv + kh) * sink * D;
-  for (int t = tid; t < ns; t += CT) {
-    const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(t) * D);
-    float dot = 0.0f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const uint4 w = row[c];
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        dot = fmaf(__uint_as_float(u[k] << 16), qv[8 * c + 2 * k], dot);
-        dot = fmaf(__uint_as_float(u[k] & 0xFFFF0000u), qv[8 * c + 2 * k + 1], dot);
-      }
+    for (int k = 0; k < 8; ++k) {
+      const float4 r = r4[k];
+      o = fmaf(pic[4 * k], r.x, o);
+      o = fmaf(pic[4 * k + 1], r.y, o);
+      o = fmaf(pic[4 * k + 2], r.z, o);
+      o = fmaf(pic[4 * k + 3], r.w, o);
     }
-    ssc[t] = dot;
-    mloc = fmaxf(mloc, dot);
+    for (int t = hf; t < ns_sink; t += 4)
+      o = fmaf(ssc[g * MAX_SINK + t], __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + ci]) << 16), o);
+    obuf[(g * 4 + hf) * D + ci] = o;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-  if (lane == 0) red[wave] = mloc;
   __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int w = 1; w < CT / 64; ++w) M = fmaxf(M, red[w]);
-  float lloc = 0.0f;
-  for (int sp = tid; sp < n_split; sp += CT) {
-    const float f = (ls[sp] > 0.0f && M != -INFINITY) ? exp2f(fs[sp] - M) : 0.0f;
-    fs[sp] = f;
-    lloc = fmaf(f, ls[sp], lloc);
-  }
-  for (int t = tid; t < ns; t += CT) {
-    const float w = exp2f(ssc[t] - M);
-    ssc[t] = w;
-    lloc += w;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
-  __syncthreads();
-  if (lane == 0) red[8 + wave] = lloc;
-  float a = 0.0f;
-#pragma unroll
-  for (int k = 0; k < PF; ++k) a = fmaf(hf + 4 * k < n_split ? fs[hf + 4 * k] : 0.0f, pa[k], a);
-  for (int sp = hf + 4 * PF; sp < n_split; sp += 4) a = fmaf(fs[sp], pp[sp * PART + 4 + i], a);
-  orot[hf][i] = a;
-  __syncthreads();
-  float Lsum = 0.0f;
-#pragma unroll
-  for (int w = 0; w < CT / 64; ++w) Lsum += red[8 + w];
-  // one inverse rotation: out_i = sum_c Pi[c][i] orot[c] (+ raw sink values)
-  float o = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int cc = 32 * hf + k;
-    o = fmaf(pic[k], orot[0][cc] + orot[1][cc] + orot[2][cc] + orot[3][cc], o);
-  }
-  for (int t = hf; t < ns; t += 4)
-    o = fmaf(ssc[t], __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + i]) << 16), o);
-  obuf[hf][i] = o;
-  __syncthreads();
-  if (tid < D) {
-    const float v = obuf[0][tid] + obuf[1][tid] + obuf[2][tid] + obuf[3][tid];
-    out[static_cast<int64_t>(bh) * D + tid] = Lsum > 0.0f ? v / Lsum : 0.0f;
+  for (int idx = tid; idx < G * D; idx += ST) {
+    const int g = idx >> 7, i = idx & (D - 1);
+    const float* og = obuf + g * 4 * D + i;
+    const float v = og[0] + og[D] + og[2 * D] + og[3 * D];
+    const float Ls = Lh[g];
+    out[head0 * D + idx] = Ls > 0.0f ? v / Ls : 0.0f;
   }
 }
 
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
-                        const tq_attn& a, const AttendPlan& plan, const int32_t* seq_lens, const uint8_t* prep,
-                        float* parts, hipStream_t st) {
-  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_split, a.hkv, a.batch), dim3(ST), 0, st,
+hipError_t launch_fused(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
+                        const tq_attn& a, const AttendPlan& plan, const float* q, const uint16_t* sink_k,
+                        const uint16_t* sink_v, const int32_t* seq_lens, float* parts, uint32_t* counters,
+                        float* out, hipStream_t st) {
+  hipLaunchKernelGGL((attend_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_split, a.hkv, a.batch), dim3(ST), 0, st,
                      ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms, vc.cap,
-                     seq_lens, prep, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.v_skip);
+                     seq_lens, q, sink_k, sink_v, parts, counters, out, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk,
+                     a.v_skip, a.scale * LOG2E);
   return hipGetLastError();
 }
 
+struct FusedArgs {
+  const Tables* ktab;
+  const tq_cache* kc;
+  const Tables* vtab;
+  const tq_cache* vc;
+  const tq_attn* a;
+  const AttendPlan* plan;
+  const float* q;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
+  const int32_t* seq_lens;
+  float* parts;
+  uint32_t* counters;
+  float* out;
+  hipStream_t st;
+};
+
+template <int KLO, int KHI, int VLO, int VHI>
+hipError_t launch_q(bool qjl, const FusedArgs& f) {
+  return qjl ? launch_fused<KLO, KHI, VLO, VHI, true>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
+                                                      f.sink_v, f.seq_lens, f.parts, f.counters, f.out, f.st)
+             : launch_fused<KLO, KHI, VLO, VHI, false>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
+                                                       f.sink_v, f.seq_lens, f.parts, f.counters, f.out, f.st);
+}
+
 template <int KLO, int KHI>
-hipError_t dispatch_v(int vkey, bool qjl, const Tables* ktab, const tq_cache& kc, const Tables* vtab,
-                      const tq_cache& vc, const tq_attn& a, const AttendPlan& plan, const int32_t* sl,
-                      const uint8_t* prep, float* parts, hipStream_t st) {
-#define TQ_V(VL, VH)                                                                                     \
-  case VL * 10 + VH:                                                                                     \
-    return qjl ? launch_split<KLO, KHI, VL, VH, true>(ktab, kc, vtab, vc, a, plan, sl, prep, parts, st)  \
-               : launch_split<KLO, KHI, VL, VH, false>(ktab, kc, vtab, vc, a, plan, sl, prep, parts, st);
+hipError_t dispatch_v(int vkey, bool qjl, const FusedArgs& f) {
   switch (vkey) {
-    TQ_V(2, 2)
-    TQ_V(3, 3)
-    TQ_V(4, 4)
-    TQ_V(4, 3)
-    TQ_V(3, 2)
+    case 22: return launch_q<KLO, KHI, 2, 2>(qjl, f);
+    case 33: return launch_q<KLO, KHI, 3, 3>(qjl, f);
+    case 44: return launch_q<KLO, KHI, 4, 4>(qjl, f);
+    case 43: return launch_q<KLO, KHI, 4, 3>(qjl, f);
+    case 32: return launch_q<KLO, KHI, 3, 2>(qjl, f);
     default: return hipErrorInvalidValue;
   }
-#undef TQ_V
 }
 
 }  // namespace
+
+size_t attend_counter_bytes(const tq_attn& a) {
+  const int64_t streams = static_cast<int64_t>(a.batch) * a.hkv;
+  return static_cast<size_t>((streams * 4 + 255) / 256 * 256);
+}
 
 AttendPlan plan_attend(const tq_attn& a) {
   AttendPlan p{};
   const int64_t streams = static_cast<int64_t>(a.batch) * a.hkv;
   const int64_t comp = a.max_len > a.sink ? a.max_len - a.sink : 0;
   const int64_t tiles = (comp + TILE - 1) / TILE;
-  // about one 8-wave workgroup per CU, and no split longer than 8192 tokens
-  // (ragged batches balance better with shorter splits)
+  // about one 8-wave workgroup per CU, no split longer than 8192 tokens
+  // (ragged batches balance better with shorter splits), at most MAX_SPLIT
   int64_t ns = streams > 0 ? (256 + streams - 1) / streams : 1;
   const int64_t by_len = (comp + 8191) / 8192;
   if (ns < by_len) ns = by_len;
   const int64_t cap_ns = (tiles + SW - 1) / SW;  // at least one tile per wave
   if (ns > cap_ns) ns = cap_ns;
+  if (ns > MAX_SPLIT) ns = MAX_SPLIT;
   if (ns < 1) ns = 1;
   int64_t chunk_tiles = (tiles + ns - 1) / ns;
   if (chunk_tiles < 1) chunk_tiles = 1;
@@ -660,7 +712,7 @@ AttendPlan plan_attend(const tq_attn& a) {
   p.n_split = static_cast<int>(ns);
   p.chunk = chunk_tiles * TILE;
   const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
-  p.ws_bytes = static_cast<size_t>(streams) * PREP_BYTES +
+  p.ws_bytes = attend_counter_bytes(a) +
                static_cast<size_t>(heads) * static_cast<int64_t>(p.n_split) * PART * sizeof(float);
   return p;
 }
@@ -669,29 +721,19 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          const tq_cache& vc, const tq_attn& a, const AttendPlan& plan, const float* q,
                          const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                          void* workspace, hipStream_t st) {
-  const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
-  const int64_t streams = static_cast<int64_t>(a.batch) * a.hkv;
-  uint8_t* prep = static_cast<uint8_t*>(workspace);
-  float* parts = reinterpret_cast<float*>(prep + streams * PREP_BYTES);
-  hipLaunchKernelGGL(prep_kernel, dim3(static_cast<unsigned>(heads)), dim3(256), 0, st, ktab, q, prep, a.hq, a.hkv,
-                     a.scale * LOG2E, ks.qjl_m ? 1 : 0);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  uint32_t* counters = static_cast<uint32_t*>(workspace);
+  float* parts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + attend_counter_bytes(a));
+  const FusedArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, counters, out, st};
   const int vkey = vs.bits_lo * 10 + vs.bits_hi;
   const bool qjl = ks.qjl_m != 0;
-  hipError_t e;
   switch (ks.bits_lo * 10 + ks.bits_hi) {
-    case 22: e = dispatch_v<2, 2>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, prep, parts, st); break;
-    case 33: e = dispatch_v<3, 3>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, prep, parts, st); break;
-    case 44: e = dispatch_v<4, 4>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, prep, parts, st); break;
-    case 43: e = dispatch_v<4, 3>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, prep, parts, st); break;
-    case 32: e = dispatch_v<3, 2>(vkey, qjl, ktab, kc, vtab, vc, a, plan, seq_lens, prep, parts, st); break;
+    case 22: return dispatch_v<2, 2>(vkey, qjl, f);
+    case 33: return dispatch_v<3, 3>(vkey, qjl, f);
+    case 44: return dispatch_v<4, 4>(vkey, qjl, f);
+    case 43: return dispatch_v<4, 3>(vkey, qjl, f);
+    case 32: return dispatch_v<3, 2>(vkey, qjl, f);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  const size_t smem = (2 * static_cast<size_t>(plan.n_split) + static_cast<size_t>(a.sink)) * sizeof(float);
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(heads)), dim3(CT), smem, st, vtab, q, sink_k, sink_v,
-                     seq_lens, parts, out, a.hq, a.hkv, a.sink, plan.n_split, a.scale * LOG2E);
-  return hipGetLastError();
 }
 
 }  // namespace tq

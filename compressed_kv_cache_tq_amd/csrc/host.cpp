@@ -478,6 +478,7 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
   if (a.hq % a.hkv) return fail(TQ_E_ARG, "hq must be a multiple of hkv");
   if (a.hq / a.hkv > 16) return fail(TQ_E_UNSUPPORTED, "at most 16 query heads per KV head");
   if (a.sink < 0 || a.max_len < 0) return fail(TQ_E_ARG, "negative sink or max_len");
+  if (a.sink > 512) return fail(TQ_E_UNSUPPORTED, "at most 512 sink tokens");
   if (!(a.v_skip >= 0.0f) || !(a.v_skip < 1.0f)) return fail(TQ_E_ARG, "v_skip must be in [0, 1)");
   if (!std::isfinite(a.scale)) return fail(TQ_E_ARG, "scale must be finite");
   if (a.batch == 0) return TQ_OK;

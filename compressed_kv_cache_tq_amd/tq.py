@@ -261,6 +261,14 @@ def quantize_kv(spec: Spec, tables, x, cache: Cache, tok0: int = 0, n_streams: i
                                 x.stride(1), tok0, ctypes.byref(cc), st), "tq_quantize_kv")
 
 
+def alloc_attend_workspace(batch: int, hq: int, hkv: int, sink: int, max_len: int, device="cuda"):
+    """Zero-filled attention workspace (tq_attend_decode needs its counters at
+    zero before the first call and leaves them at zero after every call)."""
+    torch = _torch()
+    n = attend_workspace_bytes(batch, hq, hkv, sink, max_len)
+    return torch.zeros((n + 15) // 16 * 4, dtype=torch.float32, device=device)
+
+
 def attend_decode(kspec: Spec, ktables, kcache: Cache, vspec: Spec, vtables, vcache: Cache, q, seq_lens, out,
                   workspace, *, hkv: int, sink: int = 0, sink_k=None, sink_v=None, scale: float | None = None,
                   v_skip: float = 0.0, max_len: int | None = None, stream: int | None = None) -> None:

@@ -139,8 +139,7 @@ class Run:
         self.q = t.from_numpy(np.ascontiguousarray(inp.q, dtype=np.float32)).cuda()
         self.seq_lens = t.from_numpy(lens.astype(np.int32)).cuda()
         self.out = t.empty_like(self.q)
-        ws = tq.attend_workspace_bytes(B, wl.hq, Hkv, S, self.max_len)
-        self.ws = t.empty(ws // 4 + 4, dtype=t.float32, device="cuda")
+        self.ws = tq.alloc_attend_workspace(B, wl.hq, Hkv, S, self.max_len)
 
     def quantize(self):
         wl, S = self.wl, self.wl.sink
