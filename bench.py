@@ -62,7 +62,7 @@ CALIB_BYTES = 512 << 20
 STEP_KERNELS = {
     "quantize_k": ["quantize_kernel<4, 4, 0, false, false>"],
     "quantize_v": ["quantize_kernel<3, 3, 0, true, false>"],
-    "attend": ["attend_kernel<4, 4, 3, 3, false>"],
+    "attend": ["split_kernel<4, 4, 3, 3, false>", "combine_kernel"],
 }
 STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0], "attend": KERNEL_SOURCES[1]}
 
@@ -283,7 +283,7 @@ def main() -> int:
     att_traffic = read_traffic("attend")
     roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
-                       "kernel": "attend_kernel<4,4,3,3> (one fused decode step)",
+                       "kernel": "split_kernel<4,4,3,3> + combine_kernel (one decode step)",
                        "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms.mean() * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(dec_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

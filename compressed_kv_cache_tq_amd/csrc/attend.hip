@@ -7,21 +7,21 @@
 // to Share!": item 1 (the first ~128 tokens stay uncompressed) and item 3
 // (value dequantization is skipped when the attention weight is below 1e-6).
 //
-// One launch, one workgroup of 8 waves per (split, kv head, sequence):
-//  prologue  the workgroup rotates the query heads of its group, q~ = Pi_K q
-//            (times scale * log2 e), and u = S q~, then scales each head by a
-//            power of two and splits it into fp16 hi + lo, straight into the
-//            register layout of the score MFMA's A operand;
-//  stream    each wave streams 32-token tiles with one or two tiles
-//            prefetched into registers: K records -> LUT dequantization ->
-//            scores on MFMA for all query heads of the group -> online
-//            softmax -> V tiles (coordinate-major sub-blocks) -> P V on MFMA
-//            in the rotated domain.  The waves merge in LDS and write one
-//            partial (m, l, acc[128]) per query head;
-//  combine   the last workgroup of a (sequence, kv head) to finish, found with
-//            a counter in the workspace that it resets to zero, merges the
-//            partials and the raw bf16 sink tokens (log-sum-exp), applies one
-//            inverse rotation Pi_V^T per query head and normalises.
+// Two launches on one stream:
+//  split    one workgroup of 8 waves per (split, kv head, sequence).
+//           Prologue: the workgroup rotates the query heads of its group,
+//           q~ = Pi_K q (times scale * log2 e), and u = S q~, scales each
+//           head by a power of two and splits it into fp16 hi + lo, straight
+//           into the register layout of the score MFMA's A operand.  Stream:
+//           each wave streams 32-token tiles with one tile prefetched into
+//           registers: K records -> LUT dequantization -> scores on MFMA for
+//           all query heads of the group -> online softmax -> V tiles
+//           (coordinate-major sub-blocks) -> P V on MFMA in the rotated
+//           domain.  The waves merge in LDS and write one partial
+//           (m, l, acc[128]) per query head;
+//  combine  one workgroup per (sequence, query head, output slice):
+//           log-sum-exp merge of the partials and the raw bf16 sink tokens,
+//           the slice of one inverse rotation Pi_V^T, normalisation.
 //
 // Codebook LUTs: entry e of width B maps two codes to their two fp16
 // centroids.  The centroids depend only on (d, B), so one LUT per width
@@ -78,15 +78,6 @@ struct LutPlan {
   template <int B>
   static constexpr int off() { return B == 4 ? off4 : B == 3 ? off3 : off2; }
 };
-
-// Stores and loads of the split partials, coherent across the XCDs' L2s
-// without a whole-cache write-back.
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
@@ -168,31 +159,26 @@ __device__ __forceinline__ float f4get(const float4 (&v)[2], int e) {
   return k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
 }
 
-// The fused kernel: one workgroup of 8 waves per (split, kv head, sequence).
+// Split kernel: one workgroup of 8 waves per (split, kv head, sequence).
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-__global__ __launch_bounds__(ST, 1) void attend_kernel(
+__global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
     const uint8_t* __restrict__ ksigns, const float* __restrict__ krn, int64_t kcap,
     const Tables* __restrict__ vtab, const uint8_t* __restrict__ vcodes, const float* __restrict__ vnorms,
-    int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q,
-    const uint16_t* __restrict__ sink_k, const uint16_t* __restrict__ sink_v, float* __restrict__ parts,
-    uint32_t* __restrict__ counters, float* __restrict__ out, int hq, int hkv, int sink, int n_split,
-    int64_t chunk, float v_skip, float qscale) {
+    int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q, float* __restrict__ parts,
+    int hq, int hkv, int sink, int n_split, int64_t chunk, float v_skip, float qscale) {
   using LP = LutPlan<KLO, KHI, VLO, VHI>;
   constexpr int KBYTES = 8 * (KLO + KHI);
   constexpr int VBYTES = 8 * (VLO + VHI);
   // LDS: [LUTs | query prologue] while streaming, then reused by the wave
-  // merge and by the combine.
+  // merge.
   constexpr int PRO_OFF = (LP::bytes + 255) / 256 * 256;
   constexpr int PRO = (GMAX * D + 4 * GMAX * D + GMAX * D + (QJL ? GMAX * D : 0) + 2 * GMAX) * 4;
   constexpr int MRG = SW * 16 * (D + 2) * 4;
-  constexpr int CMB = (2 * GMAX * MAX_SPLIT + GMAX * MAX_SINK + 2 * GMAX * D + GMAX * 4 * D + GMAX) * 4;
-  constexpr int SMEM = (PRO_OFF + PRO > MRG ? PRO_OFF + PRO : MRG) > CMB ? (PRO_OFF + PRO > MRG ? PRO_OFF + PRO : MRG)
-                                                                          : CMB;
+  constexpr int SMEM = PRO_OFF + PRO > MRG ? PRO_OFF + PRO : MRG;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ uint32_t lutz[4];
-  __shared__ int last_flag;
 
   const int split = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int G = hq / hkv;
@@ -336,18 +322,24 @@ __global__ __launch_bounds__(ST, 1) void attend_kernel(
   const uint8_t* lut_vlo = smem + LP::template off<VLO>();
   const uint8_t* lut_vhi = smem + LP::template off<VHI>();
 
+  // Online softmax state per query head (replicated over its 4 token lanes).
+  // The running maximum is kept lazily: it only moves when a score exceeds it
+  // by more than RESCALE_SLACK, so probabilities stay below 2^0.5 and most
+  // tiles skip the accumulator rescale.
+  constexpr float RESCALE_SLACK = 0.5f;
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f32x4{};
+  const bool vskip_on = v_skip > 0.0f;
 
-  auto tile_step = [&]<bool FULL>(const TileRegs& tr, uint32_t t0c) {
+  auto tile_step = [&]<bool FULL, bool VSKIP>(const TileRegs& tr, uint32_t t0c) {
     const int nvalid = FULL ? 8 : static_cast<int>(t_end) - static_cast<int>(t0c + 8 * j);
-    // four independent accumulator chains (M-block x hi/lo) keep the matrix
-    // pipe busy; hi and lo partial dots are added afterwards
-    f32x4 sk[2], sl[2], sz[2], szl[2];
+    // two accumulator chains per M-block: hi and lo query parts accumulate
+    // into one; the QJL sign products into another
+    f32x4 sk[2], sz[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) sk[mb] = sl[mb] = sz[mb] = szl[mb] = f32x4{};
+    for (int mb = 0; mb < 2; ++mb) sk[mb] = sz[mb] = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       half8 a[2];
@@ -358,8 +350,6 @@ __global__ __launch_bounds__(ST, 1) void attend_kernel(
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], qh[ks], sk[mb]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) sl[mb] = mfma16(a[mb], ql[ks], sl[mb]);
       if constexpr (QJL) {
         half8 z[2];
 #pragma unroll
@@ -370,7 +360,12 @@ __global__ __launch_bounds__(ST, 1) void attend_kernel(
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], uh[ks], sz[mb]);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) szl[mb] = mfma16(z[mb], ul[ks], szl[mb]);
+        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], ql[ks], sk[mb]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], ul[ks], sz[mb]);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], ql[ks], sk[mb]);
       }
     }
     float s[8];
@@ -380,27 +375,39 @@ __global__ __launch_bounds__(ST, 1) void attend_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * mb + i;
-        float dot = (sk[mb][i] + sl[mb][i]) * qinv;
-        if constexpr (QJL) dot = fmaf(f4get(tr.rn, e) * (sz[mb][i] + szl[mb][i]), uinv, dot);
+        float dot = sk[mb][i] * qinv;
+        if constexpr (QJL) dot = fmaf(f4get(tr.rn, e) * sz[mb][i], uinv, dot);
         s[e] = f4get(tr.kn, e) * dot;
         if constexpr (!FULL) s[e] = e < nvalid ? s[e] : -INFINITY;
         tmax = fmaxf(tmax, s[e]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
-    m_run = m_new;
+    // rescale only when some head's maximum grew past the slack
+    if (__any(tmax > m_run + RESCALE_SLACK)) {
+      const float m_new = tmax > m_run + RESCALE_SLACK ? tmax : m_run;
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * j + i);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k][i] *= ai;
+      }
+    }
     float psum = 0.0f;
     uint32_t pw[4];
-    bool any = false;
+    bool any = !VSKIP;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      float p0 = exp2f(s[e] - m_new), p1 = exp2f(s[e + 1] - m_new);
-      if (p0 < v_skip) p0 = 0.0f;
-      if (p1 < v_skip) p1 = 0.0f;
+      float p0 = __builtin_amdgcn_exp2f(s[e] - m_run), p1 = __builtin_amdgcn_exp2f(s[e + 1] - m_run);
+      if constexpr (VSKIP) {
+        if (p0 < v_skip) p0 = 0.0f;
+        if (p1 < v_skip) p1 = 0.0f;
+        any |= (p0 > 0.0f) | (p1 > 0.0f);
+      }
       psum += p0 + p1;
-      any |= (p0 > 0.0f) | (p1 > 0.0f);
       float v0 = f4get(tr.vn, e), v1 = f4get(tr.vn, e + 1);
       if constexpr (!FULL) {
         v0 = e < nvalid ? v0 : 0.0f;
@@ -410,18 +417,9 @@ __global__ __launch_bounds__(ST, 1) void attend_kernel(
       pw[e >> 1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
                    (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
     }
-    l_run = l_run * alpha + psum;
-    // rescale the accumulator rows (query heads 4j + i) only when a maximum moved
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * j + i);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k][i] *= ai;
-      }
-    }
+    l_run += psum;
     // skip the value work of a tile whose weights all fell below v_skip
-    if (__any(any && head_ok)) {
+    if (!VSKIP || __any(any && head_ok)) {
       const half8 pa = as_half8(pw[0], pw[1], pw[2], pw[3]);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
@@ -433,15 +431,20 @@ __global__ __launch_bounds__(ST, 1) void attend_kernel(
     }
   };
 
-  // Tiles in flight per wave: three where the registers allow it (the
-  // buffers rotate through fixed roles), else two.
+  // Tiles in flight per wave: two (the buffers swap roles each tile); the
+  // three-deep variant is kept for register-light instances.
   constexpr uint32_t STEP = 32 * SW;
-  constexpr int DEPTH = (!QJL && KLO == KHI && VLO == VHI) ? 3 : 2;
+  constexpr int DEPTH = 2;
   auto run = [&](TileRegs& compute, TileRegs& refill, uint32_t ahead) -> bool {
     if (t0 >= t_end) return false;
     if (t0 + ahead < t_end) load_tile<KLO, KHI, VLO, VHI, QJL>(refill, t0 + ahead, n, j, kbase, vbase, knb, vnb, zb, rnb);
-    if (t0 + 32 <= t_end) tile_step.template operator()<true>(compute, t0);
-    else tile_step.template operator()<false>(compute, t0);
+    if (vskip_on) {
+      if (t0 + 32 <= t_end) tile_step.template operator()<true, true>(compute, t0);
+      else tile_step.template operator()<false, true>(compute, t0);
+    } else {
+      if (t0 + 32 <= t_end) tile_step.template operator()<true, false>(compute, t0);
+      else tile_step.template operator()<false, false>(compute, t0);
+    }
     t0 += STEP;
     return true;
   };
@@ -483,171 +486,186 @@ __global__ __launch_bounds__(ST, 1) void attend_kernel(
 #pragma unroll
       for (int w = 0; w < SW; ++w) {
         const float mw = mrg_m[w * 16 + g];
-        const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+        const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
         a = fmaf(f, mrg_acc[(w * 16 + g) * D + c], a);
         l = fmaf(f, mrg_l[w * 16 + g], l);
       }
     }
     float* part = parts + ((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * n_split + split) * PART;
-    store_agent(part + 4 + c, a);
+    part[4 + c] = a;
     if (c == 0) {
-      store_agent(part, M);
-      store_agent(part + 1, l);
+      part[0] = M;
+      part[1] = l;
     }
   }
 
-  // ---- completion: the last workgroup of this (sequence, kv head) combines.
-  // The partials went out as agent-coherent stores (through to the memory
-  // side, visible to every XCD); each wave waits for its own before the
-  // barrier, so the counter increment follows all of them.
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counters + stream, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = prev == static_cast<uint32_t>(n_split - 1);
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  if (tid == 0) __hip_atomic_store(counters + stream, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-  // Combine (one workgroup per group, run once: the code is kept compact).
-  // fw[g][s]: maximum of split s for head g, then its weight; lsp[g][s]: its
-  // sum; ssc[g][t]: sink scores, then weights; qv[g][]: scaled raw queries;
-  // rsum[g][]: rotated-domain sums; obuf[g][hf][]: output quarters.
-  const int ns_sink = static_cast<int>(L < sink ? L : sink);
-  float* fw = reinterpret_cast<float*>(smem);     // [GMAX][MAX_SPLIT]
-  float* lsp = fw + GMAX * MAX_SPLIT;             // [GMAX][MAX_SPLIT]
-  float* ssc = lsp + GMAX * MAX_SPLIT;            // [GMAX][MAX_SINK]
-  float* qv = ssc + GMAX * MAX_SINK;              // [GMAX][D]
-  float* rsum = qv + GMAX * D;                    // [GMAX][D]
-  float* obuf = rsum + GMAX * D;                  // [GMAX][4][D]
-  float* Lh = obuf + GMAX * 4 * D;                // [GMAX]
-  const int64_t head0 = static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G;
-  const float* pp = parts + head0 * n_split * PART;
-  // requested first: coordinate (tid & 127) of the first 32 splits of head
-  // (tid >> 7), the item this thread accumulates (one per thread for G <= 4)
-  constexpr int PV = 32;
-  float pv[PV];
-  const int g0 = tid >> 7, i0 = tid & (D - 1);
-  if (g0 < G) {
-#pragma unroll
-    for (int u = 0; u < PV; ++u)
-      pv[u] = u < n_split ? load_agent(pp + (static_cast<int64_t>(g0) * n_split + u) * PART + 4 + i0) : 0.0f;
-  }
-  if (ns_sink > 0)
-    for (int idx = tid; idx < G * D; idx += ST) qv[idx] = qg[idx] * qscale;
-  __syncthreads();
+// ---------------------------------------------------------------------------
+// combine: one workgroup of 256 threads per (sequence, query head, output
+// slice of 128 / NQ coordinates): log-sum-exp merge of the split partials
+// and the raw bf16 sink tokens, and the slice of the inverse rotation
+// Pi_V^T.  Many small workgroups keep the loads spread over many CUs, and
+// every global load is issued before the first barrier.
+constexpr int CT = 256;
+
+template <int NQ>
+__global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ vtab, const float* __restrict__ q,
+                                                     const uint16_t* __restrict__ sink_k,
+                                                     const uint16_t* __restrict__ sink_v,
+                                                     const int32_t* __restrict__ seq_lens,
+                                                     const float* __restrict__ parts, float* __restrict__ out,
+                                                     int hq, int hkv, int sink, int n_split, float qscale) {
+  constexpr int OW = D / NQ;         // output coordinates of this workgroup
+  constexpr int CQ = CT / OW;        // rotated-coordinate chunks
+  constexpr int CK = D / CQ;         // rotated coordinates per chunk
+  __shared__ float wsp[MAX_SPLIT];   // split maxima, then weights
+  __shared__ float lsp[MAX_SPLIT];   // split sums
+  __shared__ float ssc[MAX_SINK];    // sink scores, then weights
+  __shared__ float qv[D];
+  __shared__ float rs[2][D];         // rotated-domain sums (two split halves)
+  __shared__ float ob[CQ][OW];
+  __shared__ float red[8];
+  const int bh = blockIdx.x / NQ, qo = blockIdx.x % NQ;
+  const int b = bh / hq, h = bh % hq, kh = h / (hq / hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* pp = parts + static_cast<int64_t>(bh) * n_split * PART;
+  const int64_t L = seq_lens[b];
+  const int ns = static_cast<int>(L < sink ? L : sink);
+  const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
   const uint16_t* sk = sink_k + stream * static_cast<int64_t>(sink) * D;
   const uint16_t* sv = sink_v + stream * static_cast<int64_t>(sink) * D;
-  // one wave per head: maximum over splits and sink scores, then weights
-  for (int g = wave; g < G; g += SW) {
-    const float* pg = pp + static_cast<int64_t>(g) * n_split * PART;
-    float mx = -INFINITY;
-    for (int sp = lane; sp < n_split; sp += 64) {
-      const float m = load_agent(pg + sp * PART), l = load_agent(pg + sp * PART + 1);
-      const float mv = l > 0.0f ? m : -INFINITY;
-      fw[g * MAX_SPLIT + sp] = mv;
-      lsp[g * MAX_SPLIT + sp] = l;
-      mx = fmaxf(mx, mv);
-    }
-    for (int t = lane; t < ns_sink; t += 64) {
-      const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(t) * D);
-      const float* qr = qv + g * D;
-      float dot = 0.0f;
-      for (int c = 0; c < D / 8; ++c) {
-        const uint4 wv = row[c];
-        dot = fmaf(__uint_as_float(wv.x << 16), qr[8 * c], dot);
-        dot = fmaf(__uint_as_float(wv.x & 0xFFFF0000u), qr[8 * c + 1], dot);
-        dot = fmaf(__uint_as_float(wv.y << 16), qr[8 * c + 2], dot);
-        dot = fmaf(__uint_as_float(wv.y & 0xFFFF0000u), qr[8 * c + 3], dot);
-        dot = fmaf(__uint_as_float(wv.z << 16), qr[8 * c + 4], dot);
-        dot = fmaf(__uint_as_float(wv.z & 0xFFFF0000u), qr[8 * c + 5], dot);
-        dot = fmaf(__uint_as_float(wv.w << 16), qr[8 * c + 6], dot);
-        dot = fmaf(__uint_as_float(wv.w & 0xFFFF0000u), qr[8 * c + 7], dot);
-      }
-      ssc[g * MAX_SINK + t] = dot;
-      mx = fmaxf(mx, dot);
-    }
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float lsum = 0.0f;
-    for (int sp = lane; sp < n_split; sp += 64) {
-      const float mv = fw[g * MAX_SPLIT + sp];
-      const float f = mv == -INFINITY ? 0.0f : exp2f(mv - mx);
-      fw[g * MAX_SPLIT + sp] = f;
-      lsum = fmaf(f, lsp[g * MAX_SPLIT + sp], lsum);
-    }
-    for (int t = lane; t < ns_sink; t += 64) {
-      const float wt = exp2f(ssc[g * MAX_SINK + t] - mx);
-      ssc[g * MAX_SINK + t] = wt;
-      lsum += wt;
-    }
-    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
-    if (lane == 0) Lh[g] = lsum;
-  }
-  __syncthreads();
-  // rotated-domain sums: item (g, i) = sum_s w_s acc_s[i]
-  for (int idx = tid; idx < G * D; idx += ST) {
-    const int g = idx >> 7, i = idx & (D - 1);
-    const float* src = pp + static_cast<int64_t>(g) * n_split * PART + 4 + i;
-    const float* wg = fw + g * MAX_SPLIT;
-    float a = 0.0f;
-    int s0 = 0;
-    if (idx == tid) {  // first item: its first 32 splits are in pv already
+  // thread roles: (c, hs) for the rotated sums, (i, cq) for the rotation
+  const int c = tid & (D - 1), hs = tid >> 7;
+  const int oi = tid % OW, cq = tid / OW, gi = qo * OW + oi;
+
+  // ---- loads
+  constexpr int PA = 16;
+  float pa[PA];
 #pragma unroll
-      for (int u = 0; u < PV; ++u)
-        if (u < n_split) a = fmaf(wg[u], pv[u], a);
-      s0 = PV;
-    }
-#pragma unroll 16
-    for (int sp = s0; sp < n_split; ++sp) a = fmaf(wg[sp], load_agent(src + static_cast<int64_t>(sp) * PART), a);
-    rsum[idx] = a;
+  for (int u = 0; u < PA; ++u) {
+    const int sp = hs + 2 * u;
+    pa[u] = sp < n_split ? pp[static_cast<int64_t>(sp) * PART + 4 + c] : 0.0f;
   }
-  __syncthreads();
-  // one inverse rotation per head (+ raw sink values): thread (ci, hf) takes
-  // rotated coordinates [32 hf, 32 hf + 32) and sink tokens hf, hf + 4, ...
-  const int ci = tid & (D - 1), hf = tid >> 7;
-  float pic[32];
+  float pic[CK];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) pic[k] = vtab->pi[(32 * hf + k) * D + ci];
-  for (int g = 0; g < G; ++g) {
-    const float4* r4 = reinterpret_cast<const float4*>(rsum + g * D + 32 * hf);
-    float o = 0.0f;
+  for (int k = 0; k < CK; ++k) pic[k] = vtab->pi[(CK * cq + k) * D + gi];
+  constexpr int SVN = 16;
+  float svv[SVN];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 r = r4[k];
-      o = fmaf(pic[4 * k], r.x, o);
-      o = fmaf(pic[4 * k + 1], r.y, o);
-      o = fmaf(pic[4 * k + 2], r.z, o);
-      o = fmaf(pic[4 * k + 3], r.w, o);
-    }
-    for (int t = hf; t < ns_sink; t += 4)
-      o = fmaf(ssc[g * MAX_SINK + t], __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + ci]) << 16), o);
-    obuf[(g * 4 + hf) * D + ci] = o;
+  for (int u = 0; u < SVN; ++u) {
+    const int t = cq + CQ * u;
+    svv[u] = t < ns ? __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + gi]) << 16) : 0.0f;
   }
+  const bool has_row = tid < ns;
+  uint4 krow[D / 8];
+  if (has_row) {
+    const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(tid) * D);
+#pragma unroll
+    for (int k = 0; k < D / 8; ++k) krow[k] = row[k];
+  }
+  float mloc = -INFINITY;
+  for (int sp = tid; sp < n_split; sp += CT) {
+    const float m = pp[static_cast<int64_t>(sp) * PART], l = pp[static_cast<int64_t>(sp) * PART + 1];
+    const float mv = l > 0.0f ? m : -INFINITY;
+    wsp[sp] = mv;
+    lsp[sp] = l;
+    mloc = fmaxf(mloc, mv);
+  }
+  if (ns > 0 && tid < D) qv[tid] = q[static_cast<int64_t>(bh) * D + tid] * qscale;
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += ST) {
-    const int g = idx >> 7, i = idx & (D - 1);
-    const float* og = obuf + g * 4 * D + i;
-    const float v = og[0] + og[D] + og[2 * D] + og[3 * D];
-    const float Ls = Lh[g];
-    out[head0 * D + idx] = Ls > 0.0f ? v / Ls : 0.0f;
+
+  // ---- sink scores, maximum
+  auto row_dot = [&](const uint4 (&rw)[D / 8]) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D / 8; ++k) {
+      const uint4 wv = rw[k];
+      dot = fmaf(__uint_as_float(wv.x << 16), qv[8 * k], dot);
+      dot = fmaf(__uint_as_float(wv.x & 0xFFFF0000u), qv[8 * k + 1], dot);
+      dot = fmaf(__uint_as_float(wv.y << 16), qv[8 * k + 2], dot);
+      dot = fmaf(__uint_as_float(wv.y & 0xFFFF0000u), qv[8 * k + 3], dot);
+      dot = fmaf(__uint_as_float(wv.z << 16), qv[8 * k + 4], dot);
+      dot = fmaf(__uint_as_float(wv.z & 0xFFFF0000u), qv[8 * k + 5], dot);
+      dot = fmaf(__uint_as_float(wv.w << 16), qv[8 * k + 6], dot);
+      dot = fmaf(__uint_as_float(wv.w & 0xFFFF0000u), qv[8 * k + 7], dot);
+    }
+    return dot;
+  };
+  if (has_row) {
+    const float d0 = row_dot(krow);
+    ssc[tid] = d0;
+    mloc = fmaxf(mloc, d0);
+  }
+  for (int t = tid + CT; t < ns; t += CT) {
+    uint4 rw[D / 8];
+    const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(t) * D);
+#pragma unroll
+    for (int k = 0; k < D / 8; ++k) rw[k] = row[k];
+    const float d1 = row_dot(rw);
+    ssc[t] = d1;
+    mloc = fmaxf(mloc, d1);
+  }
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+  if (lane == 0) red[wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // ---- weights and normaliser
+  float lloc = 0.0f;
+  for (int sp = tid; sp < n_split; sp += CT) {
+    const float mv = wsp[sp];
+    const float f = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+    wsp[sp] = f;
+    lloc = fmaf(f, lsp[sp], lloc);
+  }
+  for (int t = tid; t < ns; t += CT) {
+    const float wt = __builtin_amdgcn_exp2f(ssc[t] - M);
+    ssc[t] = wt;
+    lloc += wt;
+  }
+  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
+  __syncthreads();
+  if (lane == 0) red[4 + wave] = lloc;
+  // ---- rotated-domain sums: thread (c, hs) takes splits hs, hs + 2, ...
+  float a = 0.0f;
+#pragma unroll
+  for (int u = 0; u < PA; ++u)
+    if (hs + 2 * u < n_split) a = fmaf(wsp[hs + 2 * u], pa[u], a);
+#pragma unroll 8
+  for (int sp = hs + 2 * PA; sp < n_split; sp += 2) a = fmaf(wsp[sp], pp[static_cast<int64_t>(sp) * PART + 4 + c], a);
+  rs[hs][c] = a;
+  __syncthreads();
+  const float Ls = red[4] + red[5] + red[6] + red[7];
+  // ---- slice of the inverse rotation (+ raw sink values): thread (oi, cq)
+  float o = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CK; ++k) o = fmaf(pic[k], rs[0][CK * cq + k] + rs[1][CK * cq + k], o);
+#pragma unroll
+  for (int u = 0; u < SVN; ++u)
+    if (cq + CQ * u < ns) o = fmaf(ssc[cq + CQ * u], svv[u], o);
+  for (int t = cq + CQ * SVN; t < ns; t += CQ)
+    o = fmaf(ssc[t], __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + gi]) << 16), o);
+  ob[cq][oi] = o;
+  __syncthreads();
+  if (tid < OW) {
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CQ; ++k) v += ob[k][tid];
+    out[static_cast<int64_t>(bh) * D + qo * OW + tid] = Ls > 0.0f ? v / Ls : 0.0f;
   }
 }
 
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-hipError_t launch_fused(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
-                        const tq_attn& a, const AttendPlan& plan, const float* q, const uint16_t* sink_k,
-                        const uint16_t* sink_v, const int32_t* seq_lens, float* parts, uint32_t* counters,
-                        float* out, hipStream_t st) {
-  hipLaunchKernelGGL((attend_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_split, a.hkv, a.batch), dim3(ST), 0, st,
+hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
+                        const tq_attn& a, const AttendPlan& plan, const float* q, const int32_t* seq_lens,
+                        float* parts, hipStream_t st) {
+  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_split, a.hkv, a.batch), dim3(ST), 0, st,
                      ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms, vc.cap,
-                     seq_lens, q, sink_k, sink_v, parts, counters, out, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk,
-                     a.v_skip, a.scale * LOG2E);
+                     seq_lens, q, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.v_skip, a.scale * LOG2E);
   return hipGetLastError();
 }
 
-struct FusedArgs {
+struct SplitArgs {
   const Tables* ktab;
   const tq_cache* kc;
   const Tables* vtab;
@@ -655,25 +673,21 @@ struct FusedArgs {
   const tq_attn* a;
   const AttendPlan* plan;
   const float* q;
-  const uint16_t* sink_k;
-  const uint16_t* sink_v;
   const int32_t* seq_lens;
   float* parts;
-  uint32_t* counters;
-  float* out;
   hipStream_t st;
 };
 
 template <int KLO, int KHI, int VLO, int VHI>
-hipError_t launch_q(bool qjl, const FusedArgs& f) {
-  return qjl ? launch_fused<KLO, KHI, VLO, VHI, true>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
-                                                      f.sink_v, f.seq_lens, f.parts, f.counters, f.out, f.st)
-             : launch_fused<KLO, KHI, VLO, VHI, false>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
-                                                       f.sink_v, f.seq_lens, f.parts, f.counters, f.out, f.st);
+hipError_t launch_q(bool qjl, const SplitArgs& f) {
+  return qjl ? launch_split<KLO, KHI, VLO, VHI, true>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.seq_lens,
+                                                      f.parts, f.st)
+             : launch_split<KLO, KHI, VLO, VHI, false>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.seq_lens,
+                                                       f.parts, f.st);
 }
 
 template <int KLO, int KHI>
-hipError_t dispatch_v(int vkey, bool qjl, const FusedArgs& f) {
+hipError_t dispatch_v(int vkey, bool qjl, const SplitArgs& f) {
   switch (vkey) {
     case 22: return launch_q<KLO, KHI, 2, 2>(qjl, f);
     case 33: return launch_q<KLO, KHI, 3, 3>(qjl, f);
@@ -685,11 +699,6 @@ hipError_t dispatch_v(int vkey, bool qjl, const FusedArgs& f) {
 }
 
 }  // namespace
-
-size_t attend_counter_bytes(const tq_attn& a) {
-  const int64_t streams = static_cast<int64_t>(a.batch) * a.hkv;
-  return static_cast<size_t>((streams * 4 + 255) / 256 * 256);
-}
 
 AttendPlan plan_attend(const tq_attn& a) {
   AttendPlan p{};
@@ -712,8 +721,7 @@ AttendPlan plan_attend(const tq_attn& a) {
   p.n_split = static_cast<int>(ns);
   p.chunk = chunk_tiles * TILE;
   const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
-  p.ws_bytes = attend_counter_bytes(a) +
-               static_cast<size_t>(heads) * static_cast<int64_t>(p.n_split) * PART * sizeof(float);
+  p.ws_bytes = static_cast<size_t>(heads) * static_cast<int64_t>(p.n_split) * PART * sizeof(float);
   return p;
 }
 
@@ -721,19 +729,29 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          const tq_cache& vc, const tq_attn& a, const AttendPlan& plan, const float* q,
                          const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                          void* workspace, hipStream_t st) {
-  uint32_t* counters = static_cast<uint32_t*>(workspace);
-  float* parts = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + attend_counter_bytes(a));
-  const FusedArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, counters, out, st};
+  float* parts = static_cast<float*>(workspace);
+  const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, seq_lens, parts, st};
   const int vkey = vs.bits_lo * 10 + vs.bits_hi;
   const bool qjl = ks.qjl_m != 0;
+  hipError_t e;
   switch (ks.bits_lo * 10 + ks.bits_hi) {
-    case 22: return dispatch_v<2, 2>(vkey, qjl, f);
-    case 33: return dispatch_v<3, 3>(vkey, qjl, f);
-    case 44: return dispatch_v<4, 4>(vkey, qjl, f);
-    case 43: return dispatch_v<4, 3>(vkey, qjl, f);
-    case 32: return dispatch_v<3, 2>(vkey, qjl, f);
+    case 22: e = dispatch_v<2, 2>(vkey, qjl, f); break;
+    case 33: e = dispatch_v<3, 3>(vkey, qjl, f); break;
+    case 44: e = dispatch_v<4, 4>(vkey, qjl, f); break;
+    case 43: e = dispatch_v<4, 3>(vkey, qjl, f); break;
+    case 32: e = dispatch_v<3, 2>(vkey, qjl, f); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
+  // four output slices per head while the heads alone would leave most CUs idle
+  const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
+  if (heads < 256)
+    hipLaunchKernelGGL(combine_kernel<4>, dim3(static_cast<unsigned>(heads * 4)), dim3(CT), 0, st, vtab, q, sink_k,
+                       sink_v, seq_lens, parts, out, a.hq, a.hkv, a.sink, plan.n_split, a.scale * LOG2E);
+  else
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(static_cast<unsigned>(heads)), dim3(CT), 0, st, vtab, q, sink_k,
+                       sink_v, seq_lens, parts, out, a.hq, a.hkv, a.sink, plan.n_split, a.scale * LOG2E);
+  return hipGetLastError();
 }
 
 }  // namespace tq

@@ -76,7 +76,6 @@ struct AttendPlan {
 };
 
 AttendPlan plan_attend(const tq_attn& a);
-size_t attend_counter_bytes(const tq_attn& a);  // leading workspace bytes holding counters
 
 hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          const Spec& vs, const Tables* vtab, const tq_cache& vc,

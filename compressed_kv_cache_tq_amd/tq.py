@@ -262,8 +262,8 @@ def quantize_kv(spec: Spec, tables, x, cache: Cache, tok0: int = 0, n_streams: i
 
 
 def alloc_attend_workspace(batch: int, hq: int, hkv: int, sink: int, max_len: int, device="cuda"):
-    """Zero-filled attention workspace (tq_attend_decode needs its counters at
-    zero before the first call and leaves them at zero after every call)."""
+    """Attention workspace for tq_attend_decode (zero-filled; the call keeps no
+    state in it)."""
     torch = _torch()
     n = attend_workspace_bytes(batch, hq, hkv, sink, max_len)
     return torch.zeros((n + 15) // 16 * 4, dtype=torch.float32, device=device)

@@ -23,8 +23,7 @@
  *  - Ownership: the caller owns every host and device buffer, including the
  *    device copy of the tables and the attention workspace.  The library
  *    allocates no device memory and keeps no state except a thread-local
- *    error string (and the completion counters it leaves at zero in a
- *    caller's attention workspace).
+ *    error string.
  *  - Errors: arguments are validated on the host before any launch.  A
  *    failed check returns a negative tq_status, launches nothing and sets
  *    tq_last_error().  A failed launch returns TQ_E_HIP with the HIP error
@@ -177,9 +176,7 @@ tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype,
                          int64_t x_row_stride, int64_t tok0, const tq_cache* cache,
                          void* stream);
 
-/* Workspace bytes tq_attend_decode needs for this problem.  The workspace
- * begins with one 32-bit completion counter per (sequence, kv head); see
- * tq_attend_decode. */
+/* Workspace bytes tq_attend_decode needs for this problem. */
 size_t tq_attend_workspace_bytes(const tq_attn* attn);
 
 /* One decode step of attention read directly from the packed cache.
@@ -195,10 +192,8 @@ size_t tq_attend_workspace_bytes(const tq_attn* attn);
  *            not exceed max_len.  A sequence of length 0 gives zeros.
  *   out      device fp32 [batch][hq][d]
  *   workspace device, >= tq_attend_workspace_bytes(attn) bytes, 16-byte
- *            aligned.  It must be zero-filled once before its first use;
- *            every call leaves it ready for the next one (its counters back
- *            at zero), so it is reused without clearing.  Calls that share a
- *            workspace must not run concurrently.
+ *            aligned; no state is kept in it between calls.  Calls that
+ *            share a workspace must not run concurrently.
  * Value norms must stay below 2^15 (the weighted values pass through fp16
  * on the way into the matrix cores).
  * scores: s_t = scale * n_t * (<Pi q, c[idx_t]> + sqrt(pi/2)/m * gamma_t *

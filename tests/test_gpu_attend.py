@@ -76,22 +76,21 @@ def test_attend_zero_length_sequence():
     assert torch().count_nonzero(run.out).item() == 0
 
 
-def test_attend_workspace_reuse_leaves_counters_zero():
-    """The workspace's completion counters start at zero and every call
-    leaves them at zero, so repeated calls (and a call of another shape on
-    the same workspace) give identical results."""
+def test_attend_workspace_reuse():
+    """Repeated calls on one workspace, and a call of another shape in
+    between, give identical results: the workspace holds no state."""
     print("[attend] workspace reuse", flush=True)
     T = torch()
     run = Run(workloads.generate("gqa_decode", ctx=1000))
     run.quantize()
     big = tq.alloc_attend_workspace(4, 32, 8, 0, 4096)
+    big.fill_(float("nan"))  # stale contents must not matter
     run.ws = big
     outs = []
     for _ in range(3):
         run.attend()
         T.cuda.synchronize()
         outs.append(run.out.clone())
-        assert T.count_nonzero(big[:64]).item() == 0
     other = Run(workloads.generate("gqa_decode", ctx=3000))
     other.quantize()
     other.ws = big
@@ -99,7 +98,6 @@ def test_attend_workspace_reuse_leaves_counters_zero():
     run.attend()
     T.cuda.synchronize()
     outs.append(run.out.clone())
-    assert T.count_nonzero(big[:64]).item() == 0
     for o in outs[1:]:
         assert T.equal(o, outs[0])
     _check(run, label="workspace reuse")
