@@ -263,28 +263,20 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
   };
   partial_dots(w, qraw);
-  __syncthreads();
-  reduce_parts(qrot, qscale);
-  if constexpr (QJL) {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) w[k] = ktab->sit[(32 * kq + k) * D + pi_i];
-    __syncthreads();
-    partial_dots(w, qrot);
-    __syncthreads();
-    reduce_parts(urot, 1.0f);
-  }
-  __syncthreads();
-  // power-of-two scale per head so that |value| * 2^sh < 2^14
+  // Power-of-two scale per head for the fp16 operand: Pi is orthogonal, so
+  // |q~_i| <= ||q~|| = ||q|| |qscale|, and sh = 14 - exponent of that bound
+  // keeps |q~_i| 2^sh below 2^14.  (The sketch product u has no such bound;
+  // its scale comes from its maximum.)
   for (int g = wave; g < G; g += SW) {
+    const float a0 = qraw[g * D + lane], a1 = qraw[g * D + lane + 64];
+    float ss = fmaf(a0, a0, a1 * a1);
 #pragma unroll
-    for (int which = 0; which < (QJL ? 2 : 1); ++which) {
-      const float* v = (which ? urot : qrot) + g * D;
-      float mx = fmaxf(fabsf(v[lane]), fabsf(v[lane + 64]));
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if (lane == 0) {
       int ex = 0;
-      if (mx > 0.0f) frexpf(mx, &ex);
-      if (lane == 0) shx[which * GMAX + g] = 14 - ex;
+      const float nq = sqrtf(ss) * fabsf(qscale);
+      if (nq > 0.0f) frexpf(nq, &ex);
+      shx[g] = 14 - ex;
     }
   }
   __syncthreads();
@@ -292,26 +284,66 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   // query head n of the group, as fp16 hi and lo parts
   const bool head_ok = n < G;
   half8 qh[4], ql[4], uh[QJL ? 4 : 1], ul[QJL ? 4 : 1];
+  auto split_hl = [&](const float (&xs)[8], int sh, half8& hi, half8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = ldexpf(xs[e], sh);
+      const _Float16 h = static_cast<_Float16>(x);
+      hi[e] = head_ok ? h : static_cast<_Float16>(0.0f);
+      lo[e] = head_ok ? static_cast<_Float16>(x - static_cast<float>(h)) : static_cast<_Float16>(0.0f);
+    }
+  };
   auto fragments = [&](const float* v, int sh, half8 (&hi)[4], half8 (&lo)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const float4* src = reinterpret_cast<const float4*>(v + n * D + 32 * j + 8 * ks);
       const float4 x0 = src[0], x1 = src[1];
       const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = ldexpf(xs[e], sh);
-        const _Float16 h = static_cast<_Float16>(x);
-        hi[ks][e] = head_ok ? h : static_cast<_Float16>(0.0f);
-        lo[ks][e] = head_ok ? static_cast<_Float16>(x - static_cast<float>(h)) : static_cast<_Float16>(0.0f);
-      }
+      split_hl(xs, sh, hi[ks], lo[ks]);
     }
   };
+  const int nn = head_ok ? n : 0;
   const int shq = head_ok ? shx[n] : 0;
-  fragments(qrot, shq, qh, ql);
   const float qinv = head_ok ? ldexpf(1.0f, -shq) : 0.0f;
   float uinv = 0.0f;
-  if constexpr (QJL) {
+  if constexpr (!QJL) {
+    // straight from the four partial dots (same summation order as q~)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float xs[8];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float4 t[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          t[k] = *reinterpret_cast<const float4*>(ppart + (k * GMAX + nn) * D + 32 * j + 8 * ks + 4 * h2);
+        xs[4 * h2 + 0] = (t[0].x + t[1].x + t[2].x + t[3].x) * qscale;
+        xs[4 * h2 + 1] = (t[0].y + t[1].y + t[2].y + t[3].y) * qscale;
+        xs[4 * h2 + 2] = (t[0].z + t[1].z + t[2].z + t[3].z) * qscale;
+        xs[4 * h2 + 3] = (t[0].w + t[1].w + t[2].w + t[3].w) * qscale;
+      }
+      split_hl(xs, shq, qh[ks], ql[ks]);
+    }
+  } else {
+    reduce_parts(qrot, qscale);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) w[k] = ktab->sit[(32 * kq + k) * D + pi_i];
+    __syncthreads();
+    partial_dots(w, qrot);
+    __syncthreads();
+    reduce_parts(urot, 1.0f);
+    __syncthreads();
+    for (int g = wave; g < G; g += SW) {
+      const float* v = urot + g * D;
+      float mx = fmaxf(fabsf(v[lane]), fabsf(v[lane + 64]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      int ex = 0;
+      if (mx > 0.0f) frexpf(mx, &ex);
+      if (lane == 0) shx[GMAX + g] = 14 - ex;
+    }
+    __syncthreads();
+    fragments(qrot, shq, qh, ql);
     const int shu = head_ok ? shx[GMAX + n] : 0;
     fragments(urot, shu, uh, ul);
     uinv = head_ok ? ldexpf(QJL_C, -shu) : 0.0f;
