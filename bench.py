@@ -60,8 +60,8 @@ CALIB_BYTES = 512 << 20
 # Kernels of one bench step, by the name rocprofv3 reports, and the traffic
 # file each one's counters go to.
 STEP_KERNELS = {
-    "quantize_k": ["quantize_kernel<4, 4, 0, false, false>"],
-    "quantize_v": ["quantize_kernel<3, 3, 0, true, false>"],
+    "quantize_k": ["rotq_kernel<4, 4, false, false, 8>"],
+    "quantize_v": ["rotq_kernel<3, 3, false, true, 8>"],
     "attend": ["split_kernel<4, 4, 3, 3, false>", "combine_kernel"],
 }
 STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0], "attend": KERNEL_SOURCES[1]}
@@ -272,9 +272,9 @@ def main() -> int:
 
     # dominant kernel of the step (largest device time): one of the two quantize launches
     if qk_ms.mean() >= qv_ms.mean():
-        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_k", qk_ms.mean(), qk_bytes, "quantize_kernel<4,4,bf16,record>"
+        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_k", qk_ms.mean(), qk_bytes, "rotq_kernel<4,4,bf16,record>"
     else:
-        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms.mean(), qv_bytes, "quantize_kernel<3,3,bf16,tiled>"
+        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms.mean(), qv_bytes, "rotq_kernel<3,3,bf16,tiled>"
     dom_gbs = dom_bytes / (dom_ms / 1e3) / 1e9
     traffic = read_traffic(dom_name)
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -304,6 +304,36 @@ tq_status hip_status(hipError_t e, const char* where) {
   return fail(TQ_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+
+// Cell table of one codebook (fp32 boundaries, ascending).  Cell c covers
+// [c/64 - 1, (c+1)/64 - 1).  The kernel finds the cell as the fp32 round of
+// 64 y + 64 truncated, which can only move a value that lies just below an
+// edge up into the next cell; the code stays exact if no boundary lies in
+// that sliver below an edge.  Fails if a cell holds two boundaries or a
+// boundary sits within 1e-6 below an edge.
+bool cell_table(const float* bnd, int nb, uint32_t (*cell)[2]) {
+  for (int c = 0; c < tq::CELL_ENTRIES; ++c) {
+    const double lo = c / 64.0 - 1.0, hi = (c + 1) / 64.0 - 1.0;
+    uint32_t below = 0, inside = 0;
+    float b_in = INFINITY;
+    for (int j = 0; j < nb; ++j) {
+      const double t = bnd[j];
+      if (t < lo) ++below;
+      else if (t < hi) {
+        ++inside;
+        b_in = bnd[j];
+      }
+      if (t < lo && lo - t < 1e-6) return false;
+    }
+    if (inside > 1) return false;
+    uint32_t bits;
+    std::memcpy(&bits, &b_in, 4);
+    cell[c][0] = bits;
+    cell[c][1] = below;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -370,6 +400,8 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
         t->cen[h][j] = j < L ? static_cast<float>(c[j]) : 0.0f;
         t->cen16[h][j] = j < L ? to_half(c[j]) : 0;
       }
+      if (!cell_table(t->bnd[h], L - 1, t->cell[h]))
+        return fail(TQ_E_UNSUPPORTED, "codebook boundaries too close for the code cell table");
     }
     std::vector<double> m(tq::D * tq::D);
     rotation_build(tq::D, spec->rot_seed, m.data());

@@ -179,6 +179,53 @@ __device__ __forceinline__ void store_record(uint8_t* dst, const uint32_t (&w)[8
 // Tiled layout: this lane holds coordinates 4j + t (t = 0..3) of token slots
 // 16h + r (r = 0..15).  For token group gg (slots 16h + 8gg + s) the chunk
 // is rows t = 0..3 x tokens s = 0..7, code bits at (8t + s) B: B words.
+// Code of y (a rotated unit-vector coordinate) from the cell table: the
+// cell gives the number of boundaries below it and the one boundary inside.
+__device__ __forceinline__ uint32_t cell_code(float y, const uint2* cells) {
+  const float f = __builtin_amdgcn_fmed3f(fmaf(y, 64.0f, 64.0f), 0.0f, 128.0f);
+  const uint2 e = cells[static_cast<uint32_t>(f)];
+  return e.y + (y > __uint_as_float(e.x) ? 1u : 0u);
+}
+
+// 32 codes code(0..31) packed LSB-first into B dwords (code p at bits
+// [B p, B p + B)), built with shift-or chains from the last code down.
+template <int B, typename CodeF>
+__device__ __forceinline__ void pack_run(CodeF code, uint32_t* w) {
+  if constexpr (B == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t x = code(8 * k + 7);
+#pragma unroll
+      for (int e = 6; e >= 0; --e) x = (x << 4) | code(8 * k + e);
+      w[k] = x;
+    }
+  } else if constexpr (B == 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t x = code(16 * k + 15);
+#pragma unroll
+      for (int e = 14; e >= 0; --e) x = (x << 2) | code(16 * k + e);
+      w[k] = x;
+    }
+  } else {
+    static_assert(B == 3, "code width");
+    // codes 10 and 21 straddle dword boundaries
+    const uint32_t c10 = code(10), c21 = code(21);
+    uint32_t x = code(9);
+#pragma unroll
+    for (int e = 8; e >= 0; --e) x = (x << 3) | code(e);
+    w[0] = x | (c10 << 30);
+    x = c21;
+#pragma unroll
+    for (int e = 20; e >= 11; --e) x = (x << 3) | code(e);
+    w[1] = (x << 1) | (c10 >> 2);
+    x = code(31);
+#pragma unroll
+    for (int e = 30; e >= 22; --e) x = (x << 3) | code(e);
+    w[2] = (x << 2) | (c21 >> 1);
+  }
+}
+
 template <int B>
 __device__ __forceinline__ void pack_tiled(const f32x16 (&acc)[4], const float (&inv)[16], const float* tp, int gg,
                                            uint32_t (&w)[4]) {
@@ -242,6 +289,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
   __shared__ uint4 pi_frag[NPART * FRAGS];
   __shared__ uint4 s_frag[QJL ? 2 * FRAGS : 1];
   __shared__ float cen_s[2][16];
+  __shared__ uint2 cell_s[2][CELL_ENTRIES];
 
   // Stage the rotation (and sketch) fragments in LDS in the order the MFMA
   // loop reads them: fragment (part, t, ks, lane) = 8 consecutive columns
@@ -261,6 +309,9 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
     }
   }
   if (threadIdx.x < 32) cen_s[threadIdx.x >> 4][threadIdx.x & 15] = tab->cen[threadIdx.x >> 4][threadIdx.x & 15];
+  for (int c = threadIdx.x; c < 2 * CELL_ENTRIES; c += THREADS)
+    cell_s[c / CELL_ENTRIES][c % CELL_ENTRIES] =
+        make_uint2(tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][0], tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][1]);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -384,8 +435,10 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
       uint8_t* rec = codes + s * stream_code_bytes + pos * CODE_BYTES;
       if constexpr (!QJL) {
         if constexpr (BLO == BHI) {
-          load_pos_thresholds<BLO>(tab, 0, sc, tp);
-          pack_record<BLO>(acc, tp, wds);
+          // cell-table codes: lane's coordinates 0..31 then 32..63
+          const float inv = sc > 0.0f ? 1.0f / sc : 0.0f;
+          pack_run<BLO>([&](int p) { return cell_code(acc[p >> 4][p & 15] * inv, cell_s[0]); }, wds);
+          pack_run<BLO>([&](int p) { return cell_code(acc[2 + (p >> 4)][p & 15] * inv, cell_s[0]); }, wds + BLO);
           if (valid) store_record<BLO>(rec + 8 * BLO * h, wds);
         } else if (h == 0) {
           load_pos_thresholds<BLO>(tab, 0, sc, tp);
@@ -488,8 +541,9 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
         uint32_t wds[4];
         float tp[7];
         if constexpr (BLO == BHI) {
-          load_pos_thresholds<BLO>(tab, 0, 1.0f, tp);
-          pack_tiled<BLO>(acc, inv, tp, gg, wds);
+          // cell-table codes: run position 8 t + s = coordinate 4j + t, token slot s
+          pack_run<BLO>([&](int p) { return cell_code(acc[p >> 3][8 * gg + (p & 7)] * inv[8 * gg + (p & 7)],
+                                                      cell_s[0]); }, wds);
           store_tiled_chunk<BLO>(tbase + g * G + 8 * BLO * q + 4 * BLO * (j & 1), wds, vmask);
         } else if (j < 16) {
           load_pos_thresholds<BLO>(tab, 0, 1.0f, tp);
@@ -505,6 +559,371 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
     }
 #pragma unroll
     for (int k = 0; k < NW; ++k) xr[k] = xnext[k];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident rotation kernel: every spec without the QJL stage (for
+// the tiled layout, the tiles that are written whole).
+//
+// A workgroup of 4 waves works on two 32-vector tiles at a time.  Waves 2p
+// and 2p + 1 form pair p and split the 128 rotated coordinates of the pair's
+// tile: wave w of the pair owns coordinates [64 w, 64 w + 64) and keeps the
+// rows of 256 Pi for them as fp16 hi + lo MFMA fragments in registers for the
+// whole launch (the width split of a 3.5-bit spec falls on the same
+// boundary).  The pair stages its tile of x through LDS once: norm (partial
+// sums in fp32, combined in fp64), a power-of-two scale so |x| 2^sh < 2^14,
+// fp16 conversion (hi + lo for fp32 inputs), written straight in MFMA
+// operand order; further tiles of x are in flight in registers meanwhile.
+// Per tile each wave runs 32 v_mfma_f32_32x32x16_f16 (two 32-coordinate
+// blocks x 8 k-steps x hi/lo of Pi; 48 for fp32 inputs) and turns its 64
+// coordinates x 32 vectors into codes with the cell table.
+//   record layout: A = Pi rows (permuted), B = x^T.  Lane (v, h) holds the
+//     32 consecutive coordinates 64 w + 32 h + [0, 32) of vector v: one run
+//     of 32 codes, stored as B dwords.
+//   tiled layout: A = x (token slots permuted), B = Pi^T.  Lane (c, h) holds
+//     coordinate 64 w + 32 t + c of tokens 16 h + [0, 16); the 8 codes of a
+//     token group fill one dword, and the 4 lanes of a quad hold the 4
+//     coordinates of one half of a sub-block.
+// Loads and stores go through per-tile buffer resources whose extent ends at
+// the last valid row, so rows past the end read as zero and their stores
+// are dropped by the hardware: the loop has no data-dependent branches and
+// the prefetched loads stay in flight across iterations.
+constexpr int RQ_WAVES = 4;
+constexpr int RQ_THREADS = 64 * RQ_WAVES;
+constexpr int RSRC_WORD3 = 0x00020000;
+
+// token slot v of a tile -> row of the A operand that carries it (inverse of tiled_slot)
+__device__ __forceinline__ int tiled_row(int v) { return 8 * ((v >> 2) & 3) + 4 * (v >> 4) + (v & 3); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), RSRC_WORD3);
+}
+
+// N codes of run positions p0 .. p0+N-1, table lookups issued together
+template <int N, typename YF>
+__device__ __forceinline__ void cell_codes(YF yof, int p0, const uint2* cells, uint32_t (&c)[N]) {
+  float y[N];
+  uint2 e[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) y[i] = yof(p0 + i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float f = __builtin_amdgcn_fmed3f(fmaf(y[i], 64.0f, 64.0f), 0.0f, 128.0f);
+    e[i] = cells[static_cast<uint32_t>(f)];
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) c[i] = e[i].y + (y[i] > __uint_as_float(e[i].x) ? 1u : 0u);
+}
+
+// 32 codes of y(0..31) packed LSB-first into B dwords
+template <int B, typename YF>
+__device__ __forceinline__ void code_run(YF yof, const uint2* cells, uint32_t* w) {
+  if constexpr (B == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t c[8];
+      cell_codes<8>(yof, 8 * k, cells, c);
+      uint32_t x = c[7];
+#pragma unroll
+      for (int i = 6; i >= 0; --i) x = (x << 4) | c[i];
+      w[k] = x;
+    }
+  } else if constexpr (B == 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t c[16];
+      cell_codes<16>(yof, 16 * k, cells, c);
+      uint32_t x = c[15];
+#pragma unroll
+      for (int i = 14; i >= 0; --i) x = (x << 2) | c[i];
+      w[k] = x;
+    }
+  } else {
+    static_assert(B == 3, "code width");
+    uint32_t a[11], b[11], c[10];
+    cell_codes<11>(yof, 0, cells, a);    // codes 0..10 (10 straddles)
+    cell_codes<11>(yof, 11, cells, b);   // codes 11..21 (21 straddles)
+    cell_codes<10>(yof, 22, cells, c);   // codes 22..31
+    uint32_t x = a[9];
+#pragma unroll
+    for (int i = 8; i >= 0; --i) x = (x << 3) | a[i];
+    w[0] = x | (a[10] << 30);
+    x = b[10];
+#pragma unroll
+    for (int i = 9; i >= 0; --i) x = (x << 3) | b[i];
+    w[1] = (x << 1) | (a[10] >> 2);
+    x = c[9];
+#pragma unroll
+    for (int i = 8; i >= 0; --i) x = (x << 3) | c[i];
+    w[2] = (x << 2) | (b[10] >> 1);
+  }
+}
+
+template <int BLO, int BHI, bool F32IN, bool TILED, int K>
+__global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
+    const Tables* __restrict__ tab, const void* __restrict__ xv, int64_t n_tok, int64_t xss, int64_t xrs,
+    int64_t tok0, uint8_t* __restrict__ codes, float* __restrict__ norms, int64_t cap, int64_t stream_code_bytes,
+    int64_t tiles_per_stream, int64_t tile0, int64_t total_tiles) {
+  constexpr int XP = F32IN ? 2 : 1;          // fp16 parts of x
+  constexpr int ES = F32IN ? 4 : 2;          // input element bytes
+  constexpr int NQW = F32IN ? 8 : 4;         // 16-byte input words per staging thread
+  constexpr int CODE_BYTES = 8 * (BLO + BHI);
+  __shared__ uint4 xbuf[2][2][XP][8 * 64];   // [pair][buffer][part][ks * 64 + lane]
+  __shared__ float inv_s[2][2][32];          // [pair][buffer][vector]: 1 / (norm 2^(sh+8))
+  __shared__ uint2 cell_s[2][CELL_ENTRIES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform: the pair's tiles, and so the buffer resources, live in SGPRs
+  const int pair = __builtin_amdgcn_readfirstlane(tid >> 7), w = __builtin_amdgcn_readfirstlane((tid >> 6) & 1);
+  const int pt = tid & 127;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  for (int c = tid; c < 2 * CELL_ENTRIES; c += RQ_THREADS)
+    cell_s[c / CELL_ENTRIES][c % CELL_ENTRIES] =
+        make_uint2(tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][0], tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][1]);
+
+  // ---- rotation fragments of this wave's 64 coordinates, for the whole launch
+  half8 pih[2][8], pil[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    int row;
+    if constexpr (TILED) row = 64 * w + 32 * t + l32;
+    else row = 64 * w + 32 * ((l32 >> 2) & 1) + 16 * t + 4 * (l32 >> 3) + (l32 & 3);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int col = 16 * ks + 8 * h;
+      pih[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_hi + row * D + col));
+      pil[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_lo + row * D + col));
+    }
+  }
+
+  // Tile tl of the launch: stream s, tile T of the stream; its rows of x
+  // start at r0 and the first nv of its 32 positions are valid (the tiled
+  // layout only gets whole tiles here).
+  struct TileAt {
+    int64_t s, r0, p0;
+    int nv;
+  };
+  // tile counts fit in 32 bits (checked on the host): branch-free division
+  const uint32_t tps = static_cast<uint32_t>(tiles_per_stream);
+  auto tile_at = [&](int64_t tl) {
+    TileAt a;
+    const uint32_t s32 = static_cast<uint32_t>(tl) / tps;
+    a.s = s32;
+    const int64_t T = static_cast<uint32_t>(tl) - s32 * tps;
+    if constexpr (TILED) {
+      a.p0 = 32 * (tile0 + T);
+      a.r0 = a.p0 - tok0;
+      a.nv = 32;
+    } else {
+      a.r0 = 32 * T;
+      a.p0 = tok0 + a.r0;
+      const int64_t left = n_tok - a.r0;
+      a.nv = static_cast<int>(left < 32 ? left : 32);
+    }
+    if (tl >= total_tiles) a.nv = 0;
+    return a;
+  };
+  // staging role: vector (token slot) sv of the tile, elements [32 qq, 32 qq + 32)
+  const int sv = pt >> 2, qq = pt & 3;
+  // pair p of workgroup g takes tiles (2 g + p) K .. (2 g + p) K + K - 1
+  const int64_t stride = 1;
+  const int64_t first = (static_cast<int64_t>(blockIdx.x) * 2 + pair) * K;
+  auto load_x = [&](int64_t tl, uint4 (&dst)[NQW]) {
+    const TileAt a = tile_at(tl);
+    const uint8_t* base = static_cast<const uint8_t*>(xv) + (a.s * xss + a.r0 * xrs) * ES;
+    const __amdgpu_buffer_rsrc_t r = rsrc(base, a.nv > 0 ? ((a.nv - 1) * xrs + D) * ES : 0);
+    const int off = static_cast<int>((sv * xrs + 32 * qq) * ES);
+#pragma unroll
+    for (int k = 0; k < NQW; ++k)
+      dst[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0));
+  };
+  // norm, scale, fp16 conversion into buffer b; the norm goes out here too
+  auto stage = [&](int64_t tl, const uint4 (&xin)[NQW], int b) {
+    double ss = 0.0;
+    if constexpr (F32IN) {
+#pragma unroll
+      for (int k = 0; k < NQW; ++k) {
+        const float e[4] = {__uint_as_float(xin[k].x), __uint_as_float(xin[k].y), __uint_as_float(xin[k].z),
+                            __uint_as_float(xin[k].w)};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ss = fma(static_cast<double>(e[u]), static_cast<double>(e[u]), ss);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NQW; ++k) {
+        float c = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x2 pr = __builtin_bit_cast(bf16x2, word_of(xin[k], u));
+          c = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, c, false);
+        }
+        ss += static_cast<double>(c);
+      }
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    const float normf = static_cast<float>(sqrt(ss));
+    int ex = 0;
+    frexpf(normf, &ex);
+    const int sh = 14 - ex;
+    const float up = ldexpf(1.0f, sh);
+    const int arow = TILED ? tiled_row(sv) : sv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k8 = 4 * qq + c;  // 8-element chunk of the vector
+      const int fi = (k8 >> 1) * 64 + arow + 32 * (k8 & 1);
+      if constexpr (F32IN) {
+        const uint4 a0 = xin[2 * c], a1 = xin[2 * c + 1];
+        const uint32_t ww[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        half8 hi, lo;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float e = __uint_as_float(ww[u]) * up;
+          hi[u] = static_cast<_Float16>(e);
+          lo[u] = static_cast<_Float16>(e - static_cast<float>(hi[u]));
+        }
+        xbuf[pair][b][0][fi] = __builtin_bit_cast(uint4, hi);
+        xbuf[pair][b][XP - 1][fi] = __builtin_bit_cast(uint4, lo);
+      } else {
+        uint32_t ow[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t wd = word_of(xin[c], u);
+          // bf16 x 2^sh is exact in fp16 over its normal range
+          const auto hv = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(wd << 16) * up,
+                                                     __uint_as_float(wd & 0xFFFF0000u) * up);
+          ow[u] = __builtin_bit_cast(uint32_t, hv);
+        }
+        xbuf[pair][b][0][fi] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+    // the four threads of a vector write the same values
+    inv_s[pair][b][sv] = normf > 0.0f ? 1.0f / ldexpf(normf, sh + 8) : 0.0f;
+    const TileAt a = tile_at(tl);
+    const __amdgpu_buffer_rsrc_t rn = rsrc(norms + a.s * cap + a.p0, static_cast<int64_t>(a.nv) * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, 4 * sv, 0, 0);
+  };
+
+  // ---- pipeline, straight-line over the pair's K tiles: three register
+  // buffers with fixed roles (tile k+1 is staged from X[(k+1) % 3] while
+  // tiles k+2, k+3 are still loading; the buffer is then refilled with tile
+  // k+4), so the waits on in-flight loads are exact.
+  uint4 X[3][NQW];
+  load_x(first, X[0]);
+  load_x(first + 1, X[1]);
+  load_x(first + 2, X[2]);
+  stage(first, X[0], 0);
+  load_x(first + 3, X[0]);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t tl = first + k;
+    const int b = k & 1;
+    f32x16 acc[2];
+    acc[0] = acc[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const half8 xh = as_half8(xbuf[pair][b][0][ks * 64 + lane]);
+      if constexpr (TILED) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma(xh, pih[t][ks], acc[t]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma(xh, pil[t][ks], acc[t]);
+        if constexpr (F32IN) {
+          const half8 xl = as_half8(xbuf[pair][b][XP - 1][ks * 64 + lane]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[t] = mfma(xl, pih[t][ks], acc[t]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma(pih[t][ks], xh, acc[t]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma(pil[t][ks], xh, acc[t]);
+        if constexpr (F32IN) {
+          const half8 xl = as_half8(xbuf[pair][b][XP - 1][ks * 64 + lane]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[t] = mfma(pih[t][ks], xl, acc[t]);
+        }
+      }
+    }
+    const TileAt a = tile_at(tl);
+    uint8_t* sbase = codes + a.s * stream_code_bytes;
+    if constexpr (!TILED) {
+      const float inv = inv_s[pair][b][l32];
+      const __amdgpu_buffer_rsrc_t rc = rsrc(sbase + a.p0 * CODE_BYTES, static_cast<int64_t>(a.nv) * CODE_BYTES);
+      uint32_t wd[4];
+      auto yv = [&](int p) { return acc[p >> 4][p & 15] * inv; };
+      auto put = [&](auto bw, int off) {
+        constexpr int BW = decltype(bw)::value;
+        const int o = l32 * CODE_BYTES + off;
+        if constexpr (BW == 4) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)),
+                                                                    make_uint4(wd[0], wd[1], wd[2], wd[3])), rc, o, 0, 0);
+        } else if constexpr (BW == 2) {
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(rc, 0, 0, 0)),
+                                                                   make_uint2(wd[0], wd[1])), rc, o, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(wd[0], rc, o, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(wd[1], rc, o + 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(wd[2], rc, o + 8, 0, 0);
+        }
+      };
+      if (BLO == BHI || w == 0) {
+        code_run<BLO>(yv, cell_s[0], wd);
+        put(std::integral_constant<int, BLO>{}, w == 0 ? 4 * BLO * h : 8 * BLO + 4 * BLO * h);
+      } else {
+        code_run<BHI>(yv, cell_s[1], wd);
+        put(std::integral_constant<int, BHI>{}, 8 * BLO + 4 * BHI * h);
+      }
+    } else {
+      const float* invb = inv_s[pair][b] + 16 * h;
+      constexpr int G = 64 * (BLO + BHI);
+      const __amdgpu_buffer_rsrc_t rc =
+          rsrc(sbase + a.p0 * CODE_BYTES, a.nv > 0 ? static_cast<int64_t>(32) * CODE_BYTES : 0);
+      const int qa = l32 & 3;
+      auto emit = [&](auto bw, const uint2* cells) {
+        constexpr int BW = decltype(bw)::value;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int cabs = 64 * w + 32 * t + l32;
+          const int q = cabs >> 3, rh = (cabs >> 2) & 1;
+          const int qoff = q < 8 ? 8 * BLO * q : 64 * BLO + 8 * BHI * (q - 8);
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            const float4 i0 = *reinterpret_cast<const float4*>(invb + 8 * gg);
+            const float4 i1 = *reinterpret_cast<const float4*>(invb + 8 * gg + 4);
+            const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+            uint32_t c[8];
+            cell_codes<8>([&](int p) { return acc[t][8 * gg + p] * iv[p]; }, 0, cells, c);
+            uint32_t d = c[7];
+#pragma unroll
+            for (int sl = 6; sl >= 0; --sl) d = (d << BW) | c[sl];
+            // dword qa of the 32-code chunk of the quad (coordinates 4m .. 4m+3)
+            const uint32_t nx =
+                static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(d), 0x39, 0xF, 0xF, false));
+            uint32_t out;
+            if constexpr (BW == 4) out = d;
+            else if constexpr (BW == 2) out = d | (nx << 16);
+            else out = (d >> (8 * qa)) | (nx << (24 - 8 * qa));
+            const int dw = BW == 2 ? (qa >> 1) : qa;
+            const bool owner = BW == 4 || (BW == 2 ? (qa & 1) == 0 : qa < 3);
+            const int o = (2 * h + gg) * G + qoff + 4 * BW * rh + 4 * dw;
+            // non-owners store past the tile's extent (dropped)
+            __builtin_amdgcn_raw_buffer_store_b32(out, rc, owner ? o : 32 * CODE_BYTES, 0, 0);
+          }
+        }
+      };
+      if (BLO == BHI || w == 0) emit(std::integral_constant<int, BLO>{}, cell_s[0]);
+      else emit(std::integral_constant<int, BHI>{}, cell_s[1]);
+    }
+    // stage the next tile into the other buffer, refill its registers
+    if (k + 1 < K) {
+      stage(tl + 1, X[(k + 1) % 3], b ^ 1);
+      if (k + 4 < K) load_x(tl + 4, X[(k + 1) % 3]);
+      __syncthreads();
+    }
   }
 }
 
@@ -528,20 +947,67 @@ hipError_t launch_one(const Tables* tab, const void* x, int64_t n_streams, int64
   return hipGetLastError();
 }
 
+template <int BLO, int BHI, bool F32IN, bool TILED>
+hipError_t launch_rotq(const Tables* tab, const void* x, int64_t n_streams, int64_t n_tok, int64_t xss, int64_t xrs,
+                       int64_t tok0, const tq_cache& c, hipStream_t st) {
+  constexpr int CODE_BYTES = 8 * (BLO + BHI);
+  constexpr int XM = F32IN ? X_F32 : X_BF16;
+  int64_t tiles, tile0 = 0;
+  if (TILED) {
+    // whole tiles here; a partially written first or last tile merges its
+    // codes into the existing ones in the general kernel
+    const int64_t end = tok0 + n_tok;
+    const int64_t t_lo = (tok0 + TILE - 1) / TILE, t_hi = end / TILE;
+    if (t_hi <= t_lo) return launch_one<BLO, BHI, XM, true, false>(tab, x, n_streams, n_tok, xss, xrs, tok0, c, st);
+    if (tok0 < t_lo * TILE) {
+      const hipError_t e =
+          launch_one<BLO, BHI, XM, true, false>(tab, x, n_streams, t_lo * TILE - tok0, xss, xrs, tok0, c, st);
+      if (e != hipSuccess) return e;
+    }
+    if (end > t_hi * TILE) {
+      const int64_t skip = t_hi * TILE - tok0;
+      const uint8_t* xe = static_cast<const uint8_t*>(x) + skip * xrs * (F32IN ? 4 : 2);
+      const hipError_t e =
+          launch_one<BLO, BHI, XM, true, false>(tab, xe, n_streams, end - t_hi * TILE, xss, xrs, t_hi * TILE, c, st);
+      if (e != hipSuccess) return e;
+    }
+    tile0 = t_lo;
+    tiles = t_hi - t_lo;
+  } else {
+    tiles = (n_tok + TILE - 1) / TILE;
+  }
+  const int64_t total = n_streams * tiles;
+  if (total + 8 * 1024 >= (int64_t{1} << 31) || 32 * xrs * (F32IN ? 4 : 2) >= (int64_t{1} << 31))
+    return launch_one<BLO, BHI, XM, TILED, false>(tab, x, n_streams, n_tok, xss, xrs, tok0, c, st);
+  // 8 tiles per pair once that still fills every CU twice over, else 2
+  if (total >= 8 * 1024) {
+    const int64_t blocks = (total + 15) / 16;
+    hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 8>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(RQ_THREADS), 0, st, tab, x, n_tok, xss, xrs, tok0, c.codes, c.norms, c.cap,
+                       c.cap * CODE_BYTES, tiles, tile0, total);
+  } else {
+    const int64_t blocks = (total + 3) / 4;
+    hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(RQ_THREADS), 0, st, tab, x, n_tok, xss, xrs, tok0, c.codes, c.norms, c.cap,
+                       c.cap * CODE_BYTES, tiles, tile0, total);
+  }
+  return hipGetLastError();
+}
+
 template <int BLO, int BHI>
 hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const void* x, int64_t ns, int64_t nt,
                            int64_t xss, int64_t xrs, int64_t tok0, const tq_cache& c, hipStream_t st) {
   const bool f32 = dtype == TQ_F32;
-  if (sp.layout == TQ_LAYOUT_TILED) {
-    return f32 ? launch_one<BLO, BHI, X_F32, true, false>(tab, x, ns, nt, xss, xrs, tok0, c, st)
-               : launch_one<BLO, BHI, X_BF16, true, false>(tab, x, ns, nt, xss, xrs, tok0, c, st);
-  }
   if (sp.qjl_m) {
     return f32 ? launch_one<BLO, BHI, X_F32, false, true>(tab, x, ns, nt, xss, xrs, tok0, c, st)
                : launch_one<BLO, BHI, X_BF16_F16, false, true>(tab, x, ns, nt, xss, xrs, tok0, c, st);
   }
-  return f32 ? launch_one<BLO, BHI, X_F32, false, false>(tab, x, ns, nt, xss, xrs, tok0, c, st)
-             : launch_one<BLO, BHI, X_BF16, false, false>(tab, x, ns, nt, xss, xrs, tok0, c, st);
+  if (sp.layout == TQ_LAYOUT_TILED) {
+    return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, ns, nt, xss, xrs, tok0, c, st)
+               : launch_rotq<BLO, BHI, false, true>(tab, x, ns, nt, xss, xrs, tok0, c, st);
+  }
+  return f32 ? launch_rotq<BLO, BHI, true, false>(tab, x, ns, nt, xss, xrs, tok0, c, st)
+             : launch_rotq<BLO, BHI, false, false>(tab, x, ns, nt, xss, xrs, tok0, c, st);
 }
 
 }  // namespace

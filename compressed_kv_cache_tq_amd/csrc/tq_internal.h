@@ -15,6 +15,8 @@ constexpr int D = TQ_DIM;
 constexpr int TILE = TQ_TILE_TOKENS;
 constexpr int QJL_M = TQ_QJL_M;
 constexpr uint32_t TABLES_MAGIC = 0x31515454u;  // "TTQ1"
+constexpr int CELLS = 128;        // cells of the code table over [-1, 1]
+constexpr int CELL_ENTRIES = 132; // CELLS + 1, padded
 
 // Device tables of one tq_spec, built on the host by tq_tables_build.
 //
@@ -51,6 +53,11 @@ struct alignas(256) Tables {
   float pit[D * D];
   float sit[D * D];
   uint16_t pi_b16[3][D * D];  // bf16 split of pi: hi + mid + lo keeps ~24 bits
+  // Cell table of each half's codebook: y in [-1, 1] falls in cell
+  // floor(64 (y + 1)), c in [0, 128].  Entry c = {bits of the one boundary in
+  // [c/64 - 1, (c+1)/64 - 1) or of +inf, number of boundaries below c/64 - 1},
+  // so the code of y is code_low + (y > boundary).
+  uint32_t cell[2][CELL_ENTRIES][2];
 };
 
 constexpr float PI_SCALE = 256.0f;

@@ -76,16 +76,19 @@ def _tables_view(spec):
     parts = (b16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     ref = orot.rotation(0, 128)
     assert np.max(np.abs(parts.sum(0) - ref)) <= 2.0 ** -24 * np.abs(ref).max()
+    off += 3 * 32768
+    cells = buf[off: off + 2 * 132 * 8].view(np.uint32).reshape(2, 132, 2)
     bnd = buf[32: 32 + 128].view(np.float32).reshape(2, 16)
     cen = buf[160: 160 + 128].view(np.float32).reshape(2, 16)
     cen16 = buf[288: 288 + 64].view(np.float16).reshape(2, 16)
-    return hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16
+    return hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16, cells
 
 
 def test_tables_content():
     spec = tq.Spec(4, 3, split=64, qjl_m=128)
-    hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16 = _tables_view(spec)
-    assert tq.tables_bytes() == 512 + 6 * 65536 + 3 * 32768
+    hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16, cells = _tables_view(spec)
+    assert tq.tables_bytes() >= 512 + 6 * 65536 + 3 * 32768 + 2 * 132 * 8
+    assert tq.tables_bytes() % 256 == 0
     assert hdr[0] == 0x31515454 and hdr[1] == 1 and hdr[2] == 4 and hdr[3] == 3
     ref = orot.rotation(0, 128)
     assert np.array_equal(pi, ref.astype(np.float32))
@@ -102,6 +105,35 @@ def test_tables_content():
         assert np.all(np.isinf(bnd[h, L - 1:]))
         assert np.array_equal(cen[h, :L], cb.centroids.astype(np.float32))
         assert np.array_equal(cen16[h, :L], cb.centroids.astype(np.float16))
+        # cell table: cell c covers [c/64 - 1, (c+1)/64 - 1); boundaries below it
+        # and the one boundary inside it (or +inf), from the fp32 boundaries
+        b32 = cb.boundaries.astype(np.float32).astype(np.float64)
+        for c in range(129):
+            lo, hi = c / 64 - 1, (c + 1) / 64 - 1
+            inside = b32[(b32 >= lo) & (b32 < hi)]
+            assert len(inside) <= 1
+            want = np.float32(inside[0]) if len(inside) else np.float32(np.inf)
+            assert cells[h, c, 0] == want.view(np.uint32)
+            assert cells[h, c, 1] == np.count_nonzero(b32 < lo)
+
+
+def test_cell_table_gives_the_codes():
+    """Codes from the cell rule (code_low + (y > boundary)) equal the count of
+    boundaries below y for random and boundary-adjacent fp32 values."""
+    for bits in (2, 3, 4):
+        spec = tq.Spec(bits)
+        *_, bnd, cen, cen16, cells = _tables_view(spec)
+        L = 1 << bits
+        b32 = bnd[0, : L - 1]
+        rng = np.random.default_rng(bits)
+        y = np.concatenate([rng.normal(0, 0.09, 20000), rng.uniform(-1, 1, 2000), [-1.0, 1.0, 0.0]]).astype(np.float32)
+        near = np.concatenate([np.nextafter(b32, np.float32(np.inf)), np.nextafter(b32, np.float32(-np.inf)), b32])
+        y = np.concatenate([y, near.astype(np.float32)])
+        f = np.clip(np.float32(64) * y + np.float32(64), 0, 128).astype(np.float32)
+        c = f.astype(np.int64)
+        code = cells[0, c, 1].astype(np.int64) + (y > cells[0, c, 0].view(np.float32))
+        want = np.searchsorted(b32, y, side="left")
+        assert np.array_equal(code, want)
 
 
 def test_code_bytes():
