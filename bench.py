@@ -8,7 +8,9 @@ key channels per head, K 4-bit records, V 3-bit tiles):
 Inputs are resident in HBM before timing.  Four copies of the inputs and of
 the packed cache rotate between steps, and a step attends over a cache copy
 written three steps earlier, so reads are not served from the 256 MB
-Infinity Cache.  Timing uses HIP events on the launch stream.
+Infinity Cache.  Timing uses HIP events on the launch stream.  Per-kernel
+durations (the roofline figures and `value`) come from a second timed pass
+in which each phase is launched back to back, decode over ten cache copies.
 
 Prints one JSON line.  `value` is the decode-attention throughput in GB/s of
 algorithmic bytes (packed K and V records, norms, q and out).
@@ -31,6 +33,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "packed-KV decode-attention GB/s (% HBM peak) + quantize Mvec/s at d=128"
 WORKLOAD = "gqa_decode"
 COPIES = 4
+ATT_COPIES = 10
 KERNEL_SOURCES = ["compressed_kv_cache_tq_amd/csrc/quantize.hip", "compressed_kv_cache_tq_amd/csrc/attend.hip"]
 
 
@@ -192,6 +195,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD, help="workload to time (the metric is quoted on gqa_decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 512 MiB fp32 streaming kernel (out = -in) 5 times; "
                          "its byte counts calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -210,35 +214,75 @@ def main() -> int:
     from compressed_kv_cache_tq_amd import tq, workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = workloads.WORKLOADS[WORKLOAD]
-    inp = workloads.generate(WORKLOAD)
-    B, Hkv, Hq, T = wl.batch, wl.hkv, wl.hq, wl.ctx
-    kspec = tq.Spec(wl.k.bits_lo, layout=tq.LAYOUT_RECORD)
-    vspec = tq.Spec(wl.v.bits_lo, layout=tq.LAYOUT_TILED)
+    wname = args.workload
+    wl = workloads.WORKLOADS[wname]
+    inp = workloads.generate(wname)
+    B, Hkv, Hq, S = len(inp.k), wl.hkv, wl.hq, wl.sink
+    lens_h = np.asarray(inp.seq_lens, dtype=np.int64)
+    comp_h = np.maximum(lens_h - S, 0)
+    T = int(lens_h.max())
+    cap = max(32, -(-int(comp_h.max()) // 32) * 32)
+    uniform = bool(np.all(lens_h == lens_h[0]))
+    f32 = wl.dtype == "f32"
+    kspec = tq.Spec(wl.k.bits_lo, wl.k.bits_hi, split=wl.k.split, qjl_m=wl.k.qjl_m, layout=tq.LAYOUT_RECORD,
+                    rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed)
+    vspec = tq.Spec(wl.v.bits_lo, wl.v.bits_hi, split=wl.v.split, layout=tq.LAYOUT_TILED, rot_seed=wl.v.rot_seed)
     ktab, vtab = tq.device_tables(kspec), tq.device_tables(vspec)
-    xk_host = np.stack(inp.k_bf16).reshape(B * Hkv, T, 128)
-    xv_host = np.stack(inp.v_bf16).reshape(B * Hkv, T, 128)
-    xk = [torch.from_numpy(xk_host.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(COPIES)]
-    xv = [torch.from_numpy(xv_host.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(COPIES)]
-    kc = [tq.alloc_cache(kspec, B * Hkv, T) for _ in range(COPIES)]
-    vc = [tq.alloc_cache(vspec, B * Hkv, T) for _ in range(COPIES)]
-    q = torch.from_numpy(inp.q).cuda()
-    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+
+    def device_input(parts):
+        """[B * Hkv, cap, 128] zero-padded compressed tokens (bf16 bits or fp32)."""
+        host = np.zeros((B * Hkv, cap, 128), dtype=np.float32 if f32 else np.uint16)
+        for b in range(B):
+            n = int(comp_h[b])
+            if n:
+                src = parts[b][:, S:S + n]
+                host[b * Hkv:(b + 1) * Hkv, :n] = src if f32 else workloads.bf16_bits(src)
+        t = torch.from_numpy(host if f32 else host.view(np.int16)).cuda()
+        return t if f32 else t.view(torch.bfloat16)
+
+    xk = [device_input(inp.k)]
+    xv = [device_input(inp.v)]
+    for _ in range(COPIES - 1):
+        xk.append(xk[0].clone())
+        xv.append(xv[0].clone())
+    kc = [tq.alloc_cache(kspec, B * Hkv, cap) for _ in range(COPIES)]
+    vc = [tq.alloc_cache(vspec, B * Hkv, cap) for _ in range(COPIES)]
+    sink_k = sink_v = None
+    if S:
+        sk = np.stack([inp.k[b][:, :S] for b in range(B)])
+        sv = np.stack([inp.v[b][:, :S] for b in range(B)])
+        sink_k = torch.from_numpy(workloads.bf16_bits(sk).view(np.int16)).cuda()
+        sink_v = torch.from_numpy(workloads.bf16_bits(sv).view(np.int16)).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(inp.q, dtype=np.float32)).cuda()
+    lens = torch.from_numpy(lens_h.astype(np.int32)).cuda()
     out = torch.empty_like(q)
-    ws = tq.alloc_attend_workspace(B, Hq, Hkv, 0, T)
+    ws = tq.alloc_attend_workspace(B, Hq, Hkv, S, T)
     stream = torch.cuda.current_stream()
+
+    def quantize(spec, tab, x, cache):
+        if uniform:
+            tq.quantize_kv(spec, tab, x[:, :int(comp_h[0])], cache)
+        else:  # one launch per sequence: each appends its own length
+            for b in range(B):
+                n = int(comp_h[b])
+                if n:
+                    tq.quantize_kv(spec, tab, x[b * Hkv:(b + 1) * Hkv, :n], cache.streams(b * Hkv, Hkv))
+
+    def attend(kcache, vcache):
+        tq.attend_decode(kspec, ktab, kcache, vspec, vtab, vcache, q, lens, out, ws, hkv=Hkv, sink=S,
+                         sink_k=sink_k, sink_v=sink_v, v_skip=wl.v_skip, max_len=T)
 
     def step(i, ev=None):
         s, a = i % COPIES, (i + 1) % COPIES
         if ev is not None:
             ev[0].record(stream)
-        tq.quantize_kv(kspec, ktab, xk[s], kc[s])
+        quantize(kspec, ktab, xk[s], kc[s])
         if ev is not None:
             ev[1].record(stream)
-        tq.quantize_kv(vspec, vtab, xv[s], vc[s])
+        quantize(vspec, vtab, xv[s], vc[s])
         if ev is not None:
             ev[2].record(stream)
-        tq.attend_decode(kspec, ktab, kc[a], vspec, vtab, vc[a], q, lens, out, ws, hkv=Hkv, max_len=T)
+        attend(kc[a], vc[a])
         if ev is not None:
             ev[3].record(stream)
 
@@ -255,48 +299,81 @@ def main() -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    qk_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    qv_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    at_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    qk_step = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    qv_step = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    at_step = np.array([e[2].elapsed_time(e[3]) for e in evs])
 
-    n_vec = B * Hkv * T
+    # Per-kernel launch durations: each phase launched back to back over the
+    # rotating copies between two events (no event packets between launches),
+    # as many launches as timed steps.
+    def back_to_back(fn):
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        eb.record(stream)
+        torch.cuda.synchronize()
+        return ea.elapsed_time(eb) / args.steps
+
+    qk_ms = back_to_back(lambda i: quantize(kspec, ktab, xk[i % COPIES], kc[i % COPIES]))
+    qv_ms = back_to_back(lambda i: quantize(vspec, vtab, xv[i % COPIES], vc[i % COPIES]))
+    # decode reads 31.5 MB per step: rotate over ten cache copies (315 MB, more
+    # than the 256 MB Infinity Cache) so back-to-back steps still read HBM
+    kc_b = kc + [tq.clone_cache(kc[i % COPIES]) for i in range(ATT_COPIES - COPIES)]
+    vc_b = vc + [tq.clone_cache(vc[i % COPIES]) for i in range(ATT_COPIES - COPIES)]
+    at_ms = back_to_back(lambda i: attend(kc_b[i % ATT_COPIES], vc_b[i % ATT_COPIES]))
+
+    n_vec = int(Hkv * comp_h.sum())                        # compressed vectors per tensor
     kcb, vcb = tq.code_bytes(kspec), tq.code_bytes(vspec)
-    dec_bytes = n_vec * (kcb + 4 + vcb + 4) + 2 * B * Hq * 128 * 4
-    qk_bytes = n_vec * (128 * 2 + kcb + 4)
-    qv_bytes = n_vec * (128 * 2 + vcb + 4)
-    dec_s = at_ms.mean() / 1e3
-    quant_s = (qk_ms.mean() + qv_ms.mean()) / 1e3
+    k_tok = kcb + 4 + (kspec.qjl_m // 8 + 4 if kspec.qjl_m else 0)   # codes, norm (+ signs, residual norm)
+    v_tok = vcb + 4
+    in_b = 512 if f32 else 256
+    sink_bytes = int(Hkv * np.minimum(lens_h, S).sum()) * 2 * 128 * 2
+    dec_bytes = n_vec * (k_tok + v_tok) + sink_bytes + 2 * B * Hq * 128 * 4
+    qk_bytes = n_vec * (in_b + k_tok)
+    qv_bytes = n_vec * (in_b + v_tok)
+    dec_s = at_ms / 1e3
+    quant_s = (qk_ms + qv_ms) / 1e3
     dec_gbs = dec_bytes / dec_s / 1e9
     quant_mvec = 2 * n_vec / quant_s / 1e6
     quant_gbs = (qk_bytes + qv_bytes) / quant_s / 1e9
 
     # dominant kernel of the step (largest device time): one of the two quantize launches
-    if qk_ms.mean() >= qv_ms.mean():
-        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_k", qk_ms.mean(), qk_bytes, "rotq_kernel<4,4,bf16,record>"
+    ktag = f"{wl.k.bits_lo},{wl.k.bits_hi},{'f32' if f32 else 'bf16'},record{',qjl' if kspec.qjl_m else ''}"
+    vtag = f"{wl.v.bits_lo},{wl.v.bits_hi},{'f32' if f32 else 'bf16'},tiled"
+    kkern = "quantize_kernel" if kspec.qjl_m else "rotq_kernel"
+    if qk_ms >= qv_ms:
+        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_k", qk_ms, qk_bytes, f"{kkern}<{ktag}>"
     else:
-        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms.mean(), qv_bytes, "rotq_kernel<3,3,bf16,tiled>"
+        dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms, qv_bytes, f"rotq_kernel<{vtag}>"
     dom_gbs = dom_bytes / (dom_ms / 1e3) / 1e9
-    traffic = read_traffic(dom_name)
+    traffic = read_traffic(dom_name) if wname == WORKLOAD else None
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom_kernel,
                 "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2)}
-    att_traffic = read_traffic("attend")
+    att_traffic = read_traffic("attend") if wname == WORKLOAD else None
     roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
-                       "kernel": "split_kernel<4,4,3,3> + combine_kernel (one decode step)",
-                       "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms.mean() * 1e3, 2)}
+                       "kernel": f"split_kernel<{wl.k.bits_lo},{wl.k.bits_hi},{wl.v.bits_lo},{wl.v.bits_hi}"
+                                 f"{',qjl' if kspec.qjl_m else ''}> + combine_kernel (one decode step)",
+                       "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(dec_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": WORKLOAD, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "d": 128, "context": T,
-                   "kv_dtype": "bf16", "k_bits": wl.k.bits_lo, "v_bits": wl.v.bits_lo, "qjl": False,
-                   "structure": "4 key channels per head x10"},
+        "config": {"workload": wname, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "d": 128,
+                   "context": T if uniform else f"ragged {int(lens_h.min())}..{T}, sum {int(lens_h.sum())}",
+                   "kv_dtype": wl.dtype, "k_bits": [wl.k.bits_lo, wl.k.bits_hi], "v_bits": [wl.v.bits_lo, wl.v.bits_hi],
+                   "split": wl.k.split, "qjl": bool(kspec.qjl_m), "sink": S, "v_skip": wl.v_skip,
+                   "structure": wl.structure},
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
-        "decode_us": round(at_ms.mean() * 1e3, 2),
+        "decode_us": round(at_ms * 1e3, 2),
         "quantize_Mvec_s": round(quant_mvec, 1), "quantize_GB_s": round(quant_gbs, 2),
         "quantize_pct_hbm_peak": round(100 * quant_gbs / HBM_PEAK_GBS, 2),
-        "quantize_us": {"k": round(qk_ms.mean() * 1e3, 2), "v": round(qv_ms.mean() * 1e3, 2)},
+        "quantize_us": {"k": round(qk_ms * 1e3, 2), "v": round(qv_ms * 1e3, 2)},
+        "in_step_us": {"quantize_k": round(qk_step.mean() * 1e3, 2), "quantize_v": round(qv_step.mean() * 1e3, 2),
+                       "decode": round(at_step.mean() * 1e3, 2)},
         "roofline": roofline, "roofline_attend": roofline_attend,
     }
     if args.copy_calibration:
@@ -306,7 +383,7 @@ def main() -> int:
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wname == WORKLOAD:
         a = (args.warmup + args.steps) % COPIES
         nb_k, nb_v = tq.cache_code_bytes(kspec, T), tq.cache_code_bytes(vspec, T)
         kraw = [kc[a].codes[h * nb_k:(h + 1) * nb_k].cpu().numpy().reshape(T, kcb) for h in range(Hkv)]

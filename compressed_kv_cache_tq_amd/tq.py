@@ -261,6 +261,13 @@ def quantize_kv(spec: Spec, tables, x, cache: Cache, tok0: int = 0, n_streams: i
                                 x.stride(1), tok0, ctypes.byref(cc), st), "tq_quantize_kv")
 
 
+def clone_cache(c: "Cache") -> "Cache":
+    """Device copy of a cache (same spec and capacity)."""
+    return Cache(c.spec, c.cap, c.codes.clone(), c.norms.clone(),
+                 None if c.qjl_signs is None else c.qjl_signs.clone(),
+                 None if c.qjl_rnorms is None else c.qjl_rnorms.clone())
+
+
 def alloc_attend_workspace(batch: int, hq: int, hkv: int, sink: int, max_len: int, device="cuda"):
     """Attention workspace for tq_attend_decode (zero-filled; the call keeps no
     state in it)."""
