@@ -8,20 +8,23 @@
 // (value dequantization is skipped when the attention weight is below 1e-6).
 //
 // Two launches on one stream:
-//  split    one workgroup of 8 waves per (split, kv head, sequence).
+//  split    one workgroup of 8 waves per (split, kv head, sequence), plus one
+//           more split per (kv head, sequence) for the raw sink tokens.
 //           Prologue: the workgroup rotates the query heads of its group,
 //           q~ = Pi_K q (times scale * log2 e), and u = S q~, scales each
-//           head by a power of two and splits it into fp16 hi + lo, straight
-//           into the register layout of the score MFMA's A operand.  Stream:
-//           each wave streams 32-token tiles with one tile prefetched into
-//           registers: K records -> LUT dequantization -> scores on MFMA for
-//           all query heads of the group -> online softmax -> V tiles
-//           (coordinate-major sub-blocks) -> P V on MFMA in the rotated
-//           domain.  The waves merge in LDS and write one partial
-//           (m, l, acc[128]) per query head;
+//           head by a power of two and splits it into fp16 hi + lo operand
+//           fragments in LDS.  Stream: each wave streams 32-token tiles with
+//           two tiles in flight in registers: K records -> LUT
+//           dequantization -> scores on MFMA for all query heads of the
+//           group -> online softmax -> V tiles (coordinate-major sub-blocks)
+//           -> P V on MFMA in the rotated domain.  The waves merge in LDS and
+//           write one partial (m, l, acc[128]) per query head.  The sink
+//           split writes the same partial for the sink tokens, with acc in
+//           the original value domain;
 //  combine  one workgroup per (sequence, query head, output slice):
-//           log-sum-exp merge of the partials and the raw bf16 sink tokens,
-//           the slice of one inverse rotation Pi_V^T, normalisation.
+//           log-sum-exp merge of the partials, the slice of one inverse
+//           rotation Pi_V^T of the rotated sum, the sink values, and the
+//           normalisation.
 //
 // Codebook LUTs: entry e of width B maps two codes to their two fp16
 // centroids.  The centroids depend only on (d, B), so one LUT per width
@@ -36,6 +39,7 @@ namespace tq {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int SW = 8;          // waves per split workgroup
@@ -44,6 +48,7 @@ constexpr int PART = 132;      // floats per partial: m, l, 2 pad, acc[128]
 constexpr int GMAX = 16;       // query heads per kv head
 constexpr int MAX_SINK = 512;  // raw sink tokens per sequence
 constexpr int MAX_SPLIT = 512; // splits per (sequence, kv head)
+constexpr int FROW = D + 8;    // fp16 per fragment row in LDS (pad: no bank conflicts)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float QJL_C = 1.2533141373155003f / QJL_M;  // sqrt(pi/2) / m
 
@@ -65,16 +70,18 @@ __device__ __forceinline__ uint32_t row_bits(const uint32_t* w, int k) {
   return NB == 32 ? v : (v & ((1u << NB) - 1u));
 }
 
-// LDS layout of the replicated pair LUTs (bytes): width 4 first, then 3, 2.
+// LDS layout of the replicated pair LUTs (bytes): widths 3 and 2 first, then
+// 4, so every LUT base (at most 20 KiB) fits the immediate offset of the LDS
+// read and the lane-dependent part of the address is one AND-OR.
 template <int B>
 constexpr int lut_size() { return (1 << (2 * B)) * 256; }
 template <int KLO, int KHI, int VLO, int VHI>
 struct LutPlan {
   static constexpr bool has(int B) { return KLO == B || KHI == B || VLO == B || VHI == B; }
-  static constexpr int off4 = 0;
-  static constexpr int off3 = has(4) ? lut_size<4>() : 0;
+  static constexpr int off3 = 0;
   static constexpr int off2 = off3 + (has(3) ? lut_size<3>() : 0);
-  static constexpr int bytes = off2 + (has(2) ? lut_size<2>() : 0);
+  static constexpr int off4 = off2 + (has(2) ? lut_size<2>() : 0);
+  static constexpr int bytes = off4 + (has(4) ? lut_size<4>() : 0);
   template <int B>
   static constexpr int off() { return B == 4 ? off4 : B == 3 ? off3 : off2; }
 };
@@ -92,15 +99,20 @@ __device__ __forceinline__ half8 dequant8(const uint32_t* w, int k, const uint8_
 #pragma unroll
     for (int p = 0; p < 4; ++p) a[p] = __builtin_amdgcn_perm(v, lane4, 0x0C0C0000u | ((4u + p) << 8));
   } else {
+    // pair p sits at bits [2Bp, 2Bp + 2B) of the row: move it to bit 8
     const uint32_t v = row_bits<B>(w, k);
-    constexpr uint32_t M = (1u << (2 * B)) - 1u;
+    constexpr uint32_t M = ((1u << (2 * B)) - 1u) << 8;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) a[p] = (((v >> (2 * B * p)) & M) << 8) | lane4;
+    for (int p = 0; p < 4; ++p) {
+      const int sh = 8 - 2 * B * p;
+      const uint32_t t = sh >= 0 ? v << sh : v >> (-sh);
+      a[p] = (t & M) | lane4;
+    }
   }
   return as_half8(lds_u32(lut, a[0]), lds_u32(lut, a[1]), lds_u32(lut, a[2]), lds_u32(lut, a[3]));
 }
 
-// Registers of one 32-token tile for one lane (prefetched one tile ahead).
+// Registers of one 32-token tile for one lane (two tiles in flight per wave).
 struct TileRegs {
   uint32_t kw[2][4];  // K record chunk of token slots mu(0, n), mu(1, n)
   uint32_t vw[8];     // V sub-block (token group j, coordinate group n)
@@ -110,47 +122,103 @@ struct TileRegs {
   float4 rn[2];       // QJL residual norms of tokens 8j .. 8j+7
 };
 
-// Offsets are 32-bit and relative to the stream's base pointers.
+constexpr int RSRC_WORD3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), RSRC_WORD3);
+}
+
+// Buffer descriptors of one (sequence, kv head) stream.  Loads past a
+// descriptor's extent return zeros, so the stream loop issues every tile's
+// loads unconditionally and runs ahead of the last tile without branches.
+struct StreamRsrc {
+  __amdgpu_buffer_rsrc_t kc, vc, kn, vn, zs, rn;
+};
+
+// Per-lane byte offsets of tile 0 of the stream; tile t0 adds t0 times the
+// per-token stride of each array (t0 is a multiple of 32, and a V tile of
+// 32 tokens is 32 * VBYTES contiguous bytes).
+struct LaneOffsets {
+  uint32_t k[2], z[2], v, nrm;
+};
+
+template <int N>
+__device__ __forceinline__ void buf_load(uint32_t (&dst)[N], __amdgpu_buffer_rsrc_t r, uint32_t off, int first = 0) {
+  static_assert(N == 2 || N == 3 || N == 4 || N == 6 || N == 8, "load width");
+  if constexpr (N == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    dst[0] = v[0]; dst[1] = v[1];
+  } else if constexpr (N == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2];
+  } else if constexpr (N == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+    uint32_t t[N - 4];
+    buf_load<N - 4>(t, r, off + 16);
+#pragma unroll
+    for (int i = 0; i < N - 4; ++i) dst[4 + i] = t[i];
+  }
+}
+
+__device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-__device__ __forceinline__ void load_tile(TileRegs& r, uint32_t t0, int n, int j, const uint8_t* kbase,
-                                          const uint8_t* vbase, const float* knb, const float* vnb,
-                                          const uint32_t* zb, const float* rnb) {
+__device__ __forceinline__ void load_tile(TileRegs& r, uint32_t t0, const StreamRsrc& rs, const LaneOffsets& lo) {
   constexpr uint32_t KBYTES = 8 * (KLO + KHI);
   constexpr uint32_t VBYTES = 8 * (VLO + VHI);
-  constexpr uint32_t VG = 64 * (VLO + VHI);
+  constexpr int KW = KLO > KHI ? KLO : KHI;
+  constexpr int VW = 2 * (VLO > VHI ? VLO : VHI);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const uint32_t tok = t0 + 8 * (n >> 2) + 4 * mb + (n & 3);
-    if (j < 2) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(kbase + (tok * KBYTES + 4 * KLO * j));
+    uint32_t w[KW];
+    buf_load<KW>(w, rs.kc, lo.k[mb] + t0 * KBYTES);
 #pragma unroll
-      for (int w = 0; w < KLO; ++w) r.kw[mb][w] = p[w];
-    } else {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(kbase + (tok * KBYTES + 8 * KLO + 4 * KHI * (j - 2)));
-#pragma unroll
-      for (int w = 0; w < KHI; ++w) r.kw[mb][w] = p[w];
-    }
-    if constexpr (QJL) r.zw[mb] = zb[tok * (QJL_M / 32) + j];
+    for (int i = 0; i < KW; ++i) r.kw[mb][i] = w[i];
+    if constexpr (QJL) r.zw[mb] = __builtin_amdgcn_raw_buffer_load_b32(rs.zs, lo.z[mb] + t0 * (QJL_M / 8), 0, 0);
   }
-  const uint32_t tile = (t0 / TILE) * (TILE * VBYTES) + j * VG;
-  if (n < 8) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(vbase + (tile + 8 * VLO * n));
+  {
+    uint32_t w[VW];
+    buf_load<VW>(w, rs.vc, lo.v + t0 * VBYTES);
 #pragma unroll
-    for (int w = 0; w < 2 * VLO; ++w) r.vw[w] = p[w];
-  } else {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(vbase + (tile + 64 * VLO + 8 * VHI * (n - 8)));
-#pragma unroll
-    for (int w = 0; w < 2 * VHI; ++w) r.vw[w] = p[w];
+    for (int i = 0; i < VW; ++i) r.vw[i] = w[i];
   }
-  const uint32_t tb = t0 + 8 * j;
-  r.kn[0] = *reinterpret_cast<const float4*>(knb + tb);
-  r.kn[1] = *reinterpret_cast<const float4*>(knb + tb + 4);
-  r.vn[0] = *reinterpret_cast<const float4*>(vnb + tb);
-  r.vn[1] = *reinterpret_cast<const float4*>(vnb + tb + 4);
+  r.kn[0] = buf_load_f4(rs.kn, lo.nrm + 4 * t0);
+  r.kn[1] = buf_load_f4(rs.kn, lo.nrm + 4 * t0 + 16);
+  r.vn[0] = buf_load_f4(rs.vn, lo.nrm + 4 * t0);
+  r.vn[1] = buf_load_f4(rs.vn, lo.nrm + 4 * t0 + 16);
   if constexpr (QJL) {
-    r.rn[0] = *reinterpret_cast<const float4*>(rnb + tb);
-    r.rn[1] = *reinterpret_cast<const float4*>(rnb + tb + 4);
+    r.rn[0] = buf_load_f4(rs.rn, lo.nrm + 4 * t0);
+    r.rn[1] = buf_load_f4(rs.rn, lo.nrm + 4 * t0 + 16);
   }
+}
+
+// Sum over the 32 lanes of each half wave: rotations within 16-lane rows,
+// then the row-swap permute.
+__device__ __forceinline__ float sum32(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xF, 0xF, false));
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// Maximum over lanes l, l^16, l^32, l^48 (the four token groups of a head):
+// the row-swap permutes exchange 16- and 32-lane halves without LDS.
+__device__ __forceinline__ float max_xor16_32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float f4get(const float4 (&v)[2], int e) {
@@ -159,13 +227,120 @@ __device__ __forceinline__ float f4get(const float4 (&v)[2], int e) {
   return k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
 }
 
+// Partial (m, l, acc) of the raw bf16 sink tokens t < ns of one (sequence,
+// kv head) for the G query heads of the group: s = qscale <q, k_t> (log2
+// domain), m = max s, l = sum 2^(s - m), acc = sum 2^(s - m) v_t in the
+// original value domain.  Head g's partial is written at part + g * stride.
+// 512 threads.
+__device__ __forceinline__ void sink_partial(uint8_t* smem, const float* __restrict__ qg,
+                                             const uint16_t* __restrict__ sk, const uint16_t* __restrict__ sv,
+                                             int ns, int G, float qscale, float* __restrict__ part, int64_t stride) {
+  float* qs = reinterpret_cast<float*>(smem);  // [GMAX][D]
+  float* sc = qs + GMAX * D;                   // [GMAX][MAX_SINK]: scores, then weights
+  float* accp = sc + GMAX * MAX_SINK;          // [2][GMAX][D]
+  float* mls = accp + 2 * GMAX * D;            // [GMAX][2]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int idx = tid; idx < G * D; idx += ST) qs[idx] = qg[idx] * qscale;
+  __syncthreads();
+  // scores: thread t takes token t
+  if (tid < ns) {
+    uint4 row[D / 8];
+    const uint4* rp = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(tid) * D);
+#pragma unroll
+    for (int k = 0; k < D / 8; ++k) row[k] = rp[k];
+    for (int g = 0; g < G; ++g) {
+      const float4* qv = reinterpret_cast<const float4*>(qs + g * D);
+      float dot = 0.0f;
+#pragma unroll
+      for (int k = 0; k < D / 8; ++k) {
+        const float4 a = qv[2 * k], c = qv[2 * k + 1];
+        const uint4 wv = row[k];
+        dot = fmaf(__uint_as_float(wv.x << 16), a.x, dot);
+        dot = fmaf(__uint_as_float(wv.x & 0xFFFF0000u), a.y, dot);
+        dot = fmaf(__uint_as_float(wv.y << 16), a.z, dot);
+        dot = fmaf(__uint_as_float(wv.y & 0xFFFF0000u), a.w, dot);
+        dot = fmaf(__uint_as_float(wv.z << 16), c.x, dot);
+        dot = fmaf(__uint_as_float(wv.z & 0xFFFF0000u), c.y, dot);
+        dot = fmaf(__uint_as_float(wv.w << 16), c.z, dot);
+        dot = fmaf(__uint_as_float(wv.w & 0xFFFF0000u), c.w, dot);
+      }
+      sc[g * MAX_SINK + tid] = dot;
+    }
+  }
+  __syncthreads();
+  // per head: maximum, weights, their sum (wave w takes heads w, w + 8)
+  for (int g = wave; g < G; g += SW) {
+    float mx = -INFINITY;
+    for (int t = lane; t < ns; t += 64) mx = fmaxf(mx, sc[g * MAX_SINK + t]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sum = 0.0f;
+    for (int t = lane; t < ns; t += 64) {
+      const float w = __builtin_amdgcn_exp2f(sc[g * MAX_SINK + t] - mx);
+      sc[g * MAX_SINK + t] = w;
+      sum += w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) {
+      mls[2 * g] = mx;
+      mls[2 * g + 1] = sum;
+    }
+  }
+  __syncthreads();
+  // weighted values: thread (i, tq) takes coordinate i of tokens tq, tq + 4, ...
+  const int i = tid & (D - 1), tq = tid >> 7;
+  float acc[GMAX];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) acc[g] = 0.0f;
+#pragma unroll 4
+  for (int t = tq; t < ns; t += 4) {
+    const float v = __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + i]) << 16);
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+      if (g < G) acc[g] = fmaf(sc[g * MAX_SINK + t], v, acc[g]);
+  }
+  // sum the four token groups
+  if (tq >= 2) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+      if (g < G) accp[((tq - 2) * GMAX + g) * D + i] = acc[g];
+  }
+  __syncthreads();
+  if (tq < 2) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+      if (g < G) acc[g] += accp[(tq * GMAX + g) * D + i];
+  }
+  __syncthreads();
+  if (tq == 1) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+      if (g < G) accp[g * D + i] = acc[g];
+  }
+  __syncthreads();
+  if (tq == 0) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+      if (g < G) {
+        float* pg = part + g * stride;
+        pg[4 + i] = acc[g] + accp[g * D + i];
+        if (i == 0) {
+          pg[0] = mls[2 * g];
+          pg[1] = mls[2 * g + 1];
+        }
+      }
+  }
+}
+
 // Split kernel: one workgroup of 8 waves per (split, kv head, sequence).
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 __global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
     const uint8_t* __restrict__ ksigns, const float* __restrict__ krn, int64_t kcap,
     const Tables* __restrict__ vtab, const uint8_t* __restrict__ vcodes, const float* __restrict__ vnorms,
-    int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q, float* __restrict__ parts,
+    int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q,
+    const uint16_t* __restrict__ sink_k, const uint16_t* __restrict__ sink_v, float* __restrict__ parts,
     int hq, int hkv, int sink, int n_split, int64_t chunk, float v_skip, float qscale) {
   using LP = LutPlan<KLO, KHI, VLO, VHI>;
   constexpr int KBYTES = 8 * (KLO + KHI);
@@ -173,10 +348,16 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   // LDS: [LUTs | query prologue] while streaming, then reused by the wave
   // merge.
   constexpr int PRO_OFF = (LP::bytes + 255) / 256 * 256;
-  constexpr int PRO = (GMAX * D + 4 * GMAX * D + GMAX * D + (QJL ? GMAX * D : 0) + 2 * GMAX) * 4;
+  // prologue: qraw [GMAX][D] f32, ppart [4][GMAX][D] f32, qrot [GMAX][D] f32
+  // (QJL), fragments [sets][hi, lo][GMAX + 1][FROW] fp16, shx [2][GMAX],
+  // umax [GMAX]
+  constexpr int NSET = QJL ? 2 : 1;
+  constexpr int FRAG_BYTES = NSET * 2 * (GMAX + 1) * FROW * 2;
+  constexpr int PRO = (GMAX * D + 4 * GMAX * D + (QJL ? GMAX * D : 0)) * 4 + FRAG_BYTES + 3 * GMAX * 4;
   constexpr int MRG = SW * 16 * (D + 2) * 4;
   constexpr int SMEM = PRO_OFF + PRO > MRG ? PRO_OFF + PRO : MRG;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(SMEM >= (GMAX * D + GMAX * MAX_SINK + 2 * GMAX * D + 2 * GMAX) * 4, "LDS of the sink split");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ uint32_t lutz[4];
 
@@ -187,57 +368,142 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
   const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
   const int64_t L = seq_lens[b];
+  if (split == n_split) {
+    // the extra split of a call with sink tokens: their partial, in the
+    // original (unrotated) value domain
+    sink_partial(smem, q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D,
+                 sink_k + stream * sink * D, sink_v + stream * sink * D,
+                 static_cast<int>(L < sink ? L : sink), G, qscale,
+                 parts + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * gridDim.x * PART +
+                     static_cast<int64_t>(n_split) * PART,
+                 gridDim.x * PART);
+    return;
+  }
   const int64_t comp = L > sink ? L - sink : 0;
   const int64_t t_begin64 = static_cast<int64_t>(split) * chunk;
   const uint32_t t_begin = static_cast<uint32_t>(t_begin64 < comp ? t_begin64 : comp);
   const uint32_t t_end = static_cast<uint32_t>(t_begin64 + chunk < comp ? t_begin64 + chunk : comp);
+  if (t_begin >= t_end) {
+    // no compressed token falls in this split (a shorter sequence of a
+    // ragged batch): an empty partial, m = -inf, l = 0, acc = 0
+    for (int idx = threadIdx.x; idx < G * PART; idx += ST) {
+      const int g = idx / PART, c = idx % PART;
+      parts[((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * gridDim.x + split) * PART + c] =
+          c == 0 ? -INFINITY : 0.0f;
+    }
+    return;
+  }
 
-  const uint8_t* kbase = kcodes + stream * kcap * KBYTES;
-  const uint8_t* vbase = vcodes + stream * vcap * VBYTES;
-  const float* knb = knorms + stream * kcap;
-  const float* vnb = vnorms + stream * vcap;
-  const uint32_t* zb = QJL ? reinterpret_cast<const uint32_t*>(ksigns) + stream * kcap * (QJL_M / 32) : nullptr;
-  const float* rnb = QJL ? krn + stream * kcap : nullptr;
+  // stream descriptors: the whole allocated range of the stream (cap
+  // positions), so tiles past the last one read zeros
+  StreamRsrc rs;
+  rs.kc = rsrc(kcodes + stream * kcap * KBYTES, kcap * KBYTES);
+  rs.vc = rsrc(vcodes + stream * vcap * VBYTES, vcap * VBYTES);
+  rs.kn = rsrc(knorms + stream * kcap, kcap * 4);
+  rs.vn = rsrc(vnorms + stream * vcap, vcap * 4);
+  if constexpr (QJL) {
+    rs.zs = rsrc(ksigns + stream * kcap * (QJL_M / 8), kcap * (QJL_M / 8));
+    rs.rn = rsrc(krn + stream * kcap, kcap * 4);
+  } else {
+    rs.zs = rs.rn = rs.kn;
+  }
+  LaneOffsets lo;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const uint32_t tok = 8 * (n >> 2) + 4 * mb + (n & 3);
+    lo.k[mb] = tok * KBYTES + (j < 2 ? 4 * KLO * j : 8 * KLO + 4 * KHI * (j - 2));
+    lo.z[mb] = tok * (QJL_M / 8) + 4 * j;
+  }
+  lo.v = j * (64 * (VLO + VHI)) + (n < 8 ? 8 * VLO * n : 64 * VLO + 8 * VHI * (n - 8));
+  lo.nrm = 32 * j;
 
-  // First tile's loads go out before anything else.
-  TileRegs cur;
-  uint32_t t0 = t_begin + 32 * wave;
-  if (t0 < t_end) load_tile<KLO, KHI, VLO, VHI, QJL>(cur, t0, n, j, kbase, vbase, knb, vnb, zb, rnb);
+  // Tiles of this wave: first + STEP k, k < nt; the first nfull are whole.
+  constexpr uint32_t STEP = 32 * SW;
+  const uint32_t first = t_begin + 32 * wave;
+  const int nt = __builtin_amdgcn_readfirstlane(first < t_end ? static_cast<int>((t_end - first + STEP - 1) / STEP) : 0);
+  const int nfull =
+      __builtin_amdgcn_readfirstlane(first + 32 <= t_end ? static_cast<int>((t_end - first - 32) / STEP + 1) : 0);
 
   // ---- prologue: rotate the group's queries.  Thread (pi_i, kq) forms the
   // partial dot of rotated coordinate pi_i over inputs [32 kq, 32 kq + 32).
   float* qraw = reinterpret_cast<float*>(smem + PRO_OFF);  // [GMAX][D]
   float* ppart = qraw + GMAX * D;                            // [4][GMAX][D]
-  float* qrot = ppart + 4 * GMAX * D;                        // [GMAX][D]
-  float* urot = qrot + GMAX * D;                             // [GMAX][D] (QJL)
-  int* shx = reinterpret_cast<int*>(urot + (QJL ? GMAX * D : 0));  // [2][GMAX]
+  float* qrot = ppart + 4 * GMAX * D;                        // [GMAX][D] (QJL)
+  _Float16* frag = reinterpret_cast<_Float16*>(qrot + (QJL ? GMAX * D : 0));  // [NSET][2][GMAX+1][FROW]
+  int* shx = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(frag) + FRAG_BYTES);  // [2][GMAX]
+  uint32_t* umax = reinterpret_cast<uint32_t*>(shx + 2 * GMAX);                    // [GMAX] (QJL)
+  auto frag_row = [&](int set, int part, int g) { return frag + ((set * 2 + part) * (GMAX + 1) + g) * FROW; };
   const float* qg = q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D;
-  if (tid < G * (D / 4)) reinterpret_cast<float4*>(qraw)[tid] = reinterpret_cast<const float4*>(qg)[tid];
   const int pi_i = tid & (D - 1), kq = tid >> 7;
+
+  // The prologue's own loads go out first and the tile loads right after
+  // them: the prologue then waits only for its small L2-resident operands
+  // while the first two tiles stream in from HBM.
+  const float4 qv = tid < G * (D / 4) ? reinterpret_cast<const float4*>(qg)[tid] : float4{};
   float w[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) w[k] = ktab->pit[(32 * kq + k) * D + pi_i];
-
-  // replicated pair LUTs: entry e of width B at off_B + e*256 + replica*4
-  auto build_lut = [&](auto bw) {
+  // replicated pair LUTs: entry e of width B at off_B + e*256 + replica*4;
+  // thread t fills 16-byte chunks t, t + ST, ...
+  auto lut_vals = [&](auto bw, uint32_t(&v)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
     constexpr int B = decltype(bw)::value;
     if constexpr (LP::has(B)) {
       const uint16_t* cen = (KLO == B) ? ktab->cen16[0] : (KHI == B) ? ktab->cen16[1]
                           : (VLO == B) ? vtab->cen16[0] : vtab->cen16[1];
       constexpr int E = 1 << (2 * B);
       constexpr uint32_t MK = (1u << B) - 1u;
-      for (int c = threadIdx.x; c < E * 16; c += ST) {
-        const int e = c >> 4;
-        const uint32_t v = static_cast<uint32_t>(cen[e & MK]) | (static_cast<uint32_t>(cen[e >> B]) << 16);
-        reinterpret_cast<uint4*>(smem + LP::template off<B>())[c] = make_uint4(v, v, v, v);
+#pragma unroll
+      for (int r = 0; r * ST < E * 16; ++r) {
+        const int c = threadIdx.x + r * ST;
+        const int e = (c >> 4) & (E - 1);
+        v[r] = static_cast<uint32_t>(cen[e & MK]) | (static_cast<uint32_t>(cen[e >> B]) << 16);
       }
     }
   };
-  build_lut(std::integral_constant<int, 4>{});
-  build_lut(std::integral_constant<int, 3>{});
-  build_lut(std::integral_constant<int, 2>{});
+  auto lut_store = [&](auto bw, const uint32_t(&v)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
+    constexpr int B = decltype(bw)::value;
+    if constexpr (LP::has(B)) {
+      constexpr int E = 1 << (2 * B);
+#pragma unroll
+      for (int r = 0; r * ST < E * 16; ++r) {
+        const int c = threadIdx.x + r * ST;
+        if (c < E * 16) reinterpret_cast<uint4*>(smem + LP::template off<B>())[c] = make_uint4(v[r], v[r], v[r], v[r]);
+      }
+    }
+  };
+  uint32_t lv4[256 * 16 / ST + 1], lv3[64 * 16 / ST + 1], lv2[16 * 16 / ST + 1];
+  lut_vals(std::integral_constant<int, 4>{}, lv4);
+  lut_vals(std::integral_constant<int, 3>{}, lv3);
+  lut_vals(std::integral_constant<int, 2>{}, lv2);
+
+  TileRegs bufA, bufB;
+  load_tile<KLO, KHI, VLO, VHI, QJL>(bufA, first, rs, lo);
+  load_tile<KLO, KHI, VLO, VHI, QJL>(bufB, first + STEP, rs, lo);
+
+  // Power-of-two scale per head for the fp16 operand: Pi is orthogonal, so
+  // |q~_i| <= ||q~|| = ||q|| |qscale|, and sh = 14 - exponent of that bound
+  // keeps |q~_i| 2^sh below 2^14.  Head g = tid / 32 sums its squares over
+  // its 32 lanes.  (The sketch product u has no such bound; its scale comes
+  // from its maximum.)
+  {
+    const float ss = sum32(fmaf(qv.x, qv.x, fmaf(qv.y, qv.y, fmaf(qv.z, qv.z, qv.w * qv.w))));
+    if ((tid & 31) == 0 && tid < G * 32) {
+      int ex = 0;
+      const float nq = sqrtf(ss) * fabsf(qscale);
+      if (nq > 0.0f) frexpf(nq, &ex);
+      shx[tid >> 5] = 14 - ex;
+    }
+  }
+  if (tid < G * (D / 4)) reinterpret_cast<float4*>(qraw)[tid] = qv;
+  lut_store(std::integral_constant<int, 4>{}, lv4);
+  lut_store(std::integral_constant<int, 3>{}, lv3);
+  lut_store(std::integral_constant<int, 2>{}, lv2);
   if (threadIdx.x < 4)
     lutz[threadIdx.x] = ((threadIdx.x & 1) ? 0x3C00u : 0xBC00u) | (((threadIdx.x >> 1) & 1) ? 0x3C000000u : 0xBC000000u);
+  // row G of every fragment array is the zero row of the padding heads
+  if (tid < NSET * 2 * (FROW / 8))
+    reinterpret_cast<uint4*>(frag_row(tid / (2 * (FROW / 8)), (tid / (FROW / 8)) & 1, G))[tid % (FROW / 8)] = uint4{};
+  if (QJL && tid < GMAX) umax[tid] = 0u;
   __syncthreads();
 
   auto partial_dots = [&](const float (&m)[32], const float* src) {
@@ -255,99 +521,82 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       ppart[(kq * GMAX + g) * D + pi_i] = a;
     }
   };
-  auto reduce_parts = [&](float* dst, float scale) {
-    for (int idx = tid; idx < G * D; idx += ST) {
-      const int g = idx >> 7, i = idx & (D - 1);
-      dst[idx] = (ppart[(0 * GMAX + g) * D + i] + ppart[(1 * GMAX + g) * D + i] + ppart[(2 * GMAX + g) * D + i] +
-                  ppart[(3 * GMAX + g) * D + i]) * scale;
-    }
+  auto reduce_part = [&](int g, int i) {
+    return ((ppart[(0 * GMAX + g) * D + i] + ppart[(1 * GMAX + g) * D + i]) + ppart[(2 * GMAX + g) * D + i]) +
+           ppart[(3 * GMAX + g) * D + i];
+  };
+  // x 2^sh split into fp16 hi + lo, stored as coordinate i of head g
+  auto store_split = [&](int set, int g, int i, float x, int sh) {
+    const float xs = ldexpf(x, sh);
+    const _Float16 h = static_cast<_Float16>(xs);
+    frag_row(set, 0, g)[i] = h;
+    frag_row(set, 1, g)[i] = static_cast<_Float16>(xs - static_cast<float>(h));
   };
   partial_dots(w, qraw);
-  // Power-of-two scale per head for the fp16 operand: Pi is orthogonal, so
-  // |q~_i| <= ||q~|| = ||q|| |qscale|, and sh = 14 - exponent of that bound
-  // keeps |q~_i| 2^sh below 2^14.  (The sketch product u has no such bound;
-  // its scale comes from its maximum.)
-  for (int g = wave; g < G; g += SW) {
-    const float a0 = qraw[g * D + lane], a1 = qraw[g * D + lane + 64];
-    float ss = fmaf(a0, a0, a1 * a1);
+  if constexpr (QJL) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-    if (lane == 0) {
-      int ex = 0;
-      const float nq = sqrtf(ss) * fabsf(qscale);
-      if (nq > 0.0f) frexpf(nq, &ex);
-      shx[g] = 14 - ex;
+    for (int k = 0; k < 32; ++k) w[k] = ktab->sit[(32 * kq + k) * D + pi_i];
+  }
+  __syncthreads();
+  // q~ = scale * log2(e) * Pi q, one coordinate per thread and pass
+  constexpr int PER = GMAX * D / ST;
+  float uv[QJL ? PER : 1];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int idx = tid + r * ST;
+    if (idx < G * D) {
+      const int g = idx >> 7, i = idx & (D - 1);
+      const float x = reduce_part(g, i) * qscale;
+      store_split(0, g, i, x, shx[g]);
+      if constexpr (QJL) qrot[idx] = x;
+    }
+  }
+  if constexpr (QJL) {
+    // u = S q~ and its per-head maximum (the bits of a non-negative float
+    // order like the float)
+    __syncthreads();
+    partial_dots(w, qrot);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int idx = tid + r * ST;
+      uv[r] = 0.0f;
+      if (idx < G * D) {
+        uv[r] = reduce_part(idx >> 7, idx & (D - 1));
+        atomicMax(&umax[idx >> 7], __float_as_uint(fabsf(uv[r])));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int idx = tid + r * ST;
+      if (idx < G * D) {
+        const int g = idx >> 7;
+        int ex = 0;
+        const float mx = __uint_as_float(umax[g]);
+        if (mx > 0.0f) frexpf(mx, &ex);
+        store_split(1, g, idx & (D - 1), uv[r], 14 - ex);
+        if ((idx & (D - 1)) == 0) shx[GMAX + g] = 14 - ex;
+      }
     }
   }
   __syncthreads();
   // A-operand fragments: lane (n, j) holds coordinates 32 j + 8 ks + e of
-  // query head n of the group, as fp16 hi and lo parts
+  // query head n of the group (row G, zero, for padding heads)
   const bool head_ok = n < G;
+  const int frow = head_ok ? n : G;
   half8 qh[4], ql[4], uh[QJL ? 4 : 1], ul[QJL ? 4 : 1];
-  auto split_hl = [&](const float (&xs)[8], int sh, half8& hi, half8& lo) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = ldexpf(xs[e], sh);
-      const _Float16 h = static_cast<_Float16>(x);
-      hi[e] = head_ok ? h : static_cast<_Float16>(0.0f);
-      lo[e] = head_ok ? static_cast<_Float16>(x - static_cast<float>(h)) : static_cast<_Float16>(0.0f);
+  for (int ks = 0; ks < 4; ++ks) {
+    qh[ks] = *reinterpret_cast<const half8*>(frag_row(0, 0, frow) + 32 * j + 8 * ks);
+    ql[ks] = *reinterpret_cast<const half8*>(frag_row(0, 1, frow) + 32 * j + 8 * ks);
+    if constexpr (QJL) {
+      uh[ks] = *reinterpret_cast<const half8*>(frag_row(1, 0, frow) + 32 * j + 8 * ks);
+      ul[ks] = *reinterpret_cast<const half8*>(frag_row(1, 1, frow) + 32 * j + 8 * ks);
     }
-  };
-  auto fragments = [&](const float* v, int sh, half8 (&hi)[4], half8 (&lo)[4]) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const float4* src = reinterpret_cast<const float4*>(v + n * D + 32 * j + 8 * ks);
-      const float4 x0 = src[0], x1 = src[1];
-      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      split_hl(xs, sh, hi[ks], lo[ks]);
-    }
-  };
-  const int nn = head_ok ? n : 0;
-  const int shq = head_ok ? shx[n] : 0;
-  const float qinv = head_ok ? ldexpf(1.0f, -shq) : 0.0f;
-  float uinv = 0.0f;
-  if constexpr (!QJL) {
-    // straight from the four partial dots (same summation order as q~)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float xs[8];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        float4 t[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          t[k] = *reinterpret_cast<const float4*>(ppart + (k * GMAX + nn) * D + 32 * j + 8 * ks + 4 * h2);
-        xs[4 * h2 + 0] = (t[0].x + t[1].x + t[2].x + t[3].x) * qscale;
-        xs[4 * h2 + 1] = (t[0].y + t[1].y + t[2].y + t[3].y) * qscale;
-        xs[4 * h2 + 2] = (t[0].z + t[1].z + t[2].z + t[3].z) * qscale;
-        xs[4 * h2 + 3] = (t[0].w + t[1].w + t[2].w + t[3].w) * qscale;
-      }
-      split_hl(xs, shq, qh[ks], ql[ks]);
-    }
-  } else {
-    reduce_parts(qrot, qscale);
-#pragma unroll
-    for (int k = 0; k < 32; ++k) w[k] = ktab->sit[(32 * kq + k) * D + pi_i];
-    __syncthreads();
-    partial_dots(w, qrot);
-    __syncthreads();
-    reduce_parts(urot, 1.0f);
-    __syncthreads();
-    for (int g = wave; g < G; g += SW) {
-      const float* v = urot + g * D;
-      float mx = fmaxf(fabsf(v[lane]), fabsf(v[lane + 64]));
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      int ex = 0;
-      if (mx > 0.0f) frexpf(mx, &ex);
-      if (lane == 0) shx[GMAX + g] = 14 - ex;
-    }
-    __syncthreads();
-    fragments(qrot, shq, qh, ql);
-    const int shu = head_ok ? shx[GMAX + n] : 0;
-    fragments(urot, shu, uh, ul);
-    uinv = head_ok ? ldexpf(QJL_C, -shu) : 0.0f;
   }
+  const float qinv = head_ok ? ldexpf(1.0f, -shx[n]) : 0.0f;
+  const float uinv = QJL && head_ok ? ldexpf(QJL_C, -shx[GMAX + n]) : 0.0f;
 
   const uint8_t* lut_klo = smem + LP::template off<KLO>();
   const uint8_t* lut_khi = smem + LP::template off<KHI>();
@@ -363,9 +612,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   f32x4 acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f32x4{};
-  const bool vskip_on = v_skip > 0.0f;
 
-  auto tile_step = [&]<bool FULL, bool VSKIP>(const TileRegs& tr, uint32_t t0c) {
+  auto tile_step = [&]<bool FULL, bool VSKIP>(const TileRegs& tr, uint32_t t0c) __attribute__((always_inline)) {
     const int nvalid = FULL ? 8 : static_cast<int>(t_end) - static_cast<int>(t0c + 8 * j);
     // two accumulator chains per M-block: hi and lo query parts accumulate
     // into one; the QJL sign products into another
@@ -413,8 +661,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         if constexpr (!FULL) s[e] = e < nvalid ? s[e] : -INFINITY;
         tmax = fmaxf(tmax, s[e]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_xor16_32(tmax);
     // rescale only when some head's maximum grew past the slack
     if (__any(tmax > m_run + RESCALE_SLACK)) {
       const float m_new = tmax > m_run + RESCALE_SLACK ? tmax : m_run;
@@ -445,9 +692,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         v0 = e < nvalid ? v0 : 0.0f;
         v1 = e + 1 < nvalid ? v1 : 0.0f;
       }
-      const _Float16 h0 = static_cast<_Float16>(p0 * v0), h1 = static_cast<_Float16>(p1 * v1);
-      pw[e >> 1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
-                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+      const half2v h = {static_cast<_Float16>(p0 * v0), static_cast<_Float16>(p1 * v1)};
+      pw[e >> 1] = __builtin_bit_cast(uint32_t, h);
     }
     l_run += psum;
     // skip the value work of a tile whose weights all fell below v_skip
@@ -463,33 +709,30 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
   };
 
-  // Tiles in flight per wave: two (the buffers swap roles each tile); the
-  // three-deep variant is kept for register-light instances.
-  constexpr uint32_t STEP = 32 * SW;
-  constexpr int DEPTH = 2;
-  auto run = [&](TileRegs& compute, TileRegs& refill, uint32_t ahead) -> bool {
-    if (t0 >= t_end) return false;
-    if (t0 + ahead < t_end) load_tile<KLO, KHI, VLO, VHI, QJL>(refill, t0 + ahead, n, j, kbase, vbase, knb, vnb, zb, rnb);
-    if (vskip_on) {
-      if (t0 + 32 <= t_end) tile_step.template operator()<true, true>(compute, t0);
-      else tile_step.template operator()<false, true>(compute, t0);
-    } else {
-      if (t0 + 32 <= t_end) tile_step.template operator()<true, false>(compute, t0);
-      else tile_step.template operator()<false, false>(compute, t0);
+  // Two tiles in flight per wave in fixed registers: each buffer is refilled
+  // with the tile after next as soon as its tile has been consumed.  The
+  // loop body is straight-line, so the outstanding loads at every use are
+  // exactly the other buffer's.
+  auto stream_tiles = [&]<bool VSKIP>() __attribute__((always_inline)) {
+    int k = 0;
+    for (; k + 2 <= nfull; k += 2) {
+      const uint32_t ta = first + STEP * k;
+      tile_step.template operator()<true, VSKIP>(bufA, ta);
+      load_tile<KLO, KHI, VLO, VHI, QJL>(bufA, ta + 2 * STEP, rs, lo);
+      tile_step.template operator()<true, VSKIP>(bufB, ta + STEP);
+      load_tile<KLO, KHI, VLO, VHI, QJL>(bufB, ta + 3 * STEP, rs, lo);
     }
-    t0 += STEP;
-    return true;
+    // at most one whole tile and one partial tile remain
+    const uint32_t ta = first + STEP * k;
+    if (k < nfull) {
+      tile_step.template operator()<true, VSKIP>(bufA, ta);
+      if (k + 1 < nt) tile_step.template operator()<false, VSKIP>(bufB, ta + STEP);
+    } else if (k < nt) {
+      tile_step.template operator()<false, VSKIP>(bufA, ta);
+    }
   };
-  if constexpr (DEPTH == 3) {
-    TileRegs b1, b2;
-    if (t0 + STEP < t_end) load_tile<KLO, KHI, VLO, VHI, QJL>(b1, t0 + STEP, n, j, kbase, vbase, knb, vnb, zb, rnb);
-    while (run(cur, b2, 2 * STEP) && run(b1, cur, 2 * STEP) && run(b2, b1, 2 * STEP)) {
-    }
-  } else {
-    TileRegs b1;
-    while (run(cur, b1, STEP) && run(b1, cur, STEP)) {
-    }
-  }
+  if (v_skip > 0.0f) stream_tiles.template operator()<true>();
+  else stream_tiles.template operator()<false>();
 
   // ---- merge the waves; l: sum over the 4 token lanes of a head.
   l_run += __shfl_xor(l_run, 16);
@@ -523,7 +766,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         l = fmaf(f, mrg_l[w * 16 + g], l);
       }
     }
-    float* part = parts + ((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * n_split + split) * PART;
+    float* part = parts + ((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * gridDim.x + split) * PART;
     part[4 + c] = a;
     if (c == 0) {
       part[0] = M;
@@ -536,40 +779,30 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
 // ---------------------------------------------------------------------------
 // combine: one workgroup of 256 threads per (sequence, query head, output
 // slice of 128 / NQ coordinates): log-sum-exp merge of the split partials
-// and the raw bf16 sink tokens, and the slice of the inverse rotation
-// Pi_V^T.  Many small workgroups keep the loads spread over many CUs, and
-// every global load is issued before the first barrier.
+// (rotated value domain) and of the sink partial (original domain, slot
+// n_split when present), and the slice of the inverse rotation Pi_V^T.
+// Many small workgroups keep the loads spread over many CUs, and every
+// global load is issued before the first barrier.
 constexpr int CT = 256;
 
 template <int NQ>
-__global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ vtab, const float* __restrict__ q,
-                                                     const uint16_t* __restrict__ sink_k,
-                                                     const uint16_t* __restrict__ sink_v,
-                                                     const int32_t* __restrict__ seq_lens,
-                                                     const float* __restrict__ parts, float* __restrict__ out,
-                                                     int hq, int hkv, int sink, int n_split, float qscale) {
+__global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ vtab, const float* __restrict__ parts,
+                                                     float* __restrict__ out, int n_split, int n_slot) {
   constexpr int OW = D / NQ;         // output coordinates of this workgroup
   constexpr int CQ = CT / OW;        // rotated-coordinate chunks
   constexpr int CK = D / CQ;         // rotated coordinates per chunk
-  __shared__ float wsp[MAX_SPLIT];   // split maxima, then weights
-  __shared__ float lsp[MAX_SPLIT];   // split sums
-  __shared__ float ssc[MAX_SINK];    // sink scores, then weights
-  __shared__ float qv[D];
-  __shared__ float rs[2][D];         // rotated-domain sums (two split halves)
+  __shared__ float wsp[MAX_SPLIT + 1];  // slot maxima, then weights
+  __shared__ float lsp[MAX_SPLIT + 1];  // slot sums
+  __shared__ float rs[2][D];            // rotated-domain sums (two split halves)
   __shared__ float ob[CQ][OW];
   __shared__ float red[8];
   const int bh = blockIdx.x / NQ, qo = blockIdx.x % NQ;
-  const int b = bh / hq, h = bh % hq, kh = h / (hq / hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* pp = parts + static_cast<int64_t>(bh) * n_split * PART;
-  const int64_t L = seq_lens[b];
-  const int ns = static_cast<int>(L < sink ? L : sink);
-  const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
-  const uint16_t* sk = sink_k + stream * static_cast<int64_t>(sink) * D;
-  const uint16_t* sv = sink_v + stream * static_cast<int64_t>(sink) * D;
-  // thread roles: (c, hs) for the rotated sums, (i, cq) for the rotation
+  const float* pp = parts + static_cast<int64_t>(bh) * n_slot * PART;
+  // thread roles: (c, hs) for the rotated sums, (oi, cq) for the rotation
   const int c = tid & (D - 1), hs = tid >> 7;
   const int oi = tid % OW, cq = tid / OW, gi = qo * OW + oi;
+  const bool has_sink = n_slot > n_split;
 
   // ---- loads
   constexpr int PA = 16;
@@ -582,79 +815,29 @@ __global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ 
   float pic[CK];
 #pragma unroll
   for (int k = 0; k < CK; ++k) pic[k] = vtab->pi[(CK * cq + k) * D + gi];
-  constexpr int SVN = 16;
-  float svv[SVN];
-#pragma unroll
-  for (int u = 0; u < SVN; ++u) {
-    const int t = cq + CQ * u;
-    svv[u] = t < ns ? __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + gi]) << 16) : 0.0f;
-  }
-  const bool has_row = tid < ns;
-  uint4 krow[D / 8];
-  if (has_row) {
-    const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(tid) * D);
-#pragma unroll
-    for (int k = 0; k < D / 8; ++k) krow[k] = row[k];
-  }
+  const float sacc = has_sink && cq == 0 ? pp[static_cast<int64_t>(n_split) * PART + 4 + gi] : 0.0f;
   float mloc = -INFINITY;
-  for (int sp = tid; sp < n_split; sp += CT) {
+  for (int sp = tid; sp < n_slot; sp += CT) {
     const float m = pp[static_cast<int64_t>(sp) * PART], l = pp[static_cast<int64_t>(sp) * PART + 1];
     const float mv = l > 0.0f ? m : -INFINITY;
     wsp[sp] = mv;
     lsp[sp] = l;
     mloc = fmaxf(mloc, mv);
   }
-  if (ns > 0 && tid < D) qv[tid] = q[static_cast<int64_t>(bh) * D + tid] * qscale;
-  __syncthreads();
-
-  // ---- sink scores, maximum
-  auto row_dot = [&](const uint4 (&rw)[D / 8]) {
-    float dot = 0.0f;
 #pragma unroll
-    for (int k = 0; k < D / 8; ++k) {
-      const uint4 wv = rw[k];
-      dot = fmaf(__uint_as_float(wv.x << 16), qv[8 * k], dot);
-      dot = fmaf(__uint_as_float(wv.x & 0xFFFF0000u), qv[8 * k + 1], dot);
-      dot = fmaf(__uint_as_float(wv.y << 16), qv[8 * k + 2], dot);
-      dot = fmaf(__uint_as_float(wv.y & 0xFFFF0000u), qv[8 * k + 3], dot);
-      dot = fmaf(__uint_as_float(wv.z << 16), qv[8 * k + 4], dot);
-      dot = fmaf(__uint_as_float(wv.z & 0xFFFF0000u), qv[8 * k + 5], dot);
-      dot = fmaf(__uint_as_float(wv.w << 16), qv[8 * k + 6], dot);
-      dot = fmaf(__uint_as_float(wv.w & 0xFFFF0000u), qv[8 * k + 7], dot);
-    }
-    return dot;
-  };
-  if (has_row) {
-    const float d0 = row_dot(krow);
-    ssc[tid] = d0;
-    mloc = fmaxf(mloc, d0);
-  }
-  for (int t = tid + CT; t < ns; t += CT) {
-    uint4 rw[D / 8];
-    const uint4* row = reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(t) * D);
-#pragma unroll
-    for (int k = 0; k < D / 8; ++k) rw[k] = row[k];
-    const float d1 = row_dot(rw);
-    ssc[t] = d1;
-    mloc = fmaxf(mloc, d1);
-  }
   for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
   if (lane == 0) red[wave] = mloc;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   // ---- weights and normaliser
   float lloc = 0.0f;
-  for (int sp = tid; sp < n_split; sp += CT) {
+  for (int sp = tid; sp < n_slot; sp += CT) {
     const float mv = wsp[sp];
     const float f = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
     wsp[sp] = f;
     lloc = fmaf(f, lsp[sp], lloc);
   }
-  for (int t = tid; t < ns; t += CT) {
-    const float wt = __builtin_amdgcn_exp2f(ssc[t] - M);
-    ssc[t] = wt;
-    lloc += wt;
-  }
+#pragma unroll
   for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
   __syncthreads();
   if (lane == 0) red[4 + wave] = lloc;
@@ -668,15 +851,11 @@ __global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ 
   rs[hs][c] = a;
   __syncthreads();
   const float Ls = red[4] + red[5] + red[6] + red[7];
-  // ---- slice of the inverse rotation (+ raw sink values): thread (oi, cq)
+  // ---- slice of the inverse rotation (+ the sink values): thread (oi, cq)
   float o = 0.0f;
 #pragma unroll
   for (int k = 0; k < CK; ++k) o = fmaf(pic[k], rs[0][CK * cq + k] + rs[1][CK * cq + k], o);
-#pragma unroll
-  for (int u = 0; u < SVN; ++u)
-    if (cq + CQ * u < ns) o = fmaf(ssc[cq + CQ * u], svv[u], o);
-  for (int t = cq + CQ * SVN; t < ns; t += CQ)
-    o = fmaf(ssc[t], __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + gi]) << 16), o);
+  if (has_sink && cq == 0) o = fmaf(wsp[n_split], sacc, o);
   ob[cq][oi] = o;
   __syncthreads();
   if (tid < OW) {
@@ -689,11 +868,12 @@ __global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ 
 
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
-                        const tq_attn& a, const AttendPlan& plan, const float* q, const int32_t* seq_lens,
-                        float* parts, hipStream_t st) {
-  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_split, a.hkv, a.batch), dim3(ST), 0, st,
+                        const tq_attn& a, const AttendPlan& plan, const float* q, const uint16_t* sink_k,
+                        const uint16_t* sink_v, const int32_t* seq_lens, float* parts, hipStream_t st) {
+  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_slot, a.hkv, a.batch), dim3(ST), 0, st,
                      ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms, vc.cap,
-                     seq_lens, q, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.v_skip, a.scale * LOG2E);
+                     seq_lens, q, sink_k, sink_v, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.v_skip,
+                     a.scale * LOG2E);
   return hipGetLastError();
 }
 
@@ -705,6 +885,8 @@ struct SplitArgs {
   const tq_attn* a;
   const AttendPlan* plan;
   const float* q;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
   const int32_t* seq_lens;
   float* parts;
   hipStream_t st;
@@ -712,10 +894,10 @@ struct SplitArgs {
 
 template <int KLO, int KHI, int VLO, int VHI>
 hipError_t launch_q(bool qjl, const SplitArgs& f) {
-  return qjl ? launch_split<KLO, KHI, VLO, VHI, true>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.seq_lens,
-                                                      f.parts, f.st)
-             : launch_split<KLO, KHI, VLO, VHI, false>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.seq_lens,
-                                                       f.parts, f.st);
+  return qjl ? launch_split<KLO, KHI, VLO, VHI, true>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
+                                                      f.sink_v, f.seq_lens, f.parts, f.st)
+             : launch_split<KLO, KHI, VLO, VHI, false>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
+                                                       f.sink_v, f.seq_lens, f.parts, f.st);
 }
 
 template <int KLO, int KHI>
@@ -751,9 +933,10 @@ AttendPlan plan_attend(const tq_attn& a) {
   ns = (tiles + chunk_tiles - 1) / chunk_tiles;
   if (ns < 1) ns = 1;
   p.n_split = static_cast<int>(ns);
+  p.n_slot = p.n_split + (a.sink > 0 ? 1 : 0);
   p.chunk = chunk_tiles * TILE;
   const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
-  p.ws_bytes = static_cast<size_t>(heads) * static_cast<int64_t>(p.n_split) * PART * sizeof(float);
+  p.ws_bytes = static_cast<size_t>(heads) * static_cast<int64_t>(p.n_slot) * PART * sizeof(float);
   return p;
 }
 
@@ -762,7 +945,7 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                          void* workspace, hipStream_t st) {
   float* parts = static_cast<float*>(workspace);
-  const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, seq_lens, parts, st};
+  const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, st};
   const int vkey = vs.bits_lo * 10 + vs.bits_hi;
   const bool qjl = ks.qjl_m != 0;
   hipError_t e;
@@ -778,11 +961,11 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
   // four output slices per head while the heads alone would leave most CUs idle
   const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
   if (heads < 256)
-    hipLaunchKernelGGL(combine_kernel<4>, dim3(static_cast<unsigned>(heads * 4)), dim3(CT), 0, st, vtab, q, sink_k,
-                       sink_v, seq_lens, parts, out, a.hq, a.hkv, a.sink, plan.n_split, a.scale * LOG2E);
+    hipLaunchKernelGGL(combine_kernel<4>, dim3(static_cast<unsigned>(heads * 4)), dim3(CT), 0, st, vtab, parts, out,
+                       plan.n_split, plan.n_slot);
   else
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(static_cast<unsigned>(heads)), dim3(CT), 0, st, vtab, q, sink_k,
-                       sink_v, seq_lens, parts, out, a.hq, a.hkv, a.sink, plan.n_split, a.scale * LOG2E);
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(static_cast<unsigned>(heads)), dim3(CT), 0, st, vtab, parts, out,
+                       plan.n_split, plan.n_slot);
   return hipGetLastError();
 }
 

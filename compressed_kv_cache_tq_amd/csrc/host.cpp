@@ -515,6 +515,8 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
   if (!std::isfinite(a.scale)) return fail(TQ_E_ARG, "scale must be finite");
   if (a.batch == 0) return TQ_OK;
   if (vc->cap % tq::TILE || kc->cap % tq::TILE) return fail(TQ_E_ARG, "cache caps must be multiples of 32");
+  if (vc->cap > (int64_t{1} << 24) || kc->cap > (int64_t{1} << 24))
+    return fail(TQ_E_UNSUPPORTED, "cache caps above 2^24 positions");
   if (a.max_len - a.sink > std::min(kc->cap, vc->cap))
     return fail(TQ_E_ARG, "max_len - sink exceeds the cache capacity");
   if (!q || !out || !seq_lens) return fail(TQ_E_ARG, "q, out and seq_lens must be non-NULL");

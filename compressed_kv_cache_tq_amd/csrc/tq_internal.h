@@ -78,6 +78,7 @@ hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const v
 
 struct AttendPlan {
   int n_split;       // splits of the compressed token range per (b, kv head)
+  int n_slot;        // partials per query head: n_split, plus one for the sink tokens
   int64_t chunk;     // tokens per split (multiple of TILE)
   size_t ws_bytes;   // workspace needed
 };

@@ -185,7 +185,8 @@ size_t tq_attend_workspace_bytes(const tq_attn* attn);
  *   q        device fp32 [batch][hq][d]
  *   sink_k/sink_v  device bf16 [batch][hkv][sink][d] (NULL iff sink == 0);
  *            sink <= 512
- *   kc->cap and vc->cap must be multiples of 32.
+ *   kc->cap and vc->cap must be multiples of 32 and at most 2^24 (one
+ *            stream's arrays are addressed with 32-bit offsets).
  *   seq_lens device int32 [batch]: tokens of each sequence including the
  *            sink; compressed token t >= sink lives at cache position t-sink.
  *            Each value must lie in [0, sink + min(kc->cap, vc->cap)] and

@@ -200,6 +200,8 @@ def test_attend_argument_errors_without_launch():
     assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), q=None) == -1
     assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), ks_=vs, vs_=ks) == -2  # layouts swapped
     assert call(tq.TqAttn(1, 8, 2, 513, 0.1, 0.0, 600)) == -2         # sink limit
+    big = tq.TqCache(0x1000, 0x2000, None, None, (1 << 24) + 32)
+    assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), kc_=big) == -2   # cap above 2^24
     assert call(tq.TqAttn(0, 8, 2, 0, 0.1, 0.0, 64)) == 0             # empty batch: nothing launched
     ws = tq.attend_workspace_bytes(2, 32, 8, 0, 32768)
     assert ws >= 2 * 32 * (2 * 128 + 4) * 4
