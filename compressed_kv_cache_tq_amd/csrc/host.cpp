@@ -422,6 +422,17 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
       t->pi_hi[i] = hi;
       t->pi_lo[i] = to_half(v - from_half(hi));
     }
+    for (int lay = 0; lay < 2; ++lay)
+      for (int w = 0; w < 2; ++w)
+        for (int tt = 0; tt < 2; ++tt)
+          for (int ks = 0; ks < 8; ++ks)
+            for (int lane = 0; lane < 64; ++lane)
+              for (int e = 0; e < 8; ++e) {
+                const int row = tq::frag_row(lay, w, tt, lane), col = 16 * ks + 8 * (lane >> 5) + e;
+                const int dst = ((((w * 2 + tt) * 8 + ks) * 64 + lane) * 8) + e;
+                t->pi_frag[lay][0][dst] = t->pi_hi[row * tq::D + col];
+                t->pi_frag[lay][1][dst] = t->pi_lo[row * tq::D + col];
+              }
     if (sp.qjl_m) {
       gaussian_fill(spec->qjl_seed, m.data(), static_cast<size_t>(tq::QJL_M) * tq::D);
       for (int i = 0; i < tq::QJL_M; ++i)

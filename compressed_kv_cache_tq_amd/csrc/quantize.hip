@@ -679,22 +679,23 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
   const int pt = tid & 127;
   const int h = lane >> 5, l32 = lane & 31;
 
-  for (int c = tid; c < 2 * CELL_ENTRIES; c += RQ_THREADS)
-    cell_s[c / CELL_ENTRIES][c % CELL_ENTRIES] =
-        make_uint2(tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][0], tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][1]);
+  // cell tables: loaded first, stored to LDS once the first tile is staged
+  // (a store right here would hold back every later load behind this one)
+  static_assert(2 * CELL_ENTRIES <= 2 * RQ_THREADS, "cell table fill");
+  const uint2* cell_g = reinterpret_cast<const uint2*>(tab->cell);
+  const uint2 cv0 = cell_g[tid];
+  const uint2 cv1 = tid + RQ_THREADS < 2 * CELL_ENTRIES ? cell_g[tid + RQ_THREADS] : uint2{};
 
-  // ---- rotation fragments of this wave's 64 coordinates, for the whole launch
+  // ---- rotation fragments of this wave's 64 coordinates, for the whole
+  // launch (stored in fragment order: each load is a contiguous 1 KiB)
   half8 pih[2][8], pil[2][8];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    int row;
-    if constexpr (TILED) row = 64 * w + 32 * t + l32;
-    else row = 64 * w + 32 * ((l32 >> 2) & 1) + 16 * t + 4 * (l32 >> 3) + (l32 & 3);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const int col = 16 * ks + 8 * h;
-      pih[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_hi + row * D + col));
-      pil[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_lo + row * D + col));
+      const int fo = (((w * 2 + t) * 8 + ks) * 64 + lane) * 8;
+      pih[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_frag[TILED][0] + fo));
+      pil[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_frag[TILED][1] + fo));
     }
   }
 
@@ -816,6 +817,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
   load_x(first + 2, X[2]);
   stage(first, X[0], 0);
   load_x(first + 3, X[0]);
+  reinterpret_cast<uint2*>(cell_s)[tid] = cv0;
+  if (tid + RQ_THREADS < 2 * CELL_ENTRIES) reinterpret_cast<uint2*>(cell_s)[tid + RQ_THREADS] = cv1;
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < K; ++k) {

@@ -58,7 +58,22 @@ struct alignas(256) Tables {
   // [c/64 - 1, (c+1)/64 - 1) or of +inf, number of boundaries below c/64 - 1},
   // so the code of y is code_low + (y > boundary).
   uint32_t cell[2][CELL_ENTRIES][2];
+  // pi_hi / pi_lo again, in the register order of the rotation kernel's MFMA
+  // fragments so that every fragment load is one contiguous 1 KiB read:
+  // [layout (record, tiled)][hi, lo][w][t][ks][lane][8], the 8 values of
+  // row frag_row(layout, w, t, lane), columns 16 ks + 8 (lane / 32) + e.
+  uint16_t pi_frag[2][2][D * D];
 };
+
+// Row of 256 Pi held by lane `lane` (of wave w of a pair, M-block t) in the
+// rotation kernel's fragments.  Record layout: Pi is the A operand, rows
+// permuted so that a lane's 32 accumulator values are 32 consecutive rotated
+// coordinates; tiled layout: Pi^T is the B operand, row 64 w + 32 t + lane.
+inline int frag_row(int tiled, int w, int t, int lane) {
+  const int l32 = lane & 31;
+  if (tiled) return 64 * w + 32 * t + l32;
+  return 64 * w + 32 * ((l32 >> 2) & 1) + 16 * t + 4 * (l32 >> 3) + (l32 & 3);
+}
 
 constexpr float PI_SCALE = 256.0f;
 

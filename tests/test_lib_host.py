@@ -51,6 +51,32 @@ def test_sketch_matches_oracle():
     assert np.max(np.abs(s - orot.sketch(1, 128, 128))) <= 1e-13
 
 
+def _check_pi_frag(frag, pi_hi, pi_lo):
+    """The fragment-ordered copy of pi_hi / pi_lo: [layout][hi, lo][w][t][ks][lane][e]
+    holds row r(layout, w, t, lane), column 16 ks + 8 (lane // 32) + e."""
+    lane = np.arange(64)
+    l32 = lane % 32
+    for lay in range(2):
+        for w in range(2):
+            for t in range(2):
+                if lay:
+                    row = 64 * w + 32 * t + l32
+                else:
+                    row = 64 * w + 32 * ((l32 >> 2) & 1) + 16 * t + 4 * (l32 >> 3) + (l32 & 3)
+                for ks in range(8):
+                    col = 16 * ks + 8 * (lane[:, None] // 32) + np.arange(8)[None, :]
+                    assert np.array_equal(frag[lay, 0, w, t, ks], pi_hi[row[:, None], col])
+                    assert np.array_equal(frag[lay, 1, w, t, ks], pi_lo[row[:, None], col])
+    # every row appears: each (layout, w) covers 64 distinct rows per t pair
+    for lay in range(2):
+        rows = set()
+        for w in range(2):
+            for t in range(2):
+                rows |= set((64 * w + 32 * t + l32).tolist() if lay else
+                            (64 * w + 32 * ((l32 >> 2) & 1) + 16 * t + 4 * (l32 >> 3) + (l32 & 3)).tolist())
+        assert rows == set(range(128))
+
+
 def _tables_view(spec):
     buf = tq.tables_build(spec)
     hdr = buf[:32].view(np.uint32)
@@ -78,6 +104,9 @@ def _tables_view(spec):
     assert np.max(np.abs(parts.sum(0) - ref)) <= 2.0 ** -24 * np.abs(ref).max()
     off += 3 * 32768
     cells = buf[off: off + 2 * 132 * 8].view(np.uint32).reshape(2, 132, 2)
+    off += 2 * 132 * 8
+    frag = buf[off: off + 2 * 2 * 32768].view(np.float16).reshape(2, 2, 2, 2, 8, 64, 8)
+    _check_pi_frag(frag, pi_hi, pi_lo)
     bnd = buf[32: 32 + 128].view(np.float32).reshape(2, 16)
     cen = buf[160: 160 + 128].view(np.float32).reshape(2, 16)
     cen16 = buf[288: 288 + 64].view(np.float16).reshape(2, 16)
@@ -87,7 +116,7 @@ def _tables_view(spec):
 def test_tables_content():
     spec = tq.Spec(4, 3, split=64, qjl_m=128)
     hdr, pi, pi_hi, pi_lo, s, s_hi, s_lo, bnd, cen, cen16, cells = _tables_view(spec)
-    assert tq.tables_bytes() >= 512 + 6 * 65536 + 3 * 32768 + 2 * 132 * 8
+    assert tq.tables_bytes() >= 512 + 6 * 65536 + 3 * 32768 + 2 * 132 * 8 + 4 * 32768
     assert tq.tables_bytes() % 256 == 0
     assert hdr[0] == 0x31515454 and hdr[1] == 1 and hdr[2] == 4 and hdr[3] == 3
     ref = orot.rotation(0, 128)
