@@ -379,6 +379,64 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
                  gridDim.x * PART);
     return;
   }
+  // ---- prologue: rotate the group's queries.  Thread (pi_i, kq) forms the
+  // partial dot of rotated coordinate pi_i over inputs [32 kq, 32 kq + 32).
+  float* qraw = reinterpret_cast<float*>(smem + PRO_OFF);  // [GMAX][D]
+  float* ppart = qraw + GMAX * D;                            // [4][GMAX][D]
+  float* qrot = ppart + 4 * GMAX * D;                        // [GMAX][D] (QJL)
+  _Float16* frag = reinterpret_cast<_Float16*>(qrot + (QJL ? GMAX * D : 0));  // [NSET][2][GMAX+1][FROW]
+  int* shx = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(frag) + FRAG_BYTES);  // [2][GMAX]
+  uint32_t* umax = reinterpret_cast<uint32_t*>(shx + 2 * GMAX);                    // [GMAX] (QJL)
+  auto frag_row = [&](int set, int part, int g) { return frag + ((set * 2 + part) * (GMAX + 1) + g) * FROW; };
+  const float* qg = q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D;
+  const int pi_i = tid & (D - 1), kq = tid >> 7;
+
+  // The prologue's own loads go out first (the centroids before Pi, so that
+  // the LUT stores wait for them alone), the sequence length is read only
+  // then, and the tile loads follow: the prologue waits only for its small
+  // L2-resident operands while the first two tiles stream in from HBM.
+  const float4 qv = tid < G * (D / 4) ? reinterpret_cast<const float4*>(qg)[tid] : float4{};
+  // replicated pair LUTs: entry e of width B at off_B + e*256 + replica*4;
+  // thread t fills 16-byte chunks t, t + ST, ... from centroids (lo, hi)
+  auto lut_vals = [&](auto bw, uint16_t(&cl)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1],
+                      uint16_t(&ch)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
+    constexpr int B = decltype(bw)::value;
+    if constexpr (LP::has(B)) {
+      const uint16_t* cen = (KLO == B) ? ktab->cen16[0] : (KHI == B) ? ktab->cen16[1]
+                          : (VLO == B) ? vtab->cen16[0] : vtab->cen16[1];
+      constexpr int E = 1 << (2 * B);
+      constexpr uint32_t MK = (1u << B) - 1u;
+#pragma unroll
+      for (int r = 0; r * ST < E * 16; ++r) {
+        const int c = threadIdx.x + r * ST;
+        const int e = (c >> 4) & (E - 1);
+        cl[r] = cen[e & MK];
+        ch[r] = cen[e >> B];
+      }
+    }
+  };
+  auto lut_store = [&](auto bw, const uint16_t(&cl)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1],
+                       const uint16_t(&ch)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
+    constexpr int B = decltype(bw)::value;
+    if constexpr (LP::has(B)) {
+      constexpr int E = 1 << (2 * B);
+#pragma unroll
+      for (int r = 0; r * ST < E * 16; ++r) {
+        const int c = threadIdx.x + r * ST;
+        const uint32_t v = static_cast<uint32_t>(cl[r]) | (static_cast<uint32_t>(ch[r]) << 16);
+        if (c < E * 16) reinterpret_cast<uint4*>(smem + LP::template off<B>())[c] = make_uint4(v, v, v, v);
+      }
+    }
+  };
+  uint16_t l4l[256 * 16 / ST + 1], l4h[256 * 16 / ST + 1], l3l[64 * 16 / ST + 1], l3h[64 * 16 / ST + 1],
+      l2l[16 * 16 / ST + 1], l2h[16 * 16 / ST + 1];
+  lut_vals(std::integral_constant<int, 4>{}, l4l, l4h);
+  lut_vals(std::integral_constant<int, 3>{}, l3l, l3h);
+  lut_vals(std::integral_constant<int, 2>{}, l2l, l2h);
+  float w[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) w[k] = ktab->pit[(32 * kq + k) * D + pi_i];
+
   const int64_t comp = L > sink ? L - sink : 0;
   const int64_t t_begin64 = static_cast<int64_t>(split) * chunk;
   const uint32_t t_begin = static_cast<uint32_t>(t_begin64 < comp ? t_begin64 : comp);
@@ -424,58 +482,6 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   const int nfull =
       __builtin_amdgcn_readfirstlane(first + 32 <= t_end ? static_cast<int>((t_end - first - 32) / STEP + 1) : 0);
 
-  // ---- prologue: rotate the group's queries.  Thread (pi_i, kq) forms the
-  // partial dot of rotated coordinate pi_i over inputs [32 kq, 32 kq + 32).
-  float* qraw = reinterpret_cast<float*>(smem + PRO_OFF);  // [GMAX][D]
-  float* ppart = qraw + GMAX * D;                            // [4][GMAX][D]
-  float* qrot = ppart + 4 * GMAX * D;                        // [GMAX][D] (QJL)
-  _Float16* frag = reinterpret_cast<_Float16*>(qrot + (QJL ? GMAX * D : 0));  // [NSET][2][GMAX+1][FROW]
-  int* shx = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(frag) + FRAG_BYTES);  // [2][GMAX]
-  uint32_t* umax = reinterpret_cast<uint32_t*>(shx + 2 * GMAX);                    // [GMAX] (QJL)
-  auto frag_row = [&](int set, int part, int g) { return frag + ((set * 2 + part) * (GMAX + 1) + g) * FROW; };
-  const float* qg = q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D;
-  const int pi_i = tid & (D - 1), kq = tid >> 7;
-
-  // The prologue's own loads go out first and the tile loads right after
-  // them: the prologue then waits only for its small L2-resident operands
-  // while the first two tiles stream in from HBM.
-  const float4 qv = tid < G * (D / 4) ? reinterpret_cast<const float4*>(qg)[tid] : float4{};
-  float w[32];
-#pragma unroll
-  for (int k = 0; k < 32; ++k) w[k] = ktab->pit[(32 * kq + k) * D + pi_i];
-  // replicated pair LUTs: entry e of width B at off_B + e*256 + replica*4;
-  // thread t fills 16-byte chunks t, t + ST, ...
-  auto lut_vals = [&](auto bw, uint32_t(&v)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
-    constexpr int B = decltype(bw)::value;
-    if constexpr (LP::has(B)) {
-      const uint16_t* cen = (KLO == B) ? ktab->cen16[0] : (KHI == B) ? ktab->cen16[1]
-                          : (VLO == B) ? vtab->cen16[0] : vtab->cen16[1];
-      constexpr int E = 1 << (2 * B);
-      constexpr uint32_t MK = (1u << B) - 1u;
-#pragma unroll
-      for (int r = 0; r * ST < E * 16; ++r) {
-        const int c = threadIdx.x + r * ST;
-        const int e = (c >> 4) & (E - 1);
-        v[r] = static_cast<uint32_t>(cen[e & MK]) | (static_cast<uint32_t>(cen[e >> B]) << 16);
-      }
-    }
-  };
-  auto lut_store = [&](auto bw, const uint32_t(&v)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
-    constexpr int B = decltype(bw)::value;
-    if constexpr (LP::has(B)) {
-      constexpr int E = 1 << (2 * B);
-#pragma unroll
-      for (int r = 0; r * ST < E * 16; ++r) {
-        const int c = threadIdx.x + r * ST;
-        if (c < E * 16) reinterpret_cast<uint4*>(smem + LP::template off<B>())[c] = make_uint4(v[r], v[r], v[r], v[r]);
-      }
-    }
-  };
-  uint32_t lv4[256 * 16 / ST + 1], lv3[64 * 16 / ST + 1], lv2[16 * 16 / ST + 1];
-  lut_vals(std::integral_constant<int, 4>{}, lv4);
-  lut_vals(std::integral_constant<int, 3>{}, lv3);
-  lut_vals(std::integral_constant<int, 2>{}, lv2);
-
   TileRegs bufA, bufB;
   load_tile<KLO, KHI, VLO, VHI, QJL>(bufA, first, rs, lo);
   load_tile<KLO, KHI, VLO, VHI, QJL>(bufB, first + STEP, rs, lo);
@@ -495,9 +501,9 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
   }
   if (tid < G * (D / 4)) reinterpret_cast<float4*>(qraw)[tid] = qv;
-  lut_store(std::integral_constant<int, 4>{}, lv4);
-  lut_store(std::integral_constant<int, 3>{}, lv3);
-  lut_store(std::integral_constant<int, 2>{}, lv2);
+  lut_store(std::integral_constant<int, 4>{}, l4l, l4h);
+  lut_store(std::integral_constant<int, 3>{}, l3l, l3h);
+  lut_store(std::integral_constant<int, 2>{}, l2l, l2h);
   if (threadIdx.x < 4)
     lutz[threadIdx.x] = ((threadIdx.x & 1) ? 0x3C00u : 0xBC00u) | (((threadIdx.x >> 1) & 1) ? 0x3C000000u : 0xBC000000u);
   // row G of every fragment array is the zero row of the padding heads
