@@ -452,16 +452,19 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     return;
   }
 
-  // stream descriptors: the whole allocated range of the stream (cap
-  // positions), so tiles past the last one read zeros
+  // stream descriptors ending at the split's last token (for the value
+  // tiles, at the end of its tile): the loads of tiles past a wave's last one
+  // read zeros without touching memory, and so do a partial tile's tokens
+  // past the end
   StreamRsrc rs;
-  rs.kc = rsrc(kcodes + stream * kcap * KBYTES, kcap * KBYTES);
-  rs.vc = rsrc(vcodes + stream * vcap * VBYTES, vcap * VBYTES);
-  rs.kn = rsrc(knorms + stream * kcap, kcap * 4);
-  rs.vn = rsrc(vnorms + stream * vcap, vcap * 4);
+  const int64_t vend = (static_cast<int64_t>(t_end) + TILE - 1) / TILE * TILE;
+  rs.kc = rsrc(kcodes + stream * kcap * KBYTES, static_cast<int64_t>(t_end) * KBYTES);
+  rs.vc = rsrc(vcodes + stream * vcap * VBYTES, vend * VBYTES);
+  rs.kn = rsrc(knorms + stream * kcap, static_cast<int64_t>(t_end) * 4);
+  rs.vn = rsrc(vnorms + stream * vcap, static_cast<int64_t>(t_end) * 4);
   if constexpr (QJL) {
-    rs.zs = rsrc(ksigns + stream * kcap * (QJL_M / 8), kcap * (QJL_M / 8));
-    rs.rn = rsrc(krn + stream * kcap, kcap * 4);
+    rs.zs = rsrc(ksigns + stream * kcap * (QJL_M / 8), static_cast<int64_t>(t_end) * (QJL_M / 8));
+    rs.rn = rsrc(krn + stream * kcap, static_cast<int64_t>(t_end) * 4);
   } else {
     rs.zs = rs.rn = rs.kn;
   }
@@ -591,16 +594,23 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   // query head n of the group (row G, zero, for padding heads)
   const bool head_ok = n < G;
   const int frow = head_ok ? n : G;
-  half8 qh[4], ql[4], uh[QJL ? 4 : 1], ul[QJL ? 4 : 1];
+  // Without the sketch the query fragments live in registers; with it the
+  // registers go to the sign and residual-norm tiles, and all four fragment
+  // sets are read from LDS per tile instead.
+  half8 qh[QJL ? 1 : 4], ql[QJL ? 1 : 4];
+  const _Float16* fbase[4] = {frag_row(0, 0, frow) + 32 * j, frag_row(0, 1, frow) + 32 * j,
+                              frag_row(QJL ? 1 : 0, 0, frow) + 32 * j, frag_row(QJL ? 1 : 0, 1, frow) + 32 * j};
+  if constexpr (!QJL) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    qh[ks] = *reinterpret_cast<const half8*>(frag_row(0, 0, frow) + 32 * j + 8 * ks);
-    ql[ks] = *reinterpret_cast<const half8*>(frag_row(0, 1, frow) + 32 * j + 8 * ks);
-    if constexpr (QJL) {
-      uh[ks] = *reinterpret_cast<const half8*>(frag_row(1, 0, frow) + 32 * j + 8 * ks);
-      ul[ks] = *reinterpret_cast<const half8*>(frag_row(1, 1, frow) + 32 * j + 8 * ks);
+    for (int ks = 0; ks < 4; ++ks) {
+      qh[ks] = *reinterpret_cast<const half8*>(fbase[0] + 8 * ks);
+      ql[ks] = *reinterpret_cast<const half8*>(fbase[1] + 8 * ks);
     }
   }
+  auto frag_at = [&](int set, int ks) -> half8 {
+    if constexpr (!QJL) return set == 0 ? qh[ks] : ql[ks];
+    else return *reinterpret_cast<const half8*>(fbase[set] + 8 * ks);
+  };
   const float qinv = head_ok ? ldexpf(1.0f, -shx[n]) : 0.0f;
   const float uinv = QJL && head_ok ? ldexpf(QJL_C, -shx[GMAX + n]) : 0.0f;
 
@@ -620,6 +630,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   for (int k = 0; k < 8; ++k) acc[k] = f32x4{};
 
   auto tile_step = [&]<bool FULL, bool VSKIP>(const TileRegs& tr, uint32_t t0c) __attribute__((always_inline)) {
+    // keeps the LDS fragment reads of the sketch variant inside the loop
+    if constexpr (QJL) __asm__ volatile("" ::: "memory");
     const int nvalid = FULL ? 8 : static_cast<int>(t_end) - static_cast<int>(t0c + 8 * j);
     // two accumulator chains per M-block: hi and lo query parts accumulate
     // into one; the QJL sign products into another
@@ -635,7 +647,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         else a[mb] = j < 2 ? dequant8<KLO>(tr.kw[mb], ks, lut_klo, lane4) : dequant8<KHI>(tr.kw[mb], ks, lut_khi, lane4);
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], qh[ks], sk[mb]);
+      for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], frag_at(0, ks), sk[mb]);
       if constexpr (QJL) {
         half8 z[2];
 #pragma unroll
@@ -644,14 +656,14 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
           z[mb] = as_half8(lutz[zv & 3], lutz[(zv >> 2) & 3], lutz[(zv >> 4) & 3], lutz[zv >> 6]);
         }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], uh[ks], sz[mb]);
+        for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], frag_at(2, ks), sz[mb]);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], ql[ks], sk[mb]);
+        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], frag_at(1, ks), sk[mb]);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], ul[ks], sz[mb]);
+        for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], frag_at(3, ks), sz[mb]);
       } else {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], ql[ks], sk[mb]);
+        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], frag_at(1, ks), sk[mb]);
       }
     }
     float s[8];
