@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the TurboQuant packed-KV hot path on one MI355X.
 
-One step = one pass of the whole path over the GQA decode workload (batch 1,
-32 query heads / 8 KV heads, d = 128, context 32768, bf16 K/V with 4 outlier
-key channels per head, K 4-bit records, V 3-bit tiles):
+One step = one pass of the whole path over one workload, by default the GQA
+decode workload (batch 1, 32 query heads / 8 KV heads, d = 128, context
+32768, bf16 K/V with 4 outlier key channels per head, K 4-bit records, V
+3-bit tiles); --workload selects another of the five:
   quantize all K vectors, quantize all V vectors, one decode-attention step.
 Inputs are resident in HBM before timing.  Four copies of the inputs and of
 the packed cache rotate between steps, and a step attends over a cache copy
