@@ -139,7 +139,8 @@ struct StreamRsrc {
 // per-token stride of each array (t0 is a multiple of 32, and a V tile of
 // 32 tokens is 32 * VBYTES contiguous bytes).
 struct LaneOffsets {
-  uint32_t k[2], z[2], v, nrm;
+  uint32_t k[2], k2[2], z[2], v, v2, nrm;
+  uint32_t ksh[2];  // mixed-width keys: bit offset of each part in its two loaded dwords
 };
 
 template <int N>
@@ -176,13 +177,33 @@ __device__ __forceinline__ void load_tile(TileRegs& r, uint32_t t0, const Stream
   constexpr int VW = 2 * (VLO > VHI ? VLO : VHI);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    uint32_t w[KW];
-    buf_load<KW>(w, rs.kc, lo.k[mb] + t0 * KBYTES);
+    if constexpr (KLO != KHI) {
+      // two dwords around each width's 16 codes
+      uint32_t w[2];
+      buf_load<2>(w, rs.kc, lo.k[mb] + t0 * KBYTES);
+      r.kw[mb][0] = w[0];
+      r.kw[mb][1] = w[1];
+      buf_load<2>(w, rs.kc, lo.k2[mb] + t0 * KBYTES);
+      r.kw[mb][2] = w[0];
+      r.kw[mb][3] = w[1];
+    } else {
+      uint32_t w[KW];
+      buf_load<KW>(w, rs.kc, lo.k[mb] + t0 * KBYTES);
 #pragma unroll
-    for (int i = 0; i < KW; ++i) r.kw[mb][i] = w[i];
+      for (int i = 0; i < KW; ++i) r.kw[mb][i] = w[i];
+    }
     if constexpr (QJL) r.zw[mb] = __builtin_amdgcn_raw_buffer_load_b32(rs.zs, lo.z[mb] + t0 * (QJL_M / 8), 0, 0);
   }
-  {
+  if constexpr (VLO != VHI) {
+    // four rows of a VLO sub-block and four of a VHI sub-block
+    uint32_t w[VLO], w2[VHI];
+    buf_load<VLO>(w, rs.vc, lo.v + t0 * VBYTES);
+    buf_load<VHI>(w2, rs.vc, lo.v2 + t0 * VBYTES);
+#pragma unroll
+    for (int i = 0; i < VLO; ++i) r.vw[i] = w[i];
+#pragma unroll
+    for (int i = 0; i < VHI; ++i) r.vw[4 + i] = w2[i];
+  } else {
     uint32_t w[VW];
     buf_load<VW>(w, rs.vc, lo.v + t0 * VBYTES);
 #pragma unroll
@@ -472,10 +493,26 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const uint32_t tok = 8 * (n >> 2) + 4 * mb + (n & 3);
-    lo.k[mb] = tok * KBYTES + (j < 2 ? 4 * KLO * j : 8 * KLO + 4 * KHI * (j - 2));
+    if constexpr (KLO != KHI) {
+      // mixed widths: lane j takes codes [16 j, 16 j + 16) of each width
+      const uint32_t olo = 2 * KLO * j, ohi = 8 * KLO + 2 * KHI * j;
+      lo.k[mb] = tok * KBYTES + (olo & ~3u);
+      lo.k2[mb] = tok * KBYTES + (ohi & ~3u);
+      lo.ksh[0] = 8 * (olo & 3u);
+      lo.ksh[1] = 8 * (ohi & 3u);
+    } else {
+      lo.k[mb] = tok * KBYTES + (j < 2 ? 4 * KLO * j : 8 * KLO + 4 * KHI * (j - 2));
+    }
     lo.z[mb] = tok * (QJL_M / 8) + 4 * j;
   }
-  lo.v = j * (64 * (VLO + VHI)) + (n < 8 ? 8 * VLO * n : 64 * VLO + 8 * VHI * (n - 8));
+  if constexpr (VLO != VHI) {
+    // mixed widths: lane n takes rows 4 (n & 1) .. +3 of sub-block n / 2 of
+    // each width, i.e. coordinates 4n .. 4n+3 and 64 + 4n .. 64 + 4n+3
+    lo.v = j * (64 * (VLO + VHI)) + 8 * VLO * (n >> 1) + 4 * VLO * (n & 1);
+    lo.v2 = j * (64 * (VLO + VHI)) + 64 * VLO + 8 * VHI * (n >> 1) + 4 * VHI * (n & 1);
+  } else {
+    lo.v = j * (64 * (VLO + VHI)) + (n < 8 ? 8 * VLO * n : 64 * VLO + 8 * VHI * (n - 8));
+  }
   lo.nrm = 32 * j;
 
   // Tiles of this wave: first + STEP k, k < nt; the first nfull are whole.
@@ -598,19 +635,27 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   // registers go to the sign and residual-norm tiles, and all four fragment
   // sets are read from LDS per tile instead.
   half8 qh[QJL ? 1 : 4], ql[QJL ? 1 : 4];
-  const _Float16* fbase[4] = {frag_row(0, 0, frow) + 32 * j, frag_row(0, 1, frow) + 32 * j,
-                              frag_row(QJL ? 1 : 0, 0, frow) + 32 * j, frag_row(QJL ? 1 : 0, 1, frow) + 32 * j};
+  // k-slot (lane j, step ks) of the score MFMA -> first of its 8 rotated
+  // coordinates: with mixed key widths steps 0, 1 take the KLO coordinates
+  // 16 j .. 16 j + 15 and steps 2, 3 the KHI ones 64 + 16 j .. (the sketch
+  // sets are indexed by rows of S: 32 j + 8 ks)
+  auto kcoord = [&](int ks) { return KLO != KHI ? (ks < 2 ? 16 * j + 8 * ks : 64 + 16 * j + 8 * (ks - 2)) : 32 * j + 8 * ks; };
+  const _Float16* fbase[4] = {frag_row(0, 0, frow), frag_row(0, 1, frow), frag_row(QJL ? 1 : 0, 0, frow) + 32 * j,
+                              frag_row(QJL ? 1 : 0, 1, frow) + 32 * j};
   if constexpr (!QJL) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      qh[ks] = *reinterpret_cast<const half8*>(fbase[0] + 8 * ks);
-      ql[ks] = *reinterpret_cast<const half8*>(fbase[1] + 8 * ks);
+      qh[ks] = *reinterpret_cast<const half8*>(fbase[0] + kcoord(ks));
+      ql[ks] = *reinterpret_cast<const half8*>(fbase[1] + kcoord(ks));
     }
   }
   auto frag_at = [&](int set, int ks) -> half8 {
     if constexpr (!QJL) return set == 0 ? qh[ks] : ql[ks];
-    else return *reinterpret_cast<const half8*>(fbase[set] + 8 * ks);
+    else return *reinterpret_cast<const half8*>(fbase[set] + (set < 2 ? kcoord(ks) : 8 * ks));
   };
+  // column n of P V block nb -> rotated value coordinate (mixed value widths:
+  // blocks 0..3 from the VLO sub-blocks, 4..7 from the VHI ones)
+  auto vcoord = [&](int nn, int nb) { return VLO != VHI ? (nb < 4 ? 4 * nn + nb : 64 + 4 * nn + nb - 4) : 8 * nn + nb; };
   const float qinv = head_ok ? ldexpf(1.0f, -shx[n]) : 0.0f;
   const float uinv = QJL && head_ok ? ldexpf(QJL_C, -shx[GMAX + n]) : 0.0f;
 
@@ -643,8 +688,23 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       half8 a[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        if constexpr (KLO == KHI) a[mb] = dequant8<KLO>(tr.kw[mb], ks, lut_klo, lane4);
-        else a[mb] = j < 2 ? dequant8<KLO>(tr.kw[mb], ks, lut_klo, lane4) : dequant8<KHI>(tr.kw[mb], ks, lut_khi, lane4);
+        if constexpr (KLO == KHI) {
+          a[mb] = dequant8<KLO>(tr.kw[mb], ks, lut_klo, lane4);
+        } else {
+          // k-steps 0, 1: width KLO; 2, 3: width KHI (no divergence)
+          uint32_t wk[2];
+          const int part = ks >> 1;
+          const uint32_t sh = lo.ksh[part];
+          const bool aligned = part == 0 ? (2 * KLO) % 4 == 0 : (2 * KHI) % 4 == 0;
+          if (aligned) {
+            wk[0] = tr.kw[mb][2 * part];
+            wk[1] = tr.kw[mb][2 * part + 1];
+          } else {
+            wk[0] = __builtin_amdgcn_alignbit(tr.kw[mb][2 * part + 1], tr.kw[mb][2 * part], sh);
+            wk[1] = tr.kw[mb][2 * part + 1] >> sh;
+          }
+          a[mb] = part == 0 ? dequant8<KLO>(wk, ks & 1, lut_klo, lane4) : dequant8<KHI>(wk, ks & 1, lut_khi, lane4);
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], frag_at(0, ks), sk[mb]);
@@ -721,7 +781,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       for (int nb = 0; nb < 8; ++nb) {
         half8 bv;
         if constexpr (VLO == VHI) bv = dequant8<VLO>(tr.vw, nb, lut_vlo, lane4);
-        else bv = n < 8 ? dequant8<VLO>(tr.vw, nb, lut_vlo, lane4) : dequant8<VHI>(tr.vw, nb, lut_vhi, lane4);
+        else bv = nb < 4 ? dequant8<VLO>(tr.vw, nb, lut_vlo, lane4) : dequant8<VHI>(tr.vw + 4, nb - 4, lut_vhi, lane4);
         acc[nb] = mfma16(pa, bv, acc[nb]);
       }
     }
@@ -767,7 +827,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   for (int i = 0; i < 4; ++i)
     if (4 * j + i < G)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) mrg_acc[(wave * 16 + 4 * j + i) * D + 8 * n + nb] = acc[nb][i];
+      for (int nb = 0; nb < 8; ++nb) mrg_acc[(wave * 16 + 4 * j + i) * D + vcoord(n, nb)] = acc[nb][i];
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * D; idx += ST) {
     const int g = idx / D, c = idx % D;

@@ -65,6 +65,16 @@ def test_attend_gqa_g1_and_g16():
         _check(Run(workloads.generate(wl)), label=f"G={hq // hkv}")
 
 
+@pytest.mark.parametrize("kb,vb,qjl", [((3, 2), (3, 2), 0), ((4, 3), (3, 2), 128), ((3, 2), (4, 3), 0)])
+def test_attend_mixed_width_combinations(kb, vb, qjl):
+    """Split-width keys and values (64 coordinates at each width) in the other
+    supported combinations, with and without the sketch."""
+    print(f"[attend] mixed K{kb} V{vb} qjl={qjl}", flush=True)
+    wl = workloads.Workload(f"mix{kb}{vb}{qjl}", 2, 8, 2, "bf16", workloads.QSpec(kb[0], kb[1], 64, qjl_m=qjl),
+                            workloads.QSpec(vb[0], vb[1], 64), ctx=1111)
+    _check(Run(workloads.generate(wl)), label=f"K{kb} V{vb} qjl={qjl}")
+
+
 def test_attend_zero_length_sequence():
     print("[attend] zero-length sequence", flush=True)
     inp = workloads.generate("gqa_decode", ctx=300)
