@@ -382,7 +382,12 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ uint32_t lutz[4];
 
-  const int split = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  // grid (kv head, sequence, split): workgroups are dispatched split by
+  // split, so every stream's whole leading splits start before the partial
+  // and empty trailing ones of a ragged batch, and the short sink splits
+  // come last
+  const int kh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int n_slot = gridDim.z;
   const int G = hq / hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
@@ -395,9 +400,9 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     sink_partial(smem, q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D,
                  sink_k + stream * sink * D, sink_v + stream * sink * D,
                  static_cast<int>(L < sink ? L : sink), G, qscale,
-                 parts + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * gridDim.x * PART +
+                 parts + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * n_slot * PART +
                      static_cast<int64_t>(n_split) * PART,
-                 gridDim.x * PART);
+                 n_slot * PART);
     return;
   }
   // ---- prologue: rotate the group's queries.  Thread (pi_i, kq) forms the
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     // ragged batch): an empty partial, m = -inf, l = 0, acc = 0
     for (int idx = threadIdx.x; idx < G * PART; idx += ST) {
       const int g = idx / PART, c = idx % PART;
-      parts[((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * gridDim.x + split) * PART + c] =
+      parts[((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * n_slot + split) * PART + c] =
           c == 0 ? -INFINITY : 0.0f;
     }
     return;
@@ -844,7 +849,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         l = fmaf(f, mrg_l[w * 16 + g], l);
       }
     }
-    float* part = parts + ((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * gridDim.x + split) * PART;
+    float* part = parts + ((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * n_slot + split) * PART;
     part[4 + c] = a;
     if (c == 0) {
       part[0] = M;
@@ -948,7 +953,7 @@ template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
                         const tq_attn& a, const AttendPlan& plan, const float* q, const uint16_t* sink_k,
                         const uint16_t* sink_v, const int32_t* seq_lens, float* parts, hipStream_t st) {
-  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(plan.n_slot, a.hkv, a.batch), dim3(ST), 0, st,
+  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(a.hkv, a.batch, plan.n_slot), dim3(ST), 0, st,
                      ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms, vc.cap,
                      seq_lens, q, sink_k, sink_v, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.v_skip,
                      a.scale * LOG2E);

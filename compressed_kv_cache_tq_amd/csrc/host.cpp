@@ -520,6 +520,7 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
   if (a.batch < 0 || a.hq <= 0 || a.hkv <= 0) return fail(TQ_E_ARG, "batch, hq, hkv out of range");
   if (a.hq % a.hkv) return fail(TQ_E_ARG, "hq must be a multiple of hkv");
   if (a.hq / a.hkv > 16) return fail(TQ_E_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (a.batch > 65535) return fail(TQ_E_UNSUPPORTED, "at most 65535 sequences per call");
   if (a.sink < 0 || a.max_len < 0) return fail(TQ_E_ARG, "negative sink or max_len");
   if (a.sink > 512) return fail(TQ_E_UNSUPPORTED, "at most 512 sink tokens");
   if (!(a.v_skip >= 0.0f) || !(a.v_skip < 1.0f)) return fail(TQ_E_ARG, "v_skip must be in [0, 1)");

@@ -182,7 +182,7 @@ size_t tq_attend_workspace_bytes(const tq_attn* attn);
 /* One decode step of attention read directly from the packed cache.
  *   ks/ktables/kc  keys: TQ_LAYOUT_RECORD, optional QJL sketch
  *   vs/vtables/vc  values: TQ_LAYOUT_TILED, no QJL
- *   q        device fp32 [batch][hq][d]
+ *   q        device fp32 [batch][hq][d]; batch <= 65535, hq / hkv <= 16
  *   sink_k/sink_v  device bf16 [batch][hkv][sink][d] (NULL iff sink == 0);
  *            sink <= 512
  *   kc->cap and vc->cap must be multiples of 32 and at most 2^24 (one

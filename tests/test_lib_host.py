@@ -223,6 +223,7 @@ def test_attend_argument_errors_without_launch():
 
     assert call(tq.TqAttn(1, 6, 4, 0, 0.1, 0.0, 64)) == -1            # hq % hkv
     assert call(tq.TqAttn(1, 64, 2, 0, 0.1, 0.0, 64)) == -2           # G > 16
+    assert call(tq.TqAttn(65536, 8, 2, 0, 0.1, 0.0, 64)) == -2        # batch limit
     assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 65)) == -1            # max_len > cap
     assert call(tq.TqAttn(1, 8, 2, 4, 0.1, 0.0, 64)) == -1            # sink without buffers
     assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), ws=16) == -3     # workspace
