@@ -354,6 +354,29 @@ __device__ __forceinline__ void sink_partial(uint8_t* smem, const float* __restr
   }
 }
 
+// Index of the r-th longest of the n sequences (ties by index), for n up to
+// MAX_RANK; r itself above that.  Every workgroup ranks the lengths anew:
+// thread t counts the sequences that sort before t.
+constexpr int MAX_RANK = 512;
+__device__ __forceinline__ int rank_sequence(const int32_t* __restrict__ seq_lens, int n, int r) {
+  if (n <= 1 || n > MAX_RANK) return r;
+  __shared__ int lens_s[MAX_RANK];
+  __shared__ int order_s[MAX_RANK];
+  for (int t = threadIdx.x; t < n; t += ST) lens_s[t] = seq_lens[t];
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += ST) {
+    const int lt = lens_s[t];
+    int before = 0;
+    for (int u = 0; u < n; ++u) {
+      const int lu = lens_s[u];
+      before += (lu > lt) | ((lu == lt) & (u < t));
+    }
+    order_s[before] = t;
+  }
+  __syncthreads();
+  return order_s[r];
+}
+
 // Split kernel: one workgroup of 8 waves per (split, kv head, sequence).
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 __global__ __launch_bounds__(ST, 1) void split_kernel(
@@ -382,12 +405,14 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ uint32_t lutz[4];
 
-  // grid (kv head, sequence, split): workgroups are dispatched split by
+  // grid (kv head, sequence rank, split): workgroups are dispatched split by
   // split, so every stream's whole leading splits start before the partial
   // and empty trailing ones of a ragged batch, and the short sink splits
-  // come last
-  const int kh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  // come last.  Within a split, sequences go longest first (for batches of
+  // up to MAX_RANK sequences), so the short ones fill the tail.
+  const int kh = blockIdx.x, split = blockIdx.z;
   const int n_slot = gridDim.z;
+  const int b = rank_sequence(seq_lens, gridDim.y, blockIdx.y);
   const int G = hq / hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
@@ -1002,10 +1027,12 @@ AttendPlan plan_attend(const tq_attn& a) {
   const int64_t streams = static_cast<int64_t>(a.batch) * a.hkv;
   const int64_t comp = a.max_len > a.sink ? a.max_len - a.sink : 0;
   const int64_t tiles = (comp + TILE - 1) / TILE;
-  // about one 8-wave workgroup per CU, no split longer than 8192 tokens
-  // (ragged batches balance better with shorter splits), at most MAX_SPLIT
+  // about one 8-wave workgroup per CU, no split longer than 32768 tokens,
+  // at most MAX_SPLIT.  Once there are more streams than CUs, longer splits
+  // win: every workgroup pays a prologue, a merge and a dispatch gap, and a
+  // ragged batch then runs each stream whole.
   int64_t ns = streams > 0 ? (256 + streams - 1) / streams : 1;
-  const int64_t by_len = (comp + 8191) / 8192;
+  const int64_t by_len = (comp + 32767) / 32768;
   if (ns < by_len) ns = by_len;
   const int64_t cap_ns = (tiles + SW - 1) / SW;  // at least one tile per wave
   if (ns > cap_ns) ns = cap_ns;
