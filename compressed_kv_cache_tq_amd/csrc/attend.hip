@@ -314,7 +314,7 @@ __device__ __forceinline__ void sink_partial(uint8_t* smem, const float* __restr
   float acc[GMAX];
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) acc[g] = 0.0f;
-#pragma unroll 4
+#pragma unroll 16
   for (int t = tq; t < ns; t += 4) {
     const float v = __uint_as_float(static_cast<uint32_t>(sv[static_cast<int64_t>(t) * D + i]) << 16);
 #pragma unroll
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ vtab, const uint8_t* __restrict__ vcodes, const float* __restrict__ vnorms,
     int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q,
     const uint16_t* __restrict__ sink_k, const uint16_t* __restrict__ sink_v, float* __restrict__ parts,
-    int hq, int hkv, int sink, int n_split, int64_t chunk, float v_skip, float qscale) {
+    int hq, int hkv, int sink, int n_split, int n_slot, int64_t chunk, float v_skip, float qscale) {
   using LP = LutPlan<KLO, KHI, VLO, VHI>;
   constexpr int KBYTES = 8 * (KLO + KHI);
   constexpr int VBYTES = 8 * (VLO + VHI);
@@ -407,11 +407,10 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
 
   // grid (kv head, sequence rank, split): workgroups are dispatched split by
   // split, so every stream's whole leading splits start before the partial
-  // and empty trailing ones of a ragged batch, and the short sink splits
-  // come last.  Within a split, sequences go longest first (for batches of
-  // up to MAX_RANK sequences), so the short ones fill the tail.
+  // and empty trailing ones of a ragged batch.  Within a split, sequences go
+  // longest first (for batches of up to MAX_RANK sequences), so the short
+  // ones fill the tail.
   const int kh = blockIdx.x, split = blockIdx.z;
-  const int n_slot = gridDim.z;
   const int b = rank_sequence(seq_lens, gridDim.y, blockIdx.y);
   const int G = hq / hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -419,17 +418,23 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
   const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
   const int64_t L = seq_lens[b];
-  if (split == n_split) {
-    // the extra split of a call with sink tokens: their partial, in the
-    // original (unrotated) value domain
-    sink_partial(smem, q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D,
-                 sink_k + stream * sink * D, sink_v + stream * sink * D,
-                 static_cast<int>(L < sink ? L : sink), G, qscale,
-                 parts + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * n_slot * PART +
-                     static_cast<int64_t>(n_split) * PART,
-                 n_slot * PART);
-    return;
-  }
+  // The sink tokens' partial (slot n_split, acc in the original value
+  // domain) is computed by the stream's last split that holds compressed
+  // tokens (split 0 when there are none), after its own partial, when the
+  // whole LDS is free.
+  const int64_t comp_all = L > sink ? L - sink : 0;
+  const int last_split = comp_all > 0 ? static_cast<int>((comp_all - 1) / chunk) : 0;
+  auto sink_part = [&]() {
+    if (sink > 0 && split == last_split) {
+      __syncthreads();
+      sink_partial(smem, q + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * D,
+                   sink_k + stream * sink * D, sink_v + stream * sink * D,
+                   static_cast<int>(L < sink ? L : sink), G, qscale,
+                   parts + (static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G) * n_slot * PART +
+                       static_cast<int64_t>(n_split) * PART,
+                   n_slot * PART);
+    }
+  };
   // ---- prologue: rotate the group's queries.  Thread (pi_i, kq) forms the
   // partial dot of rotated coordinate pi_i over inputs [32 kq, 32 kq + 32).
   float* qraw = reinterpret_cast<float*>(smem + PRO_OFF);  // [GMAX][D]
@@ -500,6 +505,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       parts[((static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G + g) * n_slot + split) * PART + c] =
           c == 0 ? -INFINITY : 0.0f;
     }
+    sink_part();
     return;
   }
 
@@ -881,6 +887,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       part[1] = l;
     }
   }
+  sink_part();
 
 }
 
@@ -978,10 +985,10 @@ template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
                         const tq_attn& a, const AttendPlan& plan, const float* q, const uint16_t* sink_k,
                         const uint16_t* sink_v, const int32_t* seq_lens, float* parts, hipStream_t st) {
-  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(a.hkv, a.batch, plan.n_slot), dim3(ST), 0, st,
+  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(a.hkv, a.batch, plan.n_split), dim3(ST), 0, st,
                      ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms, vc.cap,
-                     seq_lens, q, sink_k, sink_v, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.chunk, a.v_skip,
-                     a.scale * LOG2E);
+                     seq_lens, q, sink_k, sink_v, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot, plan.chunk,
+                     a.v_skip, a.scale * LOG2E);
   return hipGetLastError();
 }
 
