@@ -35,12 +35,17 @@ METRIC = "packed-KV decode-attention GB/s (% HBM peak) + quantize Mvec/s at d=12
 WORKLOAD = "gqa_decode"
 COPIES = 4
 ATT_COPIES = 10
-KERNEL_SOURCES = ["compressed_kv_cache_tq_amd/csrc/quantize.hip", "compressed_kv_cache_tq_amd/csrc/attend.hip"]
+KERNEL_SOURCES = ["compressed_kv_cache_tq_amd/csrc/quantize.hip",
+                  "compressed_kv_cache_tq_amd/csrc/attend_split.h+compressed_kv_cache_tq_amd/csrc/attend.hip"]
 
 
-def source_hash(path: str) -> str:
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths: str) -> str:
+    """sha256 (first 16 hex digits) of the '+'-joined source files, concatenated."""
+    h = hashlib.sha256()
+    for path in paths.split("+"):
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(name: str):

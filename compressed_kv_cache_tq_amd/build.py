@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["host.cpp", "quantize.hip", "attend.hip"]
+SOURCES = ["host.cpp", "quantize.hip", "attend.hip", "attend_k22.hip", "attend_k33.hip", "attend_k44.hip",
+           "attend_k43.hip", "attend_k32.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,50 @@
+// Shared declarations of the decode-attention translation units: the split
+// kernel's constants and partial format, and the per-key-width launchers of
+// the split kernel (attend_k*.hip), which attend.hip dispatches to.
+#pragma once
+
+#include <cmath>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int SW = 8;          // waves per split workgroup
+constexpr int ST = 64 * SW;    // threads per split workgroup
+constexpr int PART = 132;      // floats per partial: m, l, 2 pad, acc[128]
+constexpr int GMAX = 16;       // query heads per kv head
+constexpr int MAX_SINK = 512;  // raw sink tokens per sequence
+constexpr int MAX_SPLIT = 512; // splits per (sequence, kv head)
+constexpr int FROW = D + 8;    // fp16 per fragment row in LDS (pad: no bank conflicts)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float QJL_C = 1.2533141373155003f / QJL_M;  // sqrt(pi/2) / m
+
+
+struct SplitArgs {
+  const Tables* ktab;
+  const tq_cache* kc;
+  const Tables* vtab;
+  const tq_cache* vc;
+  const tq_attn* a;
+  const AttendPlan* plan;
+  const float* q;
+  const uint16_t* sink_k;
+  const uint16_t* sink_v;
+  const int32_t* seq_lens;
+  float* parts;
+  hipStream_t st;
+};
+
+// Launch the split kernel for keys of widths (bits_lo, bits_hi) = key / 10,
+// key % 10 and values of widths vkey / 10, vkey % 10.
+hipError_t split_k22(int vkey, bool qjl, const SplitArgs& f);
+hipError_t split_k33(int vkey, bool qjl, const SplitArgs& f);
+hipError_t split_k44(int vkey, bool qjl, const SplitArgs& f);
+hipError_t split_k43(int vkey, bool qjl, const SplitArgs& f);
+hipError_t split_k32(int vkey, bool qjl, const SplitArgs& f);
+
+}  // namespace tq
