@@ -268,11 +268,8 @@ def main() -> int:
     def quantize(spec, tab, x, cache):
         if uniform:
             tq.quantize_kv(spec, tab, x[:, :int(comp_h[0])], cache)
-        else:  # one launch per sequence: each appends its own length
-            for b in range(B):
-                n = int(comp_h[b])
-                if n:
-                    tq.quantize_kv(spec, tab, x[b * Hkv:(b + 1) * Hkv, :n], cache.streams(b * Hkv, Hkv))
+        else:  # one ragged call: each sequence appends its own length
+            tq.quantize_kv_ragged(spec, tab, x, cache, hkv=Hkv, n_tok=comp_h)
 
     def attend(kcache, vcache):
         tq.attend_decode(kspec, ktab, kcache, vspec, vtab, vcache, q, lens, out, ws, hkv=Hkv, sink=S,

@@ -5,6 +5,7 @@
 // open-weight su Mac", sections "Il metodo TurboQuant, in breve" (random
 // rotation, per-coordinate optimal scalar quantizer, 1-bit JL sketch of the
 // residual) and "Cosa aggiunge turboquant-mlx" (Lloyd-Max codebook).
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -465,25 +466,31 @@ size_t tq_cache_code_bytes(const tq_spec* spec, int64_t cap) {
   return static_cast<size_t>(pos) * sp.code_bytes;
 }
 
-tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
-                         int64_t n_streams, int64_t n_tok, int64_t x_stream_stride,
-                         int64_t x_row_stride, int64_t tok0, const tq_cache* cache, void* stream) {
-  tq::Spec sp;
-  if (tq_status st = check_spec(spec, &sp); st != TQ_OK) return st;
-  if (tq_status st = check_tables(tables, sp, "quantize"); st != TQ_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both quantize entry points (everything but the ranges).
+tq_status check_quantize(const tq_spec* spec, const void* tables, int32_t dtype, const tq_cache* cache,
+                         tq::Spec* sp) {
+  if (tq_status st = check_spec(spec, sp); st != TQ_OK) return st;
+  if (tq_status st = check_tables(tables, *sp, "quantize"); st != TQ_OK) return st;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_E_ARG, "dtype must be TQ_F32 or TQ_BF16");
   if (!cache) return fail(TQ_E_ARG, "cache is NULL");
-  if (n_streams < 0 || n_tok < 0 || tok0 < 0) return fail(TQ_E_ARG, "negative size or offset");
-  if (cache->cap < 0 || tok0 + n_tok > cache->cap) return fail(TQ_E_ARG, "tok0 + n_tok exceeds cache cap");
-  if (sp.layout == TQ_LAYOUT_TILED && cache->cap % tq::TILE)
+  if (cache->cap < 0) return fail(TQ_E_ARG, "negative cache cap");
+  if (sp->layout == TQ_LAYOUT_TILED && cache->cap % tq::TILE)
     return fail(TQ_E_ARG, "tiled cache cap must be a multiple of 32");
-  if (n_streams == 0 || n_tok == 0) return TQ_OK;
-  const size_t es = dtype == TQ_F32 ? 4 : 2;
+  return TQ_OK;
+}
+
+tq_status check_quantize_arrays(const tq::Spec& sp, int32_t dtype, const void* x, int64_t x_stream_stride,
+                                int64_t x_row_stride, int64_t max_tok, const tq_cache* cache) {
+  const int64_t es = dtype == TQ_F32 ? 4 : 2;
   if (!x || !cache->codes || !cache->norms) return fail(TQ_E_ARG, "x, codes and norms must be non-NULL");
   if (!aligned(x, 16)) return fail(TQ_E_ARG, "x must be 16-byte aligned");
-  if ((x_row_stride * static_cast<int64_t>(es)) % 16 || (x_stream_stride * static_cast<int64_t>(es)) % 16)
+  if ((x_row_stride * es) % 16 || (x_stream_stride * es) % 16)
     return fail(TQ_E_ARG, "x strides must be multiples of 16 bytes");
-  if (x_row_stride < tq::D && n_tok > 1) return fail(TQ_E_ARG, "x_row_stride smaller than d");
+  if (x_row_stride < tq::D && max_tok > 1) return fail(TQ_E_ARG, "x_row_stride smaller than d");
   if (!aligned(cache->codes, 16) || !aligned(cache->norms, 4))
     return fail(TQ_E_ARG, "codes must be 16-byte and norms 4-byte aligned");
   if (sp.qjl_m) {
@@ -491,10 +498,57 @@ tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype,
     if (!aligned(cache->qjl_signs, 16) || !aligned(cache->qjl_rnorms, 4))
       return fail(TQ_E_ARG, "qjl_signs must be 16-byte and qjl_rnorms 4-byte aligned");
   }
-  const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x,
-                                           n_streams, n_tok, x_stream_stride, x_row_stride, tok0,
-                                           *cache, static_cast<hipStream_t>(stream));
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
+                         int64_t n_streams, int64_t n_tok, int64_t x_stream_stride,
+                         int64_t x_row_stride, int64_t tok0, const tq_cache* cache, void* stream) {
+  tq::Spec sp;
+  if (tq_status st = check_quantize(spec, tables, dtype, cache, &sp); st != TQ_OK) return st;
+  if (n_streams < 0 || n_tok < 0 || tok0 < 0) return fail(TQ_E_ARG, "negative size or offset");
+  if (tok0 + n_tok > cache->cap) return fail(TQ_E_ARG, "tok0 + n_tok exceeds cache cap");
+  if (n_streams == 0 || n_tok == 0) return TQ_OK;
+  if (tq_status st = check_quantize_arrays(sp, dtype, x, x_stream_stride, x_row_stride, n_tok, cache); st != TQ_OK)
+    return st;
+  const tq::QSeq one{0, tok0, n_tok, 0};
+  const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x, &one, 1, n_streams,
+                                           x_stream_stride, x_row_stride, *cache, static_cast<hipStream_t>(stream));
   return hip_status(e, "tq_quantize_kv launch");
+}
+
+tq_status tq_quantize_kv_ragged(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
+                                int32_t batch, int32_t hkv, const int64_t* x_off, const int64_t* tok0,
+                                const int64_t* n_tok, int64_t x_stream_stride, int64_t x_row_stride,
+                                const tq_cache* cache, void* stream) {
+  tq::Spec sp;
+  if (tq_status st = check_quantize(spec, tables, dtype, cache, &sp); st != TQ_OK) return st;
+  if (batch < 0 || hkv <= 0) return fail(TQ_E_ARG, "batch must be >= 0 and hkv > 0");
+  if (batch == 0) return TQ_OK;
+  if (!x_off || !tok0 || !n_tok) return fail(TQ_E_ARG, "x_off, tok0 and n_tok must be non-NULL");
+  const int64_t es = dtype == TQ_F32 ? 4 : 2;
+  std::vector<tq::QSeq> seqs;
+  seqs.reserve(static_cast<size_t>(batch));
+  int64_t max_tok = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (n_tok[b] < 0 || tok0[b] < 0 || x_off[b] < 0) return fail(TQ_E_ARG, "negative size or offset");
+    if (tok0[b] + n_tok[b] > cache->cap) return fail(TQ_E_ARG, "tok0 + n_tok exceeds cache cap");
+    if ((x_off[b] * es) % 16) return fail(TQ_E_ARG, "x offsets must be multiples of 16 bytes");
+    if (n_tok[b] == 0) continue;
+    max_tok = std::max(max_tok, n_tok[b]);
+    seqs.push_back(tq::QSeq{x_off[b], tok0[b], n_tok[b], static_cast<int64_t>(b) * hkv});
+  }
+  if (seqs.empty()) return TQ_OK;
+  if (tq_status st = check_quantize_arrays(sp, dtype, x, x_stream_stride, x_row_stride, max_tok, cache); st != TQ_OK)
+    return st;
+  const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x, seqs.data(),
+                                           static_cast<int64_t>(seqs.size()), hkv, x_stream_stride, x_row_stride,
+                                           *cache, static_cast<hipStream_t>(stream));
+  return hip_status(e, "tq_quantize_kv_ragged launch");
 }
 
 size_t tq_attend_workspace_bytes(const tq_attn* attn) {

@@ -29,6 +29,8 @@
 // the xor of the masks j with 2^k | (j+1), done on the scalar unit; the sign
 // turns count into code.  Each code bit is appended to the packed word with
 // one v_addc (w = 2w + bit), most significant bit first.
+#include <vector>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -586,12 +588,44 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
 //     token group fill one dword, and the 4 lanes of a quad hold the 4
 //     coordinates of one half of a sub-block.
 // Loads and stores go through per-tile buffer resources whose extent ends at
-// the last valid row, so rows past the end read as zero and their stores
-// are dropped by the hardware: the loop has no data-dependent branches and
-// the prefetched loads stay in flight across iterations.
+// the last valid row, and lanes before the first valid row use an offset
+// past every extent, so invalid rows read as zero and their stores are
+// dropped by the hardware: the loop has no data-dependent branches and the
+// prefetched loads stay in flight across iterations.  Tiled-layout tiles
+// that are only partly written (the first or last tile of a range that does
+// not start or end on a tile boundary) go to a separate launch of the MERGE
+// variant, which merges their codes into the stored ones with two returnless
+// atomics per word (clear the written tokens' bits, then set them).
+//
+// One launch covers up to RQ_MAX_SEQ sequences of a batch (ragged lengths
+// and offsets); each sequence's tiles start on a multiple of the tiles per
+// pair, so a pair finds its sequence once and all of its tiles lie in it.
 constexpr int RQ_WAVES = 4;
 constexpr int RQ_THREADS = 64 * RQ_WAVES;
 constexpr int RSRC_WORD3 = 0x00020000;
+constexpr int RQ_MAX_SEQ = 64;
+constexpr int RQ_OOB = 0x40000000;  // buffer offset beyond every extent used here
+
+struct RotqSeq {
+  int64_t x_off;    // element offset of the sequence's first stream, row 0, in x
+  int32_t tok0;     // cache position of row 0
+  int32_t n_tok;    // rows (tokens) per stream, > 0
+  int32_t stream0;  // cache stream of the sequence's first stream
+  int32_t tiles;    // tiles per stream written by this launch
+  int32_t start;    // first tile of the sequence in the launch
+  int32_t t_lo;     // tile k of a stream is t_lo + k t_step (tiled layout:
+  int32_t t_step;   //   of the cache stream; record layout: of the rows)
+};
+struct RotqArgs {
+  const Tables* tab;
+  const void* x;
+  uint8_t* codes;
+  float* norms;
+  int64_t xss, xrs, cap, stream_code_bytes;
+  int32_t hkv;  // streams per sequence
+  int32_t n_seq;
+  RotqSeq seq[RQ_MAX_SEQ];  // ascending start
+};
 
 // token slot v of a tile -> row of the A operand that carries it (inverse of tiled_slot)
 __device__ __forceinline__ int tiled_row(int v) { return 8 * ((v >> 2) & 3) + 4 * (v >> 4) + (v & 3); }
@@ -660,11 +694,10 @@ __device__ __forceinline__ void code_run(YF yof, const uint2* cells, uint32_t* w
   }
 }
 
-template <int BLO, int BHI, bool F32IN, bool TILED, int K>
-__global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
-    const Tables* __restrict__ tab, const void* __restrict__ xv, int64_t n_tok, int64_t xss, int64_t xrs,
-    int64_t tok0, uint8_t* __restrict__ codes, float* __restrict__ norms, int64_t cap, int64_t stream_code_bytes,
-    int64_t tiles_per_stream, int64_t tile0, int64_t total_tiles) {
+template <int BLO, int BHI, bool F32IN, bool TILED, int K, bool MERGE>
+__global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
+  static_assert(!MERGE || TILED, "only the tiled layout merges");
+  const Tables* __restrict__ tab = A.tab;
   constexpr int XP = F32IN ? 2 : 1;          // fp16 parts of x
   constexpr int ES = F32IN ? 4 : 2;          // input element bytes
   constexpr int NQW = F32IN ? 8 : 4;         // 16-byte input words per staging thread
@@ -672,6 +705,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
   __shared__ uint4 xbuf[2][2][XP][8 * 64];   // [pair][buffer][part][ks * 64 + lane]
   __shared__ float inv_s[2][2][32];          // [pair][buffer][vector]: 1 / (norm 2^(sh+8))
   __shared__ uint2 cell_s[2][CELL_ENTRIES];
+  __shared__ uint4 pil1_s[2][8][64];         // low parts of the t = 1 fragments: [w][ks][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform: the pair's tiles, and so the buffer resources, live in SGPRs
@@ -687,33 +721,60 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
   const uint2 cv1 = tid + RQ_THREADS < 2 * CELL_ENTRIES ? cell_g[tid + RQ_THREADS] : uint2{};
 
   // ---- rotation fragments of this wave's 64 coordinates, for the whole
-  // launch (stored in fragment order: each load is a contiguous 1 KiB)
-  half8 pih[2][8], pil[2][8];
+  // launch (stored in fragment order: each load is a contiguous 1 KiB).
+  // Three quarters stay in registers; the low parts of the second block
+  // are shared by both pairs from LDS (read once per k-step), which leaves
+  // the registers the loop needs without spilling.
+  half8 pih[2][8], pil0[8];
+  uint4 pl1[8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int fo = (((w * 2 + t) * 8 + ks) * 64 + lane) * 8;
-      pih[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_frag[TILED][0] + fo));
-      pil[t][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_frag[TILED][1] + fo));
-    }
+  for (int ks = 0; ks < 8; ++ks) {
+    const int f0 = (((w * 2 + 0) * 8 + ks) * 64 + lane) * 8, f1 = (((w * 2 + 1) * 8 + ks) * 64 + lane) * 8;
+    pih[0][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_frag[TILED][0] + f0));
+    pih[1][ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_frag[TILED][0] + f1));
+    pil0[ks] = as_half8(*reinterpret_cast<const uint4*>(tab->pi_frag[TILED][1] + f0));
+    pl1[ks] = *reinterpret_cast<const uint4*>(tab->pi_frag[TILED][1] + f1);
   }
 
-  // Tile tl of the launch: stream s, tile T of the stream; its rows of x
-  // start at r0 and the first nv of its 32 positions are valid (the tiled
-  // layout only gets whole tiles here).
+  // pair p of workgroup g takes launch tiles (2 g + p) K .. (2 g + p) K + K - 1,
+  // all in one sequence: the last one starting at or before the first
+  const int64_t first_l = (static_cast<int64_t>(blockIdx.x) * 2 + pair) * K;
+  int sq = 0;
+#pragma unroll
+  for (int step = RQ_MAX_SEQ / 2; step > 0; step >>= 1)
+    if (sq + step < A.n_seq && A.seq[sq + step].start <= first_l) sq += step;
+  const RotqSeq& Q = A.seq[sq];
+  const uint8_t* __restrict__ xv = static_cast<const uint8_t*>(A.x) + Q.x_off * ES;
+  const int64_t n_tok = Q.n_tok, tok0 = Q.tok0, xss = A.xss, xrs = A.xrs, cap = A.cap;
+  const int64_t stream_code_bytes = A.stream_code_bytes;
+  uint8_t* __restrict__ codes = A.codes + static_cast<int64_t>(Q.stream0) * A.stream_code_bytes;
+  float* __restrict__ norms = A.norms + static_cast<int64_t>(Q.stream0) * cap;
+  const int64_t tile0 = Q.t_lo, tstep = Q.t_step;
+  const int64_t total_tiles = static_cast<int64_t>(A.hkv) * Q.tiles;
+  const int64_t first = first_l - Q.start;  // within the sequence
+
+  // Tile tl of the sequence: stream s, tile T of the stream; its rows of x
+  // start at r0 and its positions [lo, nv) are written (lo > 0 only for the
+  // first tile of a range in the merge variant).
   struct TileAt {
     int64_t s, r0, p0;
-    int nv;
+    int lo, nv;
   };
   // tile counts fit in 32 bits (checked on the host): branch-free division
-  const uint32_t tps = static_cast<uint32_t>(tiles_per_stream);
+  const uint32_t tps = static_cast<uint32_t>(Q.tiles);
   auto tile_at = [&](int64_t tl) {
     TileAt a;
     const uint32_t s32 = static_cast<uint32_t>(tl) / tps;
     a.s = s32;
     const int64_t T = static_cast<uint32_t>(tl) - s32 * tps;
-    if constexpr (TILED) {
+    a.lo = 0;
+    if constexpr (MERGE) {
+      a.p0 = 32 * (tile0 + T * tstep);
+      a.r0 = a.p0 - tok0;
+      const int64_t lo = -a.r0, hi = n_tok - a.r0;
+      a.lo = lo > 0 ? static_cast<int>(lo) : 0;
+      a.nv = hi < 32 ? static_cast<int>(hi) : 32;
+    } else if constexpr (TILED) {
       a.p0 = 32 * (tile0 + T);
       a.r0 = a.p0 - tok0;
       a.nv = 32;
@@ -723,19 +784,18 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
       const int64_t left = n_tok - a.r0;
       a.nv = static_cast<int>(left < 32 ? left : 32);
     }
-    if (tl >= total_tiles) a.nv = 0;
+    if (tl >= total_tiles) a.lo = a.nv = 0;
     return a;
   };
   // staging role: vector (token slot) sv of the tile, elements [32 qq, 32 qq + 32)
   const int sv = pt >> 2, qq = pt & 3;
-  // pair p of workgroup g takes tiles (2 g + p) K .. (2 g + p) K + K - 1
-  const int64_t stride = 1;
-  const int64_t first = (static_cast<int64_t>(blockIdx.x) * 2 + pair) * K;
+  // rows before lo use an offset past the extent (read as zero)
   auto load_x = [&](int64_t tl, uint4 (&dst)[NQW]) {
     const TileAt a = tile_at(tl);
-    const uint8_t* base = static_cast<const uint8_t*>(xv) + (a.s * xss + a.r0 * xrs) * ES;
-    const __amdgpu_buffer_rsrc_t r = rsrc(base, a.nv > 0 ? ((a.nv - 1) * xrs + D) * ES : 0);
-    const int off = static_cast<int>((sv * xrs + 32 * qq) * ES);
+    const uint8_t* base = xv + (a.s * xss + (a.r0 + a.lo) * xrs) * ES;
+    const __amdgpu_buffer_rsrc_t r = rsrc(base, a.nv > a.lo ? ((a.nv - a.lo - 1) * xrs + D) * ES : 0);
+    const int off = MERGE ? (sv >= a.lo ? static_cast<int>(((sv - a.lo) * xrs + 32 * qq) * ES) : RQ_OOB)
+                          : static_cast<int>((sv * xrs + 32 * qq) * ES);
 #pragma unroll
     for (int k = 0; k < NQW; ++k)
       dst[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0));
@@ -804,7 +864,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
     inv_s[pair][b][sv] = normf > 0.0f ? 1.0f / ldexpf(normf, sh + 8) : 0.0f;
     const TileAt a = tile_at(tl);
     const __amdgpu_buffer_rsrc_t rn = rsrc(norms + a.s * cap + a.p0, static_cast<int64_t>(a.nv) * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, 4 * sv, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, !MERGE || sv >= a.lo ? 4 * sv : RQ_OOB, 0, 0);
   };
 
   // ---- pipeline, straight-line over the pair's K tiles: three register
@@ -813,10 +873,15 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
   // k+4), so the waits on in-flight loads are exact.
   uint4 X[3][NQW];
   load_x(first, X[0]);
-  load_x(first + 1, X[1]);
-  load_x(first + 2, X[2]);
+  if (K > 1) load_x(first + 1, X[1]);
+  if (K > 2) load_x(first + 2, X[2]);
+  // (the fragment loads are older than the tile loads: this waits for them only)
+  if (pair == 0) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) pil1_s[w][ks][lane] = pl1[ks];
+  }
   stage(first, X[0], 0);
-  load_x(first + 3, X[0]);
+  if (K > 3) load_x(first + 3, X[0]);
   reinterpret_cast<uint2*>(cell_s)[tid] = cv0;
   if (tid + RQ_THREADS < 2 * CELL_ENTRIES) reinterpret_cast<uint2*>(cell_s)[tid + RQ_THREADS] = cv1;
   __syncthreads();
@@ -829,11 +894,12 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const half8 xh = as_half8(xbuf[pair][b][0][ks * 64 + lane]);
+      const half8 pil[2] = {pil0[ks], as_half8(pil1_s[w][ks][lane])};
       if constexpr (TILED) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) acc[t] = mfma(xh, pih[t][ks], acc[t]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = mfma(xh, pil[t][ks], acc[t]);
+        for (int t = 0; t < 2; ++t) acc[t] = mfma(xh, pil[t], acc[t]);
         if constexpr (F32IN) {
           const half8 xl = as_half8(xbuf[pair][b][XP - 1][ks * 64 + lane]);
 #pragma unroll
@@ -843,13 +909,19 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
 #pragma unroll
         for (int t = 0; t < 2; ++t) acc[t] = mfma(pih[t][ks], xh, acc[t]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = mfma(pil[t][ks], xh, acc[t]);
+        for (int t = 0; t < 2; ++t) acc[t] = mfma(pil[t], xh, acc[t]);
         if constexpr (F32IN) {
           const half8 xl = as_half8(xbuf[pair][b][XP - 1][ks * 64 + lane]);
 #pragma unroll
           for (int t = 0; t < 2; ++t) acc[t] = mfma(pih[t][ks], xl, acc[t]);
         }
       }
+    }
+    // stage the next tile into the other buffer while the products finish,
+    // and refill its registers: they are free before the codes are made
+    if (k + 1 < K) {
+      stage(tl + 1, X[(k + 1) % 3], b ^ 1);
+      if (k + 4 < K) load_x(tl + 4, X[(k + 1) % 3]);
     }
     const TileAt a = tile_at(tl);
     uint8_t* sbase = codes + a.s * stream_code_bytes;
@@ -884,7 +956,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
       const float* invb = inv_s[pair][b] + 16 * h;
       constexpr int G = 64 * (BLO + BHI);
       const __amdgpu_buffer_rsrc_t rc =
-          rsrc(sbase + a.p0 * CODE_BYTES, a.nv > 0 ? static_cast<int64_t>(32) * CODE_BYTES : 0);
+          rsrc(sbase + a.p0 * CODE_BYTES, a.nv > a.lo ? static_cast<int64_t>(32) * CODE_BYTES : 0);
       const int qa = l32 & 3;
       auto emit = [&](auto bw, const uint2* cells) {
         constexpr int BW = decltype(bw)::value;
@@ -913,20 +985,37 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(
             const int dw = BW == 2 ? (qa >> 1) : qa;
             const bool owner = BW == 4 || (BW == 2 ? (qa & 1) == 0 : qa < 3);
             const int o = (2 * h + gg) * G + qoff + 4 * BW * rh + 4 * dw;
-            // non-owners store past the tile's extent (dropped)
-            __builtin_amdgcn_raw_buffer_store_b32(out, rc, owner ? o : 32 * CODE_BYTES, 0, 0);
+            if constexpr (!MERGE) {
+              // non-owners store past the tile's extent (dropped)
+              __builtin_amdgcn_raw_buffer_store_b32(out, rc, owner ? o : 32 * CODE_BYTES, 0, 0);
+            } else {
+              // bits of the tokens [lo, nv) of group g: in each coordinate's
+              // 8 BW-bit field, token s holds bits [s BW, s BW + BW)
+              const int g8 = 8 * (2 * h + gg);
+              const int sl = min(max(a.lo - g8, 0), 8), sh = min(max(a.nv - g8, 0), 8);
+              const uint64_t fm = sh > sl ? ((uint64_t{1} << (BW * (sh - sl))) - 1) << (BW * sl) : 0;
+              const int dbit = 32 * (BW * rh + dw);  // first bit of the word in its sub-block
+              uint32_t m = 0;
+#pragma unroll
+              for (int f = 0; f < 3; ++f) {
+                const int fs = 8 * BW * (dbit / (8 * BW) + f) - dbit;  // field start, relative to the word
+                if (fs < 32) m |= fs >= 0 ? static_cast<uint32_t>(fm << fs) : static_cast<uint32_t>(fm >> -fs);
+              }
+              // clear, then set, with returnless atomics: same lane and word,
+              // so they apply in order; m != 0 only for a word of a real tile
+              if (owner && m != 0) {
+                uint32_t* wp = reinterpret_cast<uint32_t*>(sbase + a.p0 * CODE_BYTES + o);
+                __hip_atomic_fetch_and(wp, ~m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_or(wp, out & m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+            }
           }
         }
       };
       if (BLO == BHI || w == 0) emit(std::integral_constant<int, BLO>{}, cell_s[0]);
       else emit(std::integral_constant<int, BHI>{}, cell_s[1]);
     }
-    // stage the next tile into the other buffer, refill its registers
-    if (k + 1 < K) {
-      stage(tl + 1, X[(k + 1) % 3], b ^ 1);
-      if (k + 4 < K) load_x(tl + 4, X[(k + 1) % 3]);
-      __syncthreads();
-    }
+    if (k + 1 < K) __syncthreads();
   }
 }
 
@@ -950,81 +1039,157 @@ hipError_t launch_one(const Tables* tab, const void* x, int64_t n_streams, int64
   return hipGetLastError();
 }
 
-template <int BLO, int BHI, bool F32IN, bool TILED>
-hipError_t launch_rotq(const Tables* tab, const void* x, int64_t n_streams, int64_t n_tok, int64_t xss, int64_t xrs,
-                       int64_t tok0, const tq_cache& c, hipStream_t st) {
+// cache arrays of the streams from s0 on
+tq_cache streams_from(const tq_cache& c, int64_t s0, int64_t code_bytes) {
+  tq_cache o = c;
+  o.codes = c.codes + s0 * c.cap * code_bytes;
+  o.norms = c.norms + s0 * c.cap;
+  if (c.qjl_signs) o.qjl_signs = c.qjl_signs + s0 * c.cap * (QJL_M / 8);
+  if (c.qjl_rnorms) o.qjl_rnorms = c.qjl_rnorms + s0 * c.cap;
+  return o;
+}
+
+// one general-kernel launch per sequence
+template <int BLO, int BHI, int XM, bool TILED, bool QJL>
+hipError_t launch_each(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv, int64_t xss,
+                       int64_t xrs, const tq_cache& c, hipStream_t st) {
+  constexpr int64_t ES = XM == X_F32 ? 4 : 2;
+  for (int64_t i = 0; i < n_seq; ++i) {
+    const QSeq& q = seqs[i];
+    const hipError_t e = launch_one<BLO, BHI, XM, TILED, QJL>(tab, static_cast<const uint8_t*>(x) + q.x_off * ES,
+                                                              hkv, q.n_tok, xss, xrs, q.tok0,
+                                                              streams_from(c, q.stream0, 8 * (BLO + BHI)), st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// tiles [t_lo, t_lo + t_step, ...) (tiles of them) of every stream of a sequence
+struct RotqPart {
+  QSeq q;
+  int64_t t_lo, t_step, tiles;
+};
+
+template <int BLO, int BHI, bool F32IN, bool TILED, bool MERGE>
+hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<RotqPart>& list, int64_t hkv,
+                            int64_t xss, int64_t xrs, const tq_cache& c, hipStream_t st) {
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
+  const int64_t n = static_cast<int64_t>(list.size());
+  for (int64_t b0 = 0; b0 < n; b0 += RQ_MAX_SEQ) {
+    const int nb = static_cast<int>(std::min<int64_t>(RQ_MAX_SEQ, n - b0));
+    int64_t raw = 0;
+    for (int i = 0; i < nb; ++i) raw += hkv * list[b0 + i].tiles;
+    // 8 tiles per pair once that still fills every CU twice over, else 2
+    const int K = !MERGE && raw >= 8 * 1024 ? 8 : 2;
+
+    RotqArgs a{};
+    a.tab = tab;
+    a.x = x;
+    a.codes = c.codes;
+    a.norms = c.norms;
+    a.xss = xss;
+    a.xrs = xrs;
+    a.cap = c.cap;
+    a.stream_code_bytes = c.cap * CODE_BYTES;
+    a.hkv = static_cast<int32_t>(hkv);
+    a.n_seq = nb;
+    int64_t total = 0;  // each sequence's tiles start on a multiple of K
+    for (int i = 0; i < nb; ++i) {
+      const RotqPart& p = list[b0 + i];
+      a.seq[i] = RotqSeq{p.q.x_off,
+                         static_cast<int32_t>(p.q.tok0),
+                         static_cast<int32_t>(p.q.n_tok),
+                         static_cast<int32_t>(p.q.stream0),
+                         static_cast<int32_t>(p.tiles),
+                         static_cast<int32_t>(total),
+                         static_cast<int32_t>(p.t_lo),
+                         static_cast<int32_t>(p.t_step)};
+      total += (hkv * p.tiles + K - 1) / K * K;
+    }
+    const unsigned blocks = static_cast<unsigned>((total + 2 * K - 1) / (2 * K));
+    if constexpr (MERGE) {
+      hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, true>), dim3(blocks), dim3(RQ_THREADS), 0, st, a);
+    } else {
+      if (K == 8)
+        hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 8, false>), dim3(blocks), dim3(RQ_THREADS), 0, st, a);
+      else
+        hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, false>), dim3(blocks), dim3(RQ_THREADS), 0, st, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int BLO, int BHI, bool F32IN, bool TILED>
+hipError_t launch_rotq(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv, int64_t xss,
+                       int64_t xrs, const tq_cache& c, hipStream_t st) {
+  constexpr int64_t ES = F32IN ? 4 : 2;
   constexpr int XM = F32IN ? X_F32 : X_BF16;
-  int64_t tiles, tile0 = 0;
-  if (TILED) {
-    // whole tiles here; a partially written first or last tile merges its
-    // codes into the existing ones in the general kernel
-    const int64_t end = tok0 + n_tok;
-    const int64_t t_lo = (tok0 + TILE - 1) / TILE, t_hi = end / TILE;
-    if (t_hi <= t_lo) return launch_one<BLO, BHI, XM, true, false>(tab, x, n_streams, n_tok, xss, xrs, tok0, c, st);
-    if (tok0 < t_lo * TILE) {
-      const hipError_t e =
-          launch_one<BLO, BHI, XM, true, false>(tab, x, n_streams, t_lo * TILE - tok0, xss, xrs, tok0, c, st);
-      if (e != hipSuccess) return e;
+  // whole tiles in one list; tiled-layout tiles written only in part in another
+  std::vector<RotqPart> whole, part;
+  int64_t all = 0, streams = 0;
+  for (int64_t i = 0; i < n_seq; ++i) {
+    const QSeq& q = seqs[i];
+    if constexpr (!TILED) {
+      whole.push_back(RotqPart{q, 0, 1, (q.n_tok + TILE - 1) / TILE});
+    } else {
+      const int64_t end = q.tok0 + q.n_tok;
+      const int64_t f = q.tok0 / TILE, e = (end + TILE - 1) / TILE;     // tiles touched
+      const int64_t wf = (q.tok0 + TILE - 1) / TILE, we = end / TILE;  // tiles written whole
+      if (we > wf) whole.push_back(RotqPart{q, wf, 1, we - wf});
+      const bool head = q.tok0 % TILE != 0, tail = end % TILE != 0;
+      if (f == e - 1) {
+        if (head || tail) part.push_back(RotqPart{q, f, 1, 1});
+      } else if (head && tail) {
+        part.push_back(RotqPart{q, f, e - 1 - f, 2});
+      } else if (head || tail) {
+        part.push_back(RotqPart{q, head ? f : e - 1, 1, 1});
+      }
     }
-    if (end > t_hi * TILE) {
-      const int64_t skip = t_hi * TILE - tok0;
-      const uint8_t* xe = static_cast<const uint8_t*>(x) + skip * xrs * (F32IN ? 4 : 2);
-      const hipError_t e =
-          launch_one<BLO, BHI, XM, true, false>(tab, xe, n_streams, end - t_hi * TILE, xss, xrs, t_hi * TILE, c, st);
-      if (e != hipSuccess) return e;
-    }
-    tile0 = t_lo;
-    tiles = t_hi - t_lo;
-  } else {
-    tiles = (n_tok + TILE - 1) / TILE;
+    all += hkv * ((q.n_tok + TILE - 1) / TILE + 2) + 16;
+    streams = std::max(streams, q.stream0 + hkv);
   }
-  const int64_t total = n_streams * tiles;
-  if (total + 8 * 1024 >= (int64_t{1} << 31) || 32 * xrs * (F32IN ? 4 : 2) >= (int64_t{1} << 31))
-    return launch_one<BLO, BHI, XM, TILED, false>(tab, x, n_streams, n_tok, xss, xrs, tok0, c, st);
-  // 8 tiles per pair once that still fills every CU twice over, else 2
-  if (total >= 8 * 1024) {
-    const int64_t blocks = (total + 15) / 16;
-    hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 8>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(RQ_THREADS), 0, st, tab, x, n_tok, xss, xrs, tok0, c.codes, c.norms, c.cap,
-                       c.cap * CODE_BYTES, tiles, tile0, total);
-  } else {
-    const int64_t blocks = (total + 3) / 4;
-    hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(RQ_THREADS), 0, st, tab, x, n_tok, xss, xrs, tok0, c.codes, c.norms, c.cap,
-                       c.cap * CODE_BYTES, tiles, tile0, total);
+  // 32-bit tile, position and stream arithmetic, and buffer offsets below RQ_OOB
+  if (all + 16 * 1024 >= (int64_t{1} << 31) || 32 * xrs * ES >= RQ_OOB || c.cap >= (int64_t{1} << 31) - 64 ||
+      streams >= (int64_t{1} << 31))
+    return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
+  hipError_t e = launch_rotq_list<BLO, BHI, F32IN, TILED, false>(tab, x, whole, hkv, xss, xrs, c, st);
+  if constexpr (TILED) {
+    if (e == hipSuccess && !part.empty())
+      e = launch_rotq_list<BLO, BHI, F32IN, TILED, true>(tab, x, part, hkv, xss, xrs, c, st);
   }
-  return hipGetLastError();
+  return e;
 }
 
 template <int BLO, int BHI>
-hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const void* x, int64_t ns, int64_t nt,
-                           int64_t xss, int64_t xrs, int64_t tok0, const tq_cache& c, hipStream_t st) {
+hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
+                           int64_t n_seq, int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c, hipStream_t st) {
   const bool f32 = dtype == TQ_F32;
   if (sp.qjl_m) {
-    return f32 ? launch_one<BLO, BHI, X_F32, false, true>(tab, x, ns, nt, xss, xrs, tok0, c, st)
-               : launch_one<BLO, BHI, X_BF16_F16, false, true>(tab, x, ns, nt, xss, xrs, tok0, c, st);
+    return f32 ? launch_each<BLO, BHI, X_F32, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st)
+               : launch_each<BLO, BHI, X_BF16_F16, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
   }
   if (sp.layout == TQ_LAYOUT_TILED) {
-    return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, ns, nt, xss, xrs, tok0, c, st)
-               : launch_rotq<BLO, BHI, false, true>(tab, x, ns, nt, xss, xrs, tok0, c, st);
+    return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st)
+               : launch_rotq<BLO, BHI, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
   }
-  return f32 ? launch_rotq<BLO, BHI, true, false>(tab, x, ns, nt, xss, xrs, tok0, c, st)
-             : launch_rotq<BLO, BHI, false, false>(tab, x, ns, nt, xss, xrs, tok0, c, st);
+  return f32 ? launch_rotq<BLO, BHI, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st)
+             : launch_rotq<BLO, BHI, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
 }
 
 }  // namespace
 
-hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, int64_t n_streams,
-                           int64_t n_tok, int64_t xss, int64_t xrs, int64_t tok0, const tq_cache& c,
+hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
+                           int64_t n_seq, int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c,
                            hipStream_t st) {
   const int key = sp.bits_lo * 10 + sp.bits_hi;
   switch (key) {
-    case 22: return dispatch_layout<2, 2>(sp, tab, dtype, x, n_streams, n_tok, xss, xrs, tok0, c, st);
-    case 33: return dispatch_layout<3, 3>(sp, tab, dtype, x, n_streams, n_tok, xss, xrs, tok0, c, st);
-    case 44: return dispatch_layout<4, 4>(sp, tab, dtype, x, n_streams, n_tok, xss, xrs, tok0, c, st);
-    case 43: return dispatch_layout<4, 3>(sp, tab, dtype, x, n_streams, n_tok, xss, xrs, tok0, c, st);
-    case 32: return dispatch_layout<3, 2>(sp, tab, dtype, x, n_streams, n_tok, xss, xrs, tok0, c, st);
+    case 22: return dispatch_layout<2, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
+    case 33: return dispatch_layout<3, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
+    case 44: return dispatch_layout<4, 4>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
+    case 43: return dispatch_layout<4, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
+    case 32: return dispatch_layout<3, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -86,10 +86,19 @@ struct Spec {
   int code_bytes;  // per token
 };
 
-hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x,
-                           int64_t n_streams, int64_t n_tok, int64_t x_stream_stride,
-                           int64_t x_row_stride, int64_t tok0, const tq_cache& cache,
-                           hipStream_t stream);
+// One sequence of a quantize call: hkv streams whose rows start at element
+// x_off of x (stream h at x_off + h * x_stream_stride); their n_tok (> 0)
+// vectors fill positions [tok0, tok0 + n_tok) of cache streams stream0 + h.
+struct QSeq {
+  int64_t x_off;
+  int64_t tok0;
+  int64_t n_tok;
+  int64_t stream0;
+};
+
+hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
+                           int64_t n_seq, int64_t hkv, int64_t x_stream_stride, int64_t x_row_stride,
+                           const tq_cache& cache, hipStream_t stream);
 
 struct AttendPlan {
   int n_split;       // splits of the compressed token range per (b, kv head)

@@ -26,6 +26,7 @@ STATUS = {0: "TQ_OK", -1: "TQ_E_ARG", -2: "TQ_E_UNSUPPORTED", -3: "TQ_E_WORKSPAC
 EXPORTS = [
     "tq_format_version", "tq_last_error", "tq_codebook_build", "tq_rotation_build", "tq_sketch_build",
     "tq_tables_bytes", "tq_tables_build", "tq_code_bytes", "tq_cache_code_bytes", "tq_quantize_kv",
+    "tq_quantize_kv_ragged",
     "tq_attend_workspace_bytes", "tq_attend_decode",
 ]
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         "tq_cache_code_bytes": (SZ, [ctypes.POINTER(TqSpec), I64]),
         "tq_quantize_kv": (I32, [ctypes.POINTER(TqSpec), P, I32, P, I64, I64, I64, I64, I64,
                                  ctypes.POINTER(TqCache), P]),
+        "tq_quantize_kv_ragged": (I32, [ctypes.POINTER(TqSpec), P, I32, P, I32, I32, P, P, P, I64, I64,
+                                        ctypes.POINTER(TqCache), P]),
         "tq_attend_workspace_bytes": (SZ, [ctypes.POINTER(TqAttn)]),
         "tq_attend_decode": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache), ctypes.POINTER(TqSpec), P,
                                    ctypes.POINTER(TqCache), ctypes.POINTER(TqAttn), P, P, P, P, P, P, SZ, P]),
@@ -259,6 +262,45 @@ def quantize_kv(spec: Spec, tables, x, cache: Cache, tok0: int = 0, n_streams: i
     st = _stream(x.device) if stream is None else stream
     _check(lib().tq_quantize_kv(ctypes.byref(cs), tables.data_ptr(), dt, x.data_ptr(), ns, nt, x.stride(0),
                                 x.stride(1), tok0, ctypes.byref(cc), st), "tq_quantize_kv")
+
+
+def quantize_kv_ragged(spec: Spec, tables, x, cache: Cache, *, hkv: int, n_tok, tok0=None, x_off=None,
+                       x_stream_stride: int | None = None, x_row_stride: int | None = None,
+                       stream: int | None = None) -> None:
+    """Quantize a ragged batch in one call: sequence b appends n_tok[b] vectors
+    to cache streams b*hkv .. b*hkv+hkv-1 at positions tok0[b] (default 0) on.
+
+    Without x_off, x is a padded [batch*hkv, rows, d] tensor (stream b*hkv + h
+    of sequence b, strides taken from it).  With x_off (elements, one per
+    sequence) the strides must be given and x only supplies the base pointer,
+    e.g. a packed [tokens, hkv, d] tensor with x_off[b] = start_b * hkv * d."""
+    torch = _torch()
+    if x.dtype == torch.float32:
+        dt = F32
+    elif x.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    n = np.ascontiguousarray(n_tok, dtype=np.int64)
+    B = n.shape[0]
+    t0 = np.zeros(B, np.int64) if tok0 is None else np.ascontiguousarray(tok0, dtype=np.int64)
+    if x_off is None:
+        if x.dim() != 3 or x.shape[-1] != D or x.stride(-1) != 1 or x.shape[0] < B * hkv:
+            raise ValueError("x must be [batch*hkv, rows, 128] with contiguous rows")
+        xo = np.arange(B, dtype=np.int64) * hkv * x.stride(0)
+        xss, xrs = x.stride(0), x.stride(1)
+    else:
+        if x_stream_stride is None or x_row_stride is None:
+            raise ValueError("x_off needs x_stream_stride and x_row_stride")
+        xo = np.ascontiguousarray(x_off, dtype=np.int64)
+        xss, xrs = x_stream_stride, x_row_stride
+    if t0.shape != (B,) or xo.shape != (B,):
+        raise ValueError("n_tok, tok0 and x_off must have one entry per sequence")
+    cs, cc = spec.c(), cache.c()
+    st = _stream(x.device) if stream is None else stream
+    _check(lib().tq_quantize_kv_ragged(ctypes.byref(cs), tables.data_ptr(), dt, x.data_ptr(), B, hkv,
+                                       xo.ctypes.data, t0.ctypes.data, n.ctypes.data, xss, xrs,
+                                       ctypes.byref(cc), st), "tq_quantize_kv_ragged")
 
 
 def clone_cache(c: "Cache") -> "Cache":

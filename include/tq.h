@@ -176,6 +176,26 @@ tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype,
                          int64_t x_row_stride, int64_t tok0, const tq_cache* cache,
                          void* stream);
 
+/* The same quantization for a ragged batch in one call (one launch for up to
+ * 64 sequences with a spec without the QJL stage; a spec with the QJL stage
+ * launches once per sequence).  Sequence b (0 <= b < batch) appends n_tok[b]
+ * vectors to each of its hkv streams, at positions [tok0[b], tok0[b] +
+ * n_tok[b]) of cache streams b*hkv .. b*hkv + hkv - 1 (the stream order
+ * tq_attend_decode reads).
+ *   x       device; vector i of stream h of sequence b starts at element
+ *           x_off[b] + h*x_stream_stride + i*x_row_stride (a padded
+ *           [batch][hkv][len][d] tensor and a packed [tokens][hkv][d] one
+ *           are both of this form); every offset a multiple of 16 bytes
+ *   x_off, tok0, n_tok  HOST int64 arrays [batch], read during the call
+ * Requires hkv > 0 and, for every b, tok0[b] >= 0, x_off[b] >= 0 and
+ * tok0[b] + n_tok[b] <= cache->cap; sequences with n_tok[b] == 0 are
+ * skipped.  Tables, dtype, alignment and the keeping of positions outside
+ * the written ranges are as for tq_quantize_kv. */
+tq_status tq_quantize_kv_ragged(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
+                                int32_t batch, int32_t hkv, const int64_t* x_off, const int64_t* tok0,
+                                const int64_t* n_tok, int64_t x_stream_stride, int64_t x_row_stride,
+                                const tq_cache* cache, void* stream);
+
 /* Workspace bytes tq_attend_decode needs for this problem. */
 size_t tq_attend_workspace_bytes(const tq_attn* attn);
 

@@ -128,3 +128,135 @@ def test_quantize_full_size_sampled(name):
             signs = read_signs(cache, s, n, t0) if spec.qjl_m else None
             check_quantized(spec, X[s, t0:t0 + n], idx, read_norms(cache, s, n, t0), signs=signs,
                             label=f"{name}/{tensor}/stream {s}")
+
+
+def _ragged_case(spec, lens, tok0s, hkv, cap, seed, fill_first=True):
+    """Fill every stream with one call, then append a ragged batch with one
+    ragged call; returns (x, cache, before-codes snapshot, before-norms)."""
+    B = len(lens)
+    tab = tq.device_tables(spec)
+    cache = tq.alloc_cache(spec, B * hkv, cap, fill=0x5A)
+    if fill_first:
+        base = _data(B * hkv * cap, seed=seed + 100, dtype="bf16").reshape(B * hkv, cap, 128)
+        tq.quantize_kv(spec, tab, to_device(base, "bf16"), cache)
+    torch().cuda.synchronize()
+    before = tq.clone_cache(cache)
+    L = max(max(lens), 1)
+    x = _data(B * hkv * L, seed=seed, dtype="bf16").reshape(B * hkv, L, 128)
+    tq.quantize_kv_ragged(spec, tab, to_device(x, "bf16"), cache, hkv=hkv, n_tok=lens, tok0=tok0s)
+    torch().cuda.synchronize()
+    return x, cache, before
+
+
+def _check_ragged(spec, x, cache, before, lens, tok0s, hkv, label):
+    cap = cache.cap
+    for b, (n, t0) in enumerate(zip(lens, tok0s)):
+        for h in range(hkv):
+            s = b * hkv + h
+            got = read_codes(spec, cache, s, cap)
+            old = read_codes(spec, before, s, cap)
+            keep = np.ones(cap, bool)
+            keep[t0:t0 + n] = False
+            assert np.array_equal(got[keep], old[keep]), f"{label}: stream {s} changed outside its range"
+            nm, nm_old = read_norms(cache, s, cap), read_norms(before, s, cap)
+            assert np.array_equal(nm[keep], nm_old[keep]), f"{label}: stream {s} norms changed outside"
+            if n:
+                check_quantized(spec, x[s, :n], got[t0:t0 + n], nm[t0:t0 + n], label=f"{label}/stream {s}")
+
+
+@pytest.mark.parametrize("layout", [tq.LAYOUT_RECORD, tq.LAYOUT_TILED])
+@pytest.mark.parametrize("w", [(2, None, 128), (3, None, 128), (4, 3, 64)])
+def test_quantize_ragged_batch(w, layout):
+    """One ragged call: lengths 0 .. several tiles, unaligned offsets (partial
+    first and last tiles merge into the stored codes), two streams per
+    sequence; positions outside each range keep their previous contents."""
+    print(f"[quantize] ragged widths={w} layout={layout}", flush=True)
+    spec = tq.Spec(w[0], w[1], split=w[2], layout=layout)
+    lens = [0, 1, 33, 100, 257, 31, 64]
+    tok0s = [0, 5, 31, 64, 3, 40, 96]
+    _check_ragged(spec, *_ragged_case(spec, lens, tok0s, hkv=2, cap=288, seed=w[0] + 3 * layout),
+                  lens, tok0s, 2, f"ragged {w}/{layout}")
+
+
+def test_quantize_ragged_many_sequences_and_packed_rows():
+    """More sequences than one launch takes (70), and a packed [tokens, hkv, d]
+    input addressed through per-sequence offsets."""
+    print("[quantize] ragged: 70 sequences; packed rows", flush=True)
+    rng = np.random.default_rng(11)
+    for layout in (tq.LAYOUT_RECORD, tq.LAYOUT_TILED):
+        spec = tq.Spec(4, layout=layout)
+        lens = rng.integers(0, 70, 70).tolist()
+        tok0s = rng.integers(0, 20, 70).tolist()
+        _check_ragged(spec, *_ragged_case(spec, lens, tok0s, hkv=1, cap=96, seed=21 + layout, fill_first=False),
+                      lens, tok0s, 1, f"70 sequences/{layout}")
+    # packed rows: sequence b's tokens are rows start_b .. start_b + n_b of a [tokens, hkv, d] tensor
+    hkv, lens, tok0s = 3, [17, 0, 45, 32], [0, 0, 7, 32]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    packed = _data(sum(lens) * hkv, seed=33, dtype="bf16").reshape(sum(lens), hkv, 128)
+    for layout in (tq.LAYOUT_RECORD, tq.LAYOUT_TILED):
+        spec = tq.Spec(3, layout=layout)
+        tab = tq.device_tables(spec)
+        cache = tq.alloc_cache(spec, len(lens) * hkv, 96)
+        xd = to_device(packed, "bf16")
+        tq.quantize_kv_ragged(spec, tab, xd, cache, hkv=hkv, n_tok=lens, tok0=tok0s,
+                              x_off=starts * hkv * 128, x_stream_stride=128, x_row_stride=hkv * 128)
+        torch().cuda.synchronize()
+        for b, (n, t0) in enumerate(zip(lens, tok0s)):
+            for h in range(hkv):
+                if n:
+                    s = b * hkv + h
+                    xs = packed[starts[b]:starts[b] + n, h]
+                    check_quantized(spec, xs, read_codes(spec, cache, s, n, t0), read_norms(cache, s, n, t0),
+                                    label=f"packed/{layout}/stream {s}")
+
+
+def test_quantize_ragged_qjl():
+    """A spec with the sketch goes through one launch per sequence."""
+    print("[quantize] ragged qjl", flush=True)
+    spec = tq.Spec(2, qjl_m=128)
+    lens, tok0s, hkv = [40, 0, 77], [0, 3, 9], 2
+    B = len(lens)
+    x = _data(B * hkv * 77, seed=44, dtype="bf16").reshape(B * hkv, 77, 128)
+    tab = tq.device_tables(spec)
+    cache = tq.alloc_cache(spec, B * hkv, 96)
+    tq.quantize_kv_ragged(spec, tab, to_device(x, "bf16"), cache, hkv=hkv, n_tok=lens, tok0=tok0s)
+    torch().cuda.synchronize()
+    for b, (n, t0) in enumerate(zip(lens, tok0s)):
+        for h in range(hkv):
+            s = b * hkv + h
+            if n:
+                check_quantized(spec, x[s, :n], read_codes(spec, cache, s, n, t0), read_norms(cache, s, n, t0),
+                                signs=read_signs(cache, s, n, t0), label=f"ragged qjl/stream {s}")
+
+
+def test_quantize_ragged_full_size_sampled():
+    """The 64-sequence ragged workload (lengths 1024..32768, 128 sink tokens,
+    8 KV heads) quantized with one ragged call per tensor, as the bench does;
+    sampled streams checked vector by vector against the oracle."""
+    print("[quantize] ragged full size", flush=True)
+    wl = workloads.WORKLOADS["batched_ragged"]
+    inp = workloads.generate("batched_ragged")
+    B, Hkv, S = len(inp.k), wl.hkv, wl.sink
+    comp = np.array([a.shape[1] - S for a in inp.k], np.int64)
+    cap = int(-(-comp.max() // 32) * 32)
+    rng = np.random.default_rng(5)
+    seqs = sorted(set(rng.integers(0, B, 3).tolist()))
+    for tensor, qs, layout in (("k", wl.k, tq.LAYOUT_RECORD), ("v", wl.v, tq.LAYOUT_TILED)):
+        spec = tq.Spec(qs.bits_lo, qs.bits_hi, split=qs.split, layout=layout)
+        data = inp.k if tensor == "k" else inp.v
+        host = np.zeros((B * Hkv, cap, 128), np.uint16)
+        for b in range(B):
+            host[b * Hkv:(b + 1) * Hkv, :comp[b]] = workloads.bf16_bits(data[b][:, S:])
+        xd = torch().from_numpy(host.view(np.int16)).cuda().view(torch().bfloat16)
+        del host
+        tab = tq.device_tables(spec)
+        cache = tq.alloc_cache(spec, B * Hkv, cap)
+        tq.quantize_kv_ragged(spec, tab, xd, cache, hkv=Hkv, n_tok=comp)
+        torch().cuda.synchronize()
+        del xd
+        for b in seqs:
+            h = int(rng.integers(0, Hkv))
+            n = int(comp[b])
+            xs = workloads.bf16_to_f32(workloads.bf16_bits(data[b][h, S:]))
+            check_quantized(spec, xs, read_codes(spec, cache, b * Hkv + h, n), read_norms(cache, b * Hkv + h, n),
+                            label=f"ragged/{tensor}/seq {b} head {h}")

@@ -209,6 +209,37 @@ def test_quantize_argument_errors_without_launch():
     assert L.tq_quantize_kv(ctypes.byref(ts), fake_tab, 1, 0x1000, 1, 8, 0, 128, 0, ctypes.byref(c2), None) == -1
 
 
+def test_quantize_ragged_argument_errors_without_launch():
+    L = tq.lib()
+    spec = tq.Spec(4).c()
+    cache = tq.TqCache(0x1000, 0x2000, None, None, 64)
+    tab = ctypes.c_void_p(0x10000)
+
+    def call(n, t0=None, xo=None, x=0x1000, batch=None, hkv=2, dtype=1, sp=spec, c=cache):
+        n = np.asarray(n, np.int64)
+        t0 = np.zeros_like(n) if t0 is None else np.asarray(t0, np.int64)
+        xo = np.zeros_like(n) if xo is None else np.asarray(xo, np.int64)
+        b = len(n) if batch is None else batch
+        return L.tq_quantize_kv_ragged(ctypes.byref(sp), tab, dtype, x, b, hkv, xo.ctypes.data, t0.ctypes.data,
+                                       n.ctypes.data, 128 * 64, 128, ctypes.byref(c), None)
+
+    assert call([8, 65]) == -1                      # beyond capacity
+    assert call([8, 8], t0=[0, 60]) == -1           # tok0 + n beyond capacity
+    assert call([8, -1]) == -1                      # negative length
+    assert call([8, 8], xo=[0, 4]) == -1            # offset not a multiple of 16 bytes
+    assert call([8, 8], xo=[0, -8]) == -1           # negative offset
+    assert call([8, 8], hkv=0) == -1
+    assert call([8, 8], dtype=5) == -1
+    assert call([8, 8], x=None) == -1
+    assert call([8, 8], x=0x1002) == -1             # misaligned x
+    assert call([0, 0]) == 0                        # nothing to write: no launch
+    assert call([8], batch=0) == 0
+    assert L.tq_quantize_kv_ragged(ctypes.byref(spec), tab, 1, 0x1000, 2, 2, None, None, None, 128, 128,
+                                   ctypes.byref(cache), None) == -1
+    ts = tq.Spec(3, layout=1).c()
+    assert call([8, 8], sp=ts, c=tq.TqCache(0x1000, 0x2000, None, None, 40)) == -1  # tiled cap % 32
+
+
 def test_attend_argument_errors_without_launch():
     L = tq.lib()
     ks, vs = tq.Spec(4).c(), tq.Spec(3, layout=1).c()
