@@ -1,5 +1,6 @@
 // Decode attention read directly from the packed cache: the combine kernel,
-// the split plan and the launch (the split kernel is in attend_split.h).
+// the split plan and the launch (the split kernel, which merges a stream's
+// partials itself when the stream has one split, is in attend_split.h).
 //
 // noze.it, "TurboQuant-MLX: quantizzare pesi e KV cache per LLM open-weight su
 // Mac", section "Il metodo TurboQuant, in breve": inner products in the
@@ -134,7 +135,7 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                          void* workspace, hipStream_t st) {
   float* parts = static_cast<float*>(workspace);
-  const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, st};
+  const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, out, st};
   const int vkey = vs.bits_lo * 10 + vs.bits_hi;
   const bool qjl = ks.qjl_m != 0;
   hipError_t e;
@@ -147,6 +148,8 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  // with one split per stream the split kernel has merged its own partials
+  if (plan.n_split == 1) return hipSuccess;
   // four output slices per head while the heads alone would leave most CUs idle
   const int64_t heads = static_cast<int64_t>(a.batch) * a.hq;
   if (heads < 256)

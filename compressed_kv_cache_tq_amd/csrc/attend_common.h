@@ -36,6 +36,7 @@ struct SplitArgs {
   const uint16_t* sink_v;
   const int32_t* seq_lens;
   float* parts;
+  float* out;
   hipStream_t st;
 };
 

@@ -367,6 +367,82 @@ __device__ __forceinline__ int rank_sequence(const int32_t* __restrict__ seq_len
 }
 
 // Split kernel: one workgroup of 8 waves per (split, kv head, sequence).
+// Merge of one stream's partials, run by the stream's workgroup when it is
+// the stream's only split: for each of its G query heads, the log-sum-exp weights of
+// the n_split split partials (rotated value domain) and of the sink partial
+// (slot n_split, original domain, present when n_slot > n_split), the
+// weighted rotated sum, one inverse rotation Pi_V^T, the division by l.
+// pp: partials of the group's first head; og: its output rows.
+__device__ __forceinline__ void merge_stream(uint8_t* smem, const Tables* __restrict__ vtab,
+                                             const float* __restrict__ pp, float* __restrict__ og, int G,
+                                             int n_split, int n_slot) {
+  constexpr int WROW = MAX_SPLIT + 1;
+  float* wsm = reinterpret_cast<float*>(smem);  // [GMAX][WROW]: slot maxima, then weights
+  float* pr = wsm;                              // [4][GMAX][D]: quarters of the inverse rotation (later)
+  float* lsum = wsm + GMAX * WROW;              // [GMAX]
+  float* swt = lsum + GMAX;                     // [GMAX]: weight of the sink partial
+  float* rs = swt + GMAX;                       // [GMAX][D]: weighted rotated sums
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int o = tid & (D - 1), cq = tid >> 7;
+  // this thread's slice of Pi (used last) goes out first
+  float pic[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) pic[k] = vtab->pi[(32 * cq + k) * D + o];
+  // weights: wave w takes heads w, w + SW
+  for (int g = wave; g < G; g += SW) {
+    const float* ph = pp + static_cast<int64_t>(g) * n_slot * PART;
+    float* wg = wsm + g * WROW;
+    float mloc = -INFINITY;
+    for (int sl = lane; sl < n_slot; sl += 64) {
+      const float m = ph[sl * PART], l = ph[sl * PART + 1];
+      const float mv = l > 0.0f ? m : -INFINITY;
+      wg[sl] = mv;
+      mloc = fmaxf(mloc, mv);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    float lloc = 0.0f;
+    for (int sl = lane; sl < n_slot; sl += 64) {
+      const float mv = wg[sl];
+      const float f = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - mloc);
+      wg[sl] = f;
+      lloc = fmaf(f, ph[sl * PART + 1], lloc);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lloc += __shfl_xor(lloc, off);
+    if (lane == 0) lsum[g] = lloc;
+  }
+  __syncthreads();
+  // weighted rotated sums: thread (g, c) per pass
+  for (int idx = tid; idx < G * D; idx += ST) {
+    const int g = idx >> 7, c = idx & (D - 1);
+    const float* ph = pp + static_cast<int64_t>(g) * n_slot * PART + 4 + c;
+    const float* wg = wsm + g * WROW;
+    float a = 0.0f;
+#pragma unroll 8
+    for (int sl = 0; sl < n_split; ++sl) a = fmaf(wg[sl], ph[sl * PART], a);
+    rs[idx] = a;
+  }
+  if (tid < G) swt[tid] = n_slot > n_split ? wsm[tid * WROW + n_split] : 0.0f;
+  __syncthreads();
+  // inverse rotation: thread (o, cq) takes rotated coordinates [32 cq, 32 cq + 32)
+  for (int g = 0; g < G; ++g) {
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v = fmaf(pic[k], rs[g * D + 32 * cq + k], v);
+    pr[(cq * GMAX + g) * D + o] = v;
+  }
+  __syncthreads();
+  const bool has_sink = n_slot > n_split;
+  for (int idx = tid; idx < G * D; idx += ST) {
+    const int g = idx >> 7, oo = idx & (D - 1);
+    float v = ((pr[g * D + oo] + pr[(GMAX + g) * D + oo]) + pr[(2 * GMAX + g) * D + oo]) + pr[(3 * GMAX + g) * D + oo];
+    if (has_sink) v = fmaf(swt[g], pp[(static_cast<int64_t>(g) * n_slot + n_split) * PART + 4 + oo], v);
+    const float L = lsum[g];
+    og[idx] = L > 0.0f ? v / L : 0.0f;
+  }
+}
+
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 __global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
@@ -374,7 +450,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ vtab, const uint8_t* __restrict__ vcodes, const float* __restrict__ vnorms,
     int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q,
     const uint16_t* __restrict__ sink_k, const uint16_t* __restrict__ sink_v, float* __restrict__ parts,
-    int hq, int hkv, int sink, int n_split, int n_slot, int64_t chunk, float v_skip, float qscale) {
+    float* __restrict__ out, int hq, int hkv, int sink, int n_split, int n_slot,
+    int64_t chunk, float v_skip, float qscale) {
   using LP = LutPlan<KLO, KHI, VLO, VHI>;
   constexpr int KBYTES = 8 * (KLO + KHI);
   constexpr int VBYTES = 8 * (VLO + VHI);
@@ -391,6 +468,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   constexpr int SMEM = PRO_OFF + PRO > MRG ? PRO_OFF + PRO : MRG;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert(SMEM >= (GMAX * D + GMAX * MAX_SINK + 2 * GMAX * D + 2 * GMAX) * 4, "LDS of the sink split");
+  static_assert(SMEM >= (GMAX * (MAX_SPLIT + 1) + 2 * GMAX + GMAX * D) * 4 && GMAX * (MAX_SPLIT + 1) >= 4 * GMAX * D,
+                "LDS of the stream merge");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ uint32_t lutz[4];
 
@@ -423,6 +502,15 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
                        static_cast<int64_t>(n_split) * PART,
                    n_slot * PART);
     }
+  };
+  // A stream with a single split (a large batch) is merged right here, from
+  // the partials this workgroup has just written; several splits are merged
+  // by the combine kernel.
+  auto finish = [&]() {
+    if (n_split != 1) return;
+    __syncthreads();
+    const int64_t h0 = static_cast<int64_t>(b) * hq + static_cast<int64_t>(kh) * G;
+    merge_stream(smem, vtab, parts + h0 * n_slot * PART, out + h0 * D, G, n_split, n_slot);
   };
   // ---- prologue: rotate the group's queries.  Thread (pi_i, kq) forms the
   // partial dot of rotated coordinate pi_i over inputs [32 kq, 32 kq + 32).
@@ -495,6 +583,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
           c == 0 ? -INFINITY : 0.0f;
     }
     sink_part();
+    finish();
     return;
   }
 
@@ -877,17 +966,18 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
   }
   sink_part();
-
+  finish();
 }
 
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
 hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
                         const tq_attn& a, const AttendPlan& plan, const float* q, const uint16_t* sink_k,
-                        const uint16_t* sink_v, const int32_t* seq_lens, float* parts, hipStream_t st) {
+                        const uint16_t* sink_v, const int32_t* seq_lens, float* parts, float* out,
+                        hipStream_t st) {
   hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(a.hkv, a.batch, plan.n_split), dim3(ST), 0, st,
                      ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms, vc.cap,
-                     seq_lens, q, sink_k, sink_v, parts, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot, plan.chunk,
-                     a.v_skip, a.scale * LOG2E);
+                     seq_lens, q, sink_k, sink_v, parts, out, a.hq, a.hkv, a.sink, plan.n_split,
+                     plan.n_slot, plan.chunk, a.v_skip, a.scale * LOG2E);
   return hipGetLastError();
 }
 
@@ -895,9 +985,9 @@ hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vt
 template <int KLO, int KHI, int VLO, int VHI>
 hipError_t launch_q(bool qjl, const SplitArgs& f) {
   return qjl ? launch_split<KLO, KHI, VLO, VHI, true>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
-                                                      f.sink_v, f.seq_lens, f.parts, f.st)
+                                                      f.sink_v, f.seq_lens, f.parts, f.out, f.st)
              : launch_split<KLO, KHI, VLO, VHI, false>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
-                                                       f.sink_v, f.seq_lens, f.parts, f.st);
+                                                       f.sink_v, f.seq_lens, f.parts, f.out, f.st);
 }
 
 template <int KLO, int KHI>
