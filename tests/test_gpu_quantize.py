@@ -260,3 +260,37 @@ def test_quantize_ragged_full_size_sampled():
             xs = workloads.bf16_to_f32(workloads.bf16_bits(data[b][h, S:]))
             check_quantized(spec, xs, read_codes(spec, cache, b * Hkv + h, n), read_norms(cache, b * Hkv + h, n),
                             label=f"ragged/{tensor}/seq {b} head {h}")
+
+
+def test_quantize_wide_row_stride_general_kernel():
+    """Rows 2^24 elements apart (32 MiB of bf16) exceed the rotation kernel's
+    32-bit buffer offsets, so the call goes to the general kernel, one launch
+    per sequence; records and tiles (with partly written tiles merged) must
+    still match the oracle, and the tiled neighbours must keep their codes."""
+    print("[quantize] wide row stride: general kernel", flush=True)
+    T = torch()
+    xrs, n = 1 << 24, 3
+    rng = np.random.default_rng(17)
+    rows = workloads.bf16_to_f32(workloads.bf16_bits(rng.standard_normal((n, 128), dtype=np.float32)))
+    flat = T.zeros(n * xrs + 128, dtype=T.bfloat16, device="cuda")
+    for i in range(n):
+        flat[i * xrs:i * xrs + 128] = to_device(rows[i:i + 1], "bf16")[0]
+    x = flat.as_strided((1, n, 128), (n * xrs, xrs, 1))
+    for layout in (tq.LAYOUT_RECORD, tq.LAYOUT_TILED):
+        spec = tq.Spec(4, 3, split=64, layout=layout)
+        tab = tq.device_tables(spec)
+        cache = tq.alloc_cache(spec, 1, 64)
+        base = _data(64, seed=18, dtype="bf16")
+        tq.quantize_kv(spec, tab, to_device(base, "bf16"), cache)
+        T.cuda.synchronize()
+        before = read_codes(spec, cache, 0, 64)
+        tq.quantize_kv(spec, tab, x, cache, tok0=30)  # positions 30..32: across a tile edge
+        tq.quantize_kv_ragged(spec, tab, x, cache, hkv=1, n_tok=[2], tok0=[40], x_off=[0],
+                              x_stream_stride=n * xrs, x_row_stride=xrs)
+        T.cuda.synchronize()
+        got = read_codes(spec, cache, 0, 64)
+        keep = np.ones(64, bool)
+        keep[30:33] = keep[40:42] = False
+        assert np.array_equal(got[keep], before[keep]), f"layout {layout}: neighbours changed"
+        check_quantized(spec, rows, got[30:33], read_norms(cache, 0, 3, 30), label=f"wide stride/{layout}")
+        check_quantized(spec, rows[:2], got[40:42], read_norms(cache, 0, 2, 40), label=f"wide stride ragged/{layout}")
