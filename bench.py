@@ -359,7 +359,8 @@ def main() -> int:
     roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
                        "kernel": f"split_kernel<{wl.k.bits_lo},{wl.k.bits_hi},{wl.v.bits_lo},{wl.v.bits_hi}"
-                                 f"{',qjl' if kspec.qjl_m else ''}> + combine_kernel (one decode step)",
+                                 f"{',qjl' if kspec.qjl_m else ''}> (+ combine_kernel when a stream has several splits;"
+                                 f" one decode step)",
                        "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(dec_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
