@@ -202,6 +202,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD, help="workload to time (the metric is quoted on gqa_decode)")
+    ap.add_argument("--rotation", choices=("haar", "hadamard"), default="haar",
+                    help="how the rotation is drawn (the workloads are specified with the Haar rotation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 512 MiB fp32 streaming kernel (out = -in) 5 times; "
                          "its byte counts calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -230,9 +232,11 @@ def main() -> int:
     cap = max(32, -(-int(comp_h.max()) // 32) * 32)
     uniform = bool(np.all(lens_h == lens_h[0]))
     f32 = wl.dtype == "f32"
+    rot = tq.ROT_HADAMARD if args.rotation == "hadamard" else tq.ROT_HAAR
     kspec = tq.Spec(wl.k.bits_lo, wl.k.bits_hi, split=wl.k.split, qjl_m=wl.k.qjl_m, layout=tq.LAYOUT_RECORD,
-                    rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed)
-    vspec = tq.Spec(wl.v.bits_lo, wl.v.bits_hi, split=wl.v.split, layout=tq.LAYOUT_TILED, rot_seed=wl.v.rot_seed)
+                    rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed, rotation=rot)
+    vspec = tq.Spec(wl.v.bits_lo, wl.v.bits_hi, split=wl.v.split, layout=tq.LAYOUT_TILED, rot_seed=wl.v.rot_seed,
+                    rotation=rot)
     ktab, vtab = tq.device_tables(kspec), tq.device_tables(vspec)
 
     def device_input(parts):
@@ -370,7 +374,7 @@ def main() -> int:
                    "context": T if uniform else f"ragged {int(lens_h.min())}..{T}, sum {int(lens_h.sum())}",
                    "kv_dtype": wl.dtype, "k_bits": [wl.k.bits_lo, wl.k.bits_hi], "v_bits": [wl.v.bits_lo, wl.v.bits_hi],
                    "split": wl.k.split, "qjl": bool(kspec.qjl_m), "sink": S, "v_skip": wl.v_skip,
-                   "structure": wl.structure},
+                   "structure": wl.structure, "rotation": args.rotation},
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "decode_us": round(at_ms * 1e3, 2),
         "quantize_Mvec_s": round(quant_mvec, 1), "quantize_GB_s": round(quant_gbs, 2),

@@ -105,6 +105,19 @@ void rotation_build(int d, uint64_t seed, double* pi) {
     for (int k = 0; k < d; ++k) pi[i * d + k] = q[i * d + k] * (rdiag[k] < 0 ? -1.0 : 1.0);
 }
 
+// Randomized Hadamard rotation: pi = H diag(sigma) / sqrt(d), with the Sylvester
+// Hadamard matrix H (entry (i, k) = (-1)^popcount(i & k)) and sigma_k the sign
+// given by bit 63 of the k-th SplitMix64 output.
+
+void hadamard_rotation_build(int d, uint64_t seed, double* pi) {
+  SplitMix64 g{seed};
+  std::vector<double> sigma(d);
+  for (int k = 0; k < d; ++k) sigma[k] = (g.next() >> 63) ? -1.0 : 1.0;
+  const double scale = 1.0 / std::sqrt(static_cast<double>(d));
+  for (int i = 0; i < d; ++i)
+    for (int k = 0; k < d; ++k) pi[i * d + k] = (__builtin_popcount(i & k) & 1 ? -scale : scale) * sigma[k];
+}
+
 // ---------------------------------------------------------------------------
 // Lloyd-Max codebook for the law of one coordinate X of a uniform unit vector
 // in R^d: density K_d (1-x^2)^((d-3)/2) on [-1, 1], i.e. (1+X)/2 ~
@@ -280,6 +293,9 @@ tq_status check_spec(const tq_spec* s, tq::Spec* out) {
   if (s->qjl_m != 0 && s->qjl_m != TQ_QJL_M) return fail(TQ_E_UNSUPPORTED, "qjl_m must be 0 or 128");
   if (s->qjl_m && s->layout != TQ_LAYOUT_RECORD)
     return fail(TQ_E_UNSUPPORTED, "the QJL sketch needs the record layout");
+  if (s->rotation != TQ_ROT_HAAR && s->rotation != TQ_ROT_HADAMARD)
+    return fail(TQ_E_ARG, "rotation must be TQ_ROT_HAAR or TQ_ROT_HADAMARD");
+  if (s->reserved != 0) return fail(TQ_E_ARG, "reserved must be 0");
   if (out) {
     out->bits_lo = bl;
     out->bits_hi = bhi;
@@ -366,6 +382,17 @@ tq_status tq_rotation_build(int32_t d, uint64_t seed, double* pi) {
   return TQ_OK;
 }
 
+tq_status tq_hadamard_rotation_build(int32_t d, uint64_t seed, double* pi) {
+  if (d < 1 || d > 1024 || (d & (d - 1))) return fail(TQ_E_ARG, "d must be a power of two in [1, 1024]");
+  if (!pi) return fail(TQ_E_ARG, "output pointer is NULL");
+  try {
+    hadamard_rotation_build(d, seed, pi);
+  } catch (const std::bad_alloc&) {
+    return fail(TQ_E_ARG, "out of host memory");
+  }
+  return TQ_OK;
+}
+
 tq_status tq_sketch_build(int32_t m, int32_t d, uint64_t seed, double* s) {
   if (m < 1 || m > 1024 || d < 1 || d > 1024) return fail(TQ_E_ARG, "m and d must be in [1, 1024]");
   if (!s) return fail(TQ_E_ARG, "output pointer is NULL");
@@ -405,7 +432,8 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
         return fail(TQ_E_UNSUPPORTED, "codebook boundaries too close for the code cell table");
     }
     std::vector<double> m(tq::D * tq::D);
-    rotation_build(tq::D, spec->rot_seed, m.data());
+    if (spec->rotation == TQ_ROT_HADAMARD) hadamard_rotation_build(tq::D, spec->rot_seed, m.data());
+    else rotation_build(tq::D, spec->rot_seed, m.data());
     for (int i = 0; i < tq::D; ++i)
       for (int k = 0; k < tq::D; ++k) t->pit[k * tq::D + i] = static_cast<float>(m[i * tq::D + k]);
     for (int i = 0; i < tq::D * tq::D; ++i) {

@@ -21,10 +21,12 @@ TILE = 32
 QJL_M = 128
 F32, BF16 = 0, 1
 LAYOUT_RECORD, LAYOUT_TILED = 0, 1
+ROT_HAAR, ROT_HADAMARD = 0, 1
 STATUS = {0: "TQ_OK", -1: "TQ_E_ARG", -2: "TQ_E_UNSUPPORTED", -3: "TQ_E_WORKSPACE", -4: "TQ_E_HIP"}
 
 EXPORTS = [
-    "tq_format_version", "tq_last_error", "tq_codebook_build", "tq_rotation_build", "tq_sketch_build",
+    "tq_format_version", "tq_last_error", "tq_codebook_build", "tq_rotation_build",
+    "tq_hadamard_rotation_build", "tq_sketch_build",
     "tq_tables_bytes", "tq_tables_build", "tq_code_bytes", "tq_cache_code_bytes", "tq_quantize_kv",
     "tq_quantize_kv_ragged",
     "tq_attend_workspace_bytes", "tq_attend_decode",
@@ -34,7 +36,8 @@ EXPORTS = [
 class TqSpec(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("bits_lo", ctypes.c_int32), ("bits_hi", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("qjl_m", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("rot_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64)]
+                ("rot_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64), ("rotation", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class TqCache(ctypes.Structure):
@@ -71,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "tq_last_error": (ctypes.c_char_p, []),
         "tq_codebook_build": (I32, [I32, I32, P, P]),
         "tq_rotation_build": (I32, [I32, U64, P]),
+        "tq_hadamard_rotation_build": (I32, [I32, U64, P]),
         "tq_sketch_build": (I32, [I32, I32, U64, P]),
         "tq_tables_bytes": (SZ, []),
         "tq_tables_build": (I32, [ctypes.POINTER(TqSpec), P, SZ]),
@@ -114,10 +118,11 @@ class Spec:
     layout: int = LAYOUT_RECORD
     rot_seed: int = 0
     qjl_seed: int = 1
+    rotation: int = 0      # ROT_HAAR or ROT_HADAMARD
 
     def c(self) -> TqSpec:
         return TqSpec(D, self.bits_lo, self.bits_lo if self.bits_hi is None else self.bits_hi, self.split,
-                      self.qjl_m, self.layout, self.rot_seed, self.qjl_seed)
+                      self.qjl_m, self.layout, self.rot_seed, self.qjl_seed, self.rotation, 0)
 
     @property
     def widths(self) -> np.ndarray:
@@ -138,6 +143,12 @@ def codebook_build(d: int, bits: int):
 def rotation_build(d: int, seed: int) -> np.ndarray:
     m = np.zeros((d, d))
     _check(lib().tq_rotation_build(d, seed, m.ctypes.data), "tq_rotation_build")
+    return m
+
+
+def hadamard_rotation_build(d: int, seed: int) -> np.ndarray:
+    m = np.zeros((d, d))
+    _check(lib().tq_hadamard_rotation_build(d, seed, m.ctypes.data), "tq_hadamard_rotation_build")
     return m
 
 

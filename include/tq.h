@@ -70,6 +70,12 @@ typedef enum {
  * (noze.it page, section "Il metodo TurboQuant, in breve": 3.5 and 2.5 bits
  * per channel; 3.5 bits = split 64 with 4 and 3 bits).  split == d means a
  * uniform width and bits_hi is then ignored. */
+/* How the rotation Pi is drawn from rot_seed. */
+typedef enum {
+  TQ_ROT_HAAR = 0,      /* Haar-distributed orthogonal matrix (tq_rotation_build) */
+  TQ_ROT_HADAMARD = 1   /* randomized Hadamard matrix (tq_hadamard_rotation_build) */
+} tq_rotation;
+
 typedef struct {
   int32_t d;          /* must be TQ_DIM */
   int32_t bits_lo;    /* 2, 3 or 4 */
@@ -79,6 +85,8 @@ typedef struct {
   int32_t layout;     /* tq_layout */
   uint64_t rot_seed;  /* seed of the rotation (SplitMix64 stream) */
   uint64_t qjl_seed;  /* seed of the sketch matrix S */
+  int32_t rotation;   /* tq_rotation */
+  int32_t reserved;   /* must be 0 */
 } tq_spec;
 
 /* One tensor of a packed cache, for n_streams = batch * kv_heads streams of
@@ -137,6 +145,15 @@ tq_status tq_codebook_build(int32_t d, int32_t bits, double* centroids, double* 
  * factor of a SplitMix64/Box-Muller Gaussian matrix, with column signs chosen
  * so that R has a positive diagonal (Haar measure).  1 <= d <= 1024. */
 tq_status tq_rotation_build(int32_t d, uint64_t seed, double* pi);
+
+/* Host only.  The seeded randomized Hadamard rotation (noze.it page, section
+ * "Cosa aggiunge turboquant-mlx": a Hadamard transform as the fast way to
+ * realise the random rotation): Pi = H_d diag(sigma) / sqrt(d), with H_d the
+ * Sylvester Hadamard matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]],
+ * so entry (i, k) is (-1)^popcount(i & k)) and sigma_k = -1 if bit 63 of the
+ * k-th SplitMix64 output of `seed` is set, else +1.  d a power of two,
+ * 1 <= d <= 1024; row-major, y = Pi x. */
+tq_status tq_hadamard_rotation_build(int32_t d, uint64_t seed, double* pi);
 
 /* Host only.  The QJL sketch S (m x d, row-major), i.i.d. N(0,1) from the
  * same generator seeded with `seed`.  1 <= m, d <= 1024. */

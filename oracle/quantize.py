@@ -31,7 +31,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .codebook import lloyd_max
-from .rotation import rotation, sketch
+from .rotation import hadamard_rotation, rotation, sketch
 
 
 @dataclass(frozen=True)
@@ -43,6 +43,7 @@ class Spec:
     qjl_m: int = 0        # QJL sketch rows (0 = no QJL stage)
     rot_seed: int = 0
     qjl_seed: int = 1
+    rotation: str = "haar"  # "haar" or "hadamard"
 
     def bits_of(self) -> np.ndarray:
         """Bit width of every rotated coordinate."""
@@ -56,6 +57,10 @@ class Spec:
 
 
 def rotation_of(spec: Spec) -> np.ndarray:
+    if spec.rotation == "hadamard":
+        return hadamard_rotation(spec.rot_seed, spec.d)
+    if spec.rotation != "haar":
+        raise ValueError(f"unknown rotation {spec.rotation!r}")
     return rotation(spec.rot_seed, spec.d)
 
 

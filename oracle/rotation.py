@@ -20,7 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .rng import gaussian
+from .rng import gaussian, splitmix64
 
 
 def gaussian_matrix(seed: int, rows: int, cols: int) -> np.ndarray:
@@ -38,6 +38,35 @@ def rotation(seed: int, d: int) -> np.ndarray:
     s = np.sign(np.diag(r))
     s[s == 0] = 1.0
     return q * s[None, :]
+
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Sylvester's Hadamard matrix of order d (a power of two), float64:
+    H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_signs(seed: int, d: int) -> np.ndarray:
+    """sigma_k = -1 when bit 63 of the k-th SplitMix64 output of ``seed`` is set, else +1."""
+    top = splitmix64(seed, d) >> np.uint64(63)
+    return np.where(top == 1, -1.0, 1.0)
+
+
+def hadamard_rotation(seed: int, d: int) -> np.ndarray:
+    """Randomized Hadamard rotation Pi = H_d diag(sigma) / sqrt(d) (float64).
+
+    noze.it page, section "Cosa aggiunge turboquant-mlx": the port realises
+    the random rotation as a Hadamard transform, the fast and cheap way.
+    Reading taken (the page gives no construction): random sign flips drawn
+    from the seed, applied before the transform, and the 1/sqrt(d) that makes
+    the matrix orthogonal.  y = Pi @ x as for the Haar rotation.
+    """
+    return sylvester_hadamard(d) * hadamard_signs(seed, d)[None, :] / np.sqrt(d)
 
 
 def sketch(seed: int, m: int, d: int) -> np.ndarray:

@@ -2,6 +2,8 @@
 
 The oracle reads the GPU's own codes, norms and sketch bits and evaluates the
 attention in float64; the bound is 2e-3 relative L2 over the whole output."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -44,6 +46,18 @@ def _check(run: Run, heads=None, tol=parity.ATTN_REL_L2, label=""):
 def test_attend_small(name, ctx, batch):
     print(f"[attend] small {name} ctx={ctx} batch={batch}", flush=True)
     _check(Run(workloads.generate(name, ctx=ctx, batch=batch)), label=f"{name} small")
+
+
+@pytest.mark.parametrize("name,ctx,batch", [("gqa_decode", 1500, None), ("qjl", 1000, 2), ("batched_ragged", 900, 3)])
+def test_attend_hadamard_rotation(name, ctx, batch):
+    """Keys and values rotated by the randomized Hadamard matrix (QJL keys
+    included): the same kernels, the oracle with the Hadamard Pi."""
+    print(f"[attend] hadamard {name}", flush=True)
+    run = Run(workloads.generate(name, ctx=ctx, batch=batch))
+    run.kspec = dataclasses.replace(run.kspec, rotation=tq.ROT_HADAMARD)
+    run.vspec = dataclasses.replace(run.vspec, rotation=tq.ROT_HADAMARD)
+    run.ktab, run.vtab = tq.device_tables(run.kspec), tq.device_tables(run.vspec)
+    _check(run, label=f"{name} hadamard")
 
 
 def test_attend_sink_and_peaked_v_skip():

@@ -294,3 +294,21 @@ def test_quantize_wide_row_stride_general_kernel():
         assert np.array_equal(got[keep], before[keep]), f"layout {layout}: neighbours changed"
         check_quantized(spec, rows, got[30:33], read_norms(cache, 0, 3, 30), label=f"wide stride/{layout}")
         check_quantized(spec, rows[:2], got[40:42], read_norms(cache, 0, 2, 40), label=f"wide stride ragged/{layout}")
+
+
+@pytest.mark.parametrize("layout", [tq.LAYOUT_RECORD, tq.LAYOUT_TILED])
+@pytest.mark.parametrize("w", [(4, None, 128), (4, 3, 64), (2, None, 128)])
+def test_quantize_hadamard_rotation(w, layout):
+    """The randomized Hadamard rotation runs through the same kernels (its
+    matrix sits in the tables): parity with the oracle's Hadamard Pi, with a
+    ragged tail and an unaligned second append."""
+    print(f"[quantize] hadamard widths={w} layout={layout}", flush=True)
+    spec = tq.Spec(w[0], w[1], split=w[2], layout=layout, rot_seed=3, rotation=tq.ROT_HADAMARD)
+    x = _data(1000, seed=40 + w[0] + layout, dtype="bf16")
+    cache = _quantize(spec, x, "bf16", cap=1056)
+    y = _data(37, seed=41, dtype="bf16")
+    tq.quantize_kv(spec, tq.device_tables(spec), to_device(y, "bf16"), cache, tok0=1003)
+    torch().cuda.synchronize()
+    check_quantized(spec, x[0], read_codes(spec, cache, 0, 1000), read_norms(cache, 0, 1000), label=f"hadamard {w}")
+    check_quantized(spec, y[0], read_codes(spec, cache, 0, 37, 1003), read_norms(cache, 0, 37, 1003),
+                    label=f"hadamard append {w}")

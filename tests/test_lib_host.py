@@ -46,6 +46,34 @@ def test_rotation_matches_oracle(seed):
     assert np.max(np.abs(pi - orot.rotation(seed, 128))) <= 1e-12
 
 
+@pytest.mark.parametrize("d,seed", [(1, 0), (4, 0), (128, 0), (128, 7), (1024, 3)])
+def test_hadamard_rotation_matches_oracle(d, seed):
+    assert np.array_equal(tq.hadamard_rotation_build(d, seed), orot.hadamard_rotation(seed, d))
+
+
+def test_hadamard_rotation_errors_and_spec_fields():
+    L = tq.lib()
+    m = np.zeros(16)
+    for d in (0, 3, 6, 2048):
+        assert L.tq_hadamard_rotation_build(d, 0, m.ctypes.data) == -1
+    assert L.tq_hadamard_rotation_build(4, 0, None) == -1
+    buf = np.zeros(tq.tables_bytes(), dtype=np.uint8)
+    for rot, reserved in ((2, 0), (-1, 0), (0, 1)):
+        cs = tq.Spec(4).c()
+        cs.rotation, cs.reserved = rot, reserved
+        assert tq.lib().tq_tables_build(ctypes.byref(cs), buf.ctypes.data, buf.size) == -1
+
+
+def test_hadamard_tables():
+    spec = tq.Spec(3, layout=tq.LAYOUT_TILED, rot_seed=5, rotation=tq.ROT_HADAMARD)
+    ref = orot.hadamard_rotation(5, 128)
+    hdr, pi, pi_hi, pi_lo, *_ = _tables_view(spec, ref)
+    assert np.array_equal(pi, ref.astype(np.float32))
+    assert np.array_equal(pi_hi, (256 * ref).astype(np.float16))
+    two = pi_hi.astype(np.float64) + pi_lo.astype(np.float64)
+    assert np.max(np.abs(two - 256 * ref)) <= 256 * 2.0 ** -22
+
+
 def test_sketch_matches_oracle():
     s = tq.sketch_build(128, 128, 1)
     assert np.max(np.abs(s - orot.sketch(1, 128, 128))) <= 1e-13
@@ -77,7 +105,7 @@ def _check_pi_frag(frag, pi_hi, pi_lo):
         assert rows == set(range(128))
 
 
-def _tables_view(spec):
+def _tables_view(spec, ref=None):
     buf = tq.tables_build(spec)
     hdr = buf[:32].view(np.uint32)
     off = 512
@@ -100,7 +128,7 @@ def _tables_view(spec):
     off += 65536
     b16 = buf[off: off + 3 * 32768].view(np.uint16).reshape(3, 128, 128)
     parts = (b16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    ref = orot.rotation(0, 128)
+    ref = orot.rotation(0, 128) if ref is None else ref
     assert np.max(np.abs(parts.sum(0) - ref)) <= 2.0 ** -24 * np.abs(ref).max()
     off += 3 * 32768
     cells = buf[off: off + 2 * 132 * 8].view(np.uint32).reshape(2, 132, 2)

@@ -47,13 +47,16 @@ def test_norm_rotation_and_zero_vector():
     assert np.allclose(q.y[2], -pi[:, 5], atol=1e-15)
 
 
+@pytest.mark.parametrize("rot", ["haar", "hadamard"])
 @pytest.mark.parametrize("bits", [(4, 4, 128), (3, 3, 128), (4, 3, 64)])
-def test_empirical_distortion_on_tiny_workload(bits):
+def test_empirical_distortion_on_tiny_workload(bits, rot):
     # tiny_oracle inputs (4096 K + 4096 V, fp32 N(0,1), seed 0): the measured
     # d * mean squared error of the unit vectors matches the analytic value.
+    # (For Gaussian inputs the randomized Hadamard transform also gives
+    # coordinates with the uniform-sphere marginal.)
     inp = workloads.generate("tiny_oracle")
     x = np.concatenate([inp.k[0][0], inp.v[0][0]]).astype(np.float64)
-    spec = qz.Spec(bits_lo=bits[0], bits_hi=bits[1], split=bits[2])
+    spec = qz.Spec(bits_lo=bits[0], bits_hi=bits[1], split=bits[2], rotation=rot)
     q = qz.quantize(x, spec)
     err = np.sum((q.y - qz.dequantize_rotated(q.idx, spec)) ** 2, axis=1)     # per vector
     Dlo = cbm.distortion(cbm.lloyd_max(128, bits[0]))

@@ -87,3 +87,31 @@ def test_sketch_is_rowmajor_gaussian_stream():
     s = rotation.sketch(1, 128, 128)
     assert s.shape == (128, 128)
     assert np.array_equal(s.ravel(), rng.gaussian(1, 128 * 128))
+
+
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_sylvester_hadamard_is_scipys(d):
+    from scipy.linalg import hadamard
+    assert np.array_equal(rotation.sylvester_hadamard(d), hadamard(d).astype(np.float64))
+
+
+def test_hadamard_signs_are_the_top_bits_of_splitmix64():
+    want = [-1.0 if int(r[0], 16) >> 63 else 1.0 for r in read_golden("splitmix64_seed0.txt")]
+    assert rotation.hadamard_signs(0, len(want)).tolist() == want
+
+
+def test_hadamard_rotation_worked_example_d4():
+    # seed 0: the first four SplitMix64 outputs have top bits 1, 0, 0, 1, so
+    # sigma = (-1, +1, +1, -1); Pi = H_4 diag(sigma) / 2, written out by hand
+    want = np.array([[-1, 1, 1, -1], [-1, -1, 1, 1], [-1, 1, -1, 1], [-1, -1, -1, -1]], dtype=np.float64) / 2.0
+    assert np.array_equal(rotation.hadamard_rotation(0, 4), want)
+
+
+@pytest.mark.parametrize("seed", [0, 9])
+def test_hadamard_rotation_orthogonal_with_flat_entries(seed):
+    d = 128
+    pi = rotation.hadamard_rotation(seed, d)
+    assert np.max(np.abs(pi @ pi.T - np.eye(d))) <= 1e-14
+    assert np.max(np.abs(np.abs(pi) * math.sqrt(d) - 1.0)) <= 1e-15
+    # first row is sigma / sqrt(d): the signs are the seed's
+    assert np.array_equal(np.sign(pi[0]), rotation.hadamard_signs(seed, d))
