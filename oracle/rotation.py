@@ -12,6 +12,10 @@ matrices from the classical compact groups", Notices AMS 2007).  With that sign
 convention the factorisation A = Pi R is unique, so any correct QR gives the
 same Pi up to rounding.
 
+The same page, section "Cosa aggiunge turboquant-mlx", notes that one port
+realises the random rotation with a Hadamard transform; ``hadamard_rotation``
+is that option (its reading is in its docstring).
+
 The QJL stage (same section: a 1-bit quantized Johnson-Lindenstrauss transform
 of the residual) uses an m x d matrix S of i.i.d. standard normal entries,
 drawn from its own seed and not orthogonalised.
