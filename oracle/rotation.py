@@ -16,7 +16,7 @@ The same page, section "Cosa aggiunge turboquant-mlx", notes that one port
 realises the random rotation with a Hadamard transform; ``hadamard_rotation``
 is that option (its reading is in its docstring).
 
-The QJL stage (same section: a 1-bit quantized Johnson-Lindenstrauss transform
+The QJL stage (section "Il metodo TurboQuant, in breve": a 1-bit quantized JL transform
 of the residual) uses an m x d matrix S of i.i.d. standard normal entries,
 drawn from its own seed and not orthogonalised.
 """
