@@ -50,6 +50,9 @@ def attend_rotated(q: np.ndarray, qr: np.ndarray, khat: np.ndarray, k_norm: np.n
     n_sink = 0 if sink_k is None else sink_k.shape[0]
     s_sink = scale * (np.asarray(sink_k, np.float64) @ q) if n_sink else np.zeros(0)
     s = np.concatenate((s_sink, s_comp))
+    if s.size == 0:
+        # a sequence with no tokens attends to nothing: the output is zero
+        return np.zeros(pi_v.shape[1]), s, np.zeros(0, dtype=bool)
     w = np.exp(s - s.max())
     w /= w.sum()
     w_sink, w_comp = w[:n_sink], w[n_sink:]

@@ -79,6 +79,22 @@ def test_attend_gqa_g1_and_g16():
         _check(Run(workloads.generate(wl)), label=f"G={hq // hkv}")
 
 
+@pytest.mark.parametrize("hq,hkv,sink", [(128, 128, 0), (256, 16, 32), (32, 8, 128)])
+def test_attend_single_split_streams_merge_in_place(hq, hkv, sink):
+    """256 or more (sequence, KV head) streams give one split per stream, so
+    the split kernel merges its own partials (no combine launch): G = 1, 16
+    and 4, ragged lengths including 0 and lengths below the sink."""
+    print(f"[attend] one split per stream: hq={hq} hkv={hkv} sink={sink}", flush=True)
+    B = max(1, 256 // hkv)
+    wl = workloads.Workload(f"one{hq}_{hkv}_{sink}", B, hq, hkv, "bf16", workloads.QSpec(4, 4),
+                            workloads.QSpec(2, 2), lens_range=(sink + 1, 200), sink=sink, v_skip=1e-6 if sink else 0.0)
+    inp = workloads.generate(wl)
+    inp.seq_lens[0] = 0
+    if sink:
+        inp.seq_lens[-1] = sink // 2
+    _check(Run(inp), label=f"one split hq={hq} hkv={hkv} sink={sink}")
+
+
 @pytest.mark.parametrize("kb,vb,qjl", [((3, 2), (3, 2), 0), ((4, 3), (3, 2), 128), ((3, 2), (4, 3), 0)])
 def test_attend_mixed_width_combinations(kb, vb, qjl):
     """Split-width keys and values (64 coordinates at each width) in the other

@@ -126,3 +126,12 @@ def test_qjl_scores_unbiased_over_seeds():
     vals = np.array(vals)
     se = vals.std() / math.sqrt(len(vals))
     assert abs(vals.mean() - exact) < 4 * se
+
+
+def test_empty_sequence_gives_zero_output():
+    d = 128
+    pi = np.eye(d)
+    empty = np.zeros((0, d))
+    q = np.ones(d)
+    out, w, keep = at.attend_rotated(q, q, empty, np.zeros(0), empty, np.zeros(0), pi, scale=0.1)
+    assert out.shape == (d,) and np.all(out == 0.0) and w.size == 0 and keep.size == 0
