@@ -30,7 +30,7 @@ def _check(run: Run, heads=None, tol=parity.ATTN_REL_L2, label=""):
     mask = ~np.isnan(ref[..., 0])
     assert np.all(np.isfinite(out)), f"{label}: non-finite output"
     err = parity.rel_l2(out[mask], ref[mask])
-    per = [parity.rel_l2(out[b, h], ref[b, h]) for b, h in zip(*np.nonzero(mask))]
+    per = [parity.rel_l2(out[b, h], ref[b, h]) for b, h in zip(*np.nonzero(mask)) if np.any(ref[b, h])] or [0.0]
     print(f"[attend] {label}: rel_l2={err:.3e} worst head={max(per):.3e}", flush=True)
     assert err <= tol, f"{label}: rel L2 {err:.3e} > {tol}"
     return err
