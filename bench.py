@@ -195,6 +195,67 @@ def kspec_bytes(spec) -> int:
     return tq.code_bytes(spec)
 
 
+def bench_search(args) -> int:
+    """Inner-product search: scores of the search workload's queries against
+    its packed database, back to back (prep + scores launches per call)."""
+    import torch
+    from compressed_kv_cache_tq_amd import tq, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = workloads.SEARCH
+    rot = tq.ROT_HADAMARD if args.rotation == "hadamard" else tq.ROT_HAAR
+    spec = tq.Spec(wl.bits, qjl_m=wl.qjl_m, layout=tq.LAYOUT_RECORD, rotation=rot)
+    tab = tq.device_tables(spec)
+    xd = torch.from_numpy(workloads.bf16_bits(workloads.search_database(wl)).view(np.int16)).cuda().view(torch.bfloat16)
+    cache = tq.alloc_cache(spec, wl.streams, wl.n_tok)
+    tq.quantize_kv(spec, tab, xd, cache)
+    del xd
+    # five database copies (5 x 58.7 MB) so back-to-back calls read HBM, not
+    # the 256 MB Infinity Cache
+    caches = [cache] + [tq.clone_cache(cache) for _ in range(4)]
+    q = torch.from_numpy(workloads.search_queries(wl)).cuda()
+    N = wl.streams * wl.n_tok
+    scores = torch.empty((wl.nq, N), dtype=torch.float32, device="cuda")
+    ws = tq.alloc_ip_workspace()
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        tq.ip_scores(spec, tab, caches[i % len(caches)], q, n_streams=wl.streams, n_tok=wl.n_tok, scores=scores,
+                     workspace=ws)
+
+    for i in range(max(args.warmup, len(caches))):
+        call(i)
+    torch.cuda.synchronize()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    for i in range(args.steps):
+        call(i)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    ms = ea.elapsed_time(eb) / args.steps
+    per_vec = tq.code_bytes(spec) + 4 + (wl.qjl_m // 8 + 4 if wl.qjl_m else 0)
+    db_bytes = N * per_vec + wl.nq * 128 * 4
+    out_bytes = wl.nq * N * 4
+    gbs = (db_bytes + out_bytes) / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "packed inner-product search GB/s (% HBM peak)", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": wl.name, "database": N, "streams": wl.streams, "queries": wl.nq, "d": 128,
+                   "bits": wl.bits, "qjl": bool(wl.qjl_m), "rotation": args.rotation},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "call_us": round(ms * 1e3, 2),
+        "gscores_s": round(wl.nq * N / (ms * 1e-3) / 1e9, 2),
+        "bytes": {"database_and_queries": db_bytes, "scores": out_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"ip_kernel<{wl.bits},{wl.bits}{',qjl' if wl.qjl_m else ''}> + ipq_prep_kernel",
+                     "algorithmic_bytes_per_launch": db_bytes + out_bytes, "avg_launch_us": round(ms * 1e3, 2)},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +279,8 @@ def main() -> int:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); every box here has a single "
               f"MI355X and this path is not sharded across GPUs.", file=sys.stderr)
         return 2
+    if args.workload == "ip_search":
+        return bench_search(args)
     import torch
     from compressed_kv_cache_tq_amd import tq, workloads
 

@@ -494,6 +494,36 @@ size_t tq_cache_code_bytes(const tq_spec* spec, int64_t cap) {
   return static_cast<size_t>(pos) * sp.code_bytes;
 }
 
+size_t tq_ip_workspace_bytes(void) { return tq::ip_workspace_bytes(); }
+
+tq_status tq_ip_scores(const tq_spec* spec, const void* tables, const tq_cache* db, int64_t n_streams,
+                       int64_t n_tok, const float* q, int32_t nq, float* scores, int64_t ld, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  tq::Spec sp;
+  if (tq_status st = check_spec(spec, &sp); st != TQ_OK) return st;
+  if (sp.layout != TQ_LAYOUT_RECORD) return fail(TQ_E_UNSUPPORTED, "search needs the record layout");
+  if (tq_status st = check_tables(tables, sp, "search"); st != TQ_OK) return st;
+  if (!db) return fail(TQ_E_ARG, "db is NULL");
+  if (n_streams < 0 || n_tok < 0) return fail(TQ_E_ARG, "negative n_streams or n_tok");
+  if (nq < 1 || nq > TQ_IP_MAX_QUERIES) return fail(TQ_E_UNSUPPORTED, "nq must be in [1, 64]");
+  if (n_tok > db->cap) return fail(TQ_E_ARG, "n_tok exceeds the cache capacity");
+  if (n_tok > (int64_t{1} << 24)) return fail(TQ_E_UNSUPPORTED, "at most 2^24 positions per stream");
+  if (n_streams > 65535) return fail(TQ_E_UNSUPPORTED, "at most 65535 streams per call");
+  if (ld < n_streams * n_tok) return fail(TQ_E_ARG, "ld smaller than n_streams * n_tok");
+  if (n_streams == 0 || n_tok == 0) return TQ_OK;
+  if (!q || !scores || !db->codes || !db->norms) return fail(TQ_E_ARG, "q, scores and db arrays must be non-NULL");
+  if (sp.qjl_m && (!db->qjl_signs || !db->qjl_rnorms)) return fail(TQ_E_ARG, "db QJL arrays are NULL");
+  if (!aligned(q, 4) || !aligned(scores, 4) || !aligned(db->codes, 16) || !aligned(db->norms, 16))
+    return fail(TQ_E_ARG, "q and scores must be 4-byte, codes and norms 16-byte aligned");
+  if (sp.qjl_m && (!aligned(db->qjl_signs, 16) || !aligned(db->qjl_rnorms, 16)))
+    return fail(TQ_E_ARG, "QJL arrays must be 16-byte aligned");
+  if (!workspace || ws_bytes < tq::ip_workspace_bytes()) return fail(TQ_E_WORKSPACE, "workspace too small");
+  if (!aligned(workspace, 16)) return fail(TQ_E_ARG, "workspace must be 16-byte aligned");
+  const hipError_t e = tq::launch_ip_scores(sp, static_cast<const tq::Tables*>(tables), *db, n_streams, n_tok, q, nq,
+                                            scores, ld, workspace, static_cast<hipStream_t>(stream));
+  return hip_status(e, "tq_ip_scores launch");
+}
+
 }  // extern "C"
 
 namespace {

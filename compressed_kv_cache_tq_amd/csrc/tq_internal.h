@@ -100,6 +100,12 @@ hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const v
                            int64_t n_seq, int64_t hkv, int64_t x_stream_stride, int64_t x_row_stride,
                            const tq_cache& cache, hipStream_t stream);
 
+// Inner-product scores of nq <= TQ_IP_MAX_QUERIES queries against a
+// record-layout cache (search.hip).
+size_t ip_workspace_bytes();
+hipError_t launch_ip_scores(const Spec& sp, const Tables* tab, const tq_cache& c, int64_t n_streams, int64_t n_tok,
+                            const float* q, int nq, float* scores, int64_t ld, void* workspace, hipStream_t st);
+
 struct AttendPlan {
   int n_split;       // splits of the compressed token range per (b, kv head)
   int n_slot;        // partials per query head: n_split, plus one for the sink tokens

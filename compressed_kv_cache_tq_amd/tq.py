@@ -29,8 +29,9 @@ EXPORTS = [
     "tq_hadamard_rotation_build", "tq_sketch_build",
     "tq_tables_bytes", "tq_tables_build", "tq_code_bytes", "tq_cache_code_bytes", "tq_quantize_kv",
     "tq_quantize_kv_ragged",
-    "tq_attend_workspace_bytes", "tq_attend_decode",
+    "tq_attend_workspace_bytes", "tq_attend_decode", "tq_ip_workspace_bytes", "tq_ip_scores",
 ]
+IP_MAX_QUERIES = 64
 
 
 class TqSpec(ctypes.Structure):
@@ -85,6 +86,9 @@ def lib() -> ctypes.CDLL:
         "tq_quantize_kv_ragged": (I32, [ctypes.POINTER(TqSpec), P, I32, P, I32, I32, P, P, P, I64, I64,
                                         ctypes.POINTER(TqCache), P]),
         "tq_attend_workspace_bytes": (SZ, [ctypes.POINTER(TqAttn)]),
+        "tq_ip_workspace_bytes": (SZ, []),
+        "tq_ip_scores": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache), I64, I64, P, I32, P, I64, P, SZ,
+                               P]),
         "tq_attend_decode": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache), ctypes.POINTER(TqSpec), P,
                                    ctypes.POINTER(TqCache), ctypes.POINTER(TqAttn), P, P, P, P, P, P, SZ, P]),
     }
@@ -344,3 +348,30 @@ def attend_decode(kspec: Spec, ktables, kcache: Cache, vspec: Spec, vtables, vca
                                   _ptr(sink_k), _ptr(sink_v), seq_lens.data_ptr(), out.data_ptr(),
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), st),
            "tq_attend_decode")
+
+
+def alloc_ip_workspace(device="cuda"):
+    """Workspace of ip_scores (query rows; no state is kept in it)."""
+    torch = _torch()
+    n = int(lib().tq_ip_workspace_bytes())
+    return torch.empty((n + 15) // 16 * 4, dtype=torch.float32, device=device)
+
+
+def ip_scores(spec: Spec, tables, db: Cache, q, *, n_streams: int, n_tok: int, scores=None, ld: int | None = None,
+              workspace=None, stream: int | None = None):
+    """Inner-product estimates of q [nq, d] (fp32, nq <= 64) against positions
+    [0, n_tok) of db's first n_streams streams: scores [nq, ld], column
+    s * n_tok + t for stream s, position t."""
+    torch = _torch()
+    nq = q.shape[0]
+    ld = n_streams * n_tok if ld is None else ld
+    if scores is None:
+        scores = torch.empty((nq, ld), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_ip_workspace(q.device)
+    cs, cc = spec.c(), db.c()
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().tq_ip_scores(ctypes.byref(cs), tables.data_ptr(), ctypes.byref(cc), n_streams, n_tok, q.data_ptr(),
+                              nq, scores.data_ptr(), ld, workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), st), "tq_ip_scores")
+    return scores

@@ -148,3 +148,39 @@ def generate(wl: Workload | str, seed: int | None = None, ctx: int | None = None
         inp.k_bf16.append(kbits)
         inp.v_bf16.append(vbits)
     return inp
+
+
+# ---- inner-product search (the method's second application)
+
+@dataclass(frozen=True)
+class SearchWorkload:
+    name: str
+    streams: int        # database streams (one cache stream each)
+    n_tok: int          # vectors per stream
+    nq: int             # queries per call
+    bits: int           # code width of the database vectors
+    qjl_m: int          # sketch rows (0: none)
+    seed: int = 0
+    notes: str = ""
+
+
+SEARCH = SearchWorkload(
+    "ip_search", 8, 131072, 64, 2, 128,
+    notes="1 M database vectors bf16 N(0,1) in 8 streams of 131072, 2-bit codes + 128-bit sketch "
+          "(3 bits per coordinate, the inner-product setting of the method), 64 fp32 N(0,1) queries")
+
+
+def _search_rng(wl: SearchWorkload):
+    return np.random.default_rng(wl.seed)
+
+
+def search_queries(wl: SearchWorkload = SEARCH) -> np.ndarray:
+    """[nq, d] float32 N(0,1) queries (the first draws of the seed)."""
+    return _search_rng(wl).standard_normal((wl.nq, D), dtype=np.float32)
+
+
+def search_database(wl: SearchWorkload = SEARCH) -> np.ndarray:
+    """[streams, n_tok, d] float32 N(0,1) database vectors (drawn after the queries)."""
+    rng = _search_rng(wl)
+    rng.standard_normal((wl.nq, D), dtype=np.float32)
+    return rng.standard_normal((wl.streams, wl.n_tok, D), dtype=np.float32)

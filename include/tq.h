@@ -48,6 +48,7 @@ extern "C" {
 #define TQ_FORMAT_VERSION 1   /* bit layouts described at tq_cache below */
 #define TQ_DIM 128            /* head dimension d supported by the kernels */
 #define TQ_TILE_TOKENS 32     /* tokens per tile of the tiled layout */
+#define TQ_IP_MAX_QUERIES 64  /* queries per tq_ip_scores call */
 #define TQ_QJL_M 128          /* rows m of the QJL sketch when enabled */
 
 typedef enum {
@@ -245,6 +246,28 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
                            const tq_attn* attn, const float* q, const uint16_t* sink_k,
                            const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of tq_ip_scores (the same for every call). */
+size_t tq_ip_workspace_bytes(void);
+
+/* Inner-product search over packed vectors (noze.it page, section "Il metodo
+ * TurboQuant, in breve": similarity search is the method's second
+ * application, and the 1-bit sketch makes the inner-product estimate
+ * unbiased).  For queries i < nq, streams s < n_streams and positions
+ * t < n_tok of `db`:
+ *   scores[i*ld + s*n_tok + t] = n_st (<Pi q_i, c[idx_st]>
+ *                                      + sqrt(pi/2)/m gamma_st <S Pi q_i, z_st>),
+ * the estimate of <q_i, x_st>; the second term only when spec->qjl_m != 0.
+ *   spec/tables/db  TQ_LAYOUT_RECORD vectors as written by tq_quantize_kv;
+ *            n_tok <= db->cap, n_tok <= 2^24, n_streams <= 65535
+ *   q        device fp32 [nq][d], 1 <= nq <= TQ_IP_MAX_QUERIES
+ *   scores   device fp32, 4-byte aligned; ld >= n_streams * n_tok
+ *   workspace device, >= tq_ip_workspace_bytes(), 16-byte aligned; calls
+ *            that share it must not run concurrently.
+ * Two launches on `stream` (the query rotation, then the scores). */
+tq_status tq_ip_scores(const tq_spec* spec, const void* tables, const tq_cache* db, int64_t n_streams,
+                       int64_t n_tok, const float* q, int32_t nq, float* scores, int64_t ld, void* workspace,
+                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -268,6 +268,28 @@ def test_quantize_ragged_argument_errors_without_launch():
     assert call([8, 8], sp=ts, c=tq.TqCache(0x1000, 0x2000, None, None, 40)) == -1  # tiled cap % 32
 
 
+def test_ip_scores_argument_errors_without_launch():
+    L = tq.lib()
+    spec = tq.Spec(2, qjl_m=128).c()
+    db = tq.TqCache(0x1000, 0x2000, 0x3000, 0x4000, 64)
+    tab = ctypes.c_void_p(0x10000)
+    ws = tq.lib().tq_ip_workspace_bytes()
+    assert ws >= 64 * 2 * 2 * 128 * 2
+
+    def call(ns=2, nt=64, nq=4, ld=128, sp=spec, d=db, w=ws, q=0x5000):
+        return L.tq_ip_scores(ctypes.byref(sp), tab, ctypes.byref(d), ns, nt, q, nq, 0x6000, ld, 0x8000, w, None)
+
+    assert call(nq=0) == -2 and call(nq=65) == -2          # query count
+    assert call(nt=65) == -1                                # beyond capacity
+    assert call(ld=127) == -1                               # ld < n_streams * n_tok
+    assert call(w=16) == -3                                 # workspace
+    assert call(q=None) == -1
+    assert call(d=tq.TqCache(0x1000, 0x2000, None, None, 64)) == -1  # sketch arrays missing
+    assert call(sp=tq.Spec(3, layout=tq.LAYOUT_TILED).c()) == -2     # tiled layout
+    assert call(ns=0) == 0 and call(nt=0, ld=0) == 0        # nothing to do: no launch
+    assert call(ns=70000, nt=1, ld=70000, d=tq.TqCache(0x1000, 0x2000, 0x3000, 0x4000, 64)) == -2
+
+
 def test_attend_argument_errors_without_launch():
     L = tq.lib()
     ks, vs = tq.Spec(4).c(), tq.Spec(3, layout=1).c()
