@@ -24,7 +24,7 @@ namespace {
 
 constexpr int IW = 8;             // waves per scores workgroup
 constexpr int IT = 64 * IW;
-constexpr int ITILES = 4;         // tiles per wave
+constexpr int ITILES = 8;         // tiles per wave
 constexpr int IQMAX = TQ_IP_MAX_QUERIES;
 constexpr int QROW = D + 8;       // fp16 per query row in LDS (pad: no bank conflicts)
 
@@ -278,13 +278,14 @@ __global__ __launch_bounds__(IT, 1) void ip_kernel(const Tables* __restrict__ kt
         }
       float* out = scores + static_cast<int64_t>(qi) * ld + row0;
       const int64_t left = n_tok - (static_cast<int64_t>(t0) + 8 * j);
+      // the scores are written once and not read back here: streaming stores
       if (left >= 8 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-        reinterpret_cast<float4*>(out)[0] = make_float4(v[0], v[1], v[2], v[3]);
-        reinterpret_cast<float4*>(out)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(out));
+        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(out) + 1);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (e < left) out[e] = v[e];
+          if (e < left) __builtin_nontemporal_store(v[e], out + e);
       }
     }
   };
