@@ -133,9 +133,10 @@ AttendPlan plan_attend(const tq_attn& a) {
 hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc, const Spec& vs, const Tables* vtab,
                          const tq_cache& vc, const tq_attn& a, const AttendPlan& plan, const float* q,
                          const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens, float* out,
-                         void* workspace, hipStream_t st) {
+                         void* workspace, hipStream_t st, const int32_t* block_table, int max_pages, int n_pages) {
   float* parts = static_cast<float*>(workspace);
-  const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, out, st};
+  const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, out,
+                    block_table, max_pages, n_pages, st};
   const int vkey = vs.bits_lo * 10 + vs.bits_hi;
   const bool qjl = ks.qjl_m != 0;
   hipError_t e;

@@ -37,6 +37,9 @@ struct SplitArgs {
   const int32_t* seq_lens;
   float* parts;
   float* out;
+  const int32_t* block_table;  // paged cache: [batch][max_pages] pool pages, else NULL
+  int max_pages;
+  int n_pages;
   hipStream_t st;
 };
 

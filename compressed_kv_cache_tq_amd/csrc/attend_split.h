@@ -9,9 +9,8 @@
 // to Share!": item 1 (the first ~128 tokens stay uncompressed) and item 3
 // (value dequantization is skipped when the attention weight is below 1e-6).
 //
-// Two launches on one stream:
-//  split    one workgroup of 8 waves per (split, kv head, sequence), plus one
-//           more split per (kv head, sequence) for the raw sink tokens.
+// One or two launches on one stream:
+//  split    one workgroup of 8 waves per (split, kv head, sequence).
 //           Prologue: the workgroup rotates the query heads of its group,
 //           q~ = Pi_K q (times scale * log2 e), and u = S q~, scales each
 //           head by a power of two and splits it into fp16 hi + lo operand
@@ -20,13 +19,18 @@
 //           dequantization -> scores on MFMA for all query heads of the
 //           group -> online softmax -> V tiles (coordinate-major sub-blocks)
 //           -> P V on MFMA in the rotated domain.  The waves merge in LDS and
-//           write one partial (m, l, acc[128]) per query head.  The sink
-//           split writes the same partial for the sink tokens, with acc in
-//           the original value domain;
-//  combine  one workgroup per (sequence, query head, output slice):
-//           log-sum-exp merge of the partials, the slice of one inverse
-//           rotation Pi_V^T of the rotated sum, the sink values, and the
-//           normalisation.
+//           write one partial (m, l, acc[128]) per query head.  The
+//           stream's last split with compressed tokens also writes the
+//           partial of the raw sink tokens (slot n_split, acc in the
+//           original value domain).  When the plan gives every stream a
+//           single split, the workgroup then merges its own partials into
+//           the output (no second launch).  A paged cache reads every
+//           32-token tile through descriptors over the tile's pool page,
+//           looked up in the device block table;
+//  combine  (several splits per stream only) one workgroup per (sequence,
+//           query head, output slice): log-sum-exp merge of the partials,
+//           the slice of one inverse rotation Pi_V^T of the rotated sum,
+//           the sink values, and the normalisation.
 //
 // Codebook LUTs: entry e of width B maps two codes to their two fp16
 // centroids.  The centroids depend only on (d, B), so one LUT per width
@@ -443,7 +447,7 @@ __device__ __forceinline__ void merge_stream(uint8_t* smem, const Tables* __rest
   }
 }
 
-template <int KLO, int KHI, int VLO, int VHI, bool QJL>
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED>
 __global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
     const uint8_t* __restrict__ ksigns, const float* __restrict__ krn, int64_t kcap,
@@ -451,7 +455,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     int64_t vcap, const int32_t* __restrict__ seq_lens, const float* __restrict__ q,
     const uint16_t* __restrict__ sink_k, const uint16_t* __restrict__ sink_v, float* __restrict__ parts,
     float* __restrict__ out, int hq, int hkv, int sink, int n_split, int n_slot,
-    int64_t chunk, float v_skip, float qscale) {
+    int64_t chunk, float v_skip, float qscale, const int32_t* __restrict__ block_table, int max_pages,
+    int n_pages) {
   using LP = LutPlan<KLO, KHI, VLO, VHI>;
   constexpr int KBYTES = 8 * (KLO + KHI);
   constexpr int VBYTES = 8 * (VLO + VHI);
@@ -593,6 +598,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   // past the end
   StreamRsrc rs;
   const int64_t vend = (static_cast<int64_t>(t_end) + TILE - 1) / TILE * TILE;
+  // (paged cache: the stream arguments then address the page pool, and each
+  // tile gets descriptors over its own page below)
   rs.kc = rsrc(kcodes + stream * kcap * KBYTES, static_cast<int64_t>(t_end) * KBYTES);
   rs.vc = rsrc(vcodes + stream * vcap * VBYTES, vend * VBYTES);
   rs.kn = rsrc(knorms + stream * kcap, static_cast<int64_t>(t_end) * 4);
@@ -636,9 +643,52 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   const int nfull =
       __builtin_amdgcn_readfirstlane(first + 32 <= t_end ? static_cast<int>((t_end - first - 32) / STEP + 1) : 0);
 
+  // Paged cache: compressed token c of the sequence lives at slot c % 64 of
+  // pool page block_table[b][c / 64] (pool stream page * hkv + kh).  A wave's
+  // tiles are STEP = 256 tokens apart, each inside one page; lane L holds the
+  // page of the wave's tile L (pid[0]) and L + 64 (pid[1]), -1 past the table.
+  int pid[2] = {-1, -1};
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint32_t lp = (first + STEP * static_cast<uint32_t>(lane + 64 * h2)) / TQ_PAGE_TOKENS;
+      if (first + STEP * static_cast<uint32_t>(lane + 64 * h2) < t_end && lp < static_cast<uint32_t>(max_pages))
+        pid[h2] = block_table[static_cast<int64_t>(b) * max_pages + lp];
+    }
+  }
+  // loads of the wave's tile k (first token t0): on a paged cache through
+  // descriptors over the tile's page, bounded by the split's end; a page id
+  // outside the pool reads zeros
+  auto load_at = [&](TileRegs& buf, int k, uint32_t t0) __attribute__((always_inline)) {
+    if constexpr (!PAGED) {
+      load_tile<KLO, KHI, VLO, VHI, QJL>(buf, t0, rs, lo);
+    } else {
+      const int pg = __builtin_amdgcn_readlane(k < 64 ? pid[0] : pid[1], k & 63);
+      const int64_t base = static_cast<int64_t>(t0 / TQ_PAGE_TOKENS) * TQ_PAGE_TOKENS;
+      int64_t nk = static_cast<int64_t>(t_end) - base, nvt = vend - base;
+      nk = nk < 0 ? 0 : nk > TQ_PAGE_TOKENS ? TQ_PAGE_TOKENS : nk;
+      nvt = nvt < 0 ? 0 : nvt > TQ_PAGE_TOKENS ? TQ_PAGE_TOKENS : nvt;
+      const bool ok = pg >= 0 && pg < n_pages;
+      if (!ok) nk = nvt = 0;
+      const int64_t ps = static_cast<int64_t>(ok ? pg : 0) * hkv + kh;
+      StreamRsrc pr;
+      pr.kc = rsrc(kcodes + ps * kcap * KBYTES, nk * KBYTES);
+      pr.vc = rsrc(vcodes + ps * vcap * VBYTES, nvt * VBYTES);
+      pr.kn = rsrc(knorms + ps * kcap, nk * 4);
+      pr.vn = rsrc(vnorms + ps * vcap, nk * 4);
+      if constexpr (QJL) {
+        pr.zs = rsrc(ksigns + ps * kcap * (QJL_M / 8), nk * (QJL_M / 8));
+        pr.rn = rsrc(krn + ps * kcap, nk * 4);
+      } else {
+        pr.zs = pr.rn = pr.kn;
+      }
+      load_tile<KLO, KHI, VLO, VHI, QJL>(buf, t0 % TQ_PAGE_TOKENS, pr, lo);
+    }
+  };
+
   TileRegs bufA, bufB;
-  load_tile<KLO, KHI, VLO, VHI, QJL>(bufA, first, rs, lo);
-  load_tile<KLO, KHI, VLO, VHI, QJL>(bufB, first + STEP, rs, lo);
+  load_at(bufA, 0, first);
+  load_at(bufB, 1, first + STEP);
 
   // Power-of-two scale per head for the fp16 operand: Pi is orthogonal, so
   // |q~_i| <= ||q~|| = ||q|| |qscale|, and sh = 14 - exponent of that bound
@@ -910,9 +960,9 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     for (; k + 2 <= nfull; k += 2) {
       const uint32_t ta = first + STEP * k;
       tile_step.template operator()<true, VSKIP>(bufA, ta);
-      load_tile<KLO, KHI, VLO, VHI, QJL>(bufA, ta + 2 * STEP, rs, lo);
+      load_at(bufA, k + 2, ta + 2 * STEP);
       tile_step.template operator()<true, VSKIP>(bufB, ta + STEP);
-      load_tile<KLO, KHI, VLO, VHI, QJL>(bufB, ta + 3 * STEP, rs, lo);
+      load_at(bufB, k + 3, ta + 3 * STEP);
     }
     // at most one whole tile and one partial tile remain
     const uint32_t ta = first + STEP * k;
@@ -970,24 +1020,28 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
 }
 
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-hipError_t launch_split(const Tables* ktab, const tq_cache& kc, const Tables* vtab, const tq_cache& vc,
-                        const tq_attn& a, const AttendPlan& plan, const float* q, const uint16_t* sink_k,
-                        const uint16_t* sink_v, const int32_t* seq_lens, float* parts, float* out,
-                        hipStream_t st) {
-  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL>), dim3(a.hkv, a.batch, plan.n_split), dim3(ST), 0, st,
-                     ktab, kc.codes, kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, vtab, vc.codes, vc.norms, vc.cap,
-                     seq_lens, q, sink_k, sink_v, parts, out, a.hq, a.hkv, a.sink, plan.n_split,
-                     plan.n_slot, plan.chunk, a.v_skip, a.scale * LOG2E);
+hipError_t launch_split(const SplitArgs& f) {
+  const tq_attn& a = *f.a;
+  const AttendPlan& plan = *f.plan;
+  const tq_cache &kc = *f.kc, &vc = *f.vc;
+  const dim3 grid(a.hkv, a.batch, plan.n_split);
+  if (f.block_table)
+    hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL, true>), grid, dim3(ST), 0, f.st, f.ktab, kc.codes,
+                       kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, f.vtab, vc.codes, vc.norms, vc.cap, f.seq_lens,
+                       f.q, f.sink_k, f.sink_v, f.parts, f.out, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot,
+                       plan.chunk, a.v_skip, a.scale * LOG2E, f.block_table, f.max_pages, f.n_pages);
+  else
+    hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL, false>), grid, dim3(ST), 0, f.st, f.ktab, kc.codes,
+                       kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, f.vtab, vc.codes, vc.norms, vc.cap, f.seq_lens,
+                       f.q, f.sink_k, f.sink_v, f.parts, f.out, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot,
+                       plan.chunk, a.v_skip, a.scale * LOG2E, nullptr, 0, 0);
   return hipGetLastError();
 }
 
 
 template <int KLO, int KHI, int VLO, int VHI>
 hipError_t launch_q(bool qjl, const SplitArgs& f) {
-  return qjl ? launch_split<KLO, KHI, VLO, VHI, true>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
-                                                      f.sink_v, f.seq_lens, f.parts, f.out, f.st)
-             : launch_split<KLO, KHI, VLO, VHI, false>(f.ktab, *f.kc, f.vtab, *f.vc, *f.a, *f.plan, f.q, f.sink_k,
-                                                       f.sink_v, f.seq_lens, f.parts, f.out, f.st);
+  return qjl ? launch_split<KLO, KHI, VLO, VHI, true>(f) : launch_split<KLO, KHI, VLO, VHI, false>(f);
 }
 
 template <int KLO, int KHI>

@@ -614,11 +614,17 @@ size_t tq_attend_workspace_bytes(const tq_attn* attn) {
   return tq::plan_attend(*attn).ws_bytes;
 }
 
-tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cache* kc,
-                           const tq_spec* vs, const void* vtables, const tq_cache* vc,
-                           const tq_attn* attn, const float* q, const uint16_t* sink_k,
-                           const uint16_t* sink_v, const int32_t* seq_lens, float* out,
-                           void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points: the contiguous caches (block_table == NULL) and
+// the paged pools.
+tq_status attend_checked(const tq_spec* ks, const void* ktables, const tq_cache* kc, const tq_spec* vs,
+                         const void* vtables, const tq_cache* vc, const tq_attn* attn, const float* q,
+                         const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens,
+                         const int32_t* block_table, int32_t max_pages, int64_t n_pages, float* out,
+                         void* workspace, size_t ws_bytes, void* stream, const char* what) {
   tq::Spec ksp, vsp;
   if (tq_status st = check_spec(ks, &ksp); st != TQ_OK) return st;
   if (tq_status st = check_spec(vs, &vsp); st != TQ_OK) return st;
@@ -638,11 +644,22 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
   if (!(a.v_skip >= 0.0f) || !(a.v_skip < 1.0f)) return fail(TQ_E_ARG, "v_skip must be in [0, 1)");
   if (!std::isfinite(a.scale)) return fail(TQ_E_ARG, "scale must be finite");
   if (a.batch == 0) return TQ_OK;
-  if (vc->cap % tq::TILE || kc->cap % tq::TILE) return fail(TQ_E_ARG, "cache caps must be multiples of 32");
-  if (vc->cap > (int64_t{1} << 24) || kc->cap > (int64_t{1} << 24))
-    return fail(TQ_E_UNSUPPORTED, "cache caps above 2^24 positions");
-  if (a.max_len - a.sink > std::min(kc->cap, vc->cap))
-    return fail(TQ_E_ARG, "max_len - sink exceeds the cache capacity");
+  if (block_table) {
+    if (kc->cap != TQ_PAGE_TOKENS || vc->cap != TQ_PAGE_TOKENS)
+      return fail(TQ_E_ARG, "page pools must have cap == TQ_PAGE_TOKENS");
+    if (max_pages < 1 || n_pages < 1 || n_pages > (int64_t{1} << 30))
+      return fail(TQ_E_ARG, "max_pages and n_pages must be positive (n_pages <= 2^30)");
+    if (a.max_len - a.sink > static_cast<int64_t>(max_pages) * TQ_PAGE_TOKENS)
+      return fail(TQ_E_ARG, "max_len - sink exceeds max_pages pages");
+    if (a.max_len - a.sink > (int64_t{1} << 24)) return fail(TQ_E_UNSUPPORTED, "at most 2^24 compressed tokens");
+    if (!aligned(block_table, 4)) return fail(TQ_E_ARG, "block_table must be 4-byte aligned");
+  } else {
+    if (vc->cap % tq::TILE || kc->cap % tq::TILE) return fail(TQ_E_ARG, "cache caps must be multiples of 32");
+    if (vc->cap > (int64_t{1} << 24) || kc->cap > (int64_t{1} << 24))
+      return fail(TQ_E_UNSUPPORTED, "cache caps above 2^24 positions");
+    if (a.max_len - a.sink > std::min(kc->cap, vc->cap))
+      return fail(TQ_E_ARG, "max_len - sink exceeds the cache capacity");
+  }
   if (!q || !out || !seq_lens) return fail(TQ_E_ARG, "q, out and seq_lens must be non-NULL");
   if (!kc->codes || !kc->norms || !vc->codes || !vc->norms) return fail(TQ_E_ARG, "cache arrays are NULL");
   if (ksp.qjl_m && (!kc->qjl_signs || !kc->qjl_rnorms)) return fail(TQ_E_ARG, "key QJL arrays are NULL");
@@ -660,8 +677,73 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
   const hipError_t e = tq::launch_attend(ksp, static_cast<const tq::Tables*>(ktables), *kc, vsp,
                                          static_cast<const tq::Tables*>(vtables), *vc, a, plan, q,
                                          sink_k, sink_v, seq_lens, out, workspace,
-                                         static_cast<hipStream_t>(stream));
-  return hip_status(e, "tq_attend_decode launch");
+                                         static_cast<hipStream_t>(stream), block_table, max_pages,
+                                         static_cast<int>(n_pages));
+  return hip_status(e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cache* kc,
+                           const tq_spec* vs, const void* vtables, const tq_cache* vc,
+                           const tq_attn* attn, const float* q, const uint16_t* sink_k,
+                           const uint16_t* sink_v, const int32_t* seq_lens, float* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  return attend_checked(ks, ktables, kc, vs, vtables, vc, attn, q, sink_k, sink_v, seq_lens, nullptr, 0, 0, out,
+                        workspace, ws_bytes, stream, "tq_attend_decode launch");
+}
+
+tq_status tq_attend_decode_paged(const tq_spec* ks, const void* ktables, const tq_cache* kpool,
+                                 const tq_spec* vs, const void* vtables, const tq_cache* vpool,
+                                 const tq_attn* attn, const float* q, const uint16_t* sink_k,
+                                 const uint16_t* sink_v, const int32_t* seq_lens, const int32_t* block_table,
+                                 int32_t max_pages, int64_t n_pages, float* out, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  if (!block_table) return fail(TQ_E_ARG, "block_table is NULL");
+  return attend_checked(ks, ktables, kpool, vs, vtables, vpool, attn, q, sink_k, sink_v, seq_lens, block_table,
+                        max_pages, n_pages, out, workspace, ws_bytes, stream, "tq_attend_decode_paged launch");
+}
+
+tq_status tq_quantize_kv_paged(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
+                               int32_t batch, int32_t hkv, const int64_t* x_off, const int64_t* pos0,
+                               const int64_t* n_tok, int64_t x_stream_stride, int64_t x_row_stride,
+                               const int32_t* block_table, int32_t max_pages, int64_t n_pages,
+                               const tq_cache* pool, void* stream) {
+  tq::Spec sp;
+  if (tq_status st = check_quantize(spec, tables, dtype, pool, &sp); st != TQ_OK) return st;
+  if (pool->cap != TQ_PAGE_TOKENS) return fail(TQ_E_ARG, "the page pool must have cap == TQ_PAGE_TOKENS");
+  if (batch < 0 || hkv <= 0 || max_pages < 1 || n_pages < 1)
+    return fail(TQ_E_ARG, "batch >= 0, hkv > 0, max_pages > 0 and n_pages > 0 required");
+  if (batch == 0) return TQ_OK;
+  if (!x_off || !pos0 || !n_tok || !block_table) return fail(TQ_E_ARG, "per-sequence arrays must be non-NULL");
+  const int64_t es = dtype == TQ_F32 ? 4 : 2;
+  std::vector<tq::QSeq> segs;
+  int64_t max_tok = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (n_tok[b] < 0 || pos0[b] < 0 || x_off[b] < 0) return fail(TQ_E_ARG, "negative size or offset");
+    if ((x_off[b] * es) % 16) return fail(TQ_E_ARG, "x offsets must be multiples of 16 bytes");
+    if (pos0[b] + n_tok[b] > static_cast<int64_t>(max_pages) * TQ_PAGE_TOKENS)
+      return fail(TQ_E_ARG, "pos0 + n_tok exceeds max_pages pages");
+    // split the range at page boundaries: one segment per page
+    for (int64_t p = pos0[b]; p < pos0[b] + n_tok[b];) {
+      const int64_t lp = p / TQ_PAGE_TOKENS, end = std::min(pos0[b] + n_tok[b], (lp + 1) * TQ_PAGE_TOKENS);
+      const int32_t page = block_table[static_cast<int64_t>(b) * max_pages + lp];
+      if (page < 0 || page >= n_pages) return fail(TQ_E_ARG, "block_table names a page outside the pool");
+      segs.push_back(tq::QSeq{x_off[b] + (p - pos0[b]) * x_row_stride, p - lp * TQ_PAGE_TOKENS, end - p,
+                              static_cast<int64_t>(page) * hkv});
+      max_tok = std::max(max_tok, end - p);
+      p = end;
+    }
+  }
+  if (segs.empty()) return TQ_OK;
+  if (tq_status st = check_quantize_arrays(sp, dtype, x, x_stream_stride, x_row_stride, max_tok, pool); st != TQ_OK)
+    return st;
+  const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x, segs.data(),
+                                           static_cast<int64_t>(segs.size()), hkv, x_stream_stride, x_row_stride,
+                                           *pool, static_cast<hipStream_t>(stream));
+  return hip_status(e, "tq_quantize_kv_paged launch");
 }
 
 }  // extern "C"

@@ -120,6 +120,7 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          const tq_attn& a, const AttendPlan& plan, const float* q,
                          const uint16_t* sink_k, const uint16_t* sink_v,
                          const int32_t* seq_lens, float* out, void* workspace,
-                         hipStream_t stream);
+                         hipStream_t stream, const int32_t* block_table = nullptr, int max_pages = 0,
+                         int n_pages = 0);
 
 }  // namespace tq

@@ -30,8 +30,10 @@ EXPORTS = [
     "tq_tables_bytes", "tq_tables_build", "tq_code_bytes", "tq_cache_code_bytes", "tq_quantize_kv",
     "tq_quantize_kv_ragged",
     "tq_attend_workspace_bytes", "tq_attend_decode", "tq_ip_workspace_bytes", "tq_ip_scores",
+    "tq_quantize_kv_paged", "tq_attend_decode_paged",
 ]
 IP_MAX_QUERIES = 64
+PAGE_TOKENS = 64
 
 
 class TqSpec(ctypes.Structure):
@@ -86,6 +88,11 @@ def lib() -> ctypes.CDLL:
         "tq_quantize_kv_ragged": (I32, [ctypes.POINTER(TqSpec), P, I32, P, I32, I32, P, P, P, I64, I64,
                                         ctypes.POINTER(TqCache), P]),
         "tq_attend_workspace_bytes": (SZ, [ctypes.POINTER(TqAttn)]),
+        "tq_quantize_kv_paged": (I32, [ctypes.POINTER(TqSpec), P, I32, P, I32, I32, P, P, P, I64, I64, P, I32, I64,
+                                       ctypes.POINTER(TqCache), P]),
+        "tq_attend_decode_paged": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache), ctypes.POINTER(TqSpec), P,
+                                         ctypes.POINTER(TqCache), ctypes.POINTER(TqAttn), P, P, P, P, P, I32, I64, P,
+                                         P, SZ, P]),
         "tq_ip_workspace_bytes": (SZ, []),
         "tq_ip_scores": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache), I64, I64, P, I32, P, I64, P, SZ,
                                P]),
@@ -375,3 +382,60 @@ def ip_scores(spec: Spec, tables, db: Cache, q, *, n_streams: int, n_tok: int, s
                               nq, scores.data_ptr(), ld, workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), st), "tq_ip_scores")
     return scores
+
+
+def alloc_page_pool(spec: Spec, n_pages: int, hkv: int, device="cuda") -> Cache:
+    """A pool of n_pages pages of PAGE_TOKENS positions for hkv kv heads
+    (stream page * hkv + h)."""
+    return alloc_cache(spec, n_pages * hkv, PAGE_TOKENS, device=device)
+
+
+def _dtype_code(x):
+    torch = _torch()
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("x must be float32 or bfloat16")
+
+
+def quantize_kv_paged(spec: Spec, tables, x, pool: Cache, *, hkv: int, n_tok, block_table, n_pages: int, pos0=None,
+                      x_off=None, x_stream_stride: int | None = None, x_row_stride: int | None = None,
+                      stream: int | None = None) -> None:
+    """Append sequence b's n_tok[b] vectors at compressed positions pos0[b]..
+    of a paged pool; block_table is a host int32 array [batch, max_pages].
+    x as for quantize_kv_ragged."""
+    n = np.ascontiguousarray(n_tok, dtype=np.int64)
+    B = n.shape[0]
+    p0 = np.zeros(B, np.int64) if pos0 is None else np.ascontiguousarray(pos0, dtype=np.int64)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    if bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("block_table must be [batch, max_pages]")
+    if x_off is None:
+        if x.dim() != 3 or x.shape[-1] != D or x.stride(-1) != 1 or x.shape[0] < B * hkv:
+            raise ValueError("x must be [batch*hkv, rows, 128] with contiguous rows")
+        xo = np.arange(B, dtype=np.int64) * hkv * x.stride(0)
+        xss, xrs = x.stride(0), x.stride(1)
+    else:
+        xo = np.ascontiguousarray(x_off, dtype=np.int64)
+        xss, xrs = x_stream_stride, x_row_stride
+    cs, cc = spec.c(), pool.c()
+    st = _stream(x.device) if stream is None else stream
+    _check(lib().tq_quantize_kv_paged(ctypes.byref(cs), tables.data_ptr(), _dtype_code(x), x.data_ptr(), B, hkv,
+                                      xo.ctypes.data, p0.ctypes.data, n.ctypes.data, xss, xrs, bt.ctypes.data,
+                                      bt.shape[1], n_pages, ctypes.byref(cc), st), "tq_quantize_kv_paged")
+
+
+def attend_decode_paged(kspec: Spec, ktables, kpool: Cache, vspec: Spec, vtables, vpool: Cache, q, seq_lens, out,
+                        workspace, *, hkv: int, block_table, n_pages: int, sink: int = 0, sink_k=None, sink_v=None,
+                        scale: float | None = None, v_skip: float = 0.0, max_len: int, stream: int | None = None):
+    """attend_decode over paged pools; block_table: device int32 [B, max_pages]."""
+    B, Hq, _ = q.shape
+    a = TqAttn(B, Hq, hkv, sink, (1.0 / np.sqrt(D)) if scale is None else scale, v_skip, max_len)
+    ks, vs, kc, vc = kspec.c(), vspec.c(), kpool.c(), vpool.c()
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().tq_attend_decode_paged(ctypes.byref(ks), ktables.data_ptr(), ctypes.byref(kc), ctypes.byref(vs),
+                                        vtables.data_ptr(), ctypes.byref(vc), ctypes.byref(a), q.data_ptr(),
+                                        _ptr(sink_k), _ptr(sink_v), seq_lens.data_ptr(), block_table.data_ptr(),
+                                        block_table.shape[1], n_pages, out.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), st), "tq_attend_decode_paged")

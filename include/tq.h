@@ -49,6 +49,7 @@ extern "C" {
 #define TQ_DIM 128            /* head dimension d supported by the kernels */
 #define TQ_TILE_TOKENS 32     /* tokens per tile of the tiled layout */
 #define TQ_IP_MAX_QUERIES 64  /* queries per tq_ip_scores call */
+#define TQ_PAGE_TOKENS 64     /* positions per page of a paged cache */
 #define TQ_QJL_M 128          /* rows m of the QJL sketch when enabled */
 
 typedef enum {
@@ -246,6 +247,37 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
                            const tq_attn* attn, const float* q, const uint16_t* sink_k,
                            const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Paged cache (a pool of pages shared by all sequences).  A pool of n_pages
+ * pages is a tq_cache with cap = TQ_PAGE_TOKENS and n_pages * hkv streams:
+ * page p holds TQ_PAGE_TOKENS positions of every kv head h, as stream
+ * p * hkv + h.  Compressed token c (= token t - sink) of sequence b lives at
+ * position c % TQ_PAGE_TOKENS of page block_table[b * max_pages + c /
+ * TQ_PAGE_TOKENS].  The pages of one sequence must be distinct.
+ *
+ * Quantize into a paged cache: sequence b appends n_tok[b] vectors at
+ * compressed positions [pos0[b], pos0[b] + n_tok[b]); rows of x and the
+ * per-sequence arrays as for tq_quantize_kv_ragged.  block_table is a HOST
+ * int32 array [batch][max_pages] read during the call; every page it names
+ * for the written range must lie in [0, n_pages) (else TQ_E_ARG, no launch).
+ * One launch per 64 page segments (a spec with the sketch: one per segment). */
+tq_status tq_quantize_kv_paged(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
+                               int32_t batch, int32_t hkv, const int64_t* x_off, const int64_t* pos0,
+                               const int64_t* n_tok, int64_t x_stream_stride, int64_t x_row_stride,
+                               const int32_t* block_table, int32_t max_pages, int64_t n_pages,
+                               const tq_cache* pool, void* stream);
+
+/* One decode step over paged K and V pools (same arguments and result as
+ * tq_attend_decode, the caches replaced by the pools).  block_table: DEVICE
+ * int32 [batch][max_pages]; max_pages * TQ_PAGE_TOKENS >= max_len - sink.
+ * A page id outside [0, n_pages) reads as zero codes and norms (no access).
+ * kpool->cap and vpool->cap must equal TQ_PAGE_TOKENS. */
+tq_status tq_attend_decode_paged(const tq_spec* ks, const void* ktables, const tq_cache* kpool,
+                                 const tq_spec* vs, const void* vtables, const tq_cache* vpool,
+                                 const tq_attn* attn, const float* q, const uint16_t* sink_k,
+                                 const uint16_t* sink_v, const int32_t* seq_lens, const int32_t* block_table,
+                                 int32_t max_pages, int64_t n_pages, float* out, void* workspace,
+                                 size_t ws_bytes, void* stream);
 
 /* Workspace bytes of tq_ip_scores (the same for every call). */
 size_t tq_ip_workspace_bytes(void);

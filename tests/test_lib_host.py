@@ -290,6 +290,41 @@ def test_ip_scores_argument_errors_without_launch():
     assert call(ns=70000, nt=1, ld=70000, d=tq.TqCache(0x1000, 0x2000, 0x3000, 0x4000, 64)) == -2
 
 
+def test_paged_argument_errors_without_launch():
+    L = tq.lib()
+    ks, vs = tq.Spec(4).c(), tq.Spec(3, layout=1).c()
+    pool_k = tq.TqCache(0x1000, 0x2000, None, None, 64)
+    pool_v = tq.TqCache(0x3000, 0x4000, None, None, 64)
+    tab = ctypes.c_void_p(0x10000)
+    bt = np.zeros((2, 4), np.int32)
+
+    def dec(a, kp=pool_k, max_pages=4, n_pages=8, table=0x9000):
+        return L.tq_attend_decode_paged(ctypes.byref(ks), tab, ctypes.byref(kp), ctypes.byref(vs), tab,
+                                        ctypes.byref(pool_v), ctypes.byref(a), 0x5000, None, None, 0x6000, table,
+                                        max_pages, n_pages, 0x7000, 0x8000, 1 << 20, None)
+
+    assert dec(tq.TqAttn(2, 8, 2, 0, 0.1, 0.0, 257)) == -1           # beyond max_pages pages
+    assert dec(tq.TqAttn(2, 8, 2, 0, 0.1, 0.0, 64), table=None) == -1
+    assert dec(tq.TqAttn(2, 8, 2, 0, 0.1, 0.0, 64), kp=tq.TqCache(0x1000, 0x2000, None, None, 128)) == -1
+    assert dec(tq.TqAttn(2, 8, 2, 0, 0.1, 0.0, 64), n_pages=0) == -1
+    assert dec(tq.TqAttn(0, 8, 2, 0, 0.1, 0.0, 64)) == 0
+
+    def qz(n_tok, pos0=(0, 0), table=bt, n_pages=8, pool=pool_k):
+        n, p0, xo = np.asarray(n_tok, np.int64), np.asarray(pos0, np.int64), np.zeros(2, np.int64)
+        return L.tq_quantize_kv_paged(ctypes.byref(ks), tab, 1, 0x1000, 2, 2, xo.ctypes.data, p0.ctypes.data,
+                                      n.ctypes.data, 128 * 300, 128, table.ctypes.data, table.shape[1], n_pages,
+                                      ctypes.byref(pool), None)
+
+    assert qz([10, 257]) == -1                                   # beyond max_pages pages
+    bad = bt.copy()
+    bad[1, 0] = 8
+    assert qz([10, 10], table=bad) == -1                         # page outside the pool
+    bad[1, 0] = -1
+    assert qz([10, 10], table=bad) == -1
+    assert qz([10, 10], pool=tq.TqCache(0x1000, 0x2000, None, None, 96)) == -1
+    assert qz([0, 0]) == 0                                       # nothing to write
+
+
 def test_attend_argument_errors_without_launch():
     L = tq.lib()
     ks, vs = tq.Spec(4).c(), tq.Spec(3, layout=1).c()
