@@ -265,6 +265,8 @@ def main() -> int:
     ap.add_argument("--workload", default=WORKLOAD, help="workload to time (the metric is quoted on gqa_decode)")
     ap.add_argument("--rotation", choices=("haar", "hadamard"), default="haar",
                     help="how the rotation is drawn (the workloads are specified with the Haar rotation)")
+    ap.add_argument("--paged", action="store_true",
+                    help="caches in a pool of 64-token pages, each sequence's pages in a seeded random order")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 512 MiB fp32 streaming kernel (out = -in) 5 times; "
                          "its byte counts calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -318,8 +320,23 @@ def main() -> int:
     for _ in range(COPIES - 1):
         xk.append(xk[0].clone())
         xv.append(xv[0].clone())
-    kc = [tq.alloc_cache(kspec, B * Hkv, cap) for _ in range(COPIES)]
-    vc = [tq.alloc_cache(vspec, B * Hkv, cap) for _ in range(COPIES)]
+    if args.paged:
+        # every sequence's compressed tokens on its own pages of one pool, the
+        # pool's pages handed out in a seeded random order
+        npg = -(-comp_h // tq.PAGE_TOKENS)
+        n_pages, max_pages = int(npg.sum()), max(1, int(npg.max()))
+        perm = np.random.default_rng(7).permutation(n_pages).astype(np.int32)
+        btab_h = np.full((B, max_pages), -1, dtype=np.int32)
+        at = 0
+        for b in range(B):
+            btab_h[b, :npg[b]] = perm[at:at + npg[b]]
+            at += int(npg[b])
+        btab = torch.from_numpy(btab_h).cuda()
+        kc = [tq.alloc_page_pool(kspec, n_pages, Hkv) for _ in range(COPIES)]
+        vc = [tq.alloc_page_pool(vspec, n_pages, Hkv) for _ in range(COPIES)]
+    else:
+        kc = [tq.alloc_cache(kspec, B * Hkv, cap) for _ in range(COPIES)]
+        vc = [tq.alloc_cache(vspec, B * Hkv, cap) for _ in range(COPIES)]
     sink_k = sink_v = None
     if S:
         sk = np.stack([inp.k[b][:, :S] for b in range(B)])
@@ -333,12 +350,19 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def quantize(spec, tab, x, cache):
-        if uniform:
+        if args.paged:
+            tq.quantize_kv_paged(spec, tab, x, cache, hkv=Hkv, n_tok=comp_h, block_table=btab, n_pages=n_pages)
+        elif uniform:
             tq.quantize_kv(spec, tab, x[:, :int(comp_h[0])], cache)
         else:  # one ragged call: each sequence appends its own length
             tq.quantize_kv_ragged(spec, tab, x, cache, hkv=Hkv, n_tok=comp_h)
 
     def attend(kcache, vcache):
+        if args.paged:
+            tq.attend_decode_paged(kspec, ktab, kcache, vspec, vtab, vcache, q, lens, out, ws, hkv=Hkv,
+                                   block_table=btab, n_pages=n_pages, sink=S, sink_k=sink_k, sink_v=sink_v,
+                                   v_skip=wl.v_skip, max_len=T)
+            return
         tq.attend_decode(kspec, ktab, kcache, vspec, vtab, vcache, q, lens, out, ws, hkv=Hkv, sink=S,
                          sink_k=sink_k, sink_v=sink_v, v_skip=wl.v_skip, max_len=T)
 
@@ -418,15 +442,15 @@ def main() -> int:
     else:
         dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms, qv_bytes, f"rotq_kernel<{vtag}>"
     dom_gbs = dom_bytes / (dom_ms / 1e3) / 1e9
-    traffic = read_traffic(dom_name) if wname == WORKLOAD else None
+    traffic = read_traffic(dom_name) if wname == WORKLOAD and not args.paged else None
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom_kernel,
                 "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2)}
-    att_traffic = read_traffic("attend") if wname == WORKLOAD else None
+    att_traffic = read_traffic("attend") if wname == WORKLOAD and not args.paged else None
     roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
                        "kernel": f"split_kernel<{wl.k.bits_lo},{wl.k.bits_hi},{wl.v.bits_lo},{wl.v.bits_hi}"
-                                 f"{',qjl' if kspec.qjl_m else ''}> (+ combine_kernel when a stream has several splits;"
+                                 f"{',qjl' if kspec.qjl_m else ''}{',paged' if args.paged else ''}> (+ combine_kernel when a stream has several splits;"
                                  f" one decode step)",
                        "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms * 1e3, 2)}
     res = {
@@ -437,7 +461,8 @@ def main() -> int:
                    "context": T if uniform else f"ragged {int(lens_h.min())}..{T}, sum {int(lens_h.sum())}",
                    "kv_dtype": wl.dtype, "k_bits": [wl.k.bits_lo, wl.k.bits_hi], "v_bits": [wl.v.bits_lo, wl.v.bits_hi],
                    "split": wl.k.split, "qjl": bool(kspec.qjl_m), "sink": S, "v_skip": wl.v_skip,
-                   "structure": wl.structure, "rotation": args.rotation},
+                   "structure": wl.structure, "rotation": args.rotation,
+                   "cache": f"paged ({tq.PAGE_TOKENS}-token pages)" if args.paged else "contiguous"},
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "decode_us": round(at_ms * 1e3, 2),
         "quantize_Mvec_s": round(quant_mvec, 1), "quantize_GB_s": round(quant_gbs, 2),
@@ -454,7 +479,7 @@ def main() -> int:
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline and wname == WORKLOAD:
+    if not args.no_cpu_baseline and wname == WORKLOAD and not args.paged:
         a = (args.warmup + args.steps) % COPIES
         nb_k, nb_v = tq.cache_code_bytes(kspec, T), tq.cache_code_bytes(vspec, T)
         kraw = [kc[a].codes[h * nb_k:(h + 1) * nb_k].cpu().numpy().reshape(T, kcb) for h in range(Hkv)]

@@ -573,9 +573,10 @@ tq_status tq_quantize_kv(const tq_spec* spec, const void* tables, int32_t dtype,
   if (n_streams == 0 || n_tok == 0) return TQ_OK;
   if (tq_status st = check_quantize_arrays(sp, dtype, x, x_stream_stride, x_row_stride, n_tok, cache); st != TQ_OK)
     return st;
-  const tq::QSeq one{0, tok0, n_tok, 0};
+  const tq::QSeq one{0, tok0, n_tok, 0, 0};
   const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x, &one, 1, n_streams,
-                                           x_stream_stride, x_row_stride, *cache, static_cast<hipStream_t>(stream));
+                                           x_stream_stride, x_row_stride, *cache, tq::PageMap{},
+                                           static_cast<hipStream_t>(stream));
   return hip_status(e, "tq_quantize_kv launch");
 }
 
@@ -598,14 +599,14 @@ tq_status tq_quantize_kv_ragged(const tq_spec* spec, const void* tables, int32_t
     if ((x_off[b] * es) % 16) return fail(TQ_E_ARG, "x offsets must be multiples of 16 bytes");
     if (n_tok[b] == 0) continue;
     max_tok = std::max(max_tok, n_tok[b]);
-    seqs.push_back(tq::QSeq{x_off[b], tok0[b], n_tok[b], static_cast<int64_t>(b) * hkv});
+    seqs.push_back(tq::QSeq{x_off[b], tok0[b], n_tok[b], static_cast<int64_t>(b) * hkv, 0});
   }
   if (seqs.empty()) return TQ_OK;
   if (tq_status st = check_quantize_arrays(sp, dtype, x, x_stream_stride, x_row_stride, max_tok, cache); st != TQ_OK)
     return st;
   const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x, seqs.data(),
                                            static_cast<int64_t>(seqs.size()), hkv, x_stream_stride, x_row_stride,
-                                           *cache, static_cast<hipStream_t>(stream));
+                                           *cache, tq::PageMap{}, static_cast<hipStream_t>(stream));
   return hip_status(e, "tq_quantize_kv_ragged launch");
 }
 
@@ -714,35 +715,30 @@ tq_status tq_quantize_kv_paged(const tq_spec* spec, const void* tables, int32_t 
   tq::Spec sp;
   if (tq_status st = check_quantize(spec, tables, dtype, pool, &sp); st != TQ_OK) return st;
   if (pool->cap != TQ_PAGE_TOKENS) return fail(TQ_E_ARG, "the page pool must have cap == TQ_PAGE_TOKENS");
-  if (batch < 0 || hkv <= 0 || max_pages < 1 || n_pages < 1)
-    return fail(TQ_E_ARG, "batch >= 0, hkv > 0, max_pages > 0 and n_pages > 0 required");
+  if (batch < 0 || hkv <= 0 || max_pages < 1 || n_pages < 1 || n_pages > (int64_t{1} << 30))
+    return fail(TQ_E_ARG, "batch >= 0, hkv > 0, max_pages > 0 and 0 < n_pages <= 2^30 required");
   if (batch == 0) return TQ_OK;
-  if (!x_off || !pos0 || !n_tok || !block_table) return fail(TQ_E_ARG, "per-sequence arrays must be non-NULL");
+  if (!x_off || !pos0 || !n_tok) return fail(TQ_E_ARG, "x_off, pos0 and n_tok must be non-NULL");
+  if (!block_table || !aligned(block_table, 4)) return fail(TQ_E_ARG, "block_table must be non-NULL and 4-byte aligned");
   const int64_t es = dtype == TQ_F32 ? 4 : 2;
-  std::vector<tq::QSeq> segs;
+  std::vector<tq::QSeq> seqs;
   int64_t max_tok = 0;
   for (int32_t b = 0; b < batch; ++b) {
     if (n_tok[b] < 0 || pos0[b] < 0 || x_off[b] < 0) return fail(TQ_E_ARG, "negative size or offset");
     if ((x_off[b] * es) % 16) return fail(TQ_E_ARG, "x offsets must be multiples of 16 bytes");
     if (pos0[b] + n_tok[b] > static_cast<int64_t>(max_pages) * TQ_PAGE_TOKENS)
       return fail(TQ_E_ARG, "pos0 + n_tok exceeds max_pages pages");
-    // split the range at page boundaries: one segment per page
-    for (int64_t p = pos0[b]; p < pos0[b] + n_tok[b];) {
-      const int64_t lp = p / TQ_PAGE_TOKENS, end = std::min(pos0[b] + n_tok[b], (lp + 1) * TQ_PAGE_TOKENS);
-      const int32_t page = block_table[static_cast<int64_t>(b) * max_pages + lp];
-      if (page < 0 || page >= n_pages) return fail(TQ_E_ARG, "block_table names a page outside the pool");
-      segs.push_back(tq::QSeq{x_off[b] + (p - pos0[b]) * x_row_stride, p - lp * TQ_PAGE_TOKENS, end - p,
-                              static_cast<int64_t>(page) * hkv});
-      max_tok = std::max(max_tok, end - p);
-      p = end;
-    }
+    if (n_tok[b] == 0) continue;
+    max_tok = std::max(max_tok, n_tok[b]);
+    seqs.push_back(tq::QSeq{x_off[b], pos0[b], n_tok[b], 0, b});
   }
-  if (segs.empty()) return TQ_OK;
+  if (seqs.empty()) return TQ_OK;
   if (tq_status st = check_quantize_arrays(sp, dtype, x, x_stream_stride, x_row_stride, max_tok, pool); st != TQ_OK)
     return st;
-  const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x, segs.data(),
-                                           static_cast<int64_t>(segs.size()), hkv, x_stream_stride, x_row_stride,
-                                           *pool, static_cast<hipStream_t>(stream));
+  const tq::PageMap pm{block_table, max_pages, n_pages};
+  const hipError_t e = tq::launch_quantize(sp, static_cast<const tq::Tables*>(tables), dtype, x, seqs.data(),
+                                           static_cast<int64_t>(seqs.size()), hkv, x_stream_stride, x_row_stride,
+                                           *pool, pm, static_cast<hipStream_t>(stream));
   return hip_status(e, "tq_quantize_kv_paged launch");
 }
 

@@ -29,6 +29,7 @@
 // the xor of the masks j with 2^k | (j+1), done on the scalar unit; the sign
 // turns count into code.  Each code bit is appended to the packed word with
 // one v_addc (w = 2w + bit), most significant bit first.
+#include <type_traits>
 #include <vector>
 
 #include "tq_internal.h"
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
     const Tables* __restrict__ tab, const void* __restrict__ xv, int64_t n_tok, int64_t xss, int64_t xrs,
     int64_t tok0, uint8_t* __restrict__ codes, float* __restrict__ norms, uint8_t* __restrict__ signs,
     float* __restrict__ rnorms, int64_t cap, int64_t stream_code_bytes, int64_t tiles_per_stream, int64_t tile0,
-    int64_t total_tiles) {
+    int64_t total_tiles, const int32_t* __restrict__ pages, int64_t n_pages, int64_t page_streams) {
   constexpr bool F32IN = XM == X_F32;
   constexpr int NPART = XM == X_BF16 ? 3 : 2;
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
@@ -354,7 +355,22 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
   for (int64_t w = static_cast<int64_t>(blockIdx.x) * WAVES + wave; w < total_tiles; w += stride) {
     int64_t s, T, row, pos;
     locate(w, s, T, row, pos);
-    const bool valid = row >= 0 && row < n_tok;
+    bool valid = row >= 0 && row < n_tok;
+    // destination stream ds and position dp of this lane's vector.  Paged
+    // cache: the page of the position (tiled layout: of the tile, which lies
+    // inside one page) from the sequence's block-table row; a page outside
+    // the pool is not written.
+    int64_t ds = s, dp = pos, dt = tile0 + T;
+    bool page_ok = true;
+    if (pages != nullptr) {
+      const int64_t lp = (TILED ? 32 * (tile0 + T) : pos) / TQ_PAGE_TOKENS;
+      const int pg = TILED || valid ? pages[lp] : -1;
+      page_ok = pg >= 0 && pg < n_pages;
+      ds = static_cast<int64_t>(page_ok ? pg : 0) * page_streams + s;
+      dp = pos % TQ_PAGE_TOKENS;
+      dt = (tile0 + T) % (TQ_PAGE_TOKENS / 32);
+      valid = valid && page_ok;
+    }
     // next tile's input goes out now and lands while this tile is computed
     uint4 xnext[NW];
     load_x(w + stride, xnext);
@@ -434,7 +450,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
       // ---- record layout: lane (n, h) holds coordinates 64h + 0..63 of vector n
       uint32_t wds[8];
       float tp[7];
-      uint8_t* rec = codes + s * stream_code_bytes + pos * CODE_BYTES;
+      uint8_t* rec = codes + ds * stream_code_bytes + dp * CODE_BYTES;
       if constexpr (!QJL) {
         if constexpr (BLO == BHI) {
           // cell-table codes: lane's coordinates 0..31 then 32..63
@@ -451,7 +467,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
           pack_record<BHI>(acc, tp, wds);
           if (valid) store_record<BHI>(rec + 8 * BLO, wds);
         }
-        if (valid && h == 0) norms[s * cap + pos] = normf;
+        if (valid && h == 0) norms[ds * cap + dp] = normf;
       } else {
         uint32_t idx[64];
         if (h == 0) {
@@ -464,7 +480,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
         if (valid) {
           if (h == 0) store_record<BLO>(rec, wds);
           else store_record<BHI>(rec + 8 * BLO, wds);
-          if (h == 0) norms[s * cap + pos] = normf;
+          if (h == 0) norms[ds * cap + dp] = normf;
         }
         // residual r = y - c[idx] in the rotated unit-norm domain, scaled by 2^8
         // and split into fp16 hi + lo for the sketch contraction S r.
@@ -516,8 +532,8 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
             sb[j >> 5] |= (sa[t][r] >= 0.0f ? 1u : 0u) << (j & 31);
           }
         if (valid) {
-          *reinterpret_cast<uint2*>(signs + (s * cap + pos) * (QJL_M / 8) + 8 * h) = make_uint2(sb[0], sb[1]);
-          if (h == 0) rnorms[s * cap + pos] = sqrtf(g2);
+          *reinterpret_cast<uint2*>(signs + (ds * cap + dp) * (QJL_M / 8) + 8 * h) = make_uint2(sb[0], sb[1]);
+          if (h == 0) rnorms[ds * cap + dp] = sqrtf(g2);
         }
       }
     } else {
@@ -529,7 +545,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
       const int j = n;
       const int q = j >> 1;
       constexpr int G = 64 * (BLO + BHI);
-      uint8_t* tbase = codes + s * stream_code_bytes + (tile0 + T) * (32 * CODE_BYTES);
+      uint8_t* tbase = codes + ds * stream_code_bytes + dt * (32 * CODE_BYTES);
       const int64_t p0 = 32 * (tile0 + T);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
@@ -538,7 +554,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
           const int64_t p = p0 + 8 * g + sl;
-          vmask |= (p >= tok0 && p < tok0 + n_tok) ? (1u << sl) : 0u;
+          vmask |= (page_ok && p >= tok0 && p < tok0 + n_tok) ? (1u << sl) : 0u;
         }
         uint32_t wds[4];
         float tp[7];
@@ -557,7 +573,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
           store_tiled_chunk<BHI>(tbase + g * G + 64 * BLO + 8 * BHI * (q - 8) + 4 * BHI * (j & 1), wds, vmask);
         }
       }
-      if (valid && h == 0) norms[s * cap + pos] = normf;
+      if (valid && h == 0) norms[ds * cap + dp] = normf;
     }
 #pragma unroll
     for (int k = 0; k < NW; ++k) xr[k] = xnext[k];
@@ -596,6 +612,11 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
 // not start or end on a tile boundary) go to a separate launch of the MERGE
 // variant, which merges their codes into the stored ones with two returnless
 // atomics per word (clear the written tokens' bits, then set them).
+// The PAGED variant writes a pool of 64-position pages: tiles start on
+// multiples of 32 cache positions in both layouts (so each tile lies in one
+// page, and a record-layout range's first and last tiles are written in
+// part), and the stores of a tile go to the stream and position of its page,
+// read from the block table (a scalar load per tile).
 //
 // One launch covers up to RQ_MAX_SEQ sequences of a batch (ragged lengths
 // and offsets); each sequence's tiles start on a multiple of the tiles per
@@ -613,8 +634,9 @@ struct RotqSeq {
   int32_t stream0;  // cache stream of the sequence's first stream
   int32_t tiles;    // tiles per stream written by this launch
   int32_t start;    // first tile of the sequence in the launch
-  int32_t t_lo;     // tile k of a stream is t_lo + k t_step (tiled layout:
-  int32_t t_step;   //   of the cache stream; record layout: of the rows)
+  int32_t t_lo;     // tile k of a stream is t_lo + k t_step (tiled layout
+  int32_t t_step;   //   or paged cache: of the cache positions; else of the rows)
+  int32_t page_row; // paged cache: the sequence's row of the block table
 };
 struct RotqArgs {
   const Tables* tab;
@@ -624,6 +646,9 @@ struct RotqArgs {
   int64_t xss, xrs, cap, stream_code_bytes;
   int32_t hkv;  // streams per sequence
   int32_t n_seq;
+  const int32_t* pages;     // paged cache: block table [.][page_ld] (device)
+  int64_t page_ld;
+  int32_t n_pages;
   RotqSeq seq[RQ_MAX_SEQ];  // ascending start
 };
 
@@ -694,7 +719,7 @@ __device__ __forceinline__ void code_run(YF yof, const uint2* cells, uint32_t* w
   }
 }
 
-template <int BLO, int BHI, bool F32IN, bool TILED, int K, bool MERGE>
+template <int BLO, int BHI, bool F32IN, bool TILED, int K, bool MERGE, bool PAGED>
 __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   static_assert(!MERGE || TILED, "only the tiled layout merges");
   const Tables* __restrict__ tab = A.tab;
@@ -755,7 +780,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
 
   // Tile tl of the sequence: stream s, tile T of the stream; its rows of x
   // start at r0 and its positions [lo, nv) are written (lo > 0 only for the
-  // first tile of a range in the merge variant).
+  // first tile of a range, in the merge variant and on a paged cache, whose
+  // tiles start on multiples of 32 positions, so each lies in one page).
   struct TileAt {
     int64_t s, r0, p0;
     int lo, nv;
@@ -768,7 +794,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     a.s = s32;
     const int64_t T = static_cast<uint32_t>(tl) - s32 * tps;
     a.lo = 0;
-    if constexpr (MERGE) {
+    if constexpr (MERGE || PAGED) {
       a.p0 = 32 * (tile0 + T * tstep);
       a.r0 = a.p0 - tok0;
       const int64_t lo = -a.r0, hi = n_tok - a.r0;
@@ -787,6 +813,23 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     if (tl >= total_tiles) a.lo = a.nv = 0;
     return a;
   };
+  // where tile a's positions are stored: stream s (of codes / norms) from
+  // position p on; on a paged cache the tile's page from the block table
+  // (ok = false: a page outside the pool, nothing is stored)
+  struct Dst {
+    int64_t s, p;
+    bool ok;
+  };
+  auto dest_at = [&](const TileAt& a) {
+    Dst d{a.s, a.p0, true};
+    if constexpr (PAGED) {
+      const int pg = A.pages[static_cast<int64_t>(Q.page_row) * A.page_ld + a.p0 / TQ_PAGE_TOKENS];
+      d.ok = pg >= 0 && pg < A.n_pages;
+      d.s = static_cast<int64_t>(d.ok ? pg : 0) * A.hkv + a.s;
+      d.p = a.p0 % TQ_PAGE_TOKENS;
+    }
+    return d;
+  };
   // staging role: vector (token slot) sv of the tile, elements [32 qq, 32 qq + 32)
   const int sv = pt >> 2, qq = pt & 3;
   // rows before lo use an offset past the extent (read as zero)
@@ -794,8 +837,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     const TileAt a = tile_at(tl);
     const uint8_t* base = xv + (a.s * xss + (a.r0 + a.lo) * xrs) * ES;
     const __amdgpu_buffer_rsrc_t r = rsrc(base, a.nv > a.lo ? ((a.nv - a.lo - 1) * xrs + D) * ES : 0);
-    const int off = MERGE ? (sv >= a.lo ? static_cast<int>(((sv - a.lo) * xrs + 32 * qq) * ES) : RQ_OOB)
-                          : static_cast<int>((sv * xrs + 32 * qq) * ES);
+    const int off = MERGE || PAGED ? (sv >= a.lo ? static_cast<int>(((sv - a.lo) * xrs + 32 * qq) * ES) : RQ_OOB)
+                                   : static_cast<int>((sv * xrs + 32 * qq) * ES);
 #pragma unroll
     for (int k = 0; k < NQW; ++k)
       dst[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0));
@@ -863,8 +906,10 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     // the four threads of a vector write the same values
     inv_s[pair][b][sv] = normf > 0.0f ? 1.0f / ldexpf(normf, sh + 8) : 0.0f;
     const TileAt a = tile_at(tl);
-    const __amdgpu_buffer_rsrc_t rn = rsrc(norms + a.s * cap + a.p0, static_cast<int64_t>(a.nv) * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, !MERGE || sv >= a.lo ? 4 * sv : RQ_OOB, 0, 0);
+    const Dst d = dest_at(a);
+    const __amdgpu_buffer_rsrc_t rn = rsrc(norms + d.s * cap + d.p, d.ok ? static_cast<int64_t>(a.nv) * 4 : 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, !(MERGE || PAGED) || sv >= a.lo ? 4 * sv : RQ_OOB,
+                                          0, 0);
   };
 
   // ---- pipeline, straight-line over the pair's K tiles: three register
@@ -924,15 +969,18 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
       if (k + 4 < K) load_x(tl + 4, X[(k + 1) % 3]);
     }
     const TileAt a = tile_at(tl);
-    uint8_t* sbase = codes + a.s * stream_code_bytes;
+    const Dst to = dest_at(a);
+    uint8_t* sbase = codes + to.s * stream_code_bytes;
     if constexpr (!TILED) {
       const float inv = inv_s[pair][b][l32];
-      const __amdgpu_buffer_rsrc_t rc = rsrc(sbase + a.p0 * CODE_BYTES, static_cast<int64_t>(a.nv) * CODE_BYTES);
+      const __amdgpu_buffer_rsrc_t rc =
+          rsrc(sbase + to.p * CODE_BYTES, to.ok ? static_cast<int64_t>(a.nv) * CODE_BYTES : 0);
       uint32_t wd[4];
       auto yv = [&](int p) { return acc[p >> 4][p & 15] * inv; };
       auto put = [&](auto bw, int off) {
         constexpr int BW = decltype(bw)::value;
-        const int o = l32 * CODE_BYTES + off;
+        // (slots before lo: past the extent, dropped)
+        const int o = !PAGED || l32 >= a.lo ? l32 * CODE_BYTES + off : RQ_OOB;
         if constexpr (BW == 4) {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)),
                                                                     make_uint4(wd[0], wd[1], wd[2], wd[3])), rc, o, 0, 0);
@@ -956,7 +1004,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
       const float* invb = inv_s[pair][b] + 16 * h;
       constexpr int G = 64 * (BLO + BHI);
       const __amdgpu_buffer_rsrc_t rc =
-          rsrc(sbase + a.p0 * CODE_BYTES, a.nv > a.lo ? static_cast<int64_t>(32) * CODE_BYTES : 0);
+          rsrc(sbase + to.p * CODE_BYTES, to.ok && a.nv > a.lo ? static_cast<int64_t>(32) * CODE_BYTES : 0);
       const int qa = l32 & 3;
       auto emit = [&](auto bw, const uint2* cells) {
         constexpr int BW = decltype(bw)::value;
@@ -1003,8 +1051,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
               }
               // clear, then set, with returnless atomics: same lane and word,
               // so they apply in order; m != 0 only for a word of a real tile
-              if (owner && m != 0) {
-                uint32_t* wp = reinterpret_cast<uint32_t*>(sbase + a.p0 * CODE_BYTES + o);
+              if (owner && m != 0 && to.ok) {
+                uint32_t* wp = reinterpret_cast<uint32_t*>(sbase + to.p * CODE_BYTES + o);
                 __hip_atomic_fetch_and(wp, ~m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_fetch_or(wp, out & m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               }
@@ -1021,7 +1069,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
 
 template <int BLO, int BHI, int XM, bool TILED, bool QJL>
 hipError_t launch_one(const Tables* tab, const void* x, int64_t n_streams, int64_t n_tok, int64_t xss, int64_t xrs,
-                      int64_t tok0, const tq_cache& c, hipStream_t st) {
+                      int64_t tok0, const tq_cache& c, const int32_t* pages, int64_t n_pages, hipStream_t st) {
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
   int64_t tiles, tile0 = 0;
   if (TILED) {
@@ -1035,7 +1083,7 @@ hipError_t launch_one(const Tables* tab, const void* x, int64_t n_streams, int64
   const int64_t blocks = std::min<int64_t>((total + WAVES - 1) / WAVES, 256);
   hipLaunchKernelGGL((quantize_kernel<BLO, BHI, XM, TILED, QJL>), dim3(static_cast<unsigned>(blocks)),
                      dim3(THREADS), 0, st, tab, x, n_tok, xss, xrs, tok0, c.codes, c.norms, c.qjl_signs,
-                     c.qjl_rnorms, c.cap, stream_bytes, tiles, tile0, total);
+                     c.qjl_rnorms, c.cap, stream_bytes, tiles, tile0, total, pages, n_pages, n_streams);
   return hipGetLastError();
 }
 
@@ -1052,13 +1100,15 @@ tq_cache streams_from(const tq_cache& c, int64_t s0, int64_t code_bytes) {
 // one general-kernel launch per sequence
 template <int BLO, int BHI, int XM, bool TILED, bool QJL>
 hipError_t launch_each(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv, int64_t xss,
-                       int64_t xrs, const tq_cache& c, hipStream_t st) {
+                       int64_t xrs, const tq_cache& c, const PageMap& pm, hipStream_t st) {
   constexpr int64_t ES = XM == X_F32 ? 4 : 2;
   for (int64_t i = 0; i < n_seq; ++i) {
     const QSeq& q = seqs[i];
+    const int32_t* pages = pm.table ? pm.table + q.page_row * pm.ld : nullptr;
     const hipError_t e = launch_one<BLO, BHI, XM, TILED, QJL>(tab, static_cast<const uint8_t*>(x) + q.x_off * ES,
                                                               hkv, q.n_tok, xss, xrs, q.tok0,
-                                                              streams_from(c, q.stream0, 8 * (BLO + BHI)), st);
+                                                              streams_from(c, q.stream0, 8 * (BLO + BHI)), pages,
+                                                              pm.n_pages, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1070,9 +1120,9 @@ struct RotqPart {
   int64_t t_lo, t_step, tiles;
 };
 
-template <int BLO, int BHI, bool F32IN, bool TILED, bool MERGE>
+template <int BLO, int BHI, bool F32IN, bool TILED, bool MERGE, bool PAGED>
 hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<RotqPart>& list, int64_t hkv,
-                            int64_t xss, int64_t xrs, const tq_cache& c, hipStream_t st) {
+                            int64_t xss, int64_t xrs, const tq_cache& c, const PageMap& pm, hipStream_t st) {
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
   const int64_t n = static_cast<int64_t>(list.size());
   for (int64_t b0 = 0; b0 < n; b0 += RQ_MAX_SEQ) {
@@ -1093,6 +1143,9 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
     a.stream_code_bytes = c.cap * CODE_BYTES;
     a.hkv = static_cast<int32_t>(hkv);
     a.n_seq = nb;
+    a.pages = pm.table;
+    a.page_ld = pm.ld;
+    a.n_pages = static_cast<int32_t>(pm.n_pages);
     int64_t total = 0;  // each sequence's tiles start on a multiple of K
     for (int i = 0; i < nb; ++i) {
       const RotqPart& p = list[b0 + i];
@@ -1103,17 +1156,21 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
                          static_cast<int32_t>(p.tiles),
                          static_cast<int32_t>(total),
                          static_cast<int32_t>(p.t_lo),
-                         static_cast<int32_t>(p.t_step)};
+                         static_cast<int32_t>(p.t_step),
+                         static_cast<int32_t>(p.q.page_row)};
       total += (hkv * p.tiles + K - 1) / K * K;
     }
     const unsigned blocks = static_cast<unsigned>((total + 2 * K - 1) / (2 * K));
     if constexpr (MERGE) {
-      hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, true>), dim3(blocks), dim3(RQ_THREADS), 0, st, a);
+      hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, true, PAGED>), dim3(blocks), dim3(RQ_THREADS), 0,
+                         st, a);
     } else {
       if (K == 8)
-        hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 8, false>), dim3(blocks), dim3(RQ_THREADS), 0, st, a);
+        hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 8, false, PAGED>), dim3(blocks), dim3(RQ_THREADS),
+                           0, st, a);
       else
-        hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, false>), dim3(blocks), dim3(RQ_THREADS), 0, st, a);
+        hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, false, PAGED>), dim3(blocks), dim3(RQ_THREADS),
+                           0, st, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1123,18 +1180,24 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
 
 template <int BLO, int BHI, bool F32IN, bool TILED>
 hipError_t launch_rotq(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv, int64_t xss,
-                       int64_t xrs, const tq_cache& c, hipStream_t st) {
+                       int64_t xrs, const tq_cache& c, const PageMap& pm, hipStream_t st) {
   constexpr int64_t ES = F32IN ? 4 : 2;
   constexpr int XM = F32IN ? X_F32 : X_BF16;
+  const bool paged = pm.table != nullptr;
   // whole tiles in one list; tiled-layout tiles written only in part in another
   std::vector<RotqPart> whole, part;
-  int64_t all = 0, streams = 0;
+  int64_t all = 0, streams = paged ? pm.n_pages * hkv : 0;
   for (int64_t i = 0; i < n_seq; ++i) {
     const QSeq& q = seqs[i];
+    const int64_t end = q.tok0 + q.n_tok;
     if constexpr (!TILED) {
-      whole.push_back(RotqPart{q, 0, 1, (q.n_tok + TILE - 1) / TILE});
+      // paged: tiles on multiples of 32 positions (each in one page), the
+      // first and last written in part
+      if (paged)
+        whole.push_back(RotqPart{q, q.tok0 / TILE, 1, (end + TILE - 1) / TILE - q.tok0 / TILE});
+      else
+        whole.push_back(RotqPart{q, 0, 1, (q.n_tok + TILE - 1) / TILE});
     } else {
-      const int64_t end = q.tok0 + q.n_tok;
       const int64_t f = q.tok0 / TILE, e = (end + TILE - 1) / TILE;     // tiles touched
       const int64_t wf = (q.tok0 + TILE - 1) / TILE, we = end / TILE;  // tiles written whole
       if (we > wf) whole.push_back(RotqPart{q, wf, 1, we - wf});
@@ -1148,48 +1211,53 @@ hipError_t launch_rotq(const Tables* tab, const void* x, const QSeq* seqs, int64
       }
     }
     all += hkv * ((q.n_tok + TILE - 1) / TILE + 2) + 16;
-    streams = std::max(streams, q.stream0 + hkv);
+    if (!paged) streams = std::max(streams, q.stream0 + hkv);
   }
   // 32-bit tile, position and stream arithmetic, and buffer offsets below RQ_OOB
   if (all + 16 * 1024 >= (int64_t{1} << 31) || 32 * xrs * ES >= RQ_OOB || c.cap >= (int64_t{1} << 31) - 64 ||
       streams >= (int64_t{1} << 31))
-    return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
-  hipError_t e = launch_rotq_list<BLO, BHI, F32IN, TILED, false>(tab, x, whole, hkv, xss, xrs, c, st);
-  if constexpr (TILED) {
-    if (e == hipSuccess && !part.empty())
-      e = launch_rotq_list<BLO, BHI, F32IN, TILED, true>(tab, x, part, hkv, xss, xrs, c, st);
-  }
-  return e;
+    return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+  auto run = [&](auto pg) {
+    constexpr bool P = decltype(pg)::value;
+    hipError_t e = launch_rotq_list<BLO, BHI, F32IN, TILED, false, P>(tab, x, whole, hkv, xss, xrs, c, pm, st);
+    if constexpr (TILED) {
+      if (e == hipSuccess && !part.empty())
+        e = launch_rotq_list<BLO, BHI, F32IN, TILED, true, P>(tab, x, part, hkv, xss, xrs, c, pm, st);
+    }
+    return e;
+  };
+  return paged ? run(std::true_type{}) : run(std::false_type{});
 }
 
 template <int BLO, int BHI>
 hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
-                           int64_t n_seq, int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c, hipStream_t st) {
+                           int64_t n_seq, int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c,
+                           const PageMap& pm, hipStream_t st) {
   const bool f32 = dtype == TQ_F32;
   if (sp.qjl_m) {
-    return f32 ? launch_each<BLO, BHI, X_F32, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st)
-               : launch_each<BLO, BHI, X_BF16_F16, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
+    return f32 ? launch_each<BLO, BHI, X_F32, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
+               : launch_each<BLO, BHI, X_BF16_F16, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
   }
   if (sp.layout == TQ_LAYOUT_TILED) {
-    return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st)
-               : launch_rotq<BLO, BHI, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
+    return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
+               : launch_rotq<BLO, BHI, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
   }
-  return f32 ? launch_rotq<BLO, BHI, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st)
-             : launch_rotq<BLO, BHI, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
+  return f32 ? launch_rotq<BLO, BHI, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
+             : launch_rotq<BLO, BHI, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
                            int64_t n_seq, int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c,
-                           hipStream_t st) {
+                           const PageMap& pm, hipStream_t st) {
   const int key = sp.bits_lo * 10 + sp.bits_hi;
   switch (key) {
-    case 22: return dispatch_layout<2, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
-    case 33: return dispatch_layout<3, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
-    case 44: return dispatch_layout<4, 4>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
-    case 43: return dispatch_layout<4, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
-    case 32: return dispatch_layout<3, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, st);
+    case 22: return dispatch_layout<2, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    case 33: return dispatch_layout<3, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    case 44: return dispatch_layout<4, 4>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    case 43: return dispatch_layout<4, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    case 32: return dispatch_layout<3, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -93,12 +93,22 @@ struct QSeq {
   int64_t x_off;
   int64_t tok0;
   int64_t n_tok;
-  int64_t stream0;
+  int64_t stream0;   // contiguous cache: stream of kv head 0; paged: 0
+  int64_t page_row;  // paged: the sequence's row of the block table
+};
+
+// A paged cache: position c of a sequence lives at position c % 64 of pool
+// page table[page_row * ld + c / 64] (streams page * hkv + h); table ==
+// nullptr for a contiguous cache.  Pages outside [0, n_pages) are not written.
+struct PageMap {
+  const int32_t* table = nullptr;  // device
+  int64_t ld = 0;
+  int64_t n_pages = 0;
 };
 
 hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
                            int64_t n_seq, int64_t hkv, int64_t x_stream_stride, int64_t x_row_stride,
-                           const tq_cache& cache, hipStream_t stream);
+                           const tq_cache& cache, const PageMap& pages, hipStream_t stream);
 
 // Inner-product scores of nq <= TQ_IP_MAX_QUERIES queries against a
 // record-layout cache (search.hip).

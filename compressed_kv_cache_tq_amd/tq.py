@@ -403,14 +403,16 @@ def quantize_kv_paged(spec: Spec, tables, x, pool: Cache, *, hkv: int, n_tok, bl
                       x_off=None, x_stream_stride: int | None = None, x_row_stride: int | None = None,
                       stream: int | None = None) -> None:
     """Append sequence b's n_tok[b] vectors at compressed positions pos0[b]..
-    of a paged pool; block_table is a host int32 array [batch, max_pages].
-    x as for quantize_kv_ragged."""
+    of a paged pool; block_table is a device int32 tensor [batch, max_pages]
+    (tokens whose page lies outside [0, n_pages) are not written).  x as for
+    quantize_kv_ragged."""
     n = np.ascontiguousarray(n_tok, dtype=np.int64)
     B = n.shape[0]
     p0 = np.zeros(B, np.int64) if pos0 is None else np.ascontiguousarray(pos0, dtype=np.int64)
-    bt = np.ascontiguousarray(block_table, dtype=np.int32)
-    if bt.ndim != 2 or bt.shape[0] != B:
-        raise ValueError("block_table must be [batch, max_pages]")
+    torch = _torch()
+    if (not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32 or block_table.dim() != 2
+            or block_table.shape[0] != B or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 tensor [batch, max_pages]")
     if x_off is None:
         if x.dim() != 3 or x.shape[-1] != D or x.stride(-1) != 1 or x.shape[0] < B * hkv:
             raise ValueError("x must be [batch*hkv, rows, 128] with contiguous rows")
@@ -422,8 +424,9 @@ def quantize_kv_paged(spec: Spec, tables, x, pool: Cache, *, hkv: int, n_tok, bl
     cs, cc = spec.c(), pool.c()
     st = _stream(x.device) if stream is None else stream
     _check(lib().tq_quantize_kv_paged(ctypes.byref(cs), tables.data_ptr(), _dtype_code(x), x.data_ptr(), B, hkv,
-                                      xo.ctypes.data, p0.ctypes.data, n.ctypes.data, xss, xrs, bt.ctypes.data,
-                                      bt.shape[1], n_pages, ctypes.byref(cc), st), "tq_quantize_kv_paged")
+                                      xo.ctypes.data, p0.ctypes.data, n.ctypes.data, xss, xrs,
+                                      block_table.data_ptr(), block_table.shape[1], n_pages, ctypes.byref(cc), st),
+           "tq_quantize_kv_paged")
 
 
 def attend_decode_paged(kspec: Spec, ktables, kpool: Cache, vspec: Spec, vtables, vpool: Cache, q, seq_lens, out,

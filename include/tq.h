@@ -256,11 +256,14 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
  * TQ_PAGE_TOKENS].  The pages of one sequence must be distinct.
  *
  * Quantize into a paged cache: sequence b appends n_tok[b] vectors at
- * compressed positions [pos0[b], pos0[b] + n_tok[b]); rows of x and the
- * per-sequence arrays as for tq_quantize_kv_ragged.  block_table is a HOST
- * int32 array [batch][max_pages] read during the call; every page it names
- * for the written range must lie in [0, n_pages) (else TQ_E_ARG, no launch).
- * One launch per 64 page segments (a spec with the sketch: one per segment). */
+ * compressed positions [pos0[b], pos0[b] + n_tok[b]) (host int64 arrays;
+ * pos0[b] + n_tok[b] <= max_pages * TQ_PAGE_TOKENS, else TQ_E_ARG); rows of
+ * x as for tq_quantize_kv_ragged.  block_table is DEVICE int32 [batch]
+ * [max_pages], 4-byte aligned, read by the kernels; a token whose page lies
+ * outside [0, n_pages) (n_pages <= 2^30) is not written, the others are.
+ * Only the pages of the written range are read.  The same codes, norms and
+ * sketch as tq_quantize_kv_ragged land at the mapped positions.  One launch
+ * per 64 sequences (a spec with the sketch: one per sequence). */
 tq_status tq_quantize_kv_paged(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,
                                int32_t batch, int32_t hkv, const int64_t* x_off, const int64_t* pos0,
                                const int64_t* n_tok, int64_t x_stream_stride, int64_t x_row_stride,

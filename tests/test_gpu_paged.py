@@ -1,5 +1,5 @@
-"""Paged caches: the quantize appends into pool pages through a block table
-and the decode reads through it.  The contiguous path is the reference: the
+"""Paged caches: the quantize appends into pool pages through a device block
+table and the decode reads through it.  The contiguous path is the reference: the
 same codes land at the mapped positions bit for bit, and the decode over the
 pages gives the contiguous decode's output exactly (same plan, same
 arithmetic), which is itself held to the oracle."""
@@ -28,11 +28,24 @@ def _tables(B, comp, n_pages, seed, junk=-1):
     return bt
 
 
-def _paged_quantize(run, bt, n_pages, chunk):
+def _fill(pool, byte=0xAB):
+    """Poison a pool so untouched positions are recognisable."""
+    pool.codes.fill_(byte)
+    pool.norms.fill_(-7.0)
+    if pool.qjl_signs is not None:
+        pool.qjl_signs.fill_(byte)
+        pool.qjl_rnorms.fill_(-7.0)
+
+
+def _paged_quantize(run, bt, n_pages, chunk, poison=False):
     """Appends each sequence's compressed tokens in chunks of `chunk` tokens."""
     wl, S, B, H = run.wl, run.wl.sink, run.B, run.wl.hkv
     kpool = tq.alloc_page_pool(run.kspec, n_pages, H)
     vpool = tq.alloc_page_pool(run.vspec, n_pages, H)
+    if poison:
+        _fill(kpool)
+        _fill(vpool)
+    btd = torch().from_numpy(bt).cuda()
     comp = [max(0, int(run.inp.seq_lens[b]) - S) for b in range(B)]
     xk = [to_device(run.inp.k[b], wl.dtype) for b in range(B)]
     xv = [to_device(run.inp.v[b], wl.dtype) for b in range(B)]
@@ -49,15 +62,16 @@ def _paged_quantize(run, bt, n_pages, chunk):
                 xkc[b * H:(b + 1) * H, :n[b]] = xk[b][:, S + start:S + start + n[b]]
                 xvc[b * H:(b + 1) * H, :n[b]] = xv[b][:, S + start:S + start + n[b]]
         pos0 = [start] * B
-        tq.quantize_kv_paged(run.kspec, run.ktab, xkc, kpool, hkv=H, n_tok=n, pos0=pos0, block_table=bt,
+        tq.quantize_kv_paged(run.kspec, run.ktab, xkc, kpool, hkv=H, n_tok=n, pos0=pos0, block_table=btd,
                              n_pages=n_pages)
-        tq.quantize_kv_paged(run.vspec, run.vtab, xvc, vpool, hkv=H, n_tok=n, pos0=pos0, block_table=bt,
+        tq.quantize_kv_paged(run.vspec, run.vtab, xvc, vpool, hkv=H, n_tok=n, pos0=pos0, block_table=btd,
                              n_pages=n_pages)
     torch().cuda.synchronize()
     return kpool, vpool, comp
 
 
 @pytest.mark.parametrize("name,ctx,batch,chunk", [
+    ("tiny_oracle", None, None, 45),
     ("gqa_decode", 1500, None, 37),
     ("qjl", 1000, 2, 64),
     ("batched_ragged", 900, 5, 100),
@@ -120,3 +134,44 @@ def test_paged_single_split_streams_and_bad_page_ids():
                            sink_k=run.sink_k, sink_v=run.sink_v, v_skip=1e-6, max_len=run.max_len)
     T.cuda.synchronize()
     assert T.equal(out, run.out)
+
+
+@pytest.mark.parametrize("name,chunk", [("gqa_decode", 37), ("qjl", 50)])
+def test_paged_quantize_skips_pages_outside_the_pool(name, chunk):
+    """Logical pages mapped to -1 or past the pool: their tokens are written
+    nowhere (every pool page not in the table keeps its poison), the other
+    pages hold the contiguous cache's codes exactly."""
+    print(f"[paged] out-of-pool pages {name} chunk={chunk}", flush=True)
+    run = Run(workloads.generate(name, ctx=900, batch=2))
+    run.quantize()
+    torch().cuda.synchronize()
+    H, B = run.wl.hkv, run.B
+    comp = [max(0, int(run.inp.seq_lens[b]) - run.wl.sink) for b in range(B)]
+    n_pages = sum(-(-c // P) for c in comp) + 4
+    bt = _tables(B, comp, n_pages, seed=5)
+    bt[0, 1] = -1
+    bt[1, 0] = n_pages + 3
+    bt[1, 2] = 1 << 30
+    used = set(int(v) for v in bt.ravel() if 0 <= v < n_pages)
+    kpool, vpool, comp = _paged_quantize(run, bt, n_pages, chunk, poison=True)
+    for spec, pool, cache in ((run.kspec, kpool, run.kc), (run.vspec, vpool, run.vc)):
+        nb = tq.cache_code_bytes(spec, P)
+        codes = pool.codes.cpu().numpy().reshape(n_pages, H, nb)
+        norms = pool.norms.cpu().numpy().reshape(n_pages, H, P)
+        for pg in range(n_pages):
+            if pg not in used:
+                assert np.all(codes[pg] == 0xAB) and np.all(norms[pg] == -7.0), f"page {pg} was written"
+        for b in range(B):
+            for lp in range(-(-comp[b] // P)):
+                pg = int(bt[b, lp])
+                if not 0 <= pg < n_pages:
+                    continue
+                n = min(P, comp[b] - lp * P)
+                for h in range(H):
+                    ps, s = pg * H + h, b * H + h
+                    assert np.array_equal(read_codes(spec, pool, ps, n), read_codes(spec, cache, s, n, lp * P))
+                    assert np.array_equal(read_norms(pool, ps, n), read_norms(cache, s, n, lp * P))
+                    if spec.qjl_m:
+                        zp, rp = read_signs(pool, ps, n)
+                        zc, rc = read_signs(cache, s, n, lp * P)
+                        assert np.array_equal(zp, zc) and np.array_equal(rp, rc)

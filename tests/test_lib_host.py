@@ -296,7 +296,6 @@ def test_paged_argument_errors_without_launch():
     pool_k = tq.TqCache(0x1000, 0x2000, None, None, 64)
     pool_v = tq.TqCache(0x3000, 0x4000, None, None, 64)
     tab = ctypes.c_void_p(0x10000)
-    bt = np.zeros((2, 4), np.int32)
 
     def dec(a, kp=pool_k, max_pages=4, n_pages=8, table=0x9000):
         return L.tq_attend_decode_paged(ctypes.byref(ks), tab, ctypes.byref(kp), ctypes.byref(vs), tab,
@@ -309,20 +308,22 @@ def test_paged_argument_errors_without_launch():
     assert dec(tq.TqAttn(2, 8, 2, 0, 0.1, 0.0, 64), n_pages=0) == -1
     assert dec(tq.TqAttn(0, 8, 2, 0, 0.1, 0.0, 64)) == 0
 
-    def qz(n_tok, pos0=(0, 0), table=bt, n_pages=8, pool=pool_k):
+    def qz(n_tok, pos0=(0, 0), table=0x9000, n_pages=8, pool=pool_k, max_pages=4):
         n, p0, xo = np.asarray(n_tok, np.int64), np.asarray(pos0, np.int64), np.zeros(2, np.int64)
         return L.tq_quantize_kv_paged(ctypes.byref(ks), tab, 1, 0x1000, 2, 2, xo.ctypes.data, p0.ctypes.data,
-                                      n.ctypes.data, 128 * 300, 128, table.ctypes.data, table.shape[1], n_pages,
+                                      n.ctypes.data, 128 * 300, 128, table, max_pages, n_pages,
                                       ctypes.byref(pool), None)
 
     assert qz([10, 257]) == -1                                   # beyond max_pages pages
-    bad = bt.copy()
-    bad[1, 0] = 8
-    assert qz([10, 10], table=bad) == -1                         # page outside the pool
-    bad[1, 0] = -1
-    assert qz([10, 10], table=bad) == -1
+    assert qz([10, 10], pos0=(250, 0)) == -1
+    assert qz([10, 10], table=None) == -1                        # the device table is required
+    assert qz([10, 10], table=0x9002) == -1                      # ... 4-byte aligned
+    assert qz([10, 10], n_pages=0) == -1
+    assert qz([10, 10], n_pages=(1 << 30) + 1) == -1
+    assert qz([10, 10], max_pages=0) == -1
     assert qz([10, 10], pool=tq.TqCache(0x1000, 0x2000, None, None, 96)) == -1
     assert qz([0, 0]) == 0                                       # nothing to write
+    assert qz([0, 0], table=None) == -1
 
 
 def test_attend_argument_errors_without_launch():
