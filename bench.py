@@ -69,9 +69,9 @@ CALIB_BYTES = 512 << 20
 # Kernels of one bench step, by the name rocprofv3 reports, and the traffic
 # file each one's counters go to.
 STEP_KERNELS = {
-    "quantize_k": ["rotq_kernel<4, 4, false, false, 8, false>"],
-    "quantize_v": ["rotq_kernel<3, 3, false, true, 8, false>"],
-    "attend": ["split_kernel<4, 4, 3, 3, false>", "combine_kernel"],
+    "quantize_k": ["rotq_kernel<4, 4, false, false, 8, false, false>"],
+    "quantize_v": ["rotq_kernel<3, 3, false, true, 8, false, false>"],
+    "attend": ["split_kernel<4, 4, 3, 3, false, false>", "combine_kernel"],
 }
 STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0], "attend": KERNEL_SOURCES[1]}
 
