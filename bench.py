@@ -252,8 +252,46 @@ def bench_search(args) -> int:
                      "kernel": f"ip_kernel<{wl.bits},{wl.bits}{',qjl' if wl.qjl_m else ''}> + ipq_prep_kernel",
                      "algorithmic_bytes_per_launch": db_bytes + out_bytes, "avg_launch_us": round(ms * 1e3, 2)},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_search(wl, spec, cache, q)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def cpu_baseline_search(wl, spec, cache, q):
+    """The float64 oracle on the host: estimates of all queries against the
+    first stream of the GPU's packed database (median of 3 runs)."""
+    from oracle import pack as opk
+    from oracle import quantize as oqz
+    from oracle import search as osr
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    n = wl.n_tok
+    os_ = oqz.Spec(bits_lo=wl.bits, bits_hi=wl.bits, split=128, qjl_m=wl.qjl_m,
+                   rotation="hadamard" if spec.rotation == 1 else "haar")
+    rb = kspec_bytes(spec)
+    raw = cache.codes[:n * rb].cpu().numpy().reshape(n, rb)
+    norms = cache.norms[:n].cpu().numpy()
+    signs = cache.qjl_signs[:n * wl.qjl_m // 8].cpu().numpy().reshape(n, wl.qjl_m // 8) if wl.qjl_m else None
+    gamma = cache.qjl_rnorms[:n].cpu().numpy() if wl.qjl_m else None
+    qh = q.cpu().numpy()
+
+    def once():
+        t0 = time.perf_counter()
+        idx = opk.unpack_records(raw, spec.widths)
+        bits = opk.unpack_sign_bits(signs) if wl.qjl_m else None
+        osr.ip_scores(qh, idx, norms, os_, bits=bits, gamma=gamma)
+        return time.perf_counter() - t0
+
+    t = float(np.median([once() for _ in range(3)]))
+    per_vec = rb + 4 + (wl.qjl_m // 8 + 4 if wl.qjl_m else 0)
+    nbytes = n * per_vec + wl.nq * 128 * 4 + wl.nq * n * 4
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"estimates of the {wl.nq} queries against the first stream ({n} vectors) of the GPU's "
+                      f"packed database, median of 3", "seconds": round(t, 3)}
 
 
 def main() -> int:

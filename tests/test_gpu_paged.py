@@ -175,3 +175,68 @@ def test_paged_quantize_skips_pages_outside_the_pool(name, chunk):
                         zp, rp = read_signs(pool, ps, n)
                         zc, rc = read_signs(cache, s, n, lp * P)
                         assert np.array_equal(zp, zc) and np.array_equal(rp, rc)
+
+
+@pytest.mark.parametrize("qjl", [0, 128])
+def test_paged_prefill_then_token_by_token_appends(qjl):
+    """The serving pattern: a paged prefill of each sequence's prefix, then
+    decode steps that each append one token per live sequence at its own
+    position (70 sequences: two launches of the 64-sequence table), ending
+    at different steps.  Codes and decode equal the contiguous path's."""
+    print(f"[paged] prefill + single-token appends, qjl={qjl}", flush=True)
+    T = torch()
+    wl = workloads.Workload(f"serve{qjl}", 70, 8, 2, "bf16", workloads.QSpec(2, 2, qjl_m=qjl) if qjl else workloads.QSpec(4, 4),
+                            workloads.QSpec(3, 3), lens_range=(40, 300))
+    run = Run(workloads.generate(wl))
+    run.quantize()
+    run.attend()
+    T.cuda.synchronize()
+    B, H = run.B, wl.hkv
+    comp = [int(v) for v in run.inp.seq_lens]
+    tail = np.random.default_rng(2).integers(1, 9, B)       # tokens appended one by one
+    pre = [c - int(t) for c, t in zip(comp, tail)]
+    n_pages = sum(-(-c // P) for c in comp) + 2
+    bt = _tables(B, comp, n_pages, seed=9)
+    btd = T.from_numpy(bt).cuda()
+    kpool = tq.alloc_page_pool(run.kspec, n_pages, H)
+    vpool = tq.alloc_page_pool(run.vspec, n_pages, H)
+    xk = [to_device(run.inp.k[b], wl.dtype) for b in range(B)]
+    xv = [to_device(run.inp.v[b], wl.dtype) for b in range(B)]
+
+    def append(start, count):
+        rows = max(1, max(count))
+        xkc = T.zeros((B * H, rows, 128), dtype=xk[0].dtype, device="cuda")
+        xvc = T.zeros_like(xkc)
+        for b in range(B):
+            if count[b]:
+                xkc[b * H:(b + 1) * H, :count[b]] = xk[b][:, start[b]:start[b] + count[b]]
+                xvc[b * H:(b + 1) * H, :count[b]] = xv[b][:, start[b]:start[b] + count[b]]
+        for spec, tab, x, pool in ((run.kspec, run.ktab, xkc, kpool), (run.vspec, run.vtab, xvc, vpool)):
+            tq.quantize_kv_paged(spec, tab, x, pool, hkv=H, n_tok=count, pos0=start, block_table=btd,
+                                 n_pages=n_pages)
+
+    append([0] * B, pre)
+    pos = list(pre)
+    for _ in range(int(tail.max())):
+        count = [1 if pos[b] < comp[b] else 0 for b in range(B)]
+        append(pos, count)
+        pos = [p + c for p, c in zip(pos, count)]
+    T.cuda.synchronize()
+    assert pos == comp
+    for b in range(B):
+        for h in range(H):
+            for lp in range(-(-comp[b] // P)):
+                n = min(P, comp[b] - lp * P)
+                ps, s = int(bt[b, lp]) * H + h, b * H + h
+                for spec, pool, cache in ((run.kspec, kpool, run.kc), (run.vspec, vpool, run.vc)):
+                    assert np.array_equal(read_codes(spec, pool, ps, n), read_codes(spec, cache, s, n, lp * P))
+                    assert np.array_equal(read_norms(pool, ps, n), read_norms(cache, s, n, lp * P))
+                if qjl:
+                    zp, rp = read_signs(kpool, ps, n)
+                    zc, rc = read_signs(run.kc, s, n, lp * P)
+                    assert np.array_equal(zp, zc) and np.array_equal(rp, rc)
+    out = T.empty_like(run.q)
+    tq.attend_decode_paged(run.kspec, run.ktab, kpool, run.vspec, run.vtab, vpool, run.q, run.seq_lens, out, run.ws,
+                           hkv=H, block_table=btd, n_pages=n_pages, max_len=run.max_len)
+    T.cuda.synchronize()
+    assert T.equal(out, run.out)
