@@ -303,6 +303,8 @@ def main() -> int:
     ap.add_argument("--workload", default=WORKLOAD, help="workload to time (the metric is quoted on gqa_decode)")
     ap.add_argument("--rotation", choices=("haar", "hadamard"), default="haar",
                     help="how the rotation is drawn (the workloads are specified with the Haar rotation)")
+    ap.add_argument("--kbits", type=int, choices=(8,), default=None,
+                    help="keys at 8 bits (uniform, no sketch: the K8 of a K8/V3 policy) instead of the workload's")
     ap.add_argument("--paged", action="store_true",
                     help="caches in a pool of 64-token pages, each sequence's pages in a seeded random order")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -338,6 +340,9 @@ def main() -> int:
     rot = tq.ROT_HADAMARD if args.rotation == "hadamard" else tq.ROT_HAAR
     kspec = tq.Spec(wl.k.bits_lo, wl.k.bits_hi, split=wl.k.split, qjl_m=wl.k.qjl_m, layout=tq.LAYOUT_RECORD,
                     rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed, rotation=rot)
+    if args.kbits == 8:
+        kspec = tq.Spec(8, layout=tq.LAYOUT_RECORD, rot_seed=wl.k.rot_seed, rotation=rot)
+    kb = (kspec.bits_lo, kspec.bits_lo if kspec.bits_hi is None else kspec.bits_hi)
     vspec = tq.Spec(wl.v.bits_lo, wl.v.bits_hi, split=wl.v.split, layout=tq.LAYOUT_TILED, rot_seed=wl.v.rot_seed,
                     rotation=rot)
     ktab, vtab = tq.device_tables(kspec), tq.device_tables(vspec)
@@ -472,7 +477,7 @@ def main() -> int:
     quant_gbs = (qk_bytes + qv_bytes) / quant_s / 1e9
 
     # dominant kernel of the step (largest device time): one of the two quantize launches
-    ktag = f"{wl.k.bits_lo},{wl.k.bits_hi},{'f32' if f32 else 'bf16'},record{',qjl' if kspec.qjl_m else ''}"
+    ktag = f"{kb[0]},{kb[1]},{'f32' if f32 else 'bf16'},record{',qjl' if kspec.qjl_m else ''}"
     vtag = f"{wl.v.bits_lo},{wl.v.bits_hi},{'f32' if f32 else 'bf16'},tiled"
     kkern = "quantize_kernel" if kspec.qjl_m else "rotq_kernel"
     if qk_ms >= qv_ms:
@@ -480,14 +485,15 @@ def main() -> int:
     else:
         dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms, qv_bytes, f"rotq_kernel<{vtag}>"
     dom_gbs = dom_bytes / (dom_ms / 1e3) / 1e9
-    traffic = read_traffic(dom_name) if wname == WORKLOAD and not args.paged else None
+    default_cfg = wname == WORKLOAD and not args.paged and args.kbits is None
+    traffic = read_traffic(dom_name) if default_cfg else None
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom_kernel,
                 "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2)}
-    att_traffic = read_traffic("attend") if wname == WORKLOAD and not args.paged else None
+    att_traffic = read_traffic("attend") if default_cfg else None
     roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
-                       "kernel": f"split_kernel<{wl.k.bits_lo},{wl.k.bits_hi},{wl.v.bits_lo},{wl.v.bits_hi}"
+                       "kernel": f"split_kernel<{kb[0]},{kb[1]},{wl.v.bits_lo},{wl.v.bits_hi}"
                                  f"{',qjl' if kspec.qjl_m else ''}{',paged' if args.paged else ''}> (+ combine_kernel when a stream has several splits;"
                                  f" one decode step)",
                        "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": round(at_ms * 1e3, 2)}
@@ -497,8 +503,8 @@ def main() -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": wname, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "d": 128,
                    "context": T if uniform else f"ragged {int(lens_h.min())}..{T}, sum {int(lens_h.sum())}",
-                   "kv_dtype": wl.dtype, "k_bits": [wl.k.bits_lo, wl.k.bits_hi], "v_bits": [wl.v.bits_lo, wl.v.bits_hi],
-                   "split": wl.k.split, "qjl": bool(kspec.qjl_m), "sink": S, "v_skip": wl.v_skip,
+                   "kv_dtype": wl.dtype, "k_bits": list(kb), "v_bits": [wl.v.bits_lo, wl.v.bits_hi],
+                   "split": kspec.split, "qjl": bool(kspec.qjl_m), "sink": S, "v_skip": wl.v_skip,
                    "structure": wl.structure, "rotation": args.rotation,
                    "cache": f"paged ({tq.PAGE_TOKENS}-token pages)" if args.paged else "contiguous"},
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
@@ -517,7 +523,7 @@ def main() -> int:
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline and wname == WORKLOAD and not args.paged:
+    if not args.no_cpu_baseline and default_cfg:
         a = (args.warmup + args.steps) % COPIES
         nb_k, nb_v = tq.cache_code_bytes(kspec, T), tq.cache_code_bytes(vspec, T)
         kraw = [kc[a].codes[h * nb_k:(h + 1) * nb_k].cpu().numpy().reshape(T, kcb) for h in range(Hkv)]

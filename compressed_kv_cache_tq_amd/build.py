@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["host.cpp", "quantize.hip", "attend.hip", "attend_k22.hip", "attend_k33.hip", "attend_k44.hip",
-           "attend_k43.hip", "attend_k32.hip", "search.hip"]
+           "attend_k43.hip", "attend_k32.hip", "attend_k88.hip", "search.hip"]
 ARCH = "gfx950"
 
 

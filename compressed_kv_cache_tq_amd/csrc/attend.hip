@@ -146,6 +146,7 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
     case 44: e = split_k44(vkey, qjl, f); break;
     case 43: e = split_k43(vkey, qjl, f); break;
     case 32: e = split_k32(vkey, qjl, f); break;
+    case 88: e = split_k88(vkey, qjl, f); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

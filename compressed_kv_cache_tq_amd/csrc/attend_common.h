@@ -50,5 +50,6 @@ hipError_t split_k33(int vkey, bool qjl, const SplitArgs& f);
 hipError_t split_k44(int vkey, bool qjl, const SplitArgs& f);
 hipError_t split_k43(int vkey, bool qjl, const SplitArgs& f);
 hipError_t split_k32(int vkey, bool qjl, const SplitArgs& f);
+hipError_t split_k88(int vkey, bool qjl, const SplitArgs& f);  // values 2 or 3 bits, no sketch
 
 }  // namespace tq

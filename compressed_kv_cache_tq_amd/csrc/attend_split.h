@@ -63,20 +63,25 @@ __device__ __forceinline__ uint32_t row_bits(const uint32_t* w, int k) {
   return NB == 32 ? v : (v & ((1u << NB) - 1u));
 }
 
-// LDS layout of the replicated pair LUTs (bytes): widths 3 and 2 first, then
-// 4, so every LUT base (at most 20 KiB) fits the immediate offset of the LDS
-// read and the lane-dependent part of the address is one AND-OR.
+// LDS layout of the replicated LUTs (bytes): widths 3 and 2 first, then 4
+// and 8, so every LUT base (at most 20 KiB) fits the immediate offset of the
+// LDS read and the lane-dependent part of the address is one AND-OR.  Widths
+// up to 4 map a code pair (one byte of 4-bit codes) to two fp16 centroids;
+// width 8 maps one code (one byte) to one fp16 centroid in the low half.
 template <int B>
-constexpr int lut_size() { return (1 << (2 * B)) * 256; }
+constexpr int lut_entries() { return B == 8 ? 256 : 1 << (2 * B); }
+template <int B>
+constexpr int lut_size() { return lut_entries<B>() * 256; }
 template <int KLO, int KHI, int VLO, int VHI>
 struct LutPlan {
   static constexpr bool has(int B) { return KLO == B || KHI == B || VLO == B || VHI == B; }
   static constexpr int off3 = 0;
   static constexpr int off2 = off3 + (has(3) ? lut_size<3>() : 0);
   static constexpr int off4 = off2 + (has(2) ? lut_size<2>() : 0);
-  static constexpr int bytes = off4 + (has(4) ? lut_size<4>() : 0);
+  static constexpr int off8 = off4 + (has(4) ? lut_size<4>() : 0);
+  static constexpr int bytes = off8 + (has(8) ? lut_size<8>() : 0);
   template <int B>
-  static constexpr int off() { return B == 4 ? off4 : B == 3 ? off3 : off2; }
+  static constexpr int off() { return B == 8 ? off8 : B == 4 ? off4 : B == 3 ? off3 : off2; }
 };
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
@@ -87,7 +92,14 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
 template <int B>
 __device__ __forceinline__ half8 dequant8(const uint32_t* w, int k, const uint8_t* lut, uint32_t lane4) {
   uint32_t a[4];
-  if constexpr (B == 4) {
+  if constexpr (B == 8) {
+    // one code per byte: codes 8k .. 8k+7 are the bytes of w[2k], w[2k+1]
+    uint32_t c[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      c[p] = lds_u32(lut, __builtin_amdgcn_perm(w[2 * k + (p >> 2)], lane4, 0x0C0C0000u | ((4u + (p & 3)) << 8)));
+    return as_half8(c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16));
+  } else if constexpr (B == 4) {
     const uint32_t v = w[k];
 #pragma unroll
     for (int p = 0; p < 4; ++p) a[p] = __builtin_amdgcn_perm(v, lane4, 0x0C0C0000u | ((4u + p) << 8));
@@ -105,9 +117,11 @@ __device__ __forceinline__ half8 dequant8(const uint32_t* w, int k, const uint8_
   return as_half8(lds_u32(lut, a[0]), lds_u32(lut, a[1]), lds_u32(lut, a[2]), lds_u32(lut, a[3]));
 }
 
-// Registers of one 32-token tile for one lane (two tiles in flight per wave).
+// Registers of one 32-token tile for one lane (two tiles in flight per wave);
+// KWD = dwords of a lane's 32 key codes (8 for 8-bit keys, else 4).
+template <int KWD>
 struct TileRegs {
-  uint32_t kw[2][4];  // K record chunk of token slots mu(0, n), mu(1, n)
+  uint32_t kw[2][KWD];  // K record chunk of token slots mu(0, n), mu(1, n)
   uint32_t vw[8];     // V sub-block (token group j, coordinate group n)
   float4 kn[2];       // K norms of tokens 8j .. 8j+7
   float4 vn[2];       // V norms of tokens 8j .. 8j+7
@@ -162,8 +176,12 @@ __device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+template <int KLO, int KHI>
+constexpr int key_dwords() { return KLO == 8 ? 8 : 4; }
+
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-__device__ __forceinline__ void load_tile(TileRegs& r, uint32_t t0, const StreamRsrc& rs, const LaneOffsets& lo) {
+__device__ __forceinline__ void load_tile(TileRegs<key_dwords<KLO, KHI>()>& r, uint32_t t0, const StreamRsrc& rs,
+                                          const LaneOffsets& lo) {
   constexpr uint32_t KBYTES = 8 * (KLO + KHI);
   constexpr uint32_t VBYTES = 8 * (VLO + VHI);
   constexpr int KW = KLO > KHI ? KLO : KHI;
@@ -536,10 +554,17 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   const float4 qv = tid < G * (D / 4) ? reinterpret_cast<const float4*>(qg)[tid] : float4{};
   // replicated pair LUTs: entry e of width B at off_B + e*256 + replica*4;
   // thread t fills 16-byte chunks t, t + ST, ... from centroids (lo, hi)
-  auto lut_vals = [&](auto bw, uint16_t(&cl)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1],
-                      uint16_t(&ch)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
+  auto lut_vals = [&](auto bw, uint16_t(&cl)[lut_entries<decltype(bw)::value>() * 16 / ST + 1],
+                      uint16_t(&ch)[lut_entries<decltype(bw)::value>() * 16 / ST + 1]) {
     constexpr int B = decltype(bw)::value;
-    if constexpr (LP::has(B)) {
+    if constexpr (LP::has(B) && B == 8) {
+      // (8-bit codes: keys only)
+#pragma unroll
+      for (int r = 0; r * ST < 256 * 16; ++r) {
+        cl[r] = ktab->cen16_8[((threadIdx.x + r * ST) >> 4) & 255];
+        ch[r] = 0;
+      }
+    } else if constexpr (LP::has(B)) {
       const uint16_t* cen = (KLO == B) ? ktab->cen16[0] : (KHI == B) ? ktab->cen16[1]
                           : (VLO == B) ? vtab->cen16[0] : vtab->cen16[1];
       constexpr int E = 1 << (2 * B);
@@ -553,11 +578,11 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       }
     }
   };
-  auto lut_store = [&](auto bw, const uint16_t(&cl)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1],
-                       const uint16_t(&ch)[(1 << (2 * decltype(bw)::value)) * 16 / ST + 1]) {
+  auto lut_store = [&](auto bw, const uint16_t(&cl)[lut_entries<decltype(bw)::value>() * 16 / ST + 1],
+                       const uint16_t(&ch)[lut_entries<decltype(bw)::value>() * 16 / ST + 1]) {
     constexpr int B = decltype(bw)::value;
     if constexpr (LP::has(B)) {
-      constexpr int E = 1 << (2 * B);
+      constexpr int E = lut_entries<B>();
 #pragma unroll
       for (int r = 0; r * ST < E * 16; ++r) {
         const int c = threadIdx.x + r * ST;
@@ -567,7 +592,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
   };
   uint16_t l4l[256 * 16 / ST + 1], l4h[256 * 16 / ST + 1], l3l[64 * 16 / ST + 1], l3h[64 * 16 / ST + 1],
-      l2l[16 * 16 / ST + 1], l2h[16 * 16 / ST + 1];
+      l2l[16 * 16 / ST + 1], l2h[16 * 16 / ST + 1], l8l[256 * 16 / ST + 1], l8h[256 * 16 / ST + 1];
+  lut_vals(std::integral_constant<int, 8>{}, l8l, l8h);
   lut_vals(std::integral_constant<int, 4>{}, l4l, l4h);
   lut_vals(std::integral_constant<int, 3>{}, l3l, l3h);
   lut_vals(std::integral_constant<int, 2>{}, l2l, l2h);
@@ -659,7 +685,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   // loads of the wave's tile k (first token t0): on a paged cache through
   // descriptors over the tile's page, bounded by the split's end; a page id
   // outside the pool reads zeros
-  auto load_at = [&](TileRegs& buf, int k, uint32_t t0) __attribute__((always_inline)) {
+  using TRg = TileRegs<key_dwords<KLO, KHI>()>;
+  auto load_at = [&](TRg& buf, int k, uint32_t t0) __attribute__((always_inline)) {
     if constexpr (!PAGED) {
       load_tile<KLO, KHI, VLO, VHI, QJL>(buf, t0, rs, lo);
     } else {
@@ -686,7 +713,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
   };
 
-  TileRegs bufA, bufB;
+  TRg bufA, bufB;
   load_at(bufA, 0, first);
   load_at(bufB, 1, first + STEP);
 
@@ -705,6 +732,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
   }
   if (tid < G * (D / 4)) reinterpret_cast<float4*>(qraw)[tid] = qv;
+  lut_store(std::integral_constant<int, 8>{}, l8l, l8h);
   lut_store(std::integral_constant<int, 4>{}, l4l, l4h);
   lut_store(std::integral_constant<int, 3>{}, l3l, l3h);
   lut_store(std::integral_constant<int, 2>{}, l2l, l2h);
@@ -838,7 +866,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f32x4{};
 
-  auto tile_step = [&]<bool FULL, bool VSKIP>(const TileRegs& tr, uint32_t t0c) __attribute__((always_inline)) {
+  auto tile_step = [&]<bool FULL, bool VSKIP>(const TRg& tr, uint32_t t0c) __attribute__((always_inline)) {
     // keeps the LDS fragment reads of the sketch variant inside the loop
     if constexpr (QJL) __asm__ volatile("" ::: "memory");
     const int nvalid = FULL ? 8 : static_cast<int>(t_end) - static_cast<int>(t0c + 8 * j);

@@ -280,11 +280,16 @@ double from_half(uint16_t h) {
 tq_status check_spec(const tq_spec* s, tq::Spec* out) {
   if (!s) return fail(TQ_E_ARG, "spec is NULL");
   if (s->d != TQ_DIM) return fail(TQ_E_UNSUPPORTED, "d must be 128");
+  if (s->bits_lo == 8) {
+    // 8-bit keys: uniform width, record layout, no sketch
+    if (s->split != 128 || s->layout != TQ_LAYOUT_RECORD || s->qjl_m != 0)
+      return fail(TQ_E_UNSUPPORTED, "8-bit codes need split 128, the record layout and no sketch");
+  }
   auto okb = [](int b) { return b >= 2 && b <= 4; };
-  if (!okb(s->bits_lo)) return fail(TQ_E_UNSUPPORTED, "bits_lo must be 2, 3 or 4");
+  if (!okb(s->bits_lo) && s->bits_lo != 8) return fail(TQ_E_UNSUPPORTED, "bits_lo must be 2, 3, 4 or 8");
   if (s->split != 64 && s->split != 128) return fail(TQ_E_UNSUPPORTED, "split must be 64 or 128");
   const int bhi = s->split == 128 ? s->bits_lo : s->bits_hi;
-  if (!okb(bhi)) return fail(TQ_E_UNSUPPORTED, "bits_hi must be 2, 3 or 4");
+  if (!okb(bhi) && bhi != 8) return fail(TQ_E_UNSUPPORTED, "bits_hi must be 2, 3 or 4");
   const int bl = s->bits_lo;
   const bool combo_ok = (bl == bhi) || (bl == 4 && bhi == 3) || (bl == 3 && bhi == 2);
   if (!combo_ok) return fail(TQ_E_UNSUPPORTED, "mixed widths supported: 4/3 and 3/2 (split 64)");
@@ -328,9 +333,14 @@ tq_status hip_status(hipError_t e, const char* where) {
 // edge up into the next cell; the code stays exact if no boundary lies in
 // that sliver below an edge.  Fails if a cell holds two boundaries or a
 // boundary sits within 1e-6 below an edge.
-bool cell_table(const float* bnd, int nb, uint32_t (*cell)[2]) {
-  for (int c = 0; c < tq::CELL_ENTRIES; ++c) {
-    const double lo = c / 64.0 - 1.0, hi = (c + 1) / 64.0 - 1.0;
+// Cell c covers [c / scale - offset, (c + 1) / scale - offset); false when a
+// cell holds two boundaries or a boundary lies less than `margin` below a
+// cell edge (the kernels' fp32 cell index fma(y, scale, scale * offset) can
+// round such a y across the edge: by at most 2^-25 at both scales used).
+bool cell_table(const float* bnd, int nb, uint32_t (*cell)[2], int entries = tq::CELL_ENTRIES, double scale = 64.0,
+                double offset = 1.0, double margin = 1e-6) {
+  for (int c = 0; c < entries; ++c) {
+    const double lo = c / scale - offset, hi = (c + 1) / scale - offset;
     uint32_t below = 0, inside = 0;
     float b_in = INFINITY;
     for (int j = 0; j < nb; ++j) {
@@ -340,7 +350,7 @@ bool cell_table(const float* bnd, int nb, uint32_t (*cell)[2]) {
         ++inside;
         b_in = bnd[j];
       }
-      if (t < lo && lo - t < 1e-6) return false;
+      if (t < lo && lo - t < margin) return false;
     }
     if (inside > 1) return false;
     uint32_t bits;
@@ -423,6 +433,18 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
       const int b = t->bits[h], L = 1 << b;
       std::vector<double> c(L), bd(L - 1);
       codebook_build(tq::D, b, c.data(), bd.data());
+      if (b == 8) {
+        if (h == 1) break;  // uniform width: one codebook
+        for (int j = 0; j < 256; ++j) {
+          t->bnd8[j] = j < 255 ? static_cast<float>(bd[j]) : INFINITY;
+          t->cen8[j] = static_cast<float>(c[j]);
+          t->cen16_8[j] = to_half(c[j]);
+        }
+        if (!(bd[0] > -0.5 && bd[254] < 0.5) ||
+            !cell_table(t->bnd8, 255, t->cell8, tq::CELL8_ENTRIES, tq::CELLS8, 0.5, 1e-7))
+          return fail(TQ_E_UNSUPPORTED, "8-bit codebook boundaries too close for the code cell table");
+        break;
+      }
       for (int j = 0; j < 16; ++j) {
         t->bnd[h][j] = j < L - 1 ? static_cast<float>(bd[j]) : INFINITY;
         t->cen[h][j] = j < L ? static_cast<float>(c[j]) : 0.0f;
@@ -502,6 +524,7 @@ tq_status tq_ip_scores(const tq_spec* spec, const void* tables, const tq_cache* 
   tq::Spec sp;
   if (tq_status st = check_spec(spec, &sp); st != TQ_OK) return st;
   if (sp.layout != TQ_LAYOUT_RECORD) return fail(TQ_E_UNSUPPORTED, "search needs the record layout");
+  if (sp.bits_lo == 8) return fail(TQ_E_UNSUPPORTED, "search takes codes of at most 4 bits");
   if (tq_status st = check_tables(tables, sp, "search"); st != TQ_OK) return st;
   if (!db) return fail(TQ_E_ARG, "db is NULL");
   if (n_streams < 0 || n_tok < 0) return fail(TQ_E_ARG, "negative n_streams or n_tok");
@@ -632,6 +655,9 @@ tq_status attend_checked(const tq_spec* ks, const void* ktables, const tq_cache*
   if (ksp.layout != TQ_LAYOUT_RECORD) return fail(TQ_E_UNSUPPORTED, "keys must use the record layout");
   if (vsp.layout != TQ_LAYOUT_TILED) return fail(TQ_E_UNSUPPORTED, "values must use the tiled layout");
   if (vsp.qjl_m) return fail(TQ_E_UNSUPPORTED, "values carry no QJL sketch");
+  if (vsp.bits_lo == 8) return fail(TQ_E_UNSUPPORTED, "8-bit codes are for keys (record layout)");
+  if (ksp.bits_lo == 8 && !(vsp.bits_lo == vsp.bits_hi && (vsp.bits_lo == 2 || vsp.bits_lo == 3)))
+    return fail(TQ_E_UNSUPPORTED, "8-bit keys decode with values of 2 or 3 bits (uniform)");
   if (tq_status st = check_tables(ktables, ksp, "key"); st != TQ_OK) return st;
   if (tq_status st = check_tables(vtables, vsp, "value"); st != TQ_OK) return st;
   if (!attn || !kc || !vc) return fail(TQ_E_ARG, "attn, kc and vc must be non-NULL");

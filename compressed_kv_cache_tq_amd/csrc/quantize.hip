@@ -675,10 +675,35 @@ __device__ __forceinline__ void cell_codes(YF yof, int p0, const uint2* cells, u
   for (int i = 0; i < N; ++i) c[i] = e[i].y + (y[i] > __uint_as_float(e[i].x) ? 1u : 0u);
 }
 
+// N 8-bit codes of run positions p0 .. p0+N-1 from the 8-bit cell table
+// (1024 cells over [-1/2, 1/2]; beyond it the end cells give 0 and 255)
+template <int N, typename YF>
+__device__ __forceinline__ void cell_codes8(YF yof, int p0, const uint2* cells, uint32_t (&c)[N]) {
+  float y[N];
+  uint2 e[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) y[i] = yof(p0 + i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float f = __builtin_amdgcn_fmed3f(fmaf(y[i], 1024.0f, 512.0f), 0.0f, 1024.0f);
+    e[i] = cells[static_cast<uint32_t>(f)];
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) c[i] = e[i].y + (y[i] > __uint_as_float(e[i].x) ? 1u : 0u);
+}
+
 // 32 codes of y(0..31) packed LSB-first into B dwords
 template <int B, typename YF>
 __device__ __forceinline__ void code_run(YF yof, const uint2* cells, uint32_t* w) {
-  if constexpr (B == 4) {
+  if constexpr (B == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t c[8];
+      cell_codes8<8>(yof, 8 * k, cells, c);
+      w[2 * k] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      w[2 * k + 1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    }
+  } else if constexpr (B == 4) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t c[8];
@@ -722,6 +747,9 @@ __device__ __forceinline__ void code_run(YF yof, const uint2* cells, uint32_t* w
 template <int BLO, int BHI, bool F32IN, bool TILED, int K, bool MERGE, bool PAGED>
 __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   static_assert(!MERGE || TILED, "only the tiled layout merges");
+  // 8-bit codes: uniform width, record layout, their own cell table
+  constexpr bool B8 = BLO == 8;
+  static_assert(!B8 || (BHI == 8 && !TILED), "8-bit codes: uniform width, record layout");
   const Tables* __restrict__ tab = A.tab;
   constexpr int XP = F32IN ? 2 : 1;          // fp16 parts of x
   constexpr int ES = F32IN ? 4 : 2;          // input element bytes
@@ -729,7 +757,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
   __shared__ uint4 xbuf[2][2][XP][8 * 64];   // [pair][buffer][part][ks * 64 + lane]
   __shared__ float inv_s[2][2][32];          // [pair][buffer][vector]: 1 / (norm 2^(sh+8))
-  __shared__ uint2 cell_s[2][CELL_ENTRIES];
+  __shared__ uint2 cell_s[B8 ? 1 : 2][B8 ? CELL8_ENTRIES : CELL_ENTRIES];
   __shared__ uint4 pil1_s[2][8][64];         // low parts of the t = 1 fragments: [w][ks][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -740,10 +768,14 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
 
   // cell tables: loaded first, stored to LDS once the first tile is staged
   // (a store right here would hold back every later load behind this one)
-  static_assert(2 * CELL_ENTRIES <= 2 * RQ_THREADS, "cell table fill");
-  const uint2* cell_g = reinterpret_cast<const uint2*>(tab->cell);
-  const uint2 cv0 = cell_g[tid];
-  const uint2 cv1 = tid + RQ_THREADS < 2 * CELL_ENTRIES ? cell_g[tid + RQ_THREADS] : uint2{};
+  constexpr int NCE = B8 ? CELL8_ENTRIES : 2 * CELL_ENTRIES;  // cell entries
+  constexpr int CPT = (NCE + RQ_THREADS - 1) / RQ_THREADS;      // per thread
+  static_assert(B8 || CPT == 2, "cell table fill");
+  const uint2* cell_g = reinterpret_cast<const uint2*>(B8 ? &tab->cell8[0][0] : &tab->cell[0][0][0]);
+  uint2 cv[CPT];
+  cv[0] = cell_g[tid];
+#pragma unroll
+  for (int i = 1; i < CPT; ++i) cv[i] = tid + i * RQ_THREADS < NCE ? cell_g[tid + i * RQ_THREADS] : uint2{};
 
   // ---- rotation fragments of this wave's 64 coordinates, for the whole
   // launch (stored in fragment order: each load is a contiguous 1 KiB).
@@ -927,8 +959,10 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   }
   stage(first, X[0], 0);
   if (K > 3) load_x(first + 3, X[0]);
-  reinterpret_cast<uint2*>(cell_s)[tid] = cv0;
-  if (tid + RQ_THREADS < 2 * CELL_ENTRIES) reinterpret_cast<uint2*>(cell_s)[tid + RQ_THREADS] = cv1;
+  reinterpret_cast<uint2*>(cell_s)[tid] = cv[0];
+#pragma unroll
+  for (int i = 1; i < CPT; ++i)
+    if (tid + i * RQ_THREADS < NCE) reinterpret_cast<uint2*>(cell_s)[tid + i * RQ_THREADS] = cv[i];
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -975,15 +1009,21 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
       const float inv = inv_s[pair][b][l32];
       const __amdgpu_buffer_rsrc_t rc =
           rsrc(sbase + to.p * CODE_BYTES, to.ok ? static_cast<int64_t>(a.nv) * CODE_BYTES : 0);
-      uint32_t wd[4];
+      uint32_t wd[B8 ? 8 : 4];
       auto yv = [&](int p) { return acc[p >> 4][p & 15] * inv; };
       auto put = [&](auto bw, int off) {
         constexpr int BW = decltype(bw)::value;
         // (slots before lo: past the extent, dropped)
         const int o = !PAGED || l32 >= a.lo ? l32 * CODE_BYTES + off : RQ_OOB;
-        if constexpr (BW == 4) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0)),
-                                                                    make_uint4(wd[0], wd[1], wd[2], wd[3])), rc, o, 0, 0);
+        using V4 = decltype(__builtin_amdgcn_raw_buffer_load_b128(rc, 0, 0, 0));
+        if constexpr (BW == 8) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V4, make_uint4(wd[0], wd[1], wd[2], wd[3])), rc, o,
+                                                 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V4, make_uint4(wd[4], wd[5], wd[6], wd[7])), rc,
+                                                 o + 16, 0, 0);
+        } else if constexpr (BW == 4) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V4, make_uint4(wd[0], wd[1], wd[2], wd[3])), rc, o,
+                                                 0, 0);
         } else if constexpr (BW == 2) {
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(rc, 0, 0, 0)),
                                                                    make_uint2(wd[0], wd[1])), rc, o, 0, 0);
@@ -997,7 +1037,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
         code_run<BLO>(yv, cell_s[0], wd);
         put(std::integral_constant<int, BLO>{}, w == 0 ? 4 * BLO * h : 8 * BLO + 4 * BLO * h);
       } else {
-        code_run<BHI>(yv, cell_s[1], wd);
+        code_run<BHI>(yv, cell_s[B8 ? 0 : 1], wd);
         put(std::integral_constant<int, BHI>{}, 8 * BLO + 4 * BHI * h);
       }
     } else {
@@ -1215,8 +1255,11 @@ hipError_t launch_rotq(const Tables* tab, const void* x, const QSeq* seqs, int64
   }
   // 32-bit tile, position and stream arithmetic, and buffer offsets below RQ_OOB
   if (all + 16 * 1024 >= (int64_t{1} << 31) || 32 * xrs * ES >= RQ_OOB || c.cap >= (int64_t{1} << 31) - 64 ||
-      streams >= (int64_t{1} << 31))
-    return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+      streams >= (int64_t{1} << 31)) {
+    // (8-bit codes have no general-kernel path)
+    if constexpr (BLO == 8) return hipErrorNotSupported;
+    else return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+  }
   auto run = [&](auto pg) {
     constexpr bool P = decltype(pg)::value;
     hipError_t e = launch_rotq_list<BLO, BHI, F32IN, TILED, false, P>(tab, x, whole, hkv, xss, xrs, c, pm, st);
@@ -1258,6 +1301,9 @@ hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const v
     case 44: return dispatch_layout<4, 4>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
     case 43: return dispatch_layout<4, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
     case 32: return dispatch_layout<3, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    case 88:  // 8-bit keys: record layout, no sketch (checked on the host)
+      return dtype == TQ_F32 ? launch_rotq<8, 8, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
+                             : launch_rotq<8, 8, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,6 +17,8 @@ constexpr int QJL_M = TQ_QJL_M;
 constexpr uint32_t TABLES_MAGIC = 0x31515454u;  // "TTQ1"
 constexpr int CELLS = 128;        // cells of the code table over [-1, 1]
 constexpr int CELL_ENTRIES = 132; // CELLS + 1, padded
+constexpr int CELLS8 = 1024;        // cells of the 8-bit code table over [-1/2, 1/2]
+constexpr int CELL8_ENTRIES = 1028; // CELLS8 + 1, padded
 
 // Device tables of one tq_spec, built on the host by tq_tables_build.
 //
@@ -63,6 +65,15 @@ struct alignas(256) Tables {
   // [layout (record, tiled)][hi, lo][w][t][ks][lane][8], the 8 values of
   // row frag_row(layout, w, t, lane), columns 16 ks + 8 (lane / 32) + e.
   uint16_t pi_frag[2][2][D * D];
+  // The 8-bit codebook (keys: uniform width, record layout, no sketch; the
+  // arrays above then hold nothing): boundaries padded with +inf, centroids
+  // in fp32 and fp16, and its cell table over [-1/2, 1/2] (every boundary
+  // lies inside): y falls in cell clamp(floor(1024 (y + 1/2)), 0, 1024),
+  // entries as in `cell`.
+  float bnd8[256];
+  float cen8[256];
+  uint16_t cen16_8[256];
+  uint32_t cell8[CELL8_ENTRIES][2];
 };
 
 // Row of 256 Pi held by lane `lane` (of wave w of a pair, M-block t) in the

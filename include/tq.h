@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define TQ_FORMAT_VERSION 1   /* bit layouts described at tq_cache below */
+#define TQ_FORMAT_VERSION 2   /* bit layouts described at tq_cache below; 2: 8-bit keys */
 #define TQ_DIM 128            /* head dimension d supported by the kernels */
 #define TQ_TILE_TOKENS 32     /* tokens per tile of the tiled layout */
 #define TQ_IP_MAX_QUERIES 64  /* queries per tq_ip_scores call */
@@ -71,7 +71,11 @@ typedef enum {
  * Rotated coordinates [0, split) use bits_lo bits, [split, d) use bits_hi
  * (noze.it page, section "Il metodo TurboQuant, in breve": 3.5 and 2.5 bits
  * per channel; 3.5 bits = split 64 with 4 and 3 bits).  split == d means a
- * uniform width and bits_hi is then ignored. */
+ * uniform width and bits_hi is then ignored.  8-bit codes (the K8 keys of
+ * the K8/V3 default that section "Cosa aggiunge turboquant-mlx" of the same
+ * page names) need split == d, the record layout and no sketch; quantize
+ * and decode take them for keys (with values of 2, 3 or 4 bits, uniform),
+ * tq_ip_scores does not. */
 /* How the rotation Pi is drawn from rot_seed. */
 typedef enum {
   TQ_ROT_HAAR = 0,      /* Haar-distributed orthogonal matrix (tq_rotation_build) */
@@ -80,7 +84,7 @@ typedef enum {
 
 typedef struct {
   int32_t d;          /* must be TQ_DIM */
-  int32_t bits_lo;    /* 2, 3 or 4 */
+  int32_t bits_lo;    /* 2, 3, 4 or 8 (see above) */
   int32_t bits_hi;    /* 2, 3 or 4 (ignored when split == d) */
   int32_t split;      /* 64 or 128 */
   int32_t qjl_m;      /* 0 (no sketch) or TQ_QJL_M; only with TQ_LAYOUT_RECORD */

@@ -158,3 +158,23 @@ def test_attend_full_size_sampled(name):
         bs = sorted(set(rng.integers(0, run.B, 3).tolist()))
         heads = [(b, h) for b in bs for h in rng.choice(wl.hq, 8, replace=False).tolist()]
     _check(run, heads=heads, label=f"{name} full")
+
+
+@pytest.mark.parametrize("vbits,batch,sink,ctx", [(3, 2, 0, 1111), (2, 5, 128, 0), (3, 1, 0, 3000)])
+def test_attend_eight_bit_keys(vbits, batch, sink, ctx):
+    """8-bit keys (K8) with 3- or 2-bit values: uniform and ragged batches,
+    sink and V-skip; the oracle reads the GPU's 8-bit codes."""
+    print(f"[attend] K8 V{vbits} batch={batch} sink={sink} ctx={ctx}", flush=True)
+    wl = workloads.Workload(f"k8v{vbits}", batch, 32, 8, "bf16", workloads.QSpec(8, 8), workloads.QSpec(vbits, vbits),
+                            ctx=ctx, lens_range=() if ctx else (sink + 1, 1500), sink=sink,
+                            v_skip=1e-6 if sink else 0.0, structure="outlier_channels" if not sink else "plain")
+    _check(Run(workloads.generate(wl)), label=f"K8 V{vbits}")
+
+
+def test_attend_eight_bit_keys_full_gqa_shape():
+    """The gqa_decode shape (8 KV heads x 32768 tokens, 32 query heads) with
+    K8/V3, full output against the oracle."""
+    print("[attend] K8/V3 at the gqa_decode shape", flush=True)
+    inp = workloads.generate("gqa_decode")
+    inp.wl = dataclasses.replace(inp.wl, k=workloads.QSpec(8, 8))
+    _check(Run(inp), label="K8/V3 gqa shape")

@@ -240,3 +240,32 @@ def test_paged_prefill_then_token_by_token_appends(qjl):
                            hkv=H, block_table=btd, n_pages=n_pages, max_len=run.max_len)
     T.cuda.synchronize()
     assert T.equal(out, run.out)
+
+
+def test_paged_eight_bit_keys():
+    """K8/V3 through the paged quantize (record tiles split at page and
+    chunk edges) and the paged decode: equal to the contiguous path."""
+    print("[paged] K8/V3", flush=True)
+    T = torch()
+    wl = workloads.Workload("pagedk8", 3, 16, 4, "bf16", workloads.QSpec(8, 8), workloads.QSpec(3, 3),
+                            lens_range=(100, 700))
+    run = Run(workloads.generate(wl))
+    run.quantize()
+    run.attend()
+    T.cuda.synchronize()
+    comp = [int(v) for v in run.inp.seq_lens]
+    n_pages = sum(-(-c // P) for c in comp) + 1
+    bt = _tables(run.B, comp, n_pages, seed=4)
+    kpool, vpool, _ = _paged_quantize(run, bt, n_pages, 45)
+    for b in range(run.B):
+        for h in range(4):
+            for lp in range(-(-comp[b] // P)):
+                n = min(P, comp[b] - lp * P)
+                ps, s = int(bt[b, lp]) * 4 + h, b * 4 + h
+                assert np.array_equal(read_codes(run.kspec, kpool, ps, n), read_codes(run.kspec, run.kc, s, n, lp * P))
+                assert np.array_equal(read_norms(kpool, ps, n), read_norms(run.kc, s, n, lp * P))
+    out = T.empty_like(run.q)
+    tq.attend_decode_paged(run.kspec, run.ktab, kpool, run.vspec, run.vtab, vpool, run.q, run.seq_lens, out, run.ws,
+                           hkv=4, block_table=T.from_numpy(bt).cuda(), n_pages=n_pages, max_len=run.max_len)
+    T.cuda.synchronize()
+    assert T.equal(out, run.out)

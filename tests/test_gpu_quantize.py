@@ -4,6 +4,7 @@ import pytest
 
 from compressed_kv_cache_tq_amd import tq, workloads
 from gpu_helpers import check_quantized, read_codes, read_norms, read_signs, to_device, torch
+from oracle import pack as opk
 
 pytestmark = pytest.mark.gpu
 
@@ -312,3 +313,46 @@ def test_quantize_hadamard_rotation(w, layout):
     check_quantized(spec, x[0], read_codes(spec, cache, 0, 1000), read_norms(cache, 0, 1000), label=f"hadamard {w}")
     check_quantized(spec, y[0], read_codes(spec, cache, 0, 37, 1003), read_norms(cache, 0, 37, 1003),
                     label=f"hadamard append {w}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_eight_bit_keys(dtype):
+    """8-bit keys (record layout, 1024-cell code table): 1000 vectors (a
+    ragged tail), then three streams written from position 37 with zero
+    vectors among them."""
+    print(f"[quantize] 8-bit keys dtype={dtype}", flush=True)
+    spec = tq.Spec(8)
+    n = 1000
+    x = _data(n, seed=88, dtype=dtype)
+    cache = _quantize(spec, x, dtype)
+    check_quantized(spec, x[0], read_codes(spec, cache, 0, n), read_norms(cache, 0, n), label=f"8-bit {dtype}")
+    x = np.random.default_rng(89).standard_normal((3, 70, 128), dtype=np.float32)
+    x[1, 5] = 0.0
+    if dtype == "bf16":
+        x = workloads.bf16_to_f32(workloads.bf16_bits(x))
+    cache = _quantize(spec, x, dtype, cap=160, tok0=37)
+    for s in range(3):
+        check_quantized(spec, x[s], read_codes(spec, cache, s, 70, 37), read_norms(cache, s, 70, 37),
+                        label=f"8-bit stream {s}")
+    # a zero vector: norm 0, y = 0, code 127 (the 127 negative boundaries lie
+    # below 0; the middle boundary is 0 itself, not below)
+    assert read_norms(cache, 1, 1, 42)[0] == 0.0
+    assert np.all(read_codes(spec, cache, 1, 1, 42) == 127)
+
+
+def test_quantize_eight_bit_full_size_sampled():
+    """The gqa_decode key tensor (8 x 32768 bf16 vectors with outlier
+    channels) at 8 bits in one launch; sampled vectors against the oracle."""
+    print("[quantize] 8-bit keys, full gqa_decode key tensor", flush=True)
+    inp = workloads.generate("gqa_decode")
+    spec = tq.Spec(8)
+    xk = np.asarray(inp.k[0])                    # [8, 32768, 128]
+    n = xk.shape[1]
+    cache = _quantize(spec, xk, "bf16")
+    codes = cache.codes.cpu().numpy().reshape(8, n, 128)
+    norms = cache.norms.cpu().numpy().reshape(8, n)
+    rng = np.random.default_rng(3)
+    for s in range(8):
+        rows = np.sort(rng.choice(n, 200, replace=False))
+        idx = opk.unpack_records(codes[s, rows], spec.widths)
+        check_quantized(spec, xk[s, rows], idx, norms[s, rows], label=f"8-bit full stream {s}")

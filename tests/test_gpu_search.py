@@ -97,3 +97,15 @@ def test_ip_scores_full_size_sampled():
         err = parity.rel_l2(cols, ref)
         print(f"[search]   stream {s} tokens {t0}..: rel_l2={err:.3e}", flush=True)
         assert err <= parity.ATTN_REL_L2
+
+
+def test_search_rejects_eight_bit_codes():
+    """Search takes codes of at most 4 bits: an 8-bit spec is refused before
+    any launch."""
+    spec = tq.Spec(8)
+    tab = tq.device_tables(spec)
+    cache = tq.alloc_cache(spec, 1, 64)
+    q = torch().zeros((1, 128), dtype=torch().float32, device="cuda")
+    scores = torch().empty((1, 64), dtype=torch().float32, device="cuda")
+    with pytest.raises(tq.TqError):
+        tq.ip_scores(spec, tab, cache, q, n_streams=1, n_tok=64, scores=scores, workspace=tq.alloc_ip_workspace())

@@ -33,7 +33,7 @@ def test_d3_is_uniform_quantizer(bits):
     assert cbm.mse(cb) == pytest.approx((2.0 / L) ** 2 / 12.0, rel=1e-10)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_fixed_point_conditions_by_quadrature(bits):
     # Centroid condition checked with adaptive quadrature, independent of the
     # closed-form mass / first moment used by the iteration.
@@ -101,3 +101,19 @@ def test_mse_identity_with_centroid_energy():
         edges = np.concatenate(([-1.0], cb.boundaries, [1.0]))
         P = cbm.cell_mass(edges[:-1], edges[1:], 128)
         assert cbm.distortion(cb) == pytest.approx(1 - 128 * np.sum(P * cb.centroids ** 2), rel=1e-9)
+
+
+def test_eight_bit_distortion_matches_high_resolution_formula():
+    """At 256 levels the optimum approaches the Panter-Dite high-resolution
+    distortion (1 / (12 L^2)) (integral of f^(1/3))^3 per coordinate (Panter
+    and Dite 1951; Gersho and Gray, "Vector Quantization and Signal
+    Compression", section 6.3), evaluated here by quadrature of the
+    coordinate density; the iteration never sees this formula."""
+    d, L = 128, 256
+    g = integrate.quad(lambda x: cbm.density(x, d) ** (1.0 / 3.0), -1, 1, epsabs=0, epsrel=1e-12, limit=400)[0]
+    pd = g ** 3 / (12 * L * L)
+    cb = cbm.lloyd_max(d, 8)
+    assert cbm.distortion(cb) == pytest.approx(d * pd, rel=0.01)
+    # and a quarter of the 7-bit distortion, as the formula's 4^-b scaling says
+    ratio = cbm.distortion(cbm.lloyd_max(d, 7)) / cbm.distortion(cb)
+    assert 3.9 < ratio < 4.1
