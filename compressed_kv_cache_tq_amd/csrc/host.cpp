@@ -178,6 +178,10 @@ struct CoordLaw {
     return ibeta(a, a, 0.5 * (1.0 - x));
   }
   double mass(double lo, double hi) const { return upper_tail(lo) - upper_tail(hi); }
+  double density(double x) const {
+    const double t = 1.0 - x * x;
+    return t <= 0.0 ? 0.0 : kd * std::pow(t, 0.5 * (d - 3));
+  }
   double moment(double lo, double hi) const {
     const double p = 0.5 * (d - 1);
     auto g = [p](double x) { const double t = 1.0 - x * x; return t <= 0.0 ? 0.0 : std::pow(t, p); };
@@ -204,7 +208,10 @@ void codebook_build(int d, int bits, double* cen, double* bnd) {
   for (int j = 0; j < L; ++j) c[j] = law.moment(e[j], e[j + 1]) / law.mass(e[j], e[j + 1]);
   double best = INFINITY;
   int stall = 0;
-  for (int it = 0; it < 200000; ++it) {
+  // Above 16 levels the Lloyd map contracts slowly (tens of thousands of
+  // steps at 256 levels): a few hundred steps, then Newton below.
+  const int lloyd_steps = L > 16 ? 300 : 200000;
+  for (int it = 0; it < lloyd_steps; ++it) {
     for (int j = 1; j < L; ++j) e[j] = 0.5 * (c[j - 1] + c[j]);
     std::vector<double> cn(L);
     for (int j = 0; j < L; ++j) cn[j] = law.moment(e[j], e[j + 1]) / law.mass(e[j], e[j + 1]);
@@ -217,6 +224,65 @@ void codebook_build(int d, int bits, double* cen, double* bnd) {
     if (step < 1e-15) break;
     if (step < best) { best = step; stall = 0; }
     else if (++stall > 50 && step < 1e-13) break;
+  }
+  if (L > 16) {
+    // Newton on the fixed-point conditions G_k = e_k - (c_{k-1} + c_k) / 2 = 0
+    // over the interior edges e_1 .. e_{L-1}, c_j the centroid of [e_j,
+    // e_{j+1}].  With P_j the cell mass and f the density,
+    // dc_j/de_{j+1} = f(e_{j+1}) (e_{j+1} - c_j) / P_j and
+    // dc_j/de_j = f(e_j) (c_j - e_j) / P_j, so the Jacobian is tridiagonal
+    // (Thomas algorithm); steps are halved while they do not reduce max |G|.
+    for (int j = 1; j < L; ++j) e[j] = 0.5 * (c[j - 1] + c[j]);
+    std::vector<double> P(L), G(L), lo_d(L), di(L), up_d(L), rhs(L), en(L + 1);
+    auto eval = [&](const std::vector<double>& ed, std::vector<double>& cc, std::vector<double>& pp,
+                    std::vector<double>& gg) {
+      double gmax = 0.0;
+      for (int j = 0; j < L; ++j) {
+        pp[j] = law.mass(ed[j], ed[j + 1]);
+        cc[j] = law.moment(ed[j], ed[j + 1]) / pp[j];
+      }
+      for (int k = 1; k < L; ++k) {
+        gg[k] = ed[k] - 0.5 * (cc[k - 1] + cc[k]);
+        gmax = std::fmax(gmax, std::fabs(gg[k]));
+      }
+      return gmax;
+    };
+    std::vector<double> cc(L), pp(L), gg(L);
+    double g = eval(e, c, P, G);
+    for (int it = 0; it < 50 && g > 1e-17; ++it) {
+      for (int k = 1; k < L; ++k) {
+        const double fk = law.density(e[k]);
+        di[k] = 1.0 - 0.5 * fk * ((e[k] - c[k - 1]) / P[k - 1] + (c[k] - e[k]) / P[k]);
+        lo_d[k] = k > 1 ? -0.5 * law.density(e[k - 1]) * (c[k - 1] - e[k - 1]) / P[k - 1] : 0.0;
+        up_d[k] = k < L - 1 ? -0.5 * law.density(e[k + 1]) * (e[k + 1] - c[k]) / P[k] : 0.0;
+        rhs[k] = G[k];
+      }
+      for (int k = 2; k < L; ++k) {  // forward elimination
+        const double m = lo_d[k] / di[k - 1];
+        di[k] -= m * up_d[k - 1];
+        rhs[k] -= m * rhs[k - 1];
+      }
+      rhs[L - 1] /= di[L - 1];
+      for (int k = L - 2; k >= 1; --k) rhs[k] = (rhs[k] - up_d[k] * rhs[k + 1]) / di[k];
+      double lam = 1.0, gn = INFINITY;
+      for (int h = 0; h < 30; ++h, lam *= 0.5) {
+        en = e;
+        for (int k = 1; k < L; ++k) en[k] = e[k] - lam * rhs[k];
+        bool ordered = true;
+        for (int k = 0; k < L; ++k) ordered = ordered && en[k] < en[k + 1];
+        if (!ordered) continue;
+        gn = eval(en, cc, pp, gg);
+        if (gn < g) break;
+      }
+      if (!(gn < g)) break;  // at the rounding floor
+      e = en;
+      c = cc;
+      P = pp;
+      G = gg;
+      g = gn;
+    }
+    for (int j = 0; j < L; ++j) cc[j] = 0.5 * (c[j] - c[L - 1 - j]);  // the law is symmetric about 0
+    c = cc;
   }
   for (int j = 0; j < L - 1; ++j) t[j] = 0.5 * (c[j] + c[j + 1]);
   if (L % 2 == 0) t[L / 2 - 1] = 0.0;

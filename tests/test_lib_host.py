@@ -36,9 +36,11 @@ def test_exports_match_header():
 def test_codebook_matches_oracle(d, bits):
     c, t = tq.codebook_build(d, bits)
     cb = ocb.lloyd_max(d, bits)
-    # With 256 levels the Lloyd map contracts slowly: both iterations stop
-    # (step < 1e-15, or stalled below 1e-13) about 1e-11 from the fixed point.
-    tol = 1e-12 if bits < 8 else 1e-10
+    # With 256 levels the Lloyd map contracts by only ~3e-5 per step: the
+    # oracle's iteration ends by its stall rule ~3e-10 from the fixed point
+    # that the library reaches with Newton steps (further Lloyd steps move
+    # the oracle's codebook toward the library's).
+    tol = 1e-12 if bits < 8 else 1e-9
     assert np.max(np.abs(c - cb.centroids)) <= tol
     assert np.max(np.abs(t - cb.boundaries)) <= tol
 
@@ -214,7 +216,7 @@ def test_eight_bit_tables_and_cell_rule():
     code = below + (y > the cell's boundary)) gives the count of boundaries
     below y for random, extreme and boundary-adjacent fp32 values."""
     bnd8, cen8, cen16_8, cells = _eight_bit_view(tq.Spec(8))
-    c, t = tq.codebook_build(128, 8)      # (within 1e-10 of the oracle's, above)
+    c, t = tq.codebook_build(128, 8)      # (within 1e-9 of the oracle's, above)
     b32 = t.astype(np.float32)
     assert np.array_equal(bnd8[:255], b32) and np.isinf(bnd8[255])
     assert np.array_equal(cen8, c.astype(np.float32))
