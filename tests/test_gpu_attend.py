@@ -178,3 +178,24 @@ def test_attend_eight_bit_keys_full_gqa_shape():
     inp = workloads.generate("gqa_decode")
     inp.wl = dataclasses.replace(inp.wl, k=workloads.QSpec(8, 8))
     _check(Run(inp), label="K8/V3 gqa shape")
+
+
+def test_attend_per_layer_policies_share_one_workspace():
+    """Per-layer K/V policies are chosen by the caller, one spec per call:
+    three layers (K4/V2, K4/V4 as for a protected boundary layer, K8/V3)
+    decode in turn on one workspace, each within the bound of its oracle."""
+    print("[attend] per-layer policies on one workspace", flush=True)
+    T = torch()
+    ws = None
+    runs = []
+    for li, (kq, vq) in enumerate([(workloads.QSpec(4, 4), workloads.QSpec(2, 2)),
+                                   (workloads.QSpec(4, 4), workloads.QSpec(4, 4)),
+                                   (workloads.QSpec(8, 8), workloads.QSpec(3, 3))]):
+        wl = workloads.Workload(f"layer{li}", 2, 16, 4, "bf16", kq, vq, ctx=900, seed=li)
+        run = Run(workloads.generate(wl))
+        ws = run.ws if ws is None else ws
+        run.ws = ws
+        runs.append(run)
+    for run in runs:
+        _check(run, label=f"layer {run.wl.name}")
+    T.cuda.synchronize()

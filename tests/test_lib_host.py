@@ -409,3 +409,13 @@ def test_attend_argument_errors_without_launch():
     ws = tq.attend_workspace_bytes(2, 32, 8, 0, 32768)
     assert ws >= 2 * 32 * (2 * 128 + 4) * 4
     assert ws % 4 == 0
+
+
+def test_paged_binding_wants_a_device_table_tensor():
+    """The paged quantize reads its block table on the device: the binding
+    refuses a host array (or a table of the wrong shape or type) before any
+    call into the library."""
+    torch = pytest.importorskip("torch")
+    for bt in (np.zeros((2, 4), np.int32), torch.zeros((2, 4), dtype=torch.int64), torch.zeros((3, 4), dtype=torch.int32)):
+        with pytest.raises(ValueError):
+            tq.quantize_kv_paged(tq.Spec(4), None, None, None, hkv=2, n_tok=[1, 1], block_table=bt, n_pages=8)
