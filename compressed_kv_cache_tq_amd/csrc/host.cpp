@@ -640,6 +640,9 @@ tq_status check_quantize_arrays(const tq::Spec& sp, int32_t dtype, const void* x
   if (x_row_stride < tq::D && max_tok > 1) return fail(TQ_E_ARG, "x_row_stride smaller than d");
   if (!aligned(cache->codes, 16) || !aligned(cache->norms, 4))
     return fail(TQ_E_ARG, "codes must be 16-byte and norms 4-byte aligned");
+  // 8-bit codes run only in the register-resident kernel (32-bit offsets)
+  if (sp.bits_lo == 8 && (32 * x_row_stride * es >= (int64_t{1} << 30) || cache->cap >= (int64_t{1} << 31) - 64))
+    return fail(TQ_E_UNSUPPORTED, "8-bit codes: x_row_stride * 32 rows must stay below 2^30 bytes and cap below 2^31 - 64");
   if (sp.qjl_m) {
     if (!cache->qjl_signs || !cache->qjl_rnorms) return fail(TQ_E_ARG, "QJL arrays must be non-NULL");
     if (!aligned(cache->qjl_signs, 16) || !aligned(cache->qjl_rnorms, 4))

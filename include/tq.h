@@ -74,8 +74,9 @@ typedef enum {
  * uniform width and bits_hi is then ignored.  8-bit codes (the K8 keys of
  * the K8/V3 default that section "Cosa aggiunge turboquant-mlx" of the same
  * page names) need split == d, the record layout and no sketch; quantize
- * and decode take them for keys (with values of 2, 3 or 4 bits, uniform),
- * tq_ip_scores does not. */
+ * and decode take them for keys (decode: with values of 2 or 3 bits,
+ * uniform), tq_ip_scores does not.  An 8-bit quantize needs 32 rows of x to
+ * span less than 2^30 bytes (else TQ_E_UNSUPPORTED). */
 /* How the rotation Pi is drawn from rot_seed. */
 typedef enum {
   TQ_ROT_HAAR = 0,      /* Haar-distributed orthogonal matrix (tq_rotation_build) */

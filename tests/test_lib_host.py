@@ -419,3 +419,14 @@ def test_paged_binding_wants_a_device_table_tensor():
     for bt in (np.zeros((2, 4), np.int32), torch.zeros((2, 4), dtype=torch.int64), torch.zeros((3, 4), dtype=torch.int32)):
         with pytest.raises(ValueError):
             tq.quantize_kv_paged(tq.Spec(4), None, None, None, hkv=2, n_tok=[1, 1], block_table=bt, n_pages=8)
+
+
+def test_eight_bit_quantize_stride_limit():
+    """8-bit codes have no general-kernel path: a row stride whose 32 rows
+    reach 2^30 bytes is refused before any launch."""
+    L = tq.lib()
+    spec = tq.Spec(8)
+    cache = tq.TqCache(0x1000, 0x2000, None, None, 64)
+    rs = (1 << 30) // (32 * 2)  # bf16 elements
+    assert L.tq_quantize_kv(ctypes.byref(spec.c()), ctypes.c_void_p(0x10000), 1, 0x4000, 1, 2, rs, rs, 0,
+                            ctypes.byref(cache), None) == -2
