@@ -342,6 +342,7 @@ def test_ip_scores_argument_errors_without_launch():
     assert call(q=None) == -1
     assert call(d=tq.TqCache(0x1000, 0x2000, None, None, 64)) == -1  # sketch arrays missing
     assert call(sp=tq.Spec(3, layout=tq.LAYOUT_TILED).c()) == -2     # tiled layout
+    assert call(sp=tq.Spec(8).c()) == -2                              # 8-bit codes
     assert call(ns=0) == 0 and call(nt=0, ld=0) == 0        # nothing to do: no launch
     assert call(ns=70000, nt=1, ld=70000, d=tq.TqCache(0x1000, 0x2000, 0x3000, 0x4000, 64)) == -2
 
@@ -406,6 +407,11 @@ def test_attend_argument_errors_without_launch():
     big = tq.TqCache(0x1000, 0x2000, None, None, (1 << 24) + 32)
     assert call(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64), kc_=big) == -2   # cap above 2^24
     assert call(tq.TqAttn(0, 8, 2, 0, 0.1, 0.0, 64)) == 0             # empty batch: nothing launched
+    k8 = tq.Spec(8).c()
+    for vspec in (tq.Spec(4, layout=1), tq.Spec(4, 3, split=64, layout=1), tq.Spec(3, 2, split=64, layout=1)):
+        assert L.tq_attend_decode(ctypes.byref(k8), tab, ctypes.byref(kc), ctypes.byref(vspec.c()), tab,
+                                  ctypes.byref(vc), ctypes.byref(tq.TqAttn(1, 8, 2, 0, 0.1, 0.0, 64)), 0x5000,
+                                  None, None, 0x6000, 0x7000, 0x8000, 1 << 20, None) == -2  # K8: V2 or V3 only
     ws = tq.attend_workspace_bytes(2, 32, 8, 0, 32768)
     assert ws >= 2 * 32 * (2 * 128 + 4) * 4
     assert ws % 4 == 0
