@@ -356,3 +356,64 @@ def test_quantize_eight_bit_full_size_sampled():
         rows = np.sort(rng.choice(n, 200, replace=False))
         idx = opk.unpack_records(codes[s, rows], spec.widths)
         check_quantized(spec, xk[s, rows], idx, norms[s, rows], label=f"8-bit full stream {s}")
+
+
+@pytest.mark.parametrize("w", [(3, None, 128), (4, 3, 64)])
+@pytest.mark.parametrize("layout", [tq.LAYOUT_RECORD, tq.LAYOUT_TILED])
+def test_token_by_token_appends_equal_one_bulk_write(w, layout):
+    """The decode-time pattern: 80 vectors appended one call per token (every
+    value tile built up by merges into its stored words) give exactly the
+    codes and norms of one bulk write of the same vectors."""
+    print(f"[quantize] token-by-token appends widths={w} layout={layout}", flush=True)
+    spec = tq.Spec(w[0], w[1], split=w[2], layout=layout)
+    x = np.random.default_rng(17).standard_normal((2, 80, 128), dtype=np.float32)
+    x = workloads.bf16_to_f32(workloads.bf16_bits(x))
+    xd = to_device(x, "bf16")
+    tab = tq.device_tables(spec)
+    bulk = tq.alloc_cache(spec, 2, 96)
+    tq.quantize_kv(spec, tab, xd, bulk)
+    step = tq.alloc_cache(spec, 2, 96)
+    for t in range(80):
+        tq.quantize_kv(spec, tab, xd[:, t:t + 1], step, tok0=t)
+    torch().cuda.synchronize()
+    for s in range(2):
+        assert np.array_equal(read_codes(spec, step, s, 80), read_codes(spec, bulk, s, 80))
+        assert np.array_equal(read_norms(step, s, 80), read_norms(bulk, s, 80))
+    check_quantized(spec, x[1], read_codes(spec, step, 1, 80), read_norms(step, 1, 80), label="appends")
+
+
+def test_ragged_single_token_steps_equal_bulk_writes():
+    """A decode step of a ragged batch: one tq_quantize_kv_ragged call per
+    step appends one token to each live sequence at its own position
+    (sequences start at different lengths and stop at different steps); the
+    cache equals per-sequence bulk writes of the same vectors, both layouts."""
+    print("[quantize] ragged single-token steps", flush=True)
+    B, H = 6, 2
+    rng = np.random.default_rng(23)
+    start = rng.integers(0, 70, B)            # prefix lengths (written in bulk first)
+    total = start + rng.integers(1, 40, B)     # final lengths
+    x = rng.standard_normal((B * H, int(total.max()), 128), dtype=np.float32)
+    x = workloads.bf16_to_f32(workloads.bf16_bits(x))
+    xd = to_device(x, "bf16")
+    for layout in (tq.LAYOUT_RECORD, tq.LAYOUT_TILED):
+        spec = tq.Spec(4, 3, split=64, layout=layout)
+        tab = tq.device_tables(spec)
+        cap = int(-(-total.max() // 32) * 32)
+        ref = tq.alloc_cache(spec, B * H, cap)
+        tq.quantize_kv_ragged(spec, tab, xd, ref, hkv=H, n_tok=total)
+        got = tq.alloc_cache(spec, B * H, cap)
+        tq.quantize_kv_ragged(spec, tab, xd, got, hkv=H, n_tok=start)
+        pos = start.copy()
+        while np.any(pos < total):
+            live = (pos < total).astype(np.int64)
+            step_x = torch().zeros((B * H, 1, 128), dtype=xd.dtype, device="cuda")
+            for b in range(B):
+                if live[b]:
+                    step_x[b * H:(b + 1) * H, 0] = xd[b * H:(b + 1) * H, pos[b]]
+            tq.quantize_kv_ragged(spec, tab, step_x, got, hkv=H, n_tok=live, tok0=pos)
+            pos = pos + live
+        torch().cuda.synchronize()
+        for s in range(B * H):
+            n = int(total[s // H])
+            assert np.array_equal(read_codes(spec, got, s, n), read_codes(spec, ref, s, n)), (layout, s)
+            assert np.array_equal(read_norms(got, s, n), read_norms(ref, s, n)), (layout, s)
