@@ -199,3 +199,18 @@ def test_attend_per_layer_policies_share_one_workspace():
     for run in runs:
         _check(run, label=f"layer {run.wl.name}")
     T.cuda.synchronize()
+
+
+@pytest.mark.parametrize("qjl,sink", [(0, 512), (128, 0), (128, 300)])
+def test_attend_sixteen_heads_per_group_edges(qjl, sink):
+    """The largest group (16 query heads per KV head) with the largest sink
+    (512 raw tokens, lengths below and above it), and with the sketch (the
+    query fragments of 16 heads read from LDS every tile)."""
+    print(f"[attend] G=16 qjl={qjl} sink={sink}", flush=True)
+    kq = workloads.QSpec(2, 2, qjl_m=qjl) if qjl else workloads.QSpec(4, 4)
+    wl = workloads.Workload(f"g16_{qjl}_{sink}", 3, 32, 2, "bf16", kq, workloads.QSpec(3, 3),
+                            lens_range=(max(sink, 1), sink + 1500), sink=sink, v_skip=1e-6 if sink else 0.0)
+    inp = workloads.generate(wl)
+    if sink:
+        inp.seq_lens[0] = sink // 3            # only sink tokens, fewer than the sink
+    _check(Run(inp), label=f"G=16 qjl={qjl} sink={sink}")
