@@ -214,3 +214,57 @@ def test_attend_sixteen_heads_per_group_edges(qjl, sink):
     if sink:
         inp.seq_lens[0] = sink // 3            # only sink tokens, fewer than the sink
     _check(Run(inp), label=f"G=16 qjl={qjl} sink={sink}")
+
+
+def test_max_capacity_stream_of_identical_tokens():
+    """One stream at the largest cache capacity (2^24 positions, 512 splits
+    merged by the combine): every key and value is the same vector, so every
+    stored code equals position 0's (sampled across the stream, including
+    its last tile), and every softmax weight is equal, so each head's output
+    is that one token's dequantized value, whatever the length."""
+    from gpu_helpers import check_quantized, ospec, to_device
+    from oracle import pack as opk
+    from oracle import quantize as oqz
+    print("[attend] 2^24-token stream of identical tokens", flush=True)
+    T = torch()
+    N = 1 << 24
+    rng = np.random.default_rng(31)
+    k0, v0 = (workloads.bf16_to_f32(workloads.bf16_bits(rng.standard_normal(128).astype(np.float32)))
+              for _ in range(2))
+    q = rng.standard_normal((1, 4, 128)).astype(np.float32)
+    kspec, vspec = tq.Spec(4, layout=tq.LAYOUT_RECORD), tq.Spec(3, layout=tq.LAYOUT_TILED)
+    ktab, vtab = tq.device_tables(kspec), tq.device_tables(vspec)
+    kc, vc = tq.alloc_cache(kspec, 1, N), tq.alloc_cache(vspec, 1, N)
+    for spec, tab, vec, cache in ((kspec, ktab, k0, kc), (vspec, vtab, v0, vc)):
+        x = to_device(vec[None, None, :], "bf16").expand(1, N, 128).contiguous()
+        tq.quantize_kv(spec, tab, x, cache)
+        T.cuda.synchronize()
+        del x
+
+    def codes_at(spec, cache, p):
+        if spec.layout == tq.LAYOUT_RECORD:
+            rb = tq.code_bytes(spec)
+            return opk.unpack_records(cache.codes[p * rb:(p + 1) * rb].cpu().numpy()[None], spec.widths)[0]
+        tb = 32 * tq.code_bytes(spec)
+        raw = cache.codes[(p // 32) * tb:(p // 32 + 1) * tb].cpu().numpy()
+        return opk.unpack_tiled(raw, spec.widths, 1, p % 32)[0]
+
+    first = {}
+    for spec, cache, vec in ((kspec, kc, k0), (vspec, vc, v0)):
+        c0, n0 = codes_at(spec, cache, 0), cache.norms[0:1].cpu().numpy()
+        check_quantized(spec, vec[None], c0[None], n0, label="identical tokens")
+        for p in (1, 31, 32, 12345, N // 2 + 7, N - 33, N - 1):
+            assert np.array_equal(codes_at(spec, cache, p), c0), (spec.layout, p)
+            assert cache.norms[p].item() == n0[0], (spec.layout, p)
+        first[spec.layout] = (c0, float(n0[0]))
+    ws = tq.alloc_attend_workspace(1, 4, 1, 0, N)
+    out = T.empty((1, 4, 128), dtype=T.float32, device="cuda")
+    tq.attend_decode(kspec, ktab, kc, vspec, vtab, vc, T.from_numpy(q).cuda(),
+                     T.tensor([N], dtype=T.int32, device="cuda"), out, ws, hkv=1, max_len=N)
+    T.cuda.synchronize()
+    cv, nv = first[tq.LAYOUT_TILED]
+    os_ = ospec(vspec)
+    want = nv * (oqz.rotation_of(os_).T @ oqz.dequantize_rotated(cv[None], os_)[0])
+    got = out.cpu().numpy().astype(np.float64)
+    for h in range(4):
+        assert parity.rel_l2(got[0, h], want) <= parity.ATTN_REL_L2, h
