@@ -19,6 +19,7 @@ algorithmic bytes (packed K and V records, norms, q and out).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -305,6 +306,8 @@ def main() -> int:
                     help="how the rotation is drawn (the workloads are specified with the Haar rotation)")
     ap.add_argument("--kbits", type=int, choices=(8,), default=None,
                     help="keys at 8 bits (uniform, no sketch: the K8 of a K8/V3 policy) instead of the workload's")
+    ap.add_argument("--norms", choices=("f32", "f16"), default="f32",
+                    help="how key and value norms are stored (f16: binary16, 2 bytes per token and tensor)")
     ap.add_argument("--paged", action="store_true",
                     help="caches in a pool of 64-token pages, each sequence's pages in a seeded random order")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -342,9 +345,11 @@ def main() -> int:
                     rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed, rotation=rot)
     if args.kbits == 8:
         kspec = tq.Spec(8, layout=tq.LAYOUT_RECORD, rot_seed=wl.k.rot_seed, rotation=rot)
+    nf16 = 1 if args.norms == "f16" else 0
+    kspec = dataclasses.replace(kspec, norm_f16=nf16)
     kb = (kspec.bits_lo, kspec.bits_lo if kspec.bits_hi is None else kspec.bits_hi)
     vspec = tq.Spec(wl.v.bits_lo, wl.v.bits_hi, split=wl.v.split, layout=tq.LAYOUT_TILED, rot_seed=wl.v.rot_seed,
-                    rotation=rot)
+                    rotation=rot, norm_f16=nf16)
     ktab, vtab = tq.device_tables(kspec), tq.device_tables(vspec)
 
     def device_input(parts):
@@ -463,8 +468,9 @@ def main() -> int:
 
     n_vec = int(Hkv * comp_h.sum())                        # compressed vectors per tensor
     kcb, vcb = tq.code_bytes(kspec), tq.code_bytes(vspec)
-    k_tok = kcb + 4 + (kspec.qjl_m // 8 + 4 if kspec.qjl_m else 0)   # codes, norm (+ signs, residual norm)
-    v_tok = vcb + 4
+    nb = 2 if nf16 else 4                                            # bytes per stored norm
+    k_tok = kcb + nb + (kspec.qjl_m // 8 + 4 if kspec.qjl_m else 0)  # codes, norm (+ signs, residual norm)
+    v_tok = vcb + nb
     in_b = 512 if f32 else 256
     sink_bytes = int(Hkv * np.minimum(lens_h, S).sum()) * 2 * 128 * 2
     dec_bytes = n_vec * (k_tok + v_tok) + sink_bytes + 2 * B * Hq * 128 * 4
@@ -485,7 +491,7 @@ def main() -> int:
     else:
         dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms, qv_bytes, f"rotq_kernel<{vtag}>"
     dom_gbs = dom_bytes / (dom_ms / 1e3) / 1e9
-    default_cfg = wname == WORKLOAD and not args.paged and args.kbits is None
+    default_cfg = wname == WORKLOAD and not args.paged and args.kbits is None and not nf16
     traffic = read_traffic(dom_name) if default_cfg else None
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom_kernel,
@@ -506,7 +512,8 @@ def main() -> int:
                    "kv_dtype": wl.dtype, "k_bits": list(kb), "v_bits": [wl.v.bits_lo, wl.v.bits_hi],
                    "split": kspec.split, "qjl": bool(kspec.qjl_m), "sink": S, "v_skip": wl.v_skip,
                    "structure": wl.structure, "rotation": args.rotation,
-                   "cache": f"paged ({tq.PAGE_TOKENS}-token pages)" if args.paged else "contiguous"},
+                   "cache": f"paged ({tq.PAGE_TOKENS}-token pages)" if args.paged else "contiguous",
+                   "norms": args.norms},
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "decode_us": round(at_ms * 1e3, 2),
         "quantize_Mvec_s": round(quant_mvec, 1), "quantize_GB_s": round(quant_gbs, 2),

@@ -136,7 +136,7 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          void* workspace, hipStream_t st, const int32_t* block_table, int max_pages, int n_pages) {
   float* parts = static_cast<float*>(workspace);
   const SplitArgs f{ktab, &kc, vtab, &vc, &a, &plan, q, sink_k, sink_v, seq_lens, parts, out,
-                    block_table, max_pages, n_pages, st};
+                    block_table, max_pages, n_pages, st, ks.norm16 != 0};
   const int vkey = vs.bits_lo * 10 + vs.bits_hi;
   const bool qjl = ks.qjl_m != 0;
   hipError_t e;

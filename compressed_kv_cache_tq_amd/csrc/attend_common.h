@@ -41,6 +41,7 @@ struct SplitArgs {
   int max_pages;
   int n_pages;
   hipStream_t st;
+  bool norm16;  // K and V norms stored as fp16
 };
 
 // Launch the split kernel for keys of widths (bits_lo, bits_hi) = key / 10,

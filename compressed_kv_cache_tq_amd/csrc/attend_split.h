@@ -123,8 +123,8 @@ template <int KWD>
 struct TileRegs {
   uint32_t kw[2][KWD];  // K record chunk of token slots mu(0, n), mu(1, n)
   uint32_t vw[8];     // V sub-block (token group j, coordinate group n)
-  float4 kn[2];       // K norms of tokens 8j .. 8j+7
-  float4 vn[2];       // V norms of tokens 8j .. 8j+7
+  float4 kn[2];       // K norms of tokens 8j .. 8j+7 (fp16 norms: their bits in kn[0])
+  float4 vn[2];       // V norms of tokens 8j .. 8j+7 (fp16 norms: their bits in vn[0])
   uint32_t zw[2];     // QJL sign dword j of token slots mu(0, n), mu(1, n)
   float4 rn[2];       // QJL residual norms of tokens 8j .. 8j+7
 };
@@ -179,7 +179,7 @@ __device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t
 template <int KLO, int KHI>
 constexpr int key_dwords() { return KLO == 8 ? 8 : 4; }
 
-template <int KLO, int KHI, int VLO, int VHI, bool QJL>
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool NF16>
 __device__ __forceinline__ void load_tile(TileRegs<key_dwords<KLO, KHI>()>& r, uint32_t t0, const StreamRsrc& rs,
                                           const LaneOffsets& lo) {
   constexpr uint32_t KBYTES = 8 * (KLO + KHI);
@@ -220,10 +220,16 @@ __device__ __forceinline__ void load_tile(TileRegs<key_dwords<KLO, KHI>()>& r, u
 #pragma unroll
     for (int i = 0; i < VW; ++i) r.vw[i] = w[i];
   }
-  r.kn[0] = buf_load_f4(rs.kn, lo.nrm + 4 * t0);
-  r.kn[1] = buf_load_f4(rs.kn, lo.nrm + 4 * t0 + 16);
-  r.vn[0] = buf_load_f4(rs.vn, lo.nrm + 4 * t0);
-  r.vn[1] = buf_load_f4(rs.vn, lo.nrm + 4 * t0 + 16);
+  if constexpr (NF16) {
+    // 8 fp16 norms in one 16-byte load, converted where they are used
+    r.kn[0] = buf_load_f4(rs.kn, (lo.nrm >> 1) + 2 * t0);
+    r.vn[0] = buf_load_f4(rs.vn, (lo.nrm >> 1) + 2 * t0);
+  } else {
+    r.kn[0] = buf_load_f4(rs.kn, lo.nrm + 4 * t0);
+    r.kn[1] = buf_load_f4(rs.kn, lo.nrm + 4 * t0 + 16);
+    r.vn[0] = buf_load_f4(rs.vn, lo.nrm + 4 * t0);
+    r.vn[1] = buf_load_f4(rs.vn, lo.nrm + 4 * t0 + 16);
+  }
   if constexpr (QJL) {
     r.rn[0] = buf_load_f4(rs.rn, lo.nrm + 4 * t0);
     r.rn[1] = buf_load_f4(rs.rn, lo.nrm + 4 * t0 + 16);
@@ -257,6 +263,16 @@ __device__ __forceinline__ float f4get(const float4 (&v)[2], int e) {
   const float4 x = v[e >> 2];
   const int k = e & 3;
   return k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
+}
+
+// norm e (0..7) of a tile's lane: fp32, or fp16 packed two per word of v[0]
+template <bool NF16>
+__device__ __forceinline__ float norm_get(const float4 (&v)[2], int e) {
+  if constexpr (!NF16) return f4get(v, e);
+  const float4 x = v[0];
+  const int k = e >> 1;
+  const uint32_t w = __float_as_uint(k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w);
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> (16 * (e & 1)))));
 }
 
 // Partial (m, l, acc) of the raw bf16 sink tokens t < ns of one (sequence,
@@ -465,7 +481,7 @@ __device__ __forceinline__ void merge_stream(uint8_t* smem, const Tables* __rest
   }
 }
 
-template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED>
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED, bool NF16>
 __global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
     const uint8_t* __restrict__ ksigns, const float* __restrict__ krn, int64_t kcap,
@@ -628,8 +644,12 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   // tile gets descriptors over its own page below)
   rs.kc = rsrc(kcodes + stream * kcap * KBYTES, static_cast<int64_t>(t_end) * KBYTES);
   rs.vc = rsrc(vcodes + stream * vcap * VBYTES, vend * VBYTES);
-  rs.kn = rsrc(knorms + stream * kcap, static_cast<int64_t>(t_end) * 4);
-  rs.vn = rsrc(vnorms + stream * vcap, static_cast<int64_t>(t_end) * 4);
+  // norms: NB bytes each (fp32, or fp16 bits)
+  constexpr int NB = NF16 ? 2 : 4;
+  const uint8_t* knb = reinterpret_cast<const uint8_t*>(knorms);
+  const uint8_t* vnb = reinterpret_cast<const uint8_t*>(vnorms);
+  rs.kn = rsrc(knb + stream * kcap * NB, static_cast<int64_t>(t_end) * NB);
+  rs.vn = rsrc(vnb + stream * vcap * NB, static_cast<int64_t>(t_end) * NB);
   if constexpr (QJL) {
     rs.zs = rsrc(ksigns + stream * kcap * (QJL_M / 8), static_cast<int64_t>(t_end) * (QJL_M / 8));
     rs.rn = rsrc(krn + stream * kcap, static_cast<int64_t>(t_end) * 4);
@@ -688,7 +708,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   using TRg = TileRegs<key_dwords<KLO, KHI>()>;
   auto load_at = [&](TRg& buf, int k, uint32_t t0) __attribute__((always_inline)) {
     if constexpr (!PAGED) {
-      load_tile<KLO, KHI, VLO, VHI, QJL>(buf, t0, rs, lo);
+      load_tile<KLO, KHI, VLO, VHI, QJL, NF16>(buf, t0, rs, lo);
     } else {
       const int pg = __builtin_amdgcn_readlane(k < 64 ? pid[0] : pid[1], k & 63);
       const int64_t base = static_cast<int64_t>(t0 / TQ_PAGE_TOKENS) * TQ_PAGE_TOKENS;
@@ -701,15 +721,15 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       StreamRsrc pr;
       pr.kc = rsrc(kcodes + ps * kcap * KBYTES, nk * KBYTES);
       pr.vc = rsrc(vcodes + ps * vcap * VBYTES, nvt * VBYTES);
-      pr.kn = rsrc(knorms + ps * kcap, nk * 4);
-      pr.vn = rsrc(vnorms + ps * vcap, nk * 4);
+      pr.kn = rsrc(knb + ps * kcap * NB, nk * NB);
+      pr.vn = rsrc(vnb + ps * vcap * NB, nk * NB);
       if constexpr (QJL) {
         pr.zs = rsrc(ksigns + ps * kcap * (QJL_M / 8), nk * (QJL_M / 8));
         pr.rn = rsrc(krn + ps * kcap, nk * 4);
       } else {
         pr.zs = pr.rn = pr.kn;
       }
-      load_tile<KLO, KHI, VLO, VHI, QJL>(buf, t0 % TQ_PAGE_TOKENS, pr, lo);
+      load_tile<KLO, KHI, VLO, VHI, QJL, NF16>(buf, t0 % TQ_PAGE_TOKENS, pr, lo);
     }
   };
 
@@ -927,7 +947,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         const int e = 4 * mb + i;
         float dot = sk[mb][i] * qinv;
         if constexpr (QJL) dot = fmaf(f4get(tr.rn, e) * sz[mb][i], uinv, dot);
-        s[e] = f4get(tr.kn, e) * dot;
+        s[e] = norm_get<NF16>(tr.kn, e) * dot;
         if constexpr (!FULL) s[e] = e < nvalid ? s[e] : -INFINITY;
         tmax = fmaxf(tmax, s[e]);
       }
@@ -957,7 +977,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         any |= (p0 > 0.0f) | (p1 > 0.0f);
       }
       psum += p0 + p1;
-      float v0 = f4get(tr.vn, e), v1 = f4get(tr.vn, e + 1);
+      float v0 = norm_get<NF16>(tr.vn, e), v1 = norm_get<NF16>(tr.vn, e + 1);
       if constexpr (!FULL) {
         v0 = e < nvalid ? v0 : 0.0f;
         v1 = e + 1 < nvalid ? v1 : 0.0f;
@@ -1047,23 +1067,27 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   finish();
 }
 
-template <int KLO, int KHI, int VLO, int VHI, bool QJL>
-hipError_t launch_split(const SplitArgs& f) {
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED, bool NF16>
+hipError_t launch_split_as(const SplitArgs& f) {
   const tq_attn& a = *f.a;
   const AttendPlan& plan = *f.plan;
   const tq_cache &kc = *f.kc, &vc = *f.vc;
   const dim3 grid(a.hkv, a.batch, plan.n_split);
-  if (f.block_table)
-    hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL, true>), grid, dim3(ST), 0, f.st, f.ktab, kc.codes,
-                       kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, f.vtab, vc.codes, vc.norms, vc.cap, f.seq_lens,
-                       f.q, f.sink_k, f.sink_v, f.parts, f.out, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot,
-                       plan.chunk, a.v_skip, a.scale * LOG2E, f.block_table, f.max_pages, f.n_pages);
-  else
-    hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL, false>), grid, dim3(ST), 0, f.st, f.ktab, kc.codes,
-                       kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, f.vtab, vc.codes, vc.norms, vc.cap, f.seq_lens,
-                       f.q, f.sink_k, f.sink_v, f.parts, f.out, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot,
-                       plan.chunk, a.v_skip, a.scale * LOG2E, nullptr, 0, 0);
+  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL, PAGED, NF16>), grid, dim3(ST), 0, f.st, f.ktab, kc.codes,
+                     kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, f.vtab, vc.codes, vc.norms, vc.cap, f.seq_lens,
+                     f.q, f.sink_k, f.sink_v, f.parts, f.out, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot,
+                     plan.chunk, a.v_skip, a.scale * LOG2E, f.block_table, PAGED ? f.max_pages : 0,
+                     PAGED ? f.n_pages : 0);
   return hipGetLastError();
+}
+
+template <int KLO, int KHI, int VLO, int VHI, bool QJL>
+hipError_t launch_split(const SplitArgs& f) {
+  if (f.norm16)
+    return f.block_table ? launch_split_as<KLO, KHI, VLO, VHI, QJL, true, true>(f)
+                         : launch_split_as<KLO, KHI, VLO, VHI, QJL, false, true>(f);
+  return f.block_table ? launch_split_as<KLO, KHI, VLO, VHI, QJL, true, false>(f)
+                       : launch_split_as<KLO, KHI, VLO, VHI, QJL, false, false>(f);
 }
 
 

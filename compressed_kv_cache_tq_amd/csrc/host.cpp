@@ -366,13 +366,14 @@ tq_status check_spec(const tq_spec* s, tq::Spec* out) {
     return fail(TQ_E_UNSUPPORTED, "the QJL sketch needs the record layout");
   if (s->rotation != TQ_ROT_HAAR && s->rotation != TQ_ROT_HADAMARD)
     return fail(TQ_E_ARG, "rotation must be TQ_ROT_HAAR or TQ_ROT_HADAMARD");
-  if (s->reserved != 0) return fail(TQ_E_ARG, "reserved must be 0");
+  if (s->norm_f16 != 0 && s->norm_f16 != 1) return fail(TQ_E_ARG, "norm_f16 must be 0 or 1");
   if (out) {
     out->bits_lo = bl;
     out->bits_hi = bhi;
     out->qjl_m = s->qjl_m;
     out->layout = s->layout;
     out->code_bytes = 8 * (bl + bhi);
+    out->norm16 = s->norm_f16;
   }
   return TQ_OK;
 }
@@ -591,6 +592,7 @@ tq_status tq_ip_scores(const tq_spec* spec, const void* tables, const tq_cache* 
   if (tq_status st = check_spec(spec, &sp); st != TQ_OK) return st;
   if (sp.layout != TQ_LAYOUT_RECORD) return fail(TQ_E_UNSUPPORTED, "search needs the record layout");
   if (sp.bits_lo == 8) return fail(TQ_E_UNSUPPORTED, "search takes codes of at most 4 bits");
+  if (sp.norm16) return fail(TQ_E_UNSUPPORTED, "search takes fp32 norms");
   if (tq_status st = check_tables(tables, sp, "search"); st != TQ_OK) return st;
   if (!db) return fail(TQ_E_ARG, "db is NULL");
   if (n_streams < 0 || n_tok < 0) return fail(TQ_E_ARG, "negative n_streams or n_tok");
@@ -727,6 +729,7 @@ tq_status attend_checked(const tq_spec* ks, const void* ktables, const tq_cache*
   if (vsp.bits_lo == 8) return fail(TQ_E_UNSUPPORTED, "8-bit codes are for keys (record layout)");
   if (ksp.bits_lo == 8 && !(vsp.bits_lo == vsp.bits_hi && (vsp.bits_lo == 2 || vsp.bits_lo == 3)))
     return fail(TQ_E_UNSUPPORTED, "8-bit keys decode with values of 2 or 3 bits (uniform)");
+  if (ksp.norm16 != vsp.norm16) return fail(TQ_E_UNSUPPORTED, "K and V specs must agree on norm_f16");
   if (tq_status st = check_tables(ktables, ksp, "key"); st != TQ_OK) return st;
   if (tq_status st = check_tables(vtables, vsp, "value"); st != TQ_OK) return st;
   if (!attn || !kc || !vc) return fail(TQ_E_ARG, "attn, kc and vc must be non-NULL");

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
     const Tables* __restrict__ tab, const void* __restrict__ xv, int64_t n_tok, int64_t xss, int64_t xrs,
     int64_t tok0, uint8_t* __restrict__ codes, float* __restrict__ norms, uint8_t* __restrict__ signs,
     float* __restrict__ rnorms, int64_t cap, int64_t stream_code_bytes, int64_t tiles_per_stream, int64_t tile0,
-    int64_t total_tiles, const int32_t* __restrict__ pages, int64_t n_pages, int64_t page_streams) {
+    int64_t total_tiles, const int32_t* __restrict__ pages, int64_t n_pages, int64_t page_streams, int norm16) {
   constexpr bool F32IN = XM == X_F32;
   constexpr int NPART = XM == X_BF16 ? 3 : 2;
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
@@ -319,6 +319,11 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, h = lane >> 5;
+  // norm i of the launch's streams: fp32, or fp16 rounded to nearest even
+  auto put_norm = [&](int64_t i, float v) {
+    if (norm16) reinterpret_cast<_Float16*>(norms)[i] = static_cast<_Float16>(v);
+    else norms[i] = v;
+  };
 
   // Row of x this lane loads for tile w (vector column n for the record
   // layout, token slot tiled_slot(n) for the tiled layout).
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
           pack_record<BHI>(acc, tp, wds);
           if (valid) store_record<BHI>(rec + 8 * BLO, wds);
         }
-        if (valid && h == 0) norms[ds * cap + dp] = normf;
+        if (valid && h == 0) put_norm(ds * cap + dp, normf);
       } else {
         uint32_t idx[64];
         if (h == 0) {
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
         if (valid) {
           if (h == 0) store_record<BLO>(rec, wds);
           else store_record<BHI>(rec + 8 * BLO, wds);
-          if (h == 0) norms[ds * cap + dp] = normf;
+          if (h == 0) put_norm(ds * cap + dp, normf);
         }
         // residual r = y - c[idx] in the rotated unit-norm domain, scaled by 2^8
         // and split into fp16 hi + lo for the sketch contraction S r.
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
           store_tiled_chunk<BHI>(tbase + g * G + 64 * BLO + 8 * BHI * (q - 8) + 4 * BHI * (j & 1), wds, vmask);
         }
       }
-      if (valid && h == 0) norms[ds * cap + dp] = normf;
+      if (valid && h == 0) put_norm(ds * cap + dp, normf);
     }
 #pragma unroll
     for (int k = 0; k < NW; ++k) xr[k] = xnext[k];
@@ -649,6 +654,7 @@ struct RotqArgs {
   const int32_t* pages;     // paged cache: block table [.][page_ld] (device)
   int64_t page_ld;
   int32_t n_pages;
+  int32_t norm16;           // norms stored as fp16 (else fp32)
   RotqSeq seq[RQ_MAX_SEQ];  // ascending start
 };
 
@@ -805,7 +811,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   const int64_t n_tok = Q.n_tok, tok0 = Q.tok0, xss = A.xss, xrs = A.xrs, cap = A.cap;
   const int64_t stream_code_bytes = A.stream_code_bytes;
   uint8_t* __restrict__ codes = A.codes + static_cast<int64_t>(Q.stream0) * A.stream_code_bytes;
-  float* __restrict__ norms = A.norms + static_cast<int64_t>(Q.stream0) * cap;
+  const int nbytes = A.norm16 ? 2 : 4;  // bytes per stored norm
+  uint8_t* __restrict__ nrm = reinterpret_cast<uint8_t*>(A.norms) + static_cast<int64_t>(Q.stream0) * cap * nbytes;
   const int64_t tile0 = Q.t_lo, tstep = Q.t_step;
   const int64_t total_tiles = static_cast<int64_t>(A.hkv) * Q.tiles;
   const int64_t first = first_l - Q.start;  // within the sequence
@@ -939,9 +946,13 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     inv_s[pair][b][sv] = normf > 0.0f ? 1.0f / ldexpf(normf, sh + 8) : 0.0f;
     const TileAt a = tile_at(tl);
     const Dst d = dest_at(a);
-    const __amdgpu_buffer_rsrc_t rn = rsrc(norms + d.s * cap + d.p, d.ok ? static_cast<int64_t>(a.nv) * 4 : 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, !(MERGE || PAGED) || sv >= a.lo ? 4 * sv : RQ_OOB,
-                                          0, 0);
+    const __amdgpu_buffer_rsrc_t rn =
+        rsrc(nrm + (d.s * cap + d.p) * nbytes, d.ok ? static_cast<int64_t>(a.nv) * nbytes : 0);
+    const int noff = !(MERGE || PAGED) || sv >= a.lo ? nbytes * sv : RQ_OOB;
+    if (A.norm16)
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(normf)), rn, noff, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, noff, 0, 0);
   };
 
   // ---- pipeline, straight-line over the pair's K tiles: three register
@@ -1109,7 +1120,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
 
 template <int BLO, int BHI, int XM, bool TILED, bool QJL>
 hipError_t launch_one(const Tables* tab, const void* x, int64_t n_streams, int64_t n_tok, int64_t xss, int64_t xrs,
-                      int64_t tok0, const tq_cache& c, const int32_t* pages, int64_t n_pages, hipStream_t st) {
+                      int64_t tok0, const tq_cache& c, const int32_t* pages, int64_t n_pages, int norm16,
+                      hipStream_t st) {
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
   int64_t tiles, tile0 = 0;
   if (TILED) {
@@ -1123,15 +1135,15 @@ hipError_t launch_one(const Tables* tab, const void* x, int64_t n_streams, int64
   const int64_t blocks = std::min<int64_t>((total + WAVES - 1) / WAVES, 256);
   hipLaunchKernelGGL((quantize_kernel<BLO, BHI, XM, TILED, QJL>), dim3(static_cast<unsigned>(blocks)),
                      dim3(THREADS), 0, st, tab, x, n_tok, xss, xrs, tok0, c.codes, c.norms, c.qjl_signs,
-                     c.qjl_rnorms, c.cap, stream_bytes, tiles, tile0, total, pages, n_pages, n_streams);
+                     c.qjl_rnorms, c.cap, stream_bytes, tiles, tile0, total, pages, n_pages, n_streams, norm16);
   return hipGetLastError();
 }
 
 // cache arrays of the streams from s0 on
-tq_cache streams_from(const tq_cache& c, int64_t s0, int64_t code_bytes) {
+tq_cache streams_from(const tq_cache& c, int64_t s0, int64_t code_bytes, int norm16) {
   tq_cache o = c;
   o.codes = c.codes + s0 * c.cap * code_bytes;
-  o.norms = c.norms + s0 * c.cap;
+  o.norms = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(c.norms) + s0 * c.cap * (norm16 ? 2 : 4));
   if (c.qjl_signs) o.qjl_signs = c.qjl_signs + s0 * c.cap * (QJL_M / 8);
   if (c.qjl_rnorms) o.qjl_rnorms = c.qjl_rnorms + s0 * c.cap;
   return o;
@@ -1140,15 +1152,15 @@ tq_cache streams_from(const tq_cache& c, int64_t s0, int64_t code_bytes) {
 // one general-kernel launch per sequence
 template <int BLO, int BHI, int XM, bool TILED, bool QJL>
 hipError_t launch_each(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv, int64_t xss,
-                       int64_t xrs, const tq_cache& c, const PageMap& pm, hipStream_t st) {
+                       int64_t xrs, const tq_cache& c, const PageMap& pm, int norm16, hipStream_t st) {
   constexpr int64_t ES = XM == X_F32 ? 4 : 2;
   for (int64_t i = 0; i < n_seq; ++i) {
     const QSeq& q = seqs[i];
     const int32_t* pages = pm.table ? pm.table + q.page_row * pm.ld : nullptr;
     const hipError_t e = launch_one<BLO, BHI, XM, TILED, QJL>(tab, static_cast<const uint8_t*>(x) + q.x_off * ES,
                                                               hkv, q.n_tok, xss, xrs, q.tok0,
-                                                              streams_from(c, q.stream0, 8 * (BLO + BHI)), pages,
-                                                              pm.n_pages, st);
+                                                              streams_from(c, q.stream0, 8 * (BLO + BHI), norm16),
+                                                              pages, pm.n_pages, norm16, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1162,7 +1174,8 @@ struct RotqPart {
 
 template <int BLO, int BHI, bool F32IN, bool TILED, bool MERGE, bool PAGED>
 hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<RotqPart>& list, int64_t hkv,
-                            int64_t xss, int64_t xrs, const tq_cache& c, const PageMap& pm, hipStream_t st) {
+                            int64_t xss, int64_t xrs, const tq_cache& c, const PageMap& pm, int norm16,
+                            hipStream_t st) {
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
   const int64_t n = static_cast<int64_t>(list.size());
   for (int64_t b0 = 0; b0 < n; b0 += RQ_MAX_SEQ) {
@@ -1186,6 +1199,7 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
     a.pages = pm.table;
     a.page_ld = pm.ld;
     a.n_pages = static_cast<int32_t>(pm.n_pages);
+    a.norm16 = norm16;
     int64_t total = 0;  // each sequence's tiles start on a multiple of K
     for (int i = 0; i < nb; ++i) {
       const RotqPart& p = list[b0 + i];
@@ -1220,7 +1234,7 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
 
 template <int BLO, int BHI, bool F32IN, bool TILED>
 hipError_t launch_rotq(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv, int64_t xss,
-                       int64_t xrs, const tq_cache& c, const PageMap& pm, hipStream_t st) {
+                       int64_t xrs, const tq_cache& c, const PageMap& pm, int norm16, hipStream_t st) {
   constexpr int64_t ES = F32IN ? 4 : 2;
   constexpr int XM = F32IN ? X_F32 : X_BF16;
   const bool paged = pm.table != nullptr;
@@ -1258,14 +1272,14 @@ hipError_t launch_rotq(const Tables* tab, const void* x, const QSeq* seqs, int64
       streams >= (int64_t{1} << 31)) {
     // (8-bit codes have no general-kernel path)
     if constexpr (BLO == 8) return hipErrorNotSupported;
-    else return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    else return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, norm16, st);
   }
   auto run = [&](auto pg) {
     constexpr bool P = decltype(pg)::value;
-    hipError_t e = launch_rotq_list<BLO, BHI, F32IN, TILED, false, P>(tab, x, whole, hkv, xss, xrs, c, pm, st);
+    hipError_t e = launch_rotq_list<BLO, BHI, F32IN, TILED, false, P>(tab, x, whole, hkv, xss, xrs, c, pm, norm16, st);
     if constexpr (TILED) {
       if (e == hipSuccess && !part.empty())
-        e = launch_rotq_list<BLO, BHI, F32IN, TILED, true, P>(tab, x, part, hkv, xss, xrs, c, pm, st);
+        e = launch_rotq_list<BLO, BHI, F32IN, TILED, true, P>(tab, x, part, hkv, xss, xrs, c, pm, norm16, st);
     }
     return e;
   };
@@ -1278,15 +1292,16 @@ hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const v
                            const PageMap& pm, hipStream_t st) {
   const bool f32 = dtype == TQ_F32;
   if (sp.qjl_m) {
-    return f32 ? launch_each<BLO, BHI, X_F32, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
-               : launch_each<BLO, BHI, X_BF16_F16, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    const int nf = sp.norm16;
+    return f32 ? launch_each<BLO, BHI, X_F32, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, nf, st)
+               : launch_each<BLO, BHI, X_BF16_F16, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, nf, st);
   }
   if (sp.layout == TQ_LAYOUT_TILED) {
-    return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
-               : launch_rotq<BLO, BHI, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+    return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, sp.norm16, st)
+               : launch_rotq<BLO, BHI, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, sp.norm16, st);
   }
-  return f32 ? launch_rotq<BLO, BHI, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
-             : launch_rotq<BLO, BHI, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+  return f32 ? launch_rotq<BLO, BHI, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, sp.norm16, st)
+             : launch_rotq<BLO, BHI, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, sp.norm16, st);
 }
 
 }  // namespace
@@ -1302,8 +1317,9 @@ hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const v
     case 43: return dispatch_layout<4, 3>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
     case 32: return dispatch_layout<3, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
     case 88:  // 8-bit keys: record layout, no sketch (checked on the host)
-      return dtype == TQ_F32 ? launch_rotq<8, 8, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st)
-                             : launch_rotq<8, 8, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);
+      return dtype == TQ_F32
+                 ? launch_rotq<8, 8, true, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, sp.norm16, st)
+                 : launch_rotq<8, 8, false, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, sp.norm16, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -95,6 +95,7 @@ struct Spec {
   int qjl_m;
   int layout;
   int code_bytes;  // per token
+  int norm16;      // norms stored as fp16 (else fp32)
 };
 
 // One sequence of a quantize call: hkv streams whose rows start at element

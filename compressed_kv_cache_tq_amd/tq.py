@@ -40,7 +40,7 @@ class TqSpec(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("bits_lo", ctypes.c_int32), ("bits_hi", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("qjl_m", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("rot_seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64), ("rotation", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("norm_f16", ctypes.c_int32)]
 
 
 class TqCache(ctypes.Structure):
@@ -130,10 +130,11 @@ class Spec:
     rot_seed: int = 0
     qjl_seed: int = 1
     rotation: int = 0      # ROT_HAAR or ROT_HADAMARD
+    norm_f16: int = 0      # 1: norms stored as fp16
 
     def c(self) -> TqSpec:
         return TqSpec(D, self.bits_lo, self.bits_lo if self.bits_hi is None else self.bits_hi, self.split,
-                      self.qjl_m, self.layout, self.rot_seed, self.qjl_seed, self.rotation, 0)
+                      self.qjl_m, self.layout, self.rot_seed, self.qjl_seed, self.rotation, self.norm_f16)
 
     @property
     def widths(self) -> np.ndarray:
@@ -256,7 +257,8 @@ def alloc_cache(spec: Spec, n_streams: int, cap: int, device="cuda", fill: int |
     codes = torch.empty(max(n_streams * nb, 16), dtype=torch.uint8, device=device)
     if fill is not None:
         codes.fill_(fill)
-    norms = torch.zeros(max(n_streams * cap, 4), dtype=torch.float32, device=device)
+    norms = torch.zeros(max(n_streams * cap, 8), dtype=torch.float16 if spec.norm_f16 else torch.float32,
+                        device=device)
     signs = rn = None
     if spec.qjl_m:
         signs = torch.zeros(max(n_streams * cap * spec.qjl_m // 8, 16), dtype=torch.uint8, device=device)

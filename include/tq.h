@@ -93,7 +93,7 @@ typedef struct {
   uint64_t rot_seed;  /* seed of the rotation (SplitMix64 stream) */
   uint64_t qjl_seed;  /* seed of the sketch matrix S */
   int32_t rotation;   /* tq_rotation */
-  int32_t reserved;   /* must be 0 */
+  int32_t norm_f16;   /* 0: fp32 norms; 1: fp16 norms (see tq_cache) */
 } tq_spec;
 
 /* One tensor of a packed cache, for n_streams = batch * kv_heads streams of
@@ -110,7 +110,11 @@ typedef struct {
  *         tokens in 8*b_q bytes at g*G + sum_{q'<q} 8*b_q' (G = sum_q 8*b_q),
  *         and (coordinate 8q+r, token 8g+s) occupies its bits
  *         [(8r+s)*b_q, (8r+s)*b_q + b_q).  cap must be a multiple of 32.
- * norms   fp32 [n_streams][cap]: Euclidean norm of the stored input vector.
+ * norms   fp32 [n_streams][cap]: Euclidean norm of the stored input vector;
+ *         with spec->norm_f16 the IEEE binary16 bits of that fp32 norm
+ *         rounded to nearest even, uint16 [n_streams][cap] (norms must then
+ *         stay below 65504; the pointer is passed as the same float*).  The
+ *         K and V specs of one decode must agree on norm_f16.
  * qjl_signs  [n_streams][cap][qjl_m/8] bytes, bit j set iff (S r)_j >= 0
  *         (r = rotated unit vector minus its centroids); NULL if qjl_m == 0.
  * qjl_rnorms fp32 [n_streams][cap]: ||r||; NULL if qjl_m == 0.

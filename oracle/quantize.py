@@ -17,7 +17,11 @@ bits per channel are quoted; the 3.5-bit mix is read as rotated coordinates
 
 Readings (the page is silent on these):
 * the norm is the float64 Euclidean norm of the stored input value, kept as
-  fp32 rounded to nearest even;
+  fp32 rounded to nearest even; with fp16 norms (a storage option of this
+  library that the pages do not describe; the port they discuss only brings
+  the cache back to float16 for attention, noze.it page, section "Cosa
+  aggiunge turboquant-mlx") that fp32 value is rounded once more, to
+  binary16, nearest even;
 * a zero vector quantizes y = 0 and stores norm 0;
 * index = number of thresholds strictly below y (exact ties go to the lower
   index);
@@ -44,6 +48,7 @@ class Spec:
     rot_seed: int = 0
     qjl_seed: int = 1
     rotation: str = "haar"  # "haar" or "hadamard"
+    norm_f16: bool = False  # norms stored as fp16 (rounded from the fp32 norm)
 
     def bits_of(self) -> np.ndarray:
         """Bit width of every rotated coordinate."""
@@ -93,7 +98,7 @@ def dequantize_rotated(idx: np.ndarray, spec: Spec) -> np.ndarray:
 @dataclass
 class Quantized:
     idx: np.ndarray        # [n, d] int64 codes
-    norms: np.ndarray      # [n] float32 (stored)
+    norms: np.ndarray      # [n] float32 (stored), float16 with spec.norm_f16
     norms64: np.ndarray    # [n] float64 (exact)
     y: np.ndarray          # [n, d] float64 rotated unit vectors
     qjl_bits: np.ndarray | None = None   # [n, m] bool, True iff (S r)_j >= 0
@@ -114,7 +119,10 @@ def quantize(x: np.ndarray, spec: Spec, pi: np.ndarray | None = None,
     y[nz] /= nrm[nz, None]
     y[~nz] = 0.0
     idx = scalar_quantize(y, spec)
-    out = Quantized(idx=idx, norms=nrm.astype(np.float32), norms64=nrm, y=y)
+    stored = nrm.astype(np.float32)
+    if spec.norm_f16:
+        stored = stored.astype(np.float16)
+    out = Quantized(idx=idx, norms=stored, norms64=nrm, y=y)
     if spec.qjl_m:
         s_mat = sketch_of(spec) if s_mat is None else s_mat
         r = y - dequantize_rotated(idx, spec)

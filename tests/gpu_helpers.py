@@ -27,7 +27,7 @@ def to_device(x_f32: np.ndarray, dtype: str):
 def ospec(s: tq.Spec) -> oqz.Spec:
     return oqz.Spec(bits_lo=s.bits_lo, bits_hi=s.bits_lo if s.bits_hi is None else s.bits_hi,
                     split=s.split, qjl_m=s.qjl_m, rot_seed=s.rot_seed, qjl_seed=s.qjl_seed,
-                    rotation="hadamard" if s.rotation == tq.ROT_HADAMARD else "haar")
+                    rotation="hadamard" if s.rotation == tq.ROT_HADAMARD else "haar", norm_f16=bool(s.norm_f16))
 
 
 def read_codes(spec: tq.Spec, cache: tq.Cache, stream: int, n_tok: int, tok0: int = 0) -> np.ndarray:
@@ -60,9 +60,13 @@ def check_quantized(spec: tq.Spec, x: np.ndarray, idx_gpu: np.ndarray, norms_gpu
     q = oqz.quantize(x.astype(np.float64), os_)
     rep = parity.compare_codes(q.idx, idx_gpu, q.y, os_)
     assert rep.ok, f"{label}: {rep}"
-    # norms: fp64 accumulation on the GPU -> equal to the correctly rounded norm up to 1 ulp
-    ulp = np.spacing(np.maximum(q.norms, np.float32(1e-30)))
-    assert np.all(np.abs(norms_gpu - q.norms) <= ulp), f"{label}: norms differ"
+    # norms: fp64 accumulation on the GPU -> equal to the correctly rounded
+    # norm up to 1 ulp of the stored type (fp32, or fp16 rounded from fp32)
+    dt = q.norms.dtype
+    assert norms_gpu.dtype == dt, f"{label}: norms stored as {norms_gpu.dtype}, expected {dt}"
+    ulp = np.spacing(np.maximum(q.norms, dt.type(np.finfo(dt).tiny))).astype(np.float64)
+    err = np.abs(norms_gpu.astype(np.float64) - q.norms.astype(np.float64))
+    assert np.all(err <= ulp), f"{label}: norms differ"
     if signs is not None:
         bits_gpu, rn_gpu = signs
         vec_ok = np.all(q.idx == idx_gpu, axis=1)
@@ -113,15 +117,16 @@ def oracle_attention(q: np.ndarray, kspec: tq.Spec, vspec: tq.Spec, seq_lens, k_
 class Run:
     """One workload pushed through the HIP path: quantize K and V, then decode attention."""
 
-    def __init__(self, inp: workloads.Inputs, device="cuda"):
+    def __init__(self, inp: workloads.Inputs, device="cuda", norm_f16: int = 0):
         t = torch()
         wl = inp.wl
         self.inp = inp
         self.wl = wl
         self.kspec = tq.Spec(wl.k.bits_lo, wl.k.bits_hi, split=wl.k.split, qjl_m=wl.k.qjl_m,
-                             layout=tq.LAYOUT_RECORD, rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed)
+                             layout=tq.LAYOUT_RECORD, rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed,
+                             norm_f16=norm_f16)
         self.vspec = tq.Spec(wl.v.bits_lo, wl.v.bits_hi, split=wl.v.split, qjl_m=0,
-                             layout=tq.LAYOUT_TILED, rot_seed=wl.v.rot_seed)
+                             layout=tq.LAYOUT_TILED, rot_seed=wl.v.rot_seed, norm_f16=norm_f16)
         B, Hkv, S = len(inp.k), wl.hkv, wl.sink
         self.B = B
         lens = inp.seq_lens

@@ -268,3 +268,12 @@ def test_max_capacity_stream_of_identical_tokens():
     got = out.cpu().numpy().astype(np.float64)
     for h in range(4):
         assert parity.rel_l2(got[0, h], want) <= parity.ATTN_REL_L2, h
+
+
+@pytest.mark.parametrize("name,ctx,batch", [("gqa_decode", 1500, None), ("qjl", 1000, 2), ("batched_ragged", 900, 3)])
+def test_attend_fp16_norms(name, ctx, batch):
+    """Key and value norms stored as fp16: the decode reads them through the
+    fp16 variant; the oracle evaluates the attention on the GPU's codes and
+    fp16 norms."""
+    print(f"[attend] fp16 norms {name}", flush=True)
+    _check(Run(workloads.generate(name, ctx=ctx, batch=batch), norm_f16=1), label=f"{name} fp16 norms")

@@ -269,3 +269,34 @@ def test_paged_eight_bit_keys():
                            hkv=4, block_table=T.from_numpy(bt).cuda(), n_pages=n_pages, max_len=run.max_len)
     T.cuda.synchronize()
     assert T.equal(out, run.out)
+
+
+def test_paged_fp16_norms():
+    """fp16 norms through the paged quantize and the paged decode: equal to
+    the contiguous path with fp16 norms."""
+    print("[paged] fp16 norms", flush=True)
+    T = torch()
+    run = Run(workloads.generate("batched_ragged", ctx=700, batch=3), norm_f16=1)
+    run.quantize()
+    run.attend()
+    T.cuda.synchronize()
+    wl, H, B = run.wl, run.wl.hkv, run.B
+    comp = [max(0, int(run.inp.seq_lens[b]) - wl.sink) for b in range(B)]
+    n_pages = sum(-(-c // P) for c in comp) + 2
+    bt = _tables(B, comp, n_pages, seed=8)
+    kpool, vpool, comp = _paged_quantize(run, bt, n_pages, 50)
+    assert kpool.norms.dtype == T.float16
+    for b in range(B):
+        for h in range(H):
+            for lp in range(-(-comp[b] // P)):
+                n = min(P, comp[b] - lp * P)
+                ps, s = int(bt[b, lp]) * H + h, b * H + h
+                for spec, pool, cache in ((run.kspec, kpool, run.kc), (run.vspec, vpool, run.vc)):
+                    assert np.array_equal(read_codes(spec, pool, ps, n), read_codes(spec, cache, s, n, lp * P))
+                    assert np.array_equal(read_norms(pool, ps, n), read_norms(cache, s, n, lp * P))
+    out = T.empty_like(run.q)
+    tq.attend_decode_paged(run.kspec, run.ktab, kpool, run.vspec, run.vtab, vpool, run.q, run.seq_lens, out, run.ws,
+                           hkv=H, block_table=T.from_numpy(bt).cuda(), n_pages=n_pages, sink=wl.sink,
+                           sink_k=run.sink_k, sink_v=run.sink_v, v_skip=wl.v_skip, max_len=run.max_len)
+    T.cuda.synchronize()
+    assert T.equal(out, run.out)

@@ -417,3 +417,20 @@ def test_ragged_single_token_steps_equal_bulk_writes():
             n = int(total[s // H])
             assert np.array_equal(read_codes(spec, got, s, n), read_codes(spec, ref, s, n)), (layout, s)
             assert np.array_equal(read_norms(got, s, n), read_norms(ref, s, n)), (layout, s)
+
+
+@pytest.mark.parametrize("bits,layout,qjl", [((4, None, 128), tq.LAYOUT_RECORD, 0), ((3, None, 128), tq.LAYOUT_TILED, 0),
+                                             ((4, 3, 64), tq.LAYOUT_TILED, 0), ((2, None, 128), tq.LAYOUT_RECORD, 128),
+                                             ((8, None, 128), tq.LAYOUT_RECORD, 0)])
+def test_quantize_fp16_norms(bits, layout, qjl):
+    """fp16 norms: the same codes (and sketch), the norm stored as the fp32
+    norm rounded to binary16 (nearest even), within one fp16 ulp; written
+    from position 37 of a stream to cover partial tiles."""
+    print(f"[quantize] fp16 norms {bits} layout={layout} qjl={qjl}", flush=True)
+    spec = tq.Spec(bits[0], bits[1], split=bits[2], layout=layout, qjl_m=qjl, norm_f16=1)
+    x = _data(1000, seed=61, dtype="bf16")
+    cache = _quantize(spec, x, "bf16", cap=1056, tok0=37)
+    assert cache.norms.dtype == torch().float16
+    signs = read_signs(cache, 0, 1000, 37) if qjl else None
+    check_quantized(spec, x[0], read_codes(spec, cache, 0, 1000, 37), read_norms(cache, 0, 1000, 37), signs=signs,
+                    label=f"fp16 norms {bits}")

@@ -63,9 +63,9 @@ def test_hadamard_rotation_errors_and_spec_fields():
         assert L.tq_hadamard_rotation_build(d, 0, m.ctypes.data) == -1
     assert L.tq_hadamard_rotation_build(4, 0, None) == -1
     buf = np.zeros(tq.tables_bytes(), dtype=np.uint8)
-    for rot, reserved in ((2, 0), (-1, 0), (0, 1)):
+    for rot, nf16 in ((2, 0), (-1, 0), (0, 2)):
         cs = tq.Spec(4).c()
-        cs.rotation, cs.reserved = rot, reserved
+        cs.rotation, cs.norm_f16 = rot, nf16
         assert tq.lib().tq_tables_build(ctypes.byref(cs), buf.ctypes.data, buf.size) == -1
 
 

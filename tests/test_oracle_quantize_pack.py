@@ -164,3 +164,21 @@ def test_tiled_equals_record_bits_per_token():
     til = pack.pack_tiled(idx, widths)
     popc = lambda a: int(np.unpackbits(a).sum())
     assert popc(rec) == popc(til)
+
+
+def test_fp16_norms_round_the_fp32_norm_to_nearest_even():
+    """Stored fp16 norms, worked by hand: sqrt(3) = 1.7320508 lies between the
+    binary16 values 1 + 749/1024 and 1 + 750/1024 and is nearer the second
+    (bits 0x3EEE); 2049 and 2051 are exact fp32 norms halfway between
+    binary16 neighbours (spacing 2 above 2048), which round to the even
+    mantissa: 2048 (0x6800) and 2052 (0x6802), not truncated or rounded up."""
+    spec = qz.Spec(bits_lo=4, bits_hi=4, norm_f16=True)
+    x = np.zeros((3, 128))
+    x[0, :3] = 1.0
+    x[1, 5] = 2049.0
+    x[2, 77] = -2051.0
+    q = qz.quantize(x, spec)
+    assert q.norms.dtype == np.float16
+    assert q.norms.view(np.uint16).tolist() == [0x3EEE, 0x6800, 0x6802]
+    # codes do not depend on how the norm is stored
+    assert np.array_equal(q.idx, qz.quantize(x, qz.Spec(bits_lo=4, bits_hi=4)).idx)
