@@ -72,7 +72,7 @@ CALIB_BYTES = 512 << 20
 STEP_KERNELS = {
     "quantize_k": ["rotq_kernel<4, 4, false, false, 8, false, false>"],
     "quantize_v": ["rotq_kernel<3, 3, false, true, 8, false, false>"],
-    "attend": ["split_kernel<4, 4, 3, 3, false, false>", "combine_kernel"],
+    "attend": ["split_kernel<4, 4, 3, 3, false, false, false>", "combine_kernel"],
 }
 STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0], "attend": KERNEL_SOURCES[1]}
 
