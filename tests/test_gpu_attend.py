@@ -277,3 +277,12 @@ def test_attend_fp16_norms(name, ctx, batch):
     fp16 norms."""
     print(f"[attend] fp16 norms {name}", flush=True)
     _check(Run(workloads.generate(name, ctx=ctx, batch=batch), norm_f16=1), label=f"{name} fp16 norms")
+
+
+def test_attend_eight_bit_keys_with_fp16_norms():
+    """K8/V3 with fp16 norms (the 8-bit key instance of the fp16-norm
+    decode): ragged batch, against the oracle on the GPU's codes and norms."""
+    print("[attend] K8/V3 + fp16 norms", flush=True)
+    wl = workloads.Workload("k8v3f16", 3, 16, 4, "bf16", workloads.QSpec(8, 8), workloads.QSpec(3, 3),
+                            lens_range=(200, 1500))
+    _check(Run(workloads.generate(wl), norm_f16=1), label="K8/V3 fp16 norms")
