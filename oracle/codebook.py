@@ -65,7 +65,7 @@ def first_moment(lo, hi, d: int):
 
 
 def cell_mass(lo, hi, d: int):
-    """P(lo < X < hi).  Uses the smaller tail on each side for accuracy."""
+    """P(lo < X < hi), the difference of the two cdf values."""
     return cdf(hi, d) - cdf(lo, d)
 
 

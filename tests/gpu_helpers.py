@@ -78,40 +78,14 @@ def check_quantized(spec: tq.Spec, x: np.ndarray, idx_gpu: np.ndarray, norms_gpu
 
 def oracle_attention(q: np.ndarray, kspec: tq.Spec, vspec: tq.Spec, seq_lens, k_idx, k_norm, v_idx, v_norm, *,
                      k_bits=None, k_gamma=None, sink_k=None, sink_v=None, sink=0, v_skip=0.0, heads=None):
-    """Oracle decode attention on the given codes; dequantizes each KV stream once.
+    """The oracle's batched decode attention (oracle.attend.attend) on the given
+    codes, with the sketch term when the key spec has one.
 
     k_idx[b][kh] etc. hold the compressed tokens (already cut to L_b - sink).
     heads: optional list of (b, h) to evaluate (others left as NaN).
     """
-    ks, vs = ospec(kspec), ospec(vspec)
-    pi_k, pi_v = oqz.rotation_of(ks), oqz.rotation_of(vs)
-    s_mat = oqz.sketch_of(ks) if ks.qjl_m else None
-    B, Hq, d = q.shape
-    Hkv = len(k_idx[0])
-    G = Hq // Hkv
-    out = np.full((B, Hq, d), np.nan)
-    want = set(heads) if heads is not None else None
-    for b in range(B):
-        ns = min(sink, int(seq_lens[b]))
-        for kh in range(Hkv):
-            hs = [h for h in range(kh * G, (kh + 1) * G) if want is None or (b, h) in want]
-            if not hs:
-                continue
-            khat = oqz.dequantize_rotated(k_idx[b][kh], ks)
-            vhat = oqz.dequantize_rotated(v_idx[b][kh], vs)
-            for h in hs:
-                qq = q[b, h].astype(np.float64)
-                qr = pi_k @ qq
-                qjl = None
-                if ks.qjl_m:
-                    z = np.where(k_bits[b][kh], 1.0, -1.0)
-                    qjl = np.sqrt(np.pi / 2) / ks.qjl_m * k_gamma[b][kh].astype(np.float64) * (z @ (s_mat @ qr))
-                o, _, _ = oat.attend_rotated(qq, qr, khat, k_norm[b][kh], vhat, v_norm[b][kh], pi_v, qjl_dots=qjl,
-                                             sink_k=None if not ns else sink_k[b][kh][:ns],
-                                             sink_v=None if not ns else sink_v[b][kh][:ns],
-                                             scale=1 / np.sqrt(d), v_skip=v_skip)
-                out[b, h] = o
-    return out
+    return oat.attend(q, ospec(kspec), ospec(vspec), seq_lens, k_idx, k_norm, v_idx, v_norm, k_bits=k_bits,
+                      k_gamma=k_gamma, sink_k=sink_k, sink_v=sink_v, sink=sink, v_skip=v_skip, heads=heads)
 
 
 class Run:

@@ -140,6 +140,50 @@ def test_tiled_worked_example():
     assert np.flatnonzero(buf).tolist() == [276] and buf[276] == 0x0C
 
 
+def test_tiled_worked_example_3bit_codes_straddle_bytes():
+    # 3-bit tiles: sub-block bytes 8 * 3 = 24, token-group bytes G = 16 * 24 = 384.
+    # (a) token 2 (group 0, slot 2), coordinate 1 (group 0, row 1), code 7: bits
+    #     (8*1 + 2) * 3 = 30, 31, 32 -> byte 3 bits 6-7 (0xC0), byte 4 bit 0 (0x01).
+    # (b) token 21 (group 2, slot 5), coordinate 42 (group 5, row 2), code 5 = 0b101:
+    #     sub-block at 2*384 + 5*24 = 888, bits (8*2 + 5) * 3 = 63, 64, 65 ->
+    #     code bit 0 at byte 895 bit 7 (0x80), bit 2 at byte 896 bit 1 (0x02).
+    # (c) tokens 8..15 (group 1), coordinate 127 (group 15, row 7), codes 0..7 in
+    #     slot order: 24 bits at sub-block 384 + 15*24 = 744, bits 168..191 ->
+    #     bytes 765, 766, 767 = 0x88 0xC6 0xFA (the record example's bytes).
+    idx = np.zeros((32, 128), dtype=np.int64)
+    idx[2, 1] = 7
+    idx[21, 42] = 5
+    idx[8:16, 127] = np.arange(8)
+    buf = pack.pack_tiled(idx, np.full(128, 3))
+    assert buf.size == 32 * 48
+    want = {3: 0xC0, 4: 0x01, 895: 0x80, 896: 0x02, 765: 0x88, 766: 0xC6, 767: 0xFA}
+    assert np.flatnonzero(buf).tolist() == sorted(want)
+    assert all(buf[k] == v for k, v in want.items())
+    assert np.array_equal(pack.unpack_tiled(buf, np.full(128, 3), 32), idx)
+
+
+def test_tiled_worked_example_mixed_4_and_3_bits():
+    # 3.5 bits (coordinates 0..63 at 4 bits, 64..127 at 3 bits): sub-blocks
+    # q < 8 hold 32 bytes, q >= 8 hold 24, G = 8*32 + 8*24 = 448 per token group.
+    #   token 3,  coord 7:   g 0, q 0,  r 7, s 3, code 10 -> bit (56+3)*4 = 236 -> byte 29 high nibble: 0xA0
+    #   token 8,  coord 64:  g 1, q 8,  r 0, s 0, code 5  -> byte 448 + 256 = 704, bits 0..2: 0x05
+    #   token 17, coord 70:  g 2, q 8,  r 6, s 1, code 6  -> 896 + 256 = 1152, bit (48+1)*3 = 147:
+    #                        code bits 1, 2 at bits 148, 149 -> byte 1152 + 18 = 1170 bits 4, 5: 0x30
+    #   token 21, coord 63:  g 2, q 7,  r 7, s 5, code 15 -> 896 + 7*32 = 1120, bit (56+5)*4 = 244 ->
+    #                        byte 1150 high nibble: 0xF0
+    #   token 31, coord 127: g 3, q 15, r 7, s 7, code 7  -> 3*448 + 256 + 7*24 = 1768, bit (56+7)*3 = 189
+    #                        -> byte 1768 + 23 = 1791 bits 5..7: 0xE0 (the tile's last byte)
+    w = np.array([4] * 64 + [3] * 64)
+    idx = np.zeros((32, 128), dtype=np.int64)
+    idx[3, 7], idx[8, 64], idx[17, 70], idx[21, 63], idx[31, 127] = 10, 5, 6, 15, 7
+    buf = pack.pack_tiled(idx, w)
+    assert buf.size == 32 * 56
+    want = {29: 0xA0, 704: 0x05, 1170: 0x30, 1150: 0xF0, 1791: 0xE0}
+    assert np.flatnonzero(buf).tolist() == sorted(want)
+    assert all(buf[k] == v for k, v in want.items())
+    assert np.array_equal(pack.unpack_tiled(buf, w, 32), idx)
+
+
 @pytest.mark.parametrize("w", [(2, 2), (3, 3), (4, 4), (4, 3)])
 def test_tiled_round_trip_and_partial_update(w):
     widths = np.array([w[0]] * 64 + [w[1]] * 64)
