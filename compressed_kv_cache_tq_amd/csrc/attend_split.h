@@ -490,7 +490,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     const uint16_t* __restrict__ sink_k, const uint16_t* __restrict__ sink_v, float* __restrict__ parts,
     float* __restrict__ out, int hq, int hkv, int sink, int n_split, int n_slot,
     int64_t chunk, float v_skip, float qscale, const int32_t* __restrict__ block_table, int max_pages,
-    int n_pages) {
+    int n_pages, int max_len) {
   using LP = LutPlan<KLO, KHI, VLO, VHI>;
   constexpr int KBYTES = 8 * (KLO + KHI);
   constexpr int VBYTES = 8 * (VLO + VHI);
@@ -524,7 +524,9 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   const int n = lane & 15, j = lane >> 4;
   const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
   const int64_t stream = static_cast<int64_t>(b) * hkv + kh;
-  const int64_t L = seq_lens[b];
+  // (a length outside [0, max_len] breaks the caller's contract; clamping it
+  // keeps every access inside the cache the host validated)
+  const int64_t L = min(max(seq_lens[b], 0), max_len);
   // The sink tokens' partial (slot n_split, acc in the original value
   // domain) is computed by the stream's last split that holds compressed
   // tokens (split 0 when there are none), after its own partial, when the
@@ -1077,7 +1079,7 @@ hipError_t launch_split_as(const SplitArgs& f) {
                      kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, f.vtab, vc.codes, vc.norms, vc.cap, f.seq_lens,
                      f.q, f.sink_k, f.sink_v, f.parts, f.out, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot,
                      plan.chunk, a.v_skip, a.scale * LOG2E, f.block_table, PAGED ? f.max_pages : 0,
-                     PAGED ? f.n_pages : 0);
+                     PAGED ? f.n_pages : 0, static_cast<int>(a.max_len));
   return hipGetLastError();
 }
 

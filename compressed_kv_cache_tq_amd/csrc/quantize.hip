@@ -44,6 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int WAVES = 8;
 constexpr int THREADS = 64 * WAVES;
+constexpr float F16_MAX = 65504.0f;  // fp16 norms saturate here instead of turning into +inf
 constexpr int FRAGS = 4 * 8 * 64;  // (tile, k-step, lane) fragments of one 128x128 16-bit matrix part
 
 // input modes
@@ -320,8 +321,9 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, h = lane >> 5;
   // norm i of the launch's streams: fp32, or fp16 rounded to nearest even
+  // and saturated at the largest finite binary16 value
   auto put_norm = [&](int64_t i, float v) {
-    if (norm16) reinterpret_cast<_Float16*>(norms)[i] = static_cast<_Float16>(v);
+    if (norm16) reinterpret_cast<_Float16*>(norms)[i] = static_cast<_Float16>(fminf(v, F16_MAX));
     else norms[i] = v;
   };
 
@@ -950,7 +952,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
         rsrc(nrm + (d.s * cap + d.p) * nbytes, d.ok ? static_cast<int64_t>(a.nv) * nbytes : 0);
     const int noff = !(MERGE || PAGED) || sv >= a.lo ? nbytes * sv : RQ_OOB;
     if (A.norm16)
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(normf)), rn, noff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(fminf(normf, F16_MAX))),
+                                            rn, noff, 0, 0);
     else
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, noff, 0, 0);
   };

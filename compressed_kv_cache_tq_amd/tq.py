@@ -266,6 +266,34 @@ def alloc_cache(spec: Spec, n_streams: int, cap: int, device="cuda", fill: int |
     return Cache(spec, cap, codes, norms, signs, rn)
 
 
+def _layout_key(s: Spec):
+    """The fields of a spec that fix the sizes and layout of a cache's arrays."""
+    hi = s.bits_lo if s.bits_hi is None or s.split == D else s.bits_hi
+    return (s.bits_lo, hi, D if hi == s.bits_lo else s.split, s.qjl_m, s.layout, int(bool(s.norm_f16)))
+
+
+def _check_cache(spec: Spec, cache: Cache, n_streams: int, what: str) -> None:
+    """Refuse a cache whose arrays were sized for another spec, or that holds
+    fewer than n_streams streams: the C side receives bare pointers and would
+    read or write past them."""
+    torch = _torch()
+    if _layout_key(spec) != _layout_key(cache.spec):
+        raise ValueError(f"{what}: spec {spec} does not match the cache's spec {cache.spec}")
+    want = torch.float16 if spec.norm_f16 else torch.float32
+    if cache.norms.dtype != want:
+        raise ValueError(f"{what}: norm_f16={spec.norm_f16} needs {want} norms, the cache holds {cache.norms.dtype}")
+    n = max(int(n_streams), 0)
+    need = [("codes", cache.codes, n * cache_code_bytes(spec, cache.cap)), ("norms", cache.norms, n * cache.cap)]
+    if spec.qjl_m:
+        if cache.qjl_signs is None or cache.qjl_rnorms is None:
+            raise ValueError(f"{what}: the spec has a sketch, the cache has no sketch arrays")
+        need += [("qjl_signs", cache.qjl_signs, n * cache.cap * spec.qjl_m // 8),
+                 ("qjl_rnorms", cache.qjl_rnorms, n * cache.cap)]
+    for name, t, elems in need:
+        if not t.is_contiguous() or t.numel() < elems:
+            raise ValueError(f"{what}: cache.{name} holds {t.numel()} elements, {n} streams need {elems}")
+
+
 def quantize_kv(spec: Spec, tables, x, cache: Cache, tok0: int = 0, n_streams: int | None = None,
                 n_tok: int | None = None, stream: int | None = None) -> None:
     """Quantize x ([n_streams, n_tok, d] view, float32 or bfloat16, rows 16-byte aligned)."""
@@ -282,6 +310,7 @@ def quantize_kv(spec: Spec, tables, x, cache: Cache, tok0: int = 0, n_streams: i
         raise ValueError("x must be [n_streams, n_tok, 128] with contiguous rows")
     ns = x.shape[0] if n_streams is None else n_streams
     nt = x.shape[1] if n_tok is None else n_tok
+    _check_cache(spec, cache, ns, "quantize_kv")
     cs, cc = spec.c(), cache.c()
     st = _stream(x.device) if stream is None else stream
     _check(lib().tq_quantize_kv(ctypes.byref(cs), tables.data_ptr(), dt, x.data_ptr(), ns, nt, x.stride(0),
@@ -320,6 +349,7 @@ def quantize_kv_ragged(spec: Spec, tables, x, cache: Cache, *, hkv: int, n_tok, 
         xss, xrs = x_stream_stride, x_row_stride
     if t0.shape != (B,) or xo.shape != (B,):
         raise ValueError("n_tok, tok0 and x_off must have one entry per sequence")
+    _check_cache(spec, cache, B * hkv, "quantize_kv_ragged")
     cs, cc = spec.c(), cache.c()
     st = _stream(x.device) if stream is None else stream
     _check(lib().tq_quantize_kv_ragged(ctypes.byref(cs), tables.data_ptr(), dt, x.data_ptr(), B, hkv,
@@ -350,6 +380,8 @@ def attend_decode(kspec: Spec, ktables, kcache: Cache, vspec: Spec, vtables, vca
     if max_len is None:
         max_len = sink + min(kcache.cap, vcache.cap)
     a = TqAttn(B, Hq, hkv, sink, (1.0 / np.sqrt(D)) if scale is None else scale, v_skip, max_len)
+    _check_cache(kspec, kcache, B * hkv, "attend_decode keys")
+    _check_cache(vspec, vcache, B * hkv, "attend_decode values")
     ks, vs, kc, vc = kspec.c(), vspec.c(), kcache.c(), vcache.c()
     st = _stream(q.device) if stream is None else stream
     _check(lib().tq_attend_decode(ctypes.byref(ks), ktables.data_ptr(), ctypes.byref(kc), ctypes.byref(vs),
@@ -378,6 +410,7 @@ def ip_scores(spec: Spec, tables, db: Cache, q, *, n_streams: int, n_tok: int, s
         scores = torch.empty((nq, ld), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = alloc_ip_workspace(q.device)
+    _check_cache(spec, db, n_streams, "ip_scores")
     cs, cc = spec.c(), db.c()
     st = _stream(q.device) if stream is None else stream
     _check(lib().tq_ip_scores(ctypes.byref(cs), tables.data_ptr(), ctypes.byref(cc), n_streams, n_tok, q.data_ptr(),
@@ -423,6 +456,7 @@ def quantize_kv_paged(spec: Spec, tables, x, pool: Cache, *, hkv: int, n_tok, bl
     else:
         xo = np.ascontiguousarray(x_off, dtype=np.int64)
         xss, xrs = x_stream_stride, x_row_stride
+    _check_cache(spec, pool, n_pages * hkv, "quantize_kv_paged")
     cs, cc = spec.c(), pool.c()
     st = _stream(x.device) if stream is None else stream
     _check(lib().tq_quantize_kv_paged(ctypes.byref(cs), tables.data_ptr(), _dtype_code(x), x.data_ptr(), B, hkv,
@@ -437,6 +471,8 @@ def attend_decode_paged(kspec: Spec, ktables, kpool: Cache, vspec: Spec, vtables
     """attend_decode over paged pools; block_table: device int32 [B, max_pages]."""
     B, Hq, _ = q.shape
     a = TqAttn(B, Hq, hkv, sink, (1.0 / np.sqrt(D)) if scale is None else scale, v_skip, max_len)
+    _check_cache(kspec, kpool, n_pages * hkv, "attend_decode_paged keys")
+    _check_cache(vspec, vpool, n_pages * hkv, "attend_decode_paged values")
     ks, vs, kc, vc = kspec.c(), vspec.c(), kpool.c(), vpool.c()
     st = _stream(q.device) if stream is None else stream
     _check(lib().tq_attend_decode_paged(ctypes.byref(ks), ktables.data_ptr(), ctypes.byref(kc), ctypes.byref(vs),

@@ -112,9 +112,11 @@ typedef struct {
  *         [(8r+s)*b_q, (8r+s)*b_q + b_q).  cap must be a multiple of 32.
  * norms   fp32 [n_streams][cap]: Euclidean norm of the stored input vector;
  *         with spec->norm_f16 the IEEE binary16 bits of that fp32 norm
- *         rounded to nearest even, uint16 [n_streams][cap] (norms must then
- *         stay below 65504; the pointer is passed as the same float*).  The
- *         K and V specs of one decode must agree on norm_f16.
+ *         rounded to nearest even and saturated at 65504, the largest finite
+ *         binary16 value (a larger norm is stored as 65504, and the decode
+ *         then scales that vector down), uint16 [n_streams][cap]; the pointer
+ *         is passed as the same float*.  The K and V specs of one decode must
+ *         agree on norm_f16.
  * qjl_signs  [n_streams][cap][qjl_m/8] bytes, bit j set iff (S r)_j >= 0
  *         (r = rotated unit vector minus its centroids); NULL if qjl_m == 0.
  * qjl_rnorms fp32 [n_streams][cap]: ||r||; NULL if qjl_m == 0.
@@ -152,9 +154,14 @@ const char* tq_last_error(void);
  * 1 <= bits <= 8.  Deterministic. */
 tq_status tq_codebook_build(int32_t d, int32_t bits, double* centroids, double* boundaries);
 
-/* Host only.  The seeded rotation Pi (d x d, row-major, y = Pi x): the Q
+/* Host only.  The seeded rotation Pi (d x d, row-major, y = Pi x) that
+ * every vector goes through before its coordinates are quantized (noze.it
+ * page, section "Il metodo TurboQuant, in breve": the vector is first rotated
+ * at random, which gives its coordinates a known law).  The page does not say
+ * how the rotation is drawn; this is the Haar-distributed reading: the Q
  * factor of a SplitMix64/Box-Muller Gaussian matrix, with column signs chosen
- * so that R has a positive diagonal (Haar measure).  1 <= d <= 1024. */
+ * so that R has a positive diagonal.  Writes d*d doubles to the caller's
+ * host buffer `pi`.  1 <= d <= 1024, else TQ_E_ARG. */
 tq_status tq_rotation_build(int32_t d, uint64_t seed, double* pi);
 
 /* Host only.  The seeded randomized Hadamard rotation (noze.it page, section
@@ -166,8 +173,12 @@ tq_status tq_rotation_build(int32_t d, uint64_t seed, double* pi);
  * 1 <= d <= 1024; row-major, y = Pi x. */
 tq_status tq_hadamard_rotation_build(int32_t d, uint64_t seed, double* pi);
 
-/* Host only.  The QJL sketch S (m x d, row-major), i.i.d. N(0,1) from the
- * same generator seeded with `seed`.  1 <= m, d <= 1024. */
+/* Host only.  The sketch matrix S (m x d, row-major) of the second stage
+ * (noze.it page, section "Il metodo TurboQuant, in breve": a 1-bit quantized
+ * Johnson-Lindenstrauss transform of the residual, which removes the bias of
+ * the inner-product estimate): i.i.d. N(0,1) entries from the same generator
+ * seeded with `seed`, not orthogonalised.  Writes m*d doubles to the
+ * caller's host buffer `s`.  1 <= m, d <= 1024, else TQ_E_ARG. */
 tq_status tq_sketch_build(int32_t m, int32_t d, uint64_t seed, double* s);
 
 /* Size in bytes of the device tables of one tq_spec (same for every spec). */
@@ -227,7 +238,12 @@ tq_status tq_quantize_kv_ragged(const tq_spec* spec, const void* tables, int32_t
 /* Workspace bytes tq_attend_decode needs for this problem. */
 size_t tq_attend_workspace_bytes(const tq_attn* attn);
 
-/* One decode step of attention read directly from the packed cache.
+/* One decode step of attention read directly from the packed cache
+ * (noze.it page, section "Il metodo TurboQuant, in breve": inner products are
+ * taken against the codebook reconstruction in the rotated domain, plus the
+ * sketch's correction of the residual; GitHub issue "Greetings from
+ * TurboQuant-MLX & Some Insights to Share!", items 1 and 3: raw sink tokens
+ * and skipped values of negligible weight).
  *   ks/ktables/kc  keys: TQ_LAYOUT_RECORD, optional QJL sketch
  *   vs/vtables/vc  values: TQ_LAYOUT_TILED, no QJL
  *   q        device fp32 [batch][hq][d]; batch <= 65535, hq / hkv <= 16
@@ -238,7 +254,10 @@ size_t tq_attend_workspace_bytes(const tq_attn* attn);
  *   seq_lens device int32 [batch]: tokens of each sequence including the
  *            sink; compressed token t >= sink lives at cache position t-sink.
  *            Each value must lie in [0, sink + min(kc->cap, vc->cap)] and
- *            not exceed max_len.  A sequence of length 0 gives zeros.
+ *            not exceed max_len (the kernels clamp a value outside [0,
+ *            max_len] into it, so no access leaves the validated cache, but
+ *            the output is then unspecified).  A sequence of length 0 gives
+ *            zeros.
  *   out      device fp32 [batch][hq][d]
  *   workspace device, >= tq_attend_workspace_bytes(attn) bytes, 16-byte
  *            aligned; no state is kept in it between calls.  Calls that

@@ -21,7 +21,8 @@ Readings (the page is silent on these):
   library that the pages do not describe; the port they discuss only brings
   the cache back to float16 for attention, noze.it page, section "Cosa
   aggiunge turboquant-mlx") that fp32 value is rounded once more, to
-  binary16, nearest even;
+  binary16, nearest even, saturating at the largest finite value 65504 (a
+  norm that would round to infinity is stored as 65504);
 * a zero vector quantizes y = 0 and stores norm 0;
 * index = number of thresholds strictly below y (exact ties go to the lower
   index);
@@ -36,6 +37,8 @@ import numpy as np
 
 from .codebook import lloyd_max
 from .rotation import hadamard_rotation, rotation, sketch
+
+F16_MAX = 65504.0   # largest finite binary16 value
 
 
 @dataclass(frozen=True)
@@ -121,7 +124,8 @@ def quantize(x: np.ndarray, spec: Spec, pi: np.ndarray | None = None,
     idx = scalar_quantize(y, spec)
     stored = nrm.astype(np.float32)
     if spec.norm_f16:
-        stored = stored.astype(np.float16)
+        # saturate at the largest finite binary16 value rather than round to +inf
+        stored = np.minimum(stored, np.float32(F16_MAX)).astype(np.float16)
     out = Quantized(idx=idx, norms=stored, norms64=nrm, y=y)
     if spec.qjl_m:
         s_mat = sketch_of(spec) if s_mat is None else s_mat

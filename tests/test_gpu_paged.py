@@ -1,13 +1,17 @@
 """Paged caches: the quantize appends into pool pages through a device block
-table and the decode reads through it.  The contiguous path is the reference: the
-same codes land at the mapped positions bit for bit, and the decode over the
-pages gives the contiguous decode's output exactly (same plan, same
-arithmetic), which is itself held to the oracle."""
+table and the decode reads through it.  The oracle is the reference: the codes,
+norms and sketch read back through the block table pass the parity rules
+against the oracle's quantization of the source vectors, and the paged decode
+output is within the attention bar of the oracle's attention on those codes.
+As extra checks, the same codes land at the mapped positions as in the
+contiguous cache, bit for bit, and the paged decode equals the contiguous
+decode exactly (same plan, same arithmetic)."""
 import numpy as np
 import pytest
 
 from compressed_kv_cache_tq_amd import tq, workloads
-from gpu_helpers import Run, read_codes, read_norms, read_signs, to_device, torch
+from gpu_helpers import Run, check_quantized, oracle_attention, read_codes, read_norms, read_signs, to_device, torch
+from oracle import parity
 
 pytestmark = pytest.mark.gpu
 P = tq.PAGE_TOKENS
@@ -70,6 +74,64 @@ def _paged_quantize(run, bt, n_pages, chunk, poison=False):
     return kpool, vpool, comp
 
 
+def _gather(run, kpool, vpool, bt, comp):
+    """Per (sequence, kv head): codes, norms (and sketch) of the compressed
+    tokens read from the pools page by page through the block table, in the
+    layout Run.gpu_codes returns."""
+    H = run.wl.hkv
+    K, Kn, V, Vn, Z, R = ([] for _ in range(6))
+    for b in range(run.B):
+        rows = [[] for _ in range(6)]
+        for h in range(H):
+            parts = [[] for _ in range(6)]
+            for lp in range(-(-comp[b] // P)):
+                n = min(P, comp[b] - lp * P)
+                ps = int(bt[b, lp]) * H + h
+                parts[0].append(read_codes(run.kspec, kpool, ps, n))
+                parts[1].append(read_norms(kpool, ps, n))
+                parts[2].append(read_codes(run.vspec, vpool, ps, n))
+                parts[3].append(read_norms(vpool, ps, n))
+                if run.kspec.qjl_m:
+                    z, r = read_signs(kpool, ps, n)
+                    parts[4].append(z)
+                    parts[5].append(r)
+            empty = [np.zeros((0, 128), np.int64), np.zeros(0, kpool.norms.cpu().numpy().dtype)]
+            for i in range(4):
+                rows[i].append(np.concatenate(parts[i]) if parts[i] else empty[i % 2])
+            if run.kspec.qjl_m:
+                rows[4].append(np.concatenate(parts[4]) if parts[4] else np.zeros((0, 128), bool))
+                rows[5].append(np.concatenate(parts[5]) if parts[5] else np.zeros(0, np.float32))
+        for dst, src in zip((K, Kn, V, Vn, Z, R), rows):
+            dst.append(src)
+    return K, Kn, V, Vn, (Z if run.kspec.qjl_m else None), (R if run.kspec.qjl_m else None)
+
+
+def _check_against_oracle(run, kpool, vpool, bt, comp, out, label):
+    """Pool contents through the block table against the oracle's quantization
+    of the source vectors, and the paged decode output against the oracle's
+    attention on those codes."""
+    wl, S = run.wl, run.wl.sink
+    K, Kn, V, Vn, Z, R = _gather(run, kpool, vpool, bt, comp)
+    for b in range(run.B):
+        if not comp[b]:
+            continue
+        for h in range(wl.hkv):
+            xk = run.inp.k[b][h, S:S + comp[b]]
+            xv = run.inp.v[b][h, S:S + comp[b]]
+            signs = (Z[b][h], R[b][h]) if Z is not None else None
+            check_quantized(run.kspec, xk, K[b][h], Kn[b][h], signs=signs, label=f"{label} K b{b} h{h}")
+            check_quantized(run.vspec, xv, V[b][h], Vn[b][h], label=f"{label} V b{b} h{h}")
+    sk = sv = None
+    if S:
+        sk = [[run.inp.k[b][h, :S].astype(np.float64) for h in range(wl.hkv)] for b in range(run.B)]
+        sv = [[run.inp.v[b][h, :S].astype(np.float64) for h in range(wl.hkv)] for b in range(run.B)]
+    ref = oracle_attention(run.inp.q, run.kspec, run.vspec, run.inp.seq_lens, K, Kn, V, Vn, k_bits=Z, k_gamma=R,
+                           sink_k=sk, sink_v=sv, sink=S, v_skip=wl.v_skip)
+    err = parity.rel_l2(out.cpu().numpy(), ref)
+    print(f"  {label}: paged decode vs oracle rel L2 {err:.2e}", flush=True)
+    assert err <= parity.ATTN_REL_L2, f"{label}: paged decode vs oracle rel L2 {err:.3e}"
+
+
 @pytest.mark.parametrize("name,ctx,batch,chunk", [
     ("tiny_oracle", None, None, 45),
     ("gqa_decode", 1500, None, 37),
@@ -110,6 +172,7 @@ def test_paged_codes_and_decode_match_contiguous(name, ctx, batch, chunk):
                            hkv=H, block_table=btd, n_pages=n_pages, sink=wl.sink, sink_k=run.sink_k,
                            sink_v=run.sink_v, v_skip=wl.v_skip, max_len=run.max_len)
     T.cuda.synchronize()
+    _check_against_oracle(run, kpool, vpool, bt, comp, out, f"paged {name}")
     assert T.equal(out, ref_out), f"{name}: paged decode differs from the contiguous decode"
 
 
@@ -239,6 +302,7 @@ def test_paged_prefill_then_token_by_token_appends(qjl):
     tq.attend_decode_paged(run.kspec, run.ktab, kpool, run.vspec, run.vtab, vpool, run.q, run.seq_lens, out, run.ws,
                            hkv=H, block_table=btd, n_pages=n_pages, max_len=run.max_len)
     T.cuda.synchronize()
+    _check_against_oracle(run, kpool, vpool, bt, comp, out, f"paged serve qjl={qjl}")
     assert T.equal(out, run.out)
 
 
@@ -268,6 +332,7 @@ def test_paged_eight_bit_keys():
     tq.attend_decode_paged(run.kspec, run.ktab, kpool, run.vspec, run.vtab, vpool, run.q, run.seq_lens, out, run.ws,
                            hkv=4, block_table=T.from_numpy(bt).cuda(), n_pages=n_pages, max_len=run.max_len)
     T.cuda.synchronize()
+    _check_against_oracle(run, kpool, vpool, bt, comp, out, "paged K8/V3")
     assert T.equal(out, run.out)
 
 
@@ -299,4 +364,5 @@ def test_paged_fp16_norms():
                            hkv=H, block_table=T.from_numpy(bt).cuda(), n_pages=n_pages, sink=wl.sink,
                            sink_k=run.sink_k, sink_v=run.sink_v, v_skip=wl.v_skip, max_len=run.max_len)
     T.cuda.synchronize()
+    _check_against_oracle(run, kpool, vpool, bt, comp, out, "paged fp16 norms")
     assert T.equal(out, run.out)

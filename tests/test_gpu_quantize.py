@@ -434,3 +434,28 @@ def test_quantize_fp16_norms(bits, layout, qjl):
     signs = read_signs(cache, 0, 1000, 37) if qjl else None
     check_quantized(spec, x[0], read_codes(spec, cache, 0, 1000, 37), read_norms(cache, 0, 1000, 37), signs=signs,
                     label=f"fp16 norms {bits}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bits,layout,qjl", [((4, None, 128), tq.LAYOUT_RECORD, 0), ((3, None, 128), tq.LAYOUT_TILED, 0),
+                                             ((2, None, 128), tq.LAYOUT_RECORD, 128)])
+def test_quantize_fp16_norms_saturate(bits, layout, qjl, dtype):
+    """fp16 norms at the top of the binary16 range: a norm that would round to
+    infinity is stored as 65504, as the oracle reads it; the codes do not
+    depend on the norm's size."""
+    print(f"[quantize] fp16 norm saturation {bits} layout={layout} qjl={qjl} {dtype}", flush=True)
+    spec = tq.Spec(bits[0], bits[1], split=bits[2], layout=layout, qjl_m=qjl, norm_f16=1)
+    x = _data(96, seed=62, dtype=dtype)
+    big = [65472.0, 65519.0, 65520.0, 65536.0, 70000.0, 1.0e6, 65280.0] if dtype == "f32" else \
+          [65280.0, 65536.0, 70144.0, 1.0e6]
+    for i, v in enumerate(big):
+        x[0, 3 * i + 1] = 0.0
+        x[0, 3 * i + 1, (17 * i) % 128] = v
+        x[0, 3 * i + 2] *= np.float32(v / 11.0)        # a full vector of that size too
+    if dtype == "bf16":
+        x = workloads.bf16_to_f32(workloads.bf16_bits(x))
+    cache = _quantize(spec, x, dtype)
+    norms = read_norms(cache, 0, 96)
+    assert np.all(np.isfinite(norms.astype(np.float32))), "an fp16 norm overflowed to infinity"
+    signs = read_signs(cache, 0, 96) if qjl else None
+    check_quantized(spec, x[0], read_codes(spec, cache, 0, 96), norms, signs=signs, label=f"fp16 saturation {bits}")

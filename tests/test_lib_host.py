@@ -436,3 +436,48 @@ def test_eight_bit_quantize_stride_limit():
     rs = (1 << 30) // (32 * 2)  # bf16 elements
     assert L.tq_quantize_kv(ctypes.byref(spec.c()), ctypes.c_void_p(0x10000), 1, 0x4000, 1, 2, rs, rs, 0,
                             ctypes.byref(cache), None) == -2
+
+
+def test_binding_refuses_a_cache_of_another_spec():
+    """The C side gets bare pointers, so the binding checks that a cache was
+    sized for the spec it is used with (widths, split, sketch, layout, norm
+    width) and holds the streams the call touches; caches on the CPU are
+    enough, nothing is launched."""
+    torch = pytest.importorskip("torch")
+    k4 = tq.Spec(4)
+    k4h = tq.Spec(4, norm_f16=1)
+    v3 = tq.Spec(3, layout=tq.LAYOUT_TILED)
+    x = torch.zeros((2, 40, 128), dtype=torch.bfloat16)
+    good = tq.alloc_cache(k4, 2, 64, device="cpu")
+    for bad_spec in (k4h, tq.Spec(3), tq.Spec(4, 3, split=64), tq.Spec(2, qjl_m=128),
+                     tq.Spec(4, layout=tq.LAYOUT_TILED)):
+        with pytest.raises(ValueError):
+            tq.quantize_kv(bad_spec, None, x, good)
+    # an fp32-norm cache with an fp16-norm spec, and the reverse, whatever spec the cache claims
+    half = tq.alloc_cache(k4h, 2, 64, device="cpu")
+    with pytest.raises(ValueError):
+        tq.quantize_kv(k4, None, x, tq.Cache(k4, 64, half.codes, half.norms))
+    with pytest.raises(ValueError):
+        tq.quantize_kv(k4h, None, x, tq.Cache(k4h, 64, good.codes, good.norms))
+    # fewer streams than the call touches
+    with pytest.raises(ValueError):
+        tq.quantize_kv(k4, None, torch.zeros((3, 40, 128), dtype=torch.bfloat16), good)
+    with pytest.raises(ValueError):
+        tq.quantize_kv_ragged(k4, None, torch.zeros((4, 40, 128), dtype=torch.bfloat16), good, hkv=2,
+                              n_tok=[10, 10])
+    vgood = tq.alloc_cache(v3, 2, 64, device="cpu")
+    q = torch.zeros((1, 8, 128))
+    lens = torch.zeros(1, dtype=torch.int32)
+    out = torch.zeros_like(q)
+    with pytest.raises(ValueError):
+        tq.attend_decode(k4, None, good, v3, None, tq.alloc_cache(tq.Spec(2, layout=tq.LAYOUT_TILED), 2, 64,
+                                                                     device="cpu"),
+                         q, lens, out, None, hkv=2)
+    with pytest.raises(ValueError):
+        tq.attend_decode(k4, None, good, v3, None, vgood, torch.zeros((2, 8, 128)), lens, out, None, hkv=2)
+    with pytest.raises(ValueError):
+        tq.ip_scores(tq.Spec(2, qjl_m=128), None, good, q[0], n_streams=2, n_tok=8, workspace=torch.zeros(4))
+    # the right spec passes the binding's checks (the call itself would need a device)
+    tq._check_cache(k4, good, 2, "ok")
+    tq._check_cache(v3, vgood, 2, "ok")
+    tq._check_cache(k4h, half, 2, "ok")

@@ -226,3 +226,16 @@ def test_fp16_norms_round_the_fp32_norm_to_nearest_even():
     assert q.norms.view(np.uint16).tolist() == [0x3EEE, 0x6800, 0x6802]
     # codes do not depend on how the norm is stored
     assert np.array_equal(q.idx, qz.quantize(x, qz.Spec(bits_lo=4, bits_hi=4)).idx)
+
+
+def test_fp16_norms_saturate_at_the_largest_finite_value():
+    """Worked by hand: 65472 = 2046 * 32 is a binary16 value (0x7BFE); 65519 is
+    nearer 65504 (0x7BFF) than the next step 65536, which binary16 cannot
+    hold; 65520 is the halfway point that nearest-even would send to
+    infinity, and 70000 lies past it: both are stored as 65504, not +inf."""
+    spec = qz.Spec(bits_lo=4, bits_hi=4, norm_f16=True)
+    x = np.zeros((4, 128))
+    x[0, 0], x[1, 9], x[2, 100], x[3, 127] = 65472.0, 65519.0, -65520.0, 70000.0
+    q = qz.quantize(x, spec)
+    assert q.norms.view(np.uint16).tolist() == [0x7BFE, 0x7BFF, 0x7BFF, 0x7BFF]
+    assert np.all(np.isfinite(q.norms))
