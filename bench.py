@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the TurboQuant packed-KV hot path on one MI355X.
 
-One step = one pass of the whole path over one workload, by default the GQA
-decode workload (batch 1, 32 query heads / 8 KV heads, d = 128, context
-32768, bf16 K/V with 4 outlier key channels per head, K 4-bit records, V
-3-bit tiles); --workload selects another of the five:
+One step = one pass of the whole path over one workload, by default the
+batched decode workload, the largest of the five that the metric names no
+single one of (64 sequences with lengths uniform in [1024, 32768], 32 query
+heads / 8 KV heads, d = 128, bf16 K/V, K 4-bit records, V 2-bit tiles, the
+first 128 tokens of every sequence raw bf16, V skipped below weight 1e-6);
+--workload selects another of the five:
   quantize all K vectors, quantize all V vectors, one decode-attention step.
 Inputs are resident in HBM before timing.  Four copies of the inputs and of
 the packed cache rotate between steps, and a step attends over a cache copy
@@ -33,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "packed-KV decode-attention GB/s (% HBM peak) + quantize Mvec/s at d=128"
-WORKLOAD = "gqa_decode"
+WORKLOAD = "batched_ragged"
 COPIES = 4
 ATT_COPIES = 10
 KERNEL_SOURCES = ["compressed_kv_cache_tq_amd/csrc/quantize.hip",
@@ -49,10 +51,11 @@ def source_hash(paths: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(name: str):
-    """Per-dispatch HBM bytes measured with rocprofv3 --pmc for a kernel, or None
-    if the summary is missing or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+def read_traffic(workload: str, name: str):
+    """Per-call HBM bytes measured with rocprofv3 --pmc for a step phase of a
+    workload, or None if the summary is missing or the kernel source changed
+    since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{name}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -63,18 +66,33 @@ def read_traffic(name: str):
     src = kv.get("source")
     if not src or kv.get("source_sha256_16") != source_hash(src):
         return None
-    return float(kv["hbm_bytes_per_dispatch"])
+    return float(kv["hbm_bytes_per_call"])
 
 
 CALIB_BYTES = 512 << 20
-# Kernels of one bench step, by the name rocprofv3 reports, and the traffic
-# file each one's counters go to.
-STEP_KERNELS = {
-    "quantize_k": ["rotq_kernel<4, 4, false, false, 8, false, false>"],
-    "quantize_v": ["rotq_kernel<3, 3, false, true, 8, false, false>"],
-    "attend": ["split_kernel<4, 4, 3, 3, false, false, false>", "combine_kernel"],
-}
 STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0], "attend": KERNEL_SOURCES[1]}
+
+
+def step_kernels(wname: str) -> dict:
+    """Kernels of one bench step of a workload (default options), by the name
+    rocprofv3 reports: the traffic of a phase is the sum over its kernels."""
+    from compressed_kv_cache_tq_amd import workloads
+    wl = workloads.WORKLOADS[wname]
+    f32 = "true" if wl.dtype == "f32" else "false"
+    k, v = wl.k, wl.v
+    # (kernel, dispatches per call)
+    if k.qjl_m:  # the sketch kernel launches once per sequence
+        qk = [(f"quantize_kernel<{k.bits_lo}, {k.bits_hi}, {2 if wl.dtype == 'f32' else 1}, false, true>", wl.batch)]
+    else:
+        qk = [(f"rotq_kernel<{k.bits_lo}, {k.bits_hi}, {f32}, false, 8, false, false>", 1)]
+    qv = [(f"rotq_kernel<{v.bits_lo}, {v.bits_hi}, {f32}, true, 8, false, false>", 1)]
+    if wl.lens_range:  # ragged lengths: the last, partly written value tile of each sequence
+        qv.append((f"rotq_kernel<{v.bits_lo}, {v.bits_hi}, {f32}, true, 2, true, false>", 1))
+    at = [(f"split_kernel<{k.bits_lo}, {k.bits_hi}, {v.bits_lo}, {v.bits_hi}, {'true' if k.qjl_m else 'false'}, "
+           f"false, false>", 1)]
+    if not wl.lens_range:
+        at.append(("combine_kernel", 1))
+    return {"quantize_k": qk, "quantize_v": qv, "attend": at}
 
 
 def _pmc_per_dispatch(run_dir: str, counter: str):
@@ -97,10 +115,12 @@ def _pmc_per_dispatch(run_dir: str, counter: str):
     return per
 
 
-def traffic_summary(fetch_dir: str, write_dir: str, command: str = "") -> int:
-    """HBM bytes per dispatch of each bench kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch) scaled by the factor that maps the same counter of the
-    calibration copy onto its known CALIB_BYTES read and written."""
+def traffic_summary(fetch_dir: str, write_dir: str, wname: str, command: str = "") -> int:
+    """HBM bytes per call of each bench phase: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch, summed over the phase's kernels) scaled by the factor that
+    maps the same counter of the calibration copy onto its known CALIB_BYTES
+    read and written."""
+    STEP_KERNELS = step_kernels(wname)
     out = {}
     for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _pmc_per_dispatch(run_dir, counter)
@@ -110,21 +130,22 @@ def traffic_summary(fetch_dir: str, write_dir: str, command: str = "") -> int:
         factor = CALIB_BYTES / (1024.0 * float(np.median(calib)))
         for key, names in STEP_KERNELS.items():
             tot, raw = 0.0, 0.0
-            for kname in names:
+            for kname, mult in names:
                 vals = [v for n, v in per.values() if kname in n.replace("(anonymous namespace)::", "")]
                 if not vals:
                     raise SystemExit(f"{run_dir}: no dispatch of {kname}")
-                tot += float(np.mean(vals)) * 1024.0 * factor
-                raw += float(np.mean(vals))
+                tot += mult * float(np.mean(vals)) * 1024.0 * factor
+                raw += mult * float(np.mean(vals))
             out.setdefault(key, {})[counter] = (tot, factor, raw, float(np.median(calib)))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for key, d in out.items():
         fetch, ff, fraw, fcal = d["FETCH_SIZE"]
         write, fw, wraw, wcal = d["WRITE_SIZE"]
         src = STEP_SOURCES[key]
-        path = os.path.join(ROOT, "profiles", f"traffic_{key}.txt")
+        path = os.path.join(ROOT, "profiles", f"traffic_{wname}_{key}.txt")
         with open(path, "w") as f:
-            f.write(f"# HBM traffic per dispatch of {', '.join(STEP_KERNELS[key])} (gqa_decode bench step),\n")
+            kl = ", ".join(f"{n}{f' x {m}' if m > 1 else ''}" for n, m in STEP_KERNELS[key])
+            f.write(f"# HBM traffic per call of {kl} ({wname} bench step),\n")
             f.write("# from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by the factor that maps\n")
             f.write(f"# the counter of a {CALIB_BYTES >> 20} MiB fp32 streaming kernel onto its known bytes.\n")
             if command:
@@ -137,17 +158,49 @@ def traffic_summary(fetch_dir: str, write_dir: str, command: str = "") -> int:
             f.write(f"calibration_write_kib_raw = {wcal:.1f}\n")
             f.write(f"fetch_factor = {ff:.4f}\n")
             f.write(f"write_factor = {fw:.4f}\n")
-            f.write(f"fetch_bytes_per_dispatch = {fetch:.0f}\n")
-            f.write(f"write_bytes_per_dispatch = {write:.0f}\n")
-            f.write(f"hbm_bytes_per_dispatch = {fetch + write:.0f}\n")
+            f.write(f"fetch_bytes_per_call = {fetch:.0f}\n")
+            f.write(f"write_bytes_per_call = {write:.0f}\n")
+            f.write(f"hbm_bytes_per_call = {fetch + write:.0f}\n")
         print(open(path).read())
     return 0
 
 
-def cpu_baseline(inp, run_codes, wl, kspec, vspec):
-    """The float64 oracle on the host: decode attention over the GPU's packed
-    cache (all heads, median of 3 runs) plus quantize + pack of one KV head's
-    keys (32768 vectors)."""
+def stats_summary(csv_path: str, out_path: str, title: str = "", command: str = "") -> int:
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run (its
+    kernel_stats.csv, durations in ns) as a short text table in microseconds."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    with open(out_path, "w") as f:
+        if title:
+            f.write(f"# {title}\n")
+        if command:
+            f.write(f"# command: {command}\n")
+        f.write("# source: rocprofv3 kernel_stats.csv; durations in microseconds\n")
+        f.write(f"{'kernel':<80} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'stddev':>8}\n")
+        for r in rows:
+            name = r["Name"].replace("(anonymous namespace)::", "")
+            name = name[:80]
+            f.write(f"{name:<80} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                    f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
+                    f"{float(r['StdDev']) / 1e3:>8.2f}\n")
+    print(open(out_path).read())
+    return 0
+
+
+def _oracle_spec(spec):
+    from oracle import quantize as oqz
+    return oqz.Spec(bits_lo=spec.bits_lo, bits_hi=spec.bits_lo if spec.bits_hi is None else spec.bits_hi,
+                    split=spec.split, qjl_m=spec.qjl_m, rot_seed=spec.rot_seed, qjl_seed=spec.qjl_seed,
+                    rotation="hadamard" if spec.rotation == 1 else "haar", norm_f16=bool(spec.norm_f16))
+
+
+def cpu_baseline(inp, wl, kspec, vspec, kc, vc, comp_h, sample, tok_bytes, n_quant=65536):
+    """The float64 oracle on the host, on a bounded sample of the step: one
+    decode step of the sampled sequences (all their KV and query heads) read
+    from the GPU's packed cache (unpacking included, median of 3 runs), and
+    quantize + pack of the first n_quant key vectors of the first sampled
+    sequence.  Also the oracle's exact V-skip count on that decode sample."""
+    from compressed_kv_cache_tq_amd import tq
     from oracle import attend as oat
     from oracle import pack as opk
     from oracle import quantize as oqz
@@ -156,39 +209,88 @@ def cpu_baseline(inp, run_codes, wl, kspec, vspec):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    ks = oqz.Spec(bits_lo=kspec.bits_lo, bits_hi=kspec.bits_lo, split=128)
-    vs = oqz.Spec(bits_lo=vspec.bits_lo, bits_hi=vspec.bits_lo, split=128)
-    kraw, kn, vraw, vn = run_codes
-    T = wl.ctx
-    G = wl.hq // wl.hkv
-    pi = oqz.rotation_of(ks)
+    ks, vs = _oracle_spec(kspec), _oracle_spec(vspec)
+    Hkv, S = wl.hkv, wl.sink
+    kcb = tq.code_bytes(kspec)
+    nbk, nbv = tq.cache_code_bytes(kspec, kc.cap), tq.cache_code_bytes(vspec, vc.cap)
+    m8 = kspec.qjl_m // 8
+    raw = []  # per sampled sequence, per kv head: the packed arrays as stored on the GPU
+    for b in sample:
+        n = int(comp_h[b])
+        rows = []
+        for h in range(Hkv):
+            st = b * Hkv + h
+            r = {"k": kc.codes[st * nbk: st * nbk + n * kcb].cpu().numpy().reshape(n, kcb),
+                 "v": vc.codes[st * nbv:(st + 1) * nbv].cpu().numpy(),
+                 "kn": kc.norms[st * kc.cap: st * kc.cap + n].cpu().numpy(),
+                 "vn": vc.norms[st * vc.cap: st * vc.cap + n].cpu().numpy()}
+            if m8:
+                r["z"] = kc.qjl_signs[st * kc.cap * m8:(st * kc.cap + n) * m8].cpu().numpy().reshape(n, m8)
+                r["g"] = kc.qjl_rnorms[st * kc.cap: st * kc.cap + n].cpu().numpy()
+            rows.append(r)
+        raw.append(rows)
+    lens = np.asarray(inp.seq_lens)[sample]
+    q = inp.q[sample]
+    sk = sv = None
+    if S:
+        sk = [[inp.k[b][h, :S] for h in range(Hkv)] for b in sample]
+        sv = [[inp.v[b][h, :S] for h in range(Hkv)] for b in sample]
+
+    def unpack():
+        K, Kn, V, Vn, Z, R = ([] for _ in range(6))
+        for i, b in enumerate(sample):
+            n = int(comp_h[b])
+            K.append([opk.unpack_records(r["k"], kspec.widths) for r in raw[i]])
+            V.append([opk.unpack_tiled(r["v"], vspec.widths, n) for r in raw[i]])
+            Kn.append([r["kn"] for r in raw[i]])
+            Vn.append([r["vn"] for r in raw[i]])
+            if m8:
+                Z.append([opk.unpack_sign_bits(r["z"]) for r in raw[i]])
+                R.append([r["g"] for r in raw[i]])
+        return K, Kn, V, Vn, (Z if m8 else None), (R if m8 else None)
 
     def decode_once():
         t0 = time.perf_counter()
-        for h in range(wl.hkv):
-            kidx = opk.unpack_records(kraw[h], kspec.widths)
-            vidx = opk.unpack_tiled(vraw[h], vspec.widths, T)
-            khat = oqz.dequantize_rotated(kidx, ks)
-            vhat = oqz.dequantize_rotated(vidx, vs)
-            for g in range(G):
-                qq = inp.q[0, h * G + g].astype(np.float64)
-                oat.attend_rotated(qq, pi @ qq, khat, kn[h], vhat, vn[h], pi, scale=1 / np.sqrt(128))
+        K, Kn, V, Vn, Z, R = unpack()
+        oat.attend(q, ks, vs, lens, K, Kn, V, Vn, k_bits=Z, k_gamma=R, sink_k=sk, sink_v=sv, sink=S,
+                   v_skip=wl.v_skip)
         return time.perf_counter() - t0
 
     t_dec = float(np.median([decode_once() for _ in range(3)]))
-    dec_bytes = wl.hkv * T * (kspec_bytes(kspec) + 4 + kspec_bytes(vspec) + 4) + 2 * wl.hq * 128 * 4
-    xs = inp.k[0][0].astype(np.float64)
+    n_tok = int(np.sum(comp_h[sample]))
+    dec_bytes = Hkv * n_tok * tok_bytes + Hkv * int(np.minimum(lens, S).sum()) * 2 * 128 * 2 + \
+        2 * len(sample) * wl.hq * 128 * 4
+    res = {"value": round(dec_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "decode_seconds": round(t_dec, 3)}
+    # the oracle's exact V-skip rule (final weight below the threshold) on the decode sample
+    skipped = total = 0
+    if wl.v_skip > 0:
+        K, Kn, V, Vn, Z, R = unpack()
+        G = wl.hq // Hkv
+        for i in range(len(sample)):
+            for h in range(Hkv):
+                _, det = oat.attend_group(q[i, h * G:(h + 1) * G], ks, K[i][h], Kn[i][h], vs, V[i][h], Vn[i][h],
+                                          k_bits=None if Z is None else Z[i][h],
+                                          k_gamma=None if R is None else R[i][h],
+                                          sink_k=None if sk is None else sk[i][h],
+                                          sink_v=None if sv is None else sv[i][h], v_skip=wl.v_skip,
+                                          return_details=True)
+                for _, keep, _ in det:
+                    skipped += int(np.sum(~keep))
+                    total += keep.size
+        res["v_skip_rate_oracle"] = round(skipped / max(total, 1), 6)
+    b0 = sample[0]
+    nq = min(n_quant, int(comp_h[b0]) * Hkv)
+    xs = inp.k[b0][:, S:S + int(comp_h[b0])].reshape(-1, 128)[:nq].astype(np.float64)
     t1 = time.perf_counter()
     qq = oqz.quantize(xs, ks)
     opk.pack_records(qq.idx, kspec.widths)
     t_q = time.perf_counter() - t1
-    return {
-        "value": round(dec_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"decode: full step (8 KV heads x {T} tokens, 32 q heads) on the GPU's packed cache, "
-                  f"median of 3; quantize: the {len(xs)} key vectors of KV head 0",
-        "decode_seconds": round(t_dec, 3),
-        "quantize_Mvec_s": round(len(xs) / t_q / 1e6, 5),
-    }
+    res["quantize_Mvec_s"] = round(nq / t_q / 1e6, 5)
+    res["sample"] = (f"decode: one step of sequences {list(map(int, sample))} ({n_tok} compressed tokens x {Hkv} "
+                     f"KV heads, {wl.hq} query heads each) read from the GPU's packed cache, unpacking "
+                     f"included, median of 3; quantize + pack: {nq} key vectors of sequence {int(b0)}")
+    return res
 
 
 def kspec_bytes(spec) -> int:
@@ -301,7 +403,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default=WORKLOAD, help="workload to time (the metric is quoted on gqa_decode)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="workload to time (default: batched_ragged, the largest single-GPU configuration)")
     ap.add_argument("--rotation", choices=("haar", "hadamard"), default="haar",
                     help="how the rotation is drawn (the workloads are specified with the Haar rotation)")
     ap.add_argument("--kbits", type=int, choices=(8,), default=None,
@@ -314,12 +417,18 @@ def main() -> int:
                     help="after timing, run a plain 512 MiB fp32 streaming kernel (out = -in) 5 times; "
                          "its byte counts calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
-                         "WRITE_SIZE, with --copy-calibration) into profiles/traffic_*.txt")
+                    help="no GPU: turn two rocprofv3 --pmc runs of this script on --workload (FETCH_SIZE, then "
+                         "WRITE_SIZE, with --copy-calibration) into profiles/traffic_<workload>_*.txt")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT"),
+                    help="no GPU: turn the kernel_stats.csv of a rocprofv3 --kernel-trace --stats run into a "
+                         "short text summary (with --command and --title)")
+    ap.add_argument("--title", default="", help="first line of the --stats-summary file")
     ap.add_argument("--command", default="", help="command line recorded by --traffic-summary")
     args = ap.parse_args()
     if args.traffic_summary:
-        return traffic_summary(*args.traffic_summary, command=args.command)
+        return traffic_summary(*args.traffic_summary, args.workload, command=args.command)
+    if args.stats_summary:
+        return stats_summary(*args.stats_summary, title=args.title, command=args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); every box here has a single "
               f"MI355X and this path is not sharded across GPUs.", file=sys.stderr)
@@ -491,12 +600,12 @@ def main() -> int:
     else:
         dom_name, dom_ms, dom_bytes, dom_kernel = "quantize_v", qv_ms, qv_bytes, f"rotq_kernel<{vtag}>"
     dom_gbs = dom_bytes / (dom_ms / 1e3) / 1e9
-    default_cfg = wname == WORKLOAD and not args.paged and args.kbits is None and not nf16
-    traffic = read_traffic(dom_name) if default_cfg else None
+    default_cfg = not args.paged and args.kbits is None and not nf16 and args.rotation == "haar"
+    traffic = read_traffic(wname, dom_name) if default_cfg else None
     roofline = {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom_kernel,
                 "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2)}
-    att_traffic = read_traffic("attend") if default_cfg else None
+    att_traffic = read_traffic(wname, "attend") if default_cfg else None
     roofline_attend = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": att_traffic,
                        "kernel": f"split_kernel<{kb[0]},{kb[1]},{wl.v.bits_lo},{wl.v.bits_hi}"
@@ -530,14 +639,24 @@ def main() -> int:
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline and default_cfg:
-        a = (args.warmup + args.steps) % COPIES
-        nb_k, nb_v = tq.cache_code_bytes(kspec, T), tq.cache_code_bytes(vspec, T)
-        kraw = [kc[a].codes[h * nb_k:(h + 1) * nb_k].cpu().numpy().reshape(T, kcb) for h in range(Hkv)]
-        vraw = [vc[a].codes[h * nb_v:(h + 1) * nb_v].cpu().numpy() for h in range(Hkv)]
-        kn = [kc[a].norms[h * T:(h + 1) * T].cpu().numpy() for h in range(Hkv)]
-        vn = [vc[a].norms[h * T:(h + 1) * T].cpu().numpy() for h in range(Hkv)]
-        res["cpu_baseline"] = cpu_baseline(inp, (kraw, kn, vraw, vn), wl, kspec, vspec)
+    if not args.no_cpu_baseline and not args.paged:
+        # a bounded sample: the first sequences up to about 600k compressed token-heads
+        sample, tot = [], 0
+        for b in range(B):
+            if tot >= 600_000:
+                break
+            if comp_h[b] > 0:
+                sample.append(b)
+                tot += int(comp_h[b]) * Hkv
+        res["cpu_baseline"] = cpu_baseline(inp, wl, kspec, vspec, kc[0], vc[0], comp_h, sample, k_tok + v_tok)
+    if wl.v_skip > 0:
+        # The value tiles are loaded two tiles ahead, before their weights are
+        # known, so a skipped token saves its dequantization and MFMA work,
+        # not its bytes: no bytes are subtracted from the decode figures.
+        res["v_skip"] = {"threshold": wl.v_skip, "v_bytes_subtracted": 0,
+                         "oracle_skip_rate": res.get("cpu_baseline", {}).get("v_skip_rate_oracle"),
+                         "note": "skip rate of the exact rule (final weight < threshold) on the cpu_baseline "
+                                 "decode sample; the kernel's one-pass rule skips a subset of those tokens"}
     print(json.dumps(res), flush=True)
     return 0
 

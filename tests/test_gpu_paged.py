@@ -112,15 +112,14 @@ def _check_against_oracle(run, kpool, vpool, bt, comp, out, label):
     attention on those codes."""
     wl, S = run.wl, run.wl.sink
     K, Kn, V, Vn, Z, R = _gather(run, kpool, vpool, bt, comp)
-    for b in range(run.B):
-        if not comp[b]:
-            continue
-        for h in range(wl.hkv):
-            xk = run.inp.k[b][h, S:S + comp[b]]
-            xv = run.inp.v[b][h, S:S + comp[b]]
-            signs = (Z[b][h], R[b][h]) if Z is not None else None
-            check_quantized(run.kspec, xk, K[b][h], Kn[b][h], signs=signs, label=f"{label} K b{b} h{h}")
-            check_quantized(run.vspec, xv, V[b][h], Vn[b][h], label=f"{label} V b{b} h{h}")
+    # the band rule's count cap applies to all codes of a tensor together
+    keys = [(b, h) for b in range(run.B) if comp[b] for h in range(wl.hkv)]
+    cat = lambda arrs: np.concatenate([arrs[b][h] for b, h in keys])
+    xk = np.concatenate([run.inp.k[b][h, S:S + comp[b]] for b, h in keys])
+    xv = np.concatenate([run.inp.v[b][h, S:S + comp[b]] for b, h in keys])
+    signs = (cat(Z), cat(R)) if Z is not None else None
+    check_quantized(run.kspec, xk, cat(K), cat(Kn), signs=signs, label=f"{label} keys")
+    check_quantized(run.vspec, xv, cat(V), cat(Vn), label=f"{label} values")
     sk = sv = None
     if S:
         sk = [[run.inp.k[b][h, :S].astype(np.float64) for h in range(wl.hkv)] for b in range(run.B)]
