@@ -711,10 +711,12 @@ size_t tq_attend_workspace_bytes(const tq_attn* attn) {
 
 }  // extern "C"
 
-namespace {
+namespace tq {
 
-// Both decode entry points: the contiguous caches (block_table == NULL) and
-// the paged pools.
+tq_status set_error(tq_status st, const char* msg) { return fail(st, msg); }
+
+// Every decode entry point: the contiguous caches (block_table == NULL) and
+// the paged pools, with a caller's workspace or the static scratch.
 tq_status attend_checked(const tq_spec* ks, const void* ktables, const tq_cache* kc, const tq_spec* vs,
                          const void* vtables, const tq_cache* vc, const tq_attn* attn, const float* q,
                          const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens,
@@ -781,7 +783,7 @@ tq_status attend_checked(const tq_spec* ks, const void* ktables, const tq_cache*
   return hip_status(e, what);
 }
 
-}  // namespace
+}  // namespace tq
 
 extern "C" {
 
@@ -790,8 +792,8 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
                            const tq_attn* attn, const float* q, const uint16_t* sink_k,
                            const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                            void* workspace, size_t ws_bytes, void* stream) {
-  return attend_checked(ks, ktables, kc, vs, vtables, vc, attn, q, sink_k, sink_v, seq_lens, nullptr, 0, 0, out,
-                        workspace, ws_bytes, stream, "tq_attend_decode launch");
+  return tq::attend_checked(ks, ktables, kc, vs, vtables, vc, attn, q, sink_k, sink_v, seq_lens, nullptr, 0, 0,
+                            out, workspace, ws_bytes, stream, "tq_attend_decode launch");
 }
 
 tq_status tq_attend_decode_paged(const tq_spec* ks, const void* ktables, const tq_cache* kpool,
@@ -801,8 +803,8 @@ tq_status tq_attend_decode_paged(const tq_spec* ks, const void* ktables, const t
                                  int32_t max_pages, int64_t n_pages, float* out, void* workspace,
                                  size_t ws_bytes, void* stream) {
   if (!block_table) return fail(TQ_E_ARG, "block_table is NULL");
-  return attend_checked(ks, ktables, kpool, vs, vtables, vpool, attn, q, sink_k, sink_v, seq_lens, block_table,
-                        max_pages, n_pages, out, workspace, ws_bytes, stream, "tq_attend_decode_paged launch");
+  return tq::attend_checked(ks, ktables, kpool, vs, vtables, vpool, attn, q, sink_k, sink_v, seq_lens, block_table,
+                            max_pages, n_pages, out, workspace, ws_bytes, stream, "tq_attend_decode_paged launch");
 }
 
 tq_status tq_quantize_kv_paged(const tq_spec* spec, const void* tables, int32_t dtype, const void* x,

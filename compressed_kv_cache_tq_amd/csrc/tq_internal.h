@@ -145,4 +145,15 @@ hipError_t launch_attend(const Spec& ks, const Tables* ktab, const tq_cache& kc,
                          hipStream_t stream, const int32_t* block_table = nullptr, int max_pages = 0,
                          int n_pages = 0);
 
+// Sets the thread's tq_last_error text and returns st.
+tq_status set_error(tq_status st, const char* msg);
+
+// Validation and launch shared by the decode entry points (host.cpp):
+// block_table == NULL for a contiguous cache.
+tq_status attend_checked(const tq_spec* ks, const void* ktables, const tq_cache* kc, const tq_spec* vs,
+                         const void* vtables, const tq_cache* vc, const tq_attn* attn, const float* q,
+                         const uint16_t* sink_k, const uint16_t* sink_v, const int32_t* seq_lens,
+                         const int32_t* block_table, int32_t max_pages, int64_t n_pages, float* out,
+                         void* workspace, size_t ws_bytes, void* stream, const char* what);
+
 }  // namespace tq

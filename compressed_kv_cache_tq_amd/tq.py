@@ -30,8 +30,9 @@ EXPORTS = [
     "tq_tables_bytes", "tq_tables_build", "tq_code_bytes", "tq_cache_code_bytes", "tq_quantize_kv",
     "tq_quantize_kv_ragged",
     "tq_attend_workspace_bytes", "tq_attend_decode", "tq_ip_workspace_bytes", "tq_ip_scores",
-    "tq_quantize_kv_paged", "tq_attend_decode_paged",
+    "tq_quantize_kv_paged", "tq_attend_decode_paged", "tq_attend_decode_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 8 << 20
 IP_MAX_QUERIES = 64
 PAGE_TOKENS = 64
 
@@ -98,6 +99,9 @@ def lib() -> ctypes.CDLL:
                                P]),
         "tq_attend_decode": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache), ctypes.POINTER(TqSpec), P,
                                    ctypes.POINTER(TqCache), ctypes.POINTER(TqAttn), P, P, P, P, P, P, SZ, P]),
+        "tq_attend_decode_noalloc": (I32, [ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache),
+                                           ctypes.POINTER(TqSpec), P, ctypes.POINTER(TqCache),
+                                           ctypes.POINTER(TqAttn), P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -389,6 +393,25 @@ def attend_decode(kspec: Spec, ktables, kcache: Cache, vspec: Spec, vtables, vca
                                   _ptr(sink_k), _ptr(sink_v), seq_lens.data_ptr(), out.data_ptr(),
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), st),
            "tq_attend_decode")
+
+
+def attend_decode_noalloc(kspec: Spec, ktables, kcache: Cache, vspec: Spec, vtables, vcache: Cache, q, seq_lens,
+                          out, *, hkv: int, sink: int = 0, sink_k=None, sink_v=None, scale: float | None = None,
+                          v_skip: float = 0.0, max_len: int | None = None, stream: int | None = None) -> None:
+    """attend_decode without a workspace: the partials go to the library's
+    static device scratch (calls that overlap on one GPU race)."""
+    B, Hq, _ = q.shape
+    if max_len is None:
+        max_len = sink + min(kcache.cap, vcache.cap)
+    a = TqAttn(B, Hq, hkv, sink, (1.0 / np.sqrt(D)) if scale is None else scale, v_skip, max_len)
+    _check_cache(kspec, kcache, B * hkv, "attend_decode_noalloc keys")
+    _check_cache(vspec, vcache, B * hkv, "attend_decode_noalloc values")
+    ks, vs, kc, vc = kspec.c(), vspec.c(), kcache.c(), vcache.c()
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().tq_attend_decode_noalloc(ctypes.byref(ks), ktables.data_ptr(), ctypes.byref(kc), ctypes.byref(vs),
+                                          vtables.data_ptr(), ctypes.byref(vc), ctypes.byref(a), q.data_ptr(),
+                                          _ptr(sink_k), _ptr(sink_v), seq_lens.data_ptr(), out.data_ptr(), st),
+           "tq_attend_decode_noalloc")
 
 
 def alloc_ip_workspace(device="cuda"):

@@ -276,6 +276,21 @@ tq_status tq_attend_decode(const tq_spec* ks, const void* ktables, const tq_cach
                            const uint16_t* sink_v, const int32_t* seq_lens, float* out,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): the decode step
+ * of tq_attend_decode, same arguments and result, without the workspace.  The
+ * split partials go to a static device array of TQ_NOALLOC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends; the call itself
+ * allocates nothing.  A problem whose tq_attend_workspace_bytes exceeds that
+ * size is refused with TQ_E_UNSUPPORTED before any launch.  All calls on one
+ * GPU share its array: calls that overlap on one GPU (other streams or
+ * threads) race and must be serialised by the caller. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+tq_status tq_attend_decode_noalloc(const tq_spec* ks, const void* ktables, const tq_cache* kc,
+                                   const tq_spec* vs, const void* vtables, const tq_cache* vc,
+                                   const tq_attn* attn, const float* q, const uint16_t* sink_k,
+                                   const uint16_t* sink_v, const int32_t* seq_lens, float* out, void* stream);
+
 /* Paged cache (a pool of pages shared by all sequences).  A pool of n_pages
  * pages is a tq_cache with cap = TQ_PAGE_TOKENS and n_pages * hkv streams:
  * page p holds TQ_PAGE_TOKENS positions of every kv head h, as stream

@@ -481,3 +481,20 @@ def test_binding_refuses_a_cache_of_another_spec():
     tq._check_cache(k4, good, 2, "ok")
     tq._check_cache(v3, vgood, 2, "ok")
     tq._check_cache(k4h, half, 2, "ok")
+
+
+def test_noalloc_refuses_a_problem_beyond_its_scratch():
+    """tq_attend_decode_noalloc checks the problem's partials against its
+    static scratch first, before anything else and with no launch."""
+    L = tq.lib()
+    ks, vs = tq.Spec(4).c(), tq.Spec(3, layout=1).c()
+    kc = tq.TqCache(0x1000, 0x2000, None, None, 64)
+    vc = tq.TqCache(0x3000, 0x4000, None, None, 64)
+    big = tq.TqAttn(4096, 32, 8, 0, 0.1, 0.0, 64)              # 131072 heads x 528 B > 8 MiB
+    assert tq.attend_workspace_bytes(4096, 32, 8, 0, 64) > tq.NOALLOC_SCRATCH_BYTES
+    st = L.tq_attend_decode_noalloc(ctypes.byref(ks), ctypes.c_void_p(0x10000), ctypes.byref(kc), ctypes.byref(vs),
+                                    ctypes.c_void_p(0x10000), ctypes.byref(vc), ctypes.byref(big), 0x5000, None,
+                                    None, 0x6000, 0x7000, None)
+    assert st == -2 and "TQ_NOALLOC_SCRATCH_BYTES" in tq.last_error()
+    assert L.tq_attend_decode_noalloc(ctypes.byref(ks), None, ctypes.byref(kc), ctypes.byref(vs), None,
+                                      ctypes.byref(vc), None, 0x5000, None, None, 0x6000, 0x7000, None) == -1
