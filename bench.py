@@ -25,6 +25,7 @@ import dataclasses
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -75,7 +76,8 @@ STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0]
 
 def step_kernels(wname: str) -> dict:
     """Kernels of one bench step of a workload (default options), by the name
-    rocprofv3 reports: the traffic of a phase is the sum over its kernels."""
+    rocprofv3 reports ('*' stands for the tiles-per-chunk argument the launch
+    picks by size): the traffic of a phase is the sum over its kernels."""
     from compressed_kv_cache_tq_amd import workloads
     wl = workloads.WORKLOADS[wname]
     f32 = "true" if wl.dtype == "f32" else "false"
@@ -84,8 +86,8 @@ def step_kernels(wname: str) -> dict:
     if k.qjl_m:  # the sketch kernel launches once per sequence
         qk = [(f"quantize_kernel<{k.bits_lo}, {k.bits_hi}, {2 if wl.dtype == 'f32' else 1}, false, true>", wl.batch)]
     else:
-        qk = [(f"rotq_kernel<{k.bits_lo}, {k.bits_hi}, {f32}, false, 8, false, false>", 1)]
-    qv = [(f"rotq_kernel<{v.bits_lo}, {v.bits_hi}, {f32}, true, 8, false, false>", 1)]
+        qk = [(f"rotq_kernel<{k.bits_lo}, {k.bits_hi}, {f32}, false, *, false, false>", 1)]
+    qv = [(f"rotq_kernel<{v.bits_lo}, {v.bits_hi}, {f32}, true, *, false, false>", 1)]
     if wl.lens_range:  # ragged lengths: the last, partly written value tile of each sequence
         qv.append((f"rotq_kernel<{v.bits_lo}, {v.bits_hi}, {f32}, true, 2, true, false>", 1))
     at = [(f"split_kernel<{k.bits_lo}, {k.bits_hi}, {v.bits_lo}, {v.bits_hi}, {'true' if k.qjl_m else 'false'}, "
@@ -131,7 +133,8 @@ def traffic_summary(fetch_dir: str, write_dir: str, wname: str, command: str = "
         for key, names in STEP_KERNELS.items():
             tot, raw = 0.0, 0.0
             for kname, mult in names:
-                vals = [v for n, v in per.values() if kname in n.replace("(anonymous namespace)::", "")]
+                pat = re.compile(re.escape(kname).replace(r"\*", r"\d+"))
+                vals = [v for n, v in per.values() if pat.search(n.replace("(anonymous namespace)::", ""))]
                 if not vals:
                     raise SystemExit(f"{run_dir}: no dispatch of {kname}")
                 tot += mult * float(np.mean(vals)) * 1024.0 * factor

@@ -13,12 +13,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int SW = 8;          // waves per split workgroup
 constexpr int ST = 64 * SW;    // threads per split workgroup
-constexpr int PART = 132;      // floats per partial: m, l, 2 pad, acc[128]
 constexpr int GMAX = 16;       // query heads per kv head
 constexpr int MAX_SINK = 512;  // raw sink tokens per sequence
-constexpr int MAX_SPLIT = 512; // splits per (sequence, kv head)
 constexpr int FROW = D + 8;    // fp16 per fragment row in LDS (pad: no bank conflicts)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float QJL_C = 1.2533141373155003f / QJL_M;  // sqrt(pi/2) / m

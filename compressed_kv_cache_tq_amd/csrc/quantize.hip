@@ -657,6 +657,8 @@ struct RotqArgs {
   int64_t page_ld;
   int32_t n_pages;
   int32_t norm16;           // norms stored as fp16 (else fp32)
+  int64_t n_chunks;         // chunks of K launch tiles
+  int32_t n_iter;           // chunks per pair (persistent launch)
   RotqSeq seq[RQ_MAX_SEQ];  // ascending start
 };
 
@@ -801,23 +803,51 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     pl1[ks] = *reinterpret_cast<const uint4*>(tab->pi_frag[TILED][1] + f1);
   }
 
-  // pair p of workgroup g takes launch tiles (2 g + p) K .. (2 g + p) K + K - 1,
-  // all in one sequence: the last one starting at or before the first
-  const int64_t first_l = (static_cast<int64_t>(blockIdx.x) * 2 + pair) * K;
-  int sq = 0;
-#pragma unroll
-  for (int step = RQ_MAX_SEQ / 2; step > 0; step >>= 1)
-    if (sq + step < A.n_seq && A.seq[sq + step].start <= first_l) sq += step;
-  const RotqSeq& Q = A.seq[sq];
-  const uint8_t* __restrict__ xv = static_cast<const uint8_t*>(A.x) + Q.x_off * ES;
-  const int64_t n_tok = Q.n_tok, tok0 = Q.tok0, xss = A.xss, xrs = A.xrs, cap = A.cap;
+  // A chunk is K consecutive launch tiles, all in one sequence (each
+  // sequence's tiles start on a multiple of K).  PERSIST: pair p of workgroup
+  // g takes chunks 2 g + p + i * 2 gridDim.x for i < A.n_iter, the same count
+  // for every pair (a chunk past A.n_chunks is empty: its loads read zeros
+  // and its stores are dropped), and its pipeline runs on across chunk
+  // boundaries, so the rotation fragments and the pipeline's start are paid
+  // once per pair.  Otherwise the pair takes chunk 2 g + p alone.
+  constexpr bool PERSIST = K % 6 == 0;  // buffer roles repeat every 3 tiles, LDS buffers every 2
+  const int64_t xss = A.xss, xrs = A.xrs, cap = A.cap;
   const int64_t stream_code_bytes = A.stream_code_bytes;
-  uint8_t* __restrict__ codes = A.codes + static_cast<int64_t>(Q.stream0) * A.stream_code_bytes;
   const int nbytes = A.norm16 ? 2 : 4;  // bytes per stored norm
-  uint8_t* __restrict__ nrm = reinterpret_cast<uint8_t*>(A.norms) + static_cast<int64_t>(Q.stream0) * cap * nbytes;
-  const int64_t tile0 = Q.t_lo, tstep = Q.t_step;
-  const int64_t total_tiles = static_cast<int64_t>(A.hkv) * Q.tiles;
-  const int64_t first = first_l - Q.start;  // within the sequence
+  // The sequence of a chunk (the last one starting at or before it) and the
+  // chunk's place in it; wave-uniform, so it lives in scalar registers.
+  struct SeqView {
+    const uint8_t* xv;
+    uint8_t* codes;
+    uint8_t* nrm;
+    int64_t n_tok, tok0, tile0, tstep, total_tiles, first;
+    uint32_t tps;
+    int32_t page_row;
+  };
+  auto view_of = [&](int64_t chunk) {
+    const int64_t first_l = chunk * K;
+    int sq = 0;
+#pragma unroll
+    for (int step = RQ_MAX_SEQ / 2; step > 0; step >>= 1)
+      if (sq + step < A.n_seq && A.seq[sq + step].start <= first_l) sq += step;
+    const RotqSeq& Q = A.seq[sq];
+    SeqView v;
+    v.xv = static_cast<const uint8_t*>(A.x) + Q.x_off * ES;
+    v.codes = A.codes + static_cast<int64_t>(Q.stream0) * A.stream_code_bytes;
+    v.nrm = reinterpret_cast<uint8_t*>(A.norms) + static_cast<int64_t>(Q.stream0) * cap * nbytes;
+    v.n_tok = Q.n_tok;
+    v.tok0 = Q.tok0;
+    v.tile0 = Q.t_lo;
+    v.tstep = Q.t_step;
+    v.total_tiles = chunk < A.n_chunks ? static_cast<int64_t>(A.hkv) * Q.tiles : 0;
+    v.first = first_l - Q.start;  // within the sequence
+    v.tps = static_cast<uint32_t>(Q.tiles);
+    v.page_row = Q.page_row;
+    return v;
+  };
+  const int64_t chunk0 = static_cast<int64_t>(blockIdx.x) * 2 + pair;
+  const int64_t chunk_step = static_cast<int64_t>(gridDim.x) * 2;
+  SeqView cur = view_of(chunk0);
 
   // Tile tl of the sequence: stream s, tile T of the stream; its rows of x
   // start at r0 and its positions [lo, nv) are written (lo > 0 only for the
@@ -828,8 +858,9 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     int lo, nv;
   };
   // tile counts fit in 32 bits (checked on the host): branch-free division
-  const uint32_t tps = static_cast<uint32_t>(Q.tiles);
-  auto tile_at = [&](int64_t tl) {
+  auto tile_at = [&](const SeqView& v, int64_t tl) {
+    const uint32_t tps = v.tps;
+    const int64_t tile0 = v.tile0, tstep = v.tstep, tok0 = v.tok0, n_tok = v.n_tok;
     TileAt a;
     const uint32_t s32 = static_cast<uint32_t>(tl) / tps;
     a.s = s32;
@@ -851,7 +882,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
       const int64_t left = n_tok - a.r0;
       a.nv = static_cast<int>(left < 32 ? left : 32);
     }
-    if (tl >= total_tiles) a.lo = a.nv = 0;
+    if (tl >= v.total_tiles) a.lo = a.nv = 0;
     return a;
   };
   // where tile a's positions are stored: stream s (of codes / norms) from
@@ -861,10 +892,10 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     int64_t s, p;
     bool ok;
   };
-  auto dest_at = [&](const TileAt& a) {
+  auto dest_at = [&](const SeqView& v, const TileAt& a) {
     Dst d{a.s, a.p0, true};
     if constexpr (PAGED) {
-      const int pg = A.pages[static_cast<int64_t>(Q.page_row) * A.page_ld + a.p0 / TQ_PAGE_TOKENS];
+      const int pg = a.nv > a.lo ? A.pages[static_cast<int64_t>(v.page_row) * A.page_ld + a.p0 / TQ_PAGE_TOKENS] : -1;
       d.ok = pg >= 0 && pg < A.n_pages;
       d.s = static_cast<int64_t>(d.ok ? pg : 0) * A.hkv + a.s;
       d.p = a.p0 % TQ_PAGE_TOKENS;
@@ -874,9 +905,9 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   // staging role: vector (token slot) sv of the tile, elements [32 qq, 32 qq + 32)
   const int sv = pt >> 2, qq = pt & 3;
   // rows before lo use an offset past the extent (read as zero)
-  auto load_x = [&](int64_t tl, uint4 (&dst)[NQW]) {
-    const TileAt a = tile_at(tl);
-    const uint8_t* base = xv + (a.s * xss + (a.r0 + a.lo) * xrs) * ES;
+  auto load_x = [&](const SeqView& v, int64_t tl, uint4 (&dst)[NQW]) {
+    const TileAt a = tile_at(v, tl);
+    const uint8_t* base = v.xv + (a.s * xss + (a.r0 + a.lo) * xrs) * ES;
     const __amdgpu_buffer_rsrc_t r = rsrc(base, a.nv > a.lo ? ((a.nv - a.lo - 1) * xrs + D) * ES : 0);
     const int off = MERGE || PAGED ? (sv >= a.lo ? static_cast<int>(((sv - a.lo) * xrs + 32 * qq) * ES) : RQ_OOB)
                                    : static_cast<int>((sv * xrs + 32 * qq) * ES);
@@ -885,7 +916,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
       dst[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0));
   };
   // norm, scale, fp16 conversion into buffer b; the norm goes out here too
-  auto stage = [&](int64_t tl, const uint4 (&xin)[NQW], int b) {
+  auto stage = [&](const SeqView& v, int64_t tl, const uint4 (&xin)[NQW], int b) {
     double ss = 0.0;
     if constexpr (F32IN) {
 #pragma unroll
@@ -946,10 +977,10 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     }
     // the four threads of a vector write the same values
     inv_s[pair][b][sv] = normf > 0.0f ? 1.0f / ldexpf(normf, sh + 8) : 0.0f;
-    const TileAt a = tile_at(tl);
-    const Dst d = dest_at(a);
+    const TileAt a = tile_at(v, tl);
+    const Dst d = dest_at(v, a);
     const __amdgpu_buffer_rsrc_t rn =
-        rsrc(nrm + (d.s * cap + d.p) * nbytes, d.ok ? static_cast<int64_t>(a.nv) * nbytes : 0);
+        rsrc(v.nrm + (d.s * cap + d.p) * nbytes, d.ok ? static_cast<int64_t>(a.nv) * nbytes : 0);
     const int noff = !(MERGE || PAGED) || sv >= a.lo ? nbytes * sv : RQ_OOB;
     if (A.norm16)
       __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(fminf(normf, F16_MAX))),
@@ -958,29 +989,33 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, noff, 0, 0);
   };
 
-  // ---- pipeline, straight-line over the pair's K tiles: three register
+  // ---- pipeline, straight-line over each chunk's K tiles: three register
   // buffers with fixed roles (tile k+1 is staged from X[(k+1) % 3] while
   // tiles k+2, k+3 are still loading; the buffer is then refilled with tile
-  // k+4), so the waits on in-flight loads are exact.
+  // k+4), so the waits on in-flight loads are exact.  PERSIST: tiles k+1 and
+  // k+4 past the chunk's end are the first tiles of the pair's next chunk.
   uint4 X[3][NQW];
-  load_x(first, X[0]);
-  if (K > 1) load_x(first + 1, X[1]);
-  if (K > 2) load_x(first + 2, X[2]);
+  load_x(cur, cur.first, X[0]);
+  if (PERSIST || K > 1) load_x(cur, cur.first + 1, X[1]);
+  if (PERSIST || K > 2) load_x(cur, cur.first + 2, X[2]);
   // (the fragment loads are older than the tile loads: this waits for them only)
   if (pair == 0) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) pil1_s[w][ks][lane] = pl1[ks];
   }
-  stage(first, X[0], 0);
-  if (K > 3) load_x(first + 3, X[0]);
+  stage(cur, cur.first, X[0], 0);
+  if (PERSIST || K > 3) load_x(cur, cur.first + 3, X[0]);
   reinterpret_cast<uint2*>(cell_s)[tid] = cv[0];
 #pragma unroll
   for (int i = 1; i < CPT; ++i)
     if (tid + i * RQ_THREADS < NCE) reinterpret_cast<uint2*>(cell_s)[tid + i * RQ_THREADS] = cv[i];
   __syncthreads();
+  const int n_iter = PERSIST ? A.n_iter : 1;
+  for (int it = 0; it < n_iter; ++it) {
+  const SeqView nxt = PERSIST ? view_of(chunk0 + (it + 1) * chunk_step) : cur;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int64_t tl = first + k;
+    const int64_t tl = cur.first + k;
     const int b = k & 1;
     f32x16 acc[2];
     acc[0] = acc[1] = f32x16{};
@@ -1013,12 +1048,16 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     // stage the next tile into the other buffer while the products finish,
     // and refill its registers: they are free before the codes are made
     if (k + 1 < K) {
-      stage(tl + 1, X[(k + 1) % 3], b ^ 1);
-      if (k + 4 < K) load_x(tl + 4, X[(k + 1) % 3]);
+      stage(cur, tl + 1, X[(k + 1) % 3], b ^ 1);
+      if (k + 4 < K) load_x(cur, tl + 4, X[(k + 1) % 3]);
+      else if (PERSIST) load_x(nxt, nxt.first + (k + 4 - K), X[(k + 1) % 3]);
+    } else if (PERSIST) {
+      stage(nxt, nxt.first, X[(k + 1) % 3], b ^ 1);
+      load_x(nxt, nxt.first + 3, X[(k + 1) % 3]);
     }
-    const TileAt a = tile_at(tl);
-    const Dst to = dest_at(a);
-    uint8_t* sbase = codes + to.s * stream_code_bytes;
+    const TileAt a = tile_at(cur, tl);
+    const Dst to = dest_at(cur, a);
+    uint8_t* sbase = cur.codes + to.s * stream_code_bytes;
     if constexpr (!TILED) {
       const float inv = inv_s[pair][b][l32];
       const __amdgpu_buffer_rsrc_t rc =
@@ -1117,7 +1156,9 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
       if (BLO == BHI || w == 0) emit(std::integral_constant<int, BLO>{}, cell_s[0]);
       else emit(std::integral_constant<int, BHI>{}, cell_s[1]);
     }
-    if (k + 1 < K) __syncthreads();
+    if (PERSIST || k + 1 < K) __syncthreads();
+  }
+  cur = nxt;
   }
 }
 
@@ -1169,6 +1210,19 @@ hipError_t launch_each(const Tables* tab, const void* x, const QSeq* seqs, int64
   return hipSuccess;
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // tiles [t_lo, t_lo + t_step, ...) (tiles of them) of every stream of a sequence
 struct RotqPart {
   QSeq q;
@@ -1185,8 +1239,11 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
     const int nb = static_cast<int>(std::min<int64_t>(RQ_MAX_SEQ, n - b0));
     int64_t raw = 0;
     for (int i = 0; i < nb; ++i) raw += hkv * list[b0 + i].tiles;
-    // 8 tiles per pair once that still fills every CU twice over, else 2
-    const int K = !MERGE && raw >= 8 * 1024 ? 8 : 2;
+    // A persistent launch (chunks of 6 tiles, each pair looping over its
+    // chunks) once every resident pair gets at least 8 chunks; else one chunk
+    // per pair: 8 tiles once that still fills every CU twice over, or 2.
+    const int64_t pairs = 4 * static_cast<int64_t>(cu_count());  // two resident workgroups of two pairs per CU
+    const int K = MERGE ? 2 : raw >= 6 * 8 * pairs ? 6 : raw >= 8 * 1024 ? 8 : 2;
 
     RotqArgs a{};
     a.tab = tab;
@@ -1217,12 +1274,24 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
                          static_cast<int32_t>(p.q.page_row)};
       total += (hkv * p.tiles + K - 1) / K * K;
     }
-    const unsigned blocks = static_cast<unsigned>((total + 2 * K - 1) / (2 * K));
+    a.n_chunks = total / K;
+    unsigned blocks = static_cast<unsigned>((a.n_chunks + 1) / 2);
+    a.n_iter = 1;
+    if (K == 6) {
+      // two resident workgroups per CU (the register budget of the kernel),
+      // each pair looping over its chunks
+      const int64_t resident = 2 * static_cast<int64_t>(cu_count());
+      if (blocks > resident) blocks = static_cast<unsigned>(resident);
+      a.n_iter = static_cast<int32_t>((a.n_chunks + 2 * blocks - 1) / (2 * blocks));
+    }
     if constexpr (MERGE) {
       hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, true, PAGED>), dim3(blocks), dim3(RQ_THREADS), 0,
                          st, a);
     } else {
-      if (K == 8)
+      if (K == 6)
+        hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 6, false, PAGED>), dim3(blocks), dim3(RQ_THREADS),
+                           0, st, a);
+      else if (K == 8)
         hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 8, false, PAGED>), dim3(blocks), dim3(RQ_THREADS),
                            0, st, a);
       else

@@ -313,7 +313,7 @@ hipError_t launch_ip(bool qjl, const Tables* tab, const tq_cache& c, int64_t n_s
 
 }  // namespace
 
-size_t ip_workspace_bytes() { return sizeof(IpWork); }
+static_assert(sizeof(IpWork) == IP_WORK_BYTES, "search workspace layout");
 
 hipError_t launch_ip_scores(const Spec& sp, const Tables* tab, const tq_cache& c, int64_t n_streams, int64_t n_tok,
                             const float* q, int nq, float* scores, int64_t ld, void* workspace, hipStream_t st) {

@@ -128,6 +128,17 @@ size_t ip_workspace_bytes();
 hipError_t launch_ip_scores(const Spec& sp, const Tables* tab, const tq_cache& c, int64_t n_streams, int64_t n_tok,
                             const float* q, int nq, float* scores, int64_t ld, void* workspace, hipStream_t st);
 
+// Decode split plan (plan.cpp): every workgroup of the split kernel has SW
+// waves; a partial is PART floats (m, l, 2 pad, acc[128]); at most
+// MAX_SPLIT splits per (sequence, kv head).
+constexpr int SW = 8;
+constexpr int PART = 132;
+constexpr int MAX_SPLIT = 512;
+
+// Bytes of the search workspace: fp16 hi + lo rows of the rotated query and
+// of u = S q~ per query, and two fp32 scales per query.
+constexpr size_t IP_WORK_BYTES = 2 * 2 * TQ_IP_MAX_QUERIES * D * 2 + 2 * TQ_IP_MAX_QUERIES * 4;
+
 struct AttendPlan {
   int n_split;       // splits of the compressed token range per (b, kv head)
   int n_slot;        // partials per query head: n_split, plus one for the sink tokens

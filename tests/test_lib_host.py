@@ -498,3 +498,32 @@ def test_noalloc_refuses_a_problem_beyond_its_scratch():
     assert st == -2 and "TQ_NOALLOC_SCRATCH_BYTES" in tq.last_error()
     assert L.tq_attend_decode_noalloc(ctypes.byref(ks), None, ctypes.byref(kc), ctypes.byref(vs), None,
                                       ctypes.byref(vc), None, 0x5000, None, None, 0x6000, 0x7000, None) == -1
+
+
+def test_host_half_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The host half of the library (host.cpp, plan.cpp) built with g++ under
+    -fsanitize=address,undefined (no device code: the launches are stubs that
+    report no device) and driven through every host-side path: codebooks,
+    rotations, sketch, tables for every spec, sizes, and the argument checks
+    of every entry point up to the launch.  Any sanitizer report aborts."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    csrc = os.path.join(ROOT, "compressed_kv_cache_tq_amd", "csrc")
+    here = os.path.join(ROOT, "tests", "host_sanitize")
+    exe = str(tmp_path / "host_san")
+    cmd = [gxx, "-std=c++20", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I" + os.path.join(ROOT, "include"), "-I" + csrc,
+           os.path.join(csrc, "host.cpp"), os.path.join(csrc, "plan.cpp"),
+           os.path.join(here, "stubs.cpp"), os.path.join(here, "driver.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "host sanitizer driver ok" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
