@@ -190,11 +190,62 @@ def stats_summary(csv_path: str, out_path: str, title: str = "", command: str = 
     return 0
 
 
+def counter_summary(run_dirs, out_path: str, title: str = "", command: str = "") -> int:
+    """Per-kernel averages (per dispatch) of the counters of rocprofv3 --pmc
+    runs of this script (csv or database output).  The per-wave cycle
+    counters (SQ_WAIT_*, SQ_ACTIVE_INST_*) are also given as a fraction of
+    SQ_WAVE_CYCLES, the cycles that waves were resident."""
+    import csv
+    import glob
+    import sqlite3
+    per = {}  # (kernel, counter) -> {dispatch: value}
+    for run_dir in run_dirs:
+        csvs = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+        rows = []
+        if csvs:
+            for path in csvs:
+                for r in csv.DictReader(open(path)):
+                    rows.append((r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"], r["Counter_Value"]))
+        else:
+            for db in glob.glob(os.path.join(run_dir, "**", "*.db"), recursive=True):
+                con = sqlite3.connect(db)
+                rows += list(con.execute(
+                    "select dispatch_id, kernel_name, counter_name, value from counters_collection"))
+        if not rows:
+            raise SystemExit(f"no counter values under {run_dir}")
+        for did, name, cname, v in rows:
+            name = re.sub(r"\(anonymous namespace\)::", "", name)
+            d = per.setdefault((name, cname), {})
+            d[(run_dir, did)] = d.get((run_dir, did), 0.0) + float(v)
+    kernels = sorted({k for k, _ in per})
+    with open(out_path, "w") as f:
+        if title:
+            f.write(f"# {title}\n")
+        if command:
+            f.write(f"# command: {command}\n")
+        f.write("# per-dispatch averages of rocprofv3 --pmc counters (summed over the counter's instances);\n")
+        f.write("# '(x of wave cycles)' = counter / SQ_WAVE_CYCLES of the same kernel\n")
+        for k in kernels:
+            cnames = sorted(c for kk, c in per if kk == k)
+            vals = {c: float(np.mean(list(per[(k, c)].values()))) for c in cnames}
+            ndisp = max(len(per[(k, c)]) for c in cnames)
+            f.write(f"\nkernel {k[:160]}\n")
+            f.write(f"  dispatches averaged: {ndisp}\n")
+            wc = vals.get("SQ_WAVE_CYCLES")
+            for c in cnames:
+                extra = ""
+                if wc and c.startswith(("SQ_WAIT", "SQ_ACTIVE_INST")):
+                    extra = f"  ({vals[c] / wc:.3f} of wave cycles)"
+                f.write(f"  {c:<28} {vals[c]:>18.1f}{extra}\n")
+    print(open(out_path).read())
+    return 0
+
+
 def _oracle_spec(spec):
     from oracle import quantize as oqz
     return oqz.Spec(bits_lo=spec.bits_lo, bits_hi=spec.bits_lo if spec.bits_hi is None else spec.bits_hi,
                     split=spec.split, qjl_m=spec.qjl_m, rot_seed=spec.rot_seed, qjl_seed=spec.qjl_seed,
-                    rotation="hadamard" if spec.rotation == 1 else "haar", norm_f16=bool(spec.norm_f16))
+                    rotation="haar" if spec.rotation == 0 else "hadamard", norm_f16=bool(spec.norm_f16))
 
 
 def cpu_baseline(inp, wl, kspec, vspec, kc, vc, comp_h, sample, tok_bytes, n_quant=65536):
@@ -309,7 +360,7 @@ def bench_search(args) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = workloads.SEARCH
-    rot = tq.ROT_HADAMARD if args.rotation == "hadamard" else tq.ROT_HAAR
+    rot = tq.ROT_HAAR if args.rotation == "haar" else tq.ROT_HADAMARD
     spec = tq.Spec(wl.bits, qjl_m=wl.qjl_m, layout=tq.LAYOUT_RECORD, rotation=rot)
     tab = tq.device_tables(spec)
     xd = torch.from_numpy(workloads.bf16_bits(workloads.search_database(wl)).view(np.int16)).cuda().view(torch.bfloat16)
@@ -377,7 +428,7 @@ def cpu_baseline_search(wl, spec, cache, q):
         threads = os.cpu_count()
     n = wl.n_tok
     os_ = oqz.Spec(bits_lo=wl.bits, bits_hi=wl.bits, split=128, qjl_m=wl.qjl_m,
-                   rotation="hadamard" if spec.rotation == 1 else "haar")
+                   rotation="haar" if spec.rotation == 0 else "hadamard")
     rb = kspec_bytes(spec)
     raw = cache.codes[:n * rb].cpu().numpy().reshape(n, rb)
     norms = cache.norms[:n].cpu().numpy()
@@ -408,8 +459,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="workload to time (default: batched_ragged, the largest single-GPU configuration)")
-    ap.add_argument("--rotation", choices=("haar", "hadamard"), default="haar",
-                    help="how the rotation is drawn (the workloads are specified with the Haar rotation)")
+    ap.add_argument("--rotation", choices=("haar", "hadamard", "hadamard_fwht"), default="haar",
+                    help="how the rotation is drawn (the workloads are specified with the Haar rotation); "
+                         "hadamard_fwht: the Hadamard matrix applied by butterflies in the key quantize")
     ap.add_argument("--kbits", type=int, choices=(8,), default=None,
                     help="keys at 8 bits (uniform, no sketch: the K8 of a K8/V3 policy) instead of the workload's")
     ap.add_argument("--norms", choices=("f32", "f16"), default="f32",
@@ -425,13 +477,21 @@ def main() -> int:
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT"),
                     help="no GPU: turn the kernel_stats.csv of a rocprofv3 --kernel-trace --stats run into a "
                          "short text summary (with --command and --title)")
-    ap.add_argument("--title", default="", help="first line of the --stats-summary file")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PATH",
+                    help="no GPU: RUN_DIR [RUN_DIR ...] OUT: per-kernel counter averages of rocprofv3 --pmc runs "
+                         "of this script, written to OUT (with --command and --title)")
+    ap.add_argument("--title", default="", help="first line of the --stats-summary / --counter-summary file")
     ap.add_argument("--command", default="", help="command line recorded by --traffic-summary")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary, args.workload, command=args.command)
     if args.stats_summary:
         return stats_summary(*args.stats_summary, title=args.title, command=args.command)
+    if args.counter_summary:
+        if len(args.counter_summary) < 2:
+            ap.error("--counter-summary needs RUN_DIR [RUN_DIR ...] OUT")
+        return counter_summary(args.counter_summary[:-1], args.counter_summary[-1], title=args.title,
+                               command=args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); every box here has a single "
               f"MI355X and this path is not sharded across GPUs.", file=sys.stderr)
@@ -452,7 +512,7 @@ def main() -> int:
     cap = max(32, -(-int(comp_h.max()) // 32) * 32)
     uniform = bool(np.all(lens_h == lens_h[0]))
     f32 = wl.dtype == "f32"
-    rot = tq.ROT_HADAMARD if args.rotation == "hadamard" else tq.ROT_HAAR
+    rot = {"haar": tq.ROT_HAAR, "hadamard": tq.ROT_HADAMARD, "hadamard_fwht": tq.ROT_HADAMARD_FWHT}[args.rotation]
     kspec = tq.Spec(wl.k.bits_lo, wl.k.bits_hi, split=wl.k.split, qjl_m=wl.k.qjl_m, layout=tq.LAYOUT_RECORD,
                     rot_seed=wl.k.rot_seed, qjl_seed=wl.k.qjl_seed, rotation=rot)
     if args.kbits == 8:

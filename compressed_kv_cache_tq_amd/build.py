@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["host.cpp", "plan.cpp", "quantize.hip", "attend.hip", "attend_k22.hip", "attend_k33.hip", "attend_k44.hip",
-           "attend_k43.hip", "attend_k32.hip", "attend_k88.hip", "search.hip", "noalloc.hip"]
+           "attend_k43.hip", "attend_k32.hip", "attend_k88.hip", "search.hip", "noalloc.hip", "fwht.hip"]
 ARCH = "gfx950"
 
 

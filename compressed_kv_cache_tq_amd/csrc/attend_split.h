@@ -147,6 +147,7 @@ struct StreamRsrc {
 // 32 tokens is 32 * VBYTES contiguous bytes).
 struct LaneOffsets {
   uint32_t k[2], k2[2], z[2], v, v2, nrm;
+  uint32_t tokc;    // compact softmax: the lane's token within its tile (its norms' index)
   uint32_t ksh[2];  // mixed-width keys: bit offset of each part in its two loaded dwords
 };
 
@@ -179,7 +180,10 @@ __device__ __forceinline__ float4 buf_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t
 template <int KLO, int KHI>
 constexpr int key_dwords() { return KLO == 8 ? 8 : 4; }
 
-template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool NF16>
+// Loads of one tile.  CG (the compact softmax of groups of at most 4 query
+// heads): each lane loads the norms (and residual norm) of one token only,
+// token lo.tokc of the tile, into component x of kn[0], vn[0], rn[0].
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool NF16, bool CG>
 __device__ __forceinline__ void load_tile(TileRegs<key_dwords<KLO, KHI>()>& r, uint32_t t0, const StreamRsrc& rs,
                                           const LaneOffsets& lo) {
   constexpr uint32_t KBYTES = 8 * (KLO + KHI);
@@ -220,6 +224,20 @@ __device__ __forceinline__ void load_tile(TileRegs<key_dwords<KLO, KHI>()>& r, u
 #pragma unroll
     for (int i = 0; i < VW; ++i) r.vw[i] = w[i];
   }
+  if constexpr (CG) {
+    constexpr uint32_t NB = NF16 ? 2 : 4;
+    if constexpr (NF16) {
+      r.kn[0].x = __uint_as_float(static_cast<uint32_t>(
+          __builtin_amdgcn_raw_buffer_load_b16(rs.kn, NB * (lo.tokc + t0), 0, 0)));
+      r.vn[0].x = __uint_as_float(static_cast<uint32_t>(
+          __builtin_amdgcn_raw_buffer_load_b16(rs.vn, NB * (lo.tokc + t0), 0, 0)));
+    } else {
+      r.kn[0].x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.kn, NB * (lo.tokc + t0), 0, 0));
+      r.vn[0].x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.vn, NB * (lo.tokc + t0), 0, 0));
+    }
+    if constexpr (QJL) r.rn[0].x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs.rn, 4 * (lo.tokc + t0), 0, 0));
+    return;
+  }
   if constexpr (NF16) {
     // 8 fp16 norms in one 16-byte load, converted where they are used
     r.kn[0] = buf_load_f4(rs.kn, (lo.nrm >> 1) + 2 * t0);
@@ -257,6 +275,32 @@ __device__ __forceinline__ float max_xor16_32(float x) {
   const uint32_t v = __float_as_uint(y);
   const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Maximum and sum over all 64 lanes (row rotations, then the row swaps).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xF, 0xF, false)));
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xF, 0xF, false)));
+  return max_xor16_32(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum32(x);
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// Row j of the result is row 0 of input j (rows are 16-lane groups): the
+// odd rows of the first operand of a 16-row swap trade places with the even
+// rows of the second, and the upper half of the first operand of a 32-lane
+// swap with the lower half of the second.
+__device__ __forceinline__ float gather_rows0(float a0, float a1, float b0, float b1) {
+  const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(b0), __float_as_uint(b1), false, false);
+  const auto f = __builtin_amdgcn_permlane32_swap(x[0], z[0], false, false);
+  return __uint_as_float(f[0]);
 }
 
 __device__ __forceinline__ float f4get(const float4 (&v)[2], int e) {
@@ -481,7 +525,15 @@ __device__ __forceinline__ void merge_stream(uint8_t* smem, const Tables* __rest
   }
 }
 
-template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED, bool NF16>
+// CG: the compact softmax for groups of at most 4 query heads.  The score
+// product is taken transposed (query fragments as the A operand), so each
+// 32-token M-block leaves the 4 heads of a token in one lane of the first
+// 16-lane row; the rows of four blocks (two tiles) are gathered into one
+// register set, the softmax then runs on 4 values per lane for 64 tokens
+// instead of 16 for 32, and the probabilities reach the P V product through
+// a per-wave LDS array.  Each lane loads the norms of its own token only,
+// which leaves registers for two pairs of tiles in flight.
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED, bool NF16, bool CG>
 __global__ __launch_bounds__(ST, 1) void split_kernel(
     const Tables* __restrict__ ktab, const uint8_t* __restrict__ kcodes, const float* __restrict__ knorms,
     const uint8_t* __restrict__ ksigns, const float* __restrict__ krn, int64_t kcap,
@@ -683,6 +735,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     lo.v = j * (64 * (VLO + VHI)) + (n < 8 ? 8 * VLO * n : 64 * VLO + 8 * VHI * (n - 8));
   }
   lo.nrm = 32 * j;
+  lo.tokc = 8 * (n >> 2) + 4 * (j & 1) + (n & 3);
 
   // Tiles of this wave: first + STEP k, k < nt; the first nfull are whole.
   constexpr uint32_t STEP = 32 * SW;
@@ -710,7 +763,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   using TRg = TileRegs<key_dwords<KLO, KHI>()>;
   auto load_at = [&](TRg& buf, int k, uint32_t t0) __attribute__((always_inline)) {
     if constexpr (!PAGED) {
-      load_tile<KLO, KHI, VLO, VHI, QJL, NF16>(buf, t0, rs, lo);
+      load_tile<KLO, KHI, VLO, VHI, QJL, NF16, CG>(buf, t0, rs, lo);
     } else {
       const int pg = __builtin_amdgcn_readlane(k < 64 ? pid[0] : pid[1], k & 63);
       const int64_t base = static_cast<int64_t>(t0 / TQ_PAGE_TOKENS) * TQ_PAGE_TOKENS;
@@ -731,13 +784,18 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       } else {
         pr.zs = pr.rn = pr.kn;
       }
-      load_tile<KLO, KHI, VLO, VHI, QJL, NF16>(buf, t0 % TQ_PAGE_TOKENS, pr, lo);
+      load_tile<KLO, KHI, VLO, VHI, QJL, NF16, CG>(buf, t0 % TQ_PAGE_TOKENS, pr, lo);
     }
   };
 
   TRg bufA, bufB;
+  TRg bufC, bufD;  // CG: the second pair of tiles in flight
   load_at(bufA, 0, first);
   load_at(bufB, 1, first + STEP);
+  if constexpr (CG) {
+    load_at(bufC, 2, first + 2 * STEP);
+    load_at(bufD, 3, first + 3 * STEP);
+  }
 
   // Power-of-two scale per head for the fp16 operand: Pi is orthogonal, so
   // |q~_i| <= ||q~|| = ||q|| |qscale|, and sh = 14 - exponent of that bound
@@ -888,13 +946,15 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f32x4{};
 
-  auto tile_step = [&]<bool FULL, bool VSKIP>(const TRg& tr, uint32_t t0c) __attribute__((always_inline)) {
+  // Score products of one tile: sk[mb] the codebook part (hi and lo query
+  // parts accumulate into one chain), sz[mb] the sketch sign products.
+  // SWAP: the query fragments are the A operand, so lane (n, j) of M-block mb
+  // holds heads 4 j + i of the block's token row n (instead of tokens
+  // 8 j + 4 mb + i of head n).
+  auto score_tile = [&]<bool SWAP>(const TRg& tr, f32x4 (&sk)[2], f32x4 (&sz)[2]) __attribute__((always_inline)) {
     // keeps the LDS fragment reads of the sketch variant inside the loop
     if constexpr (QJL) __asm__ volatile("" ::: "memory");
-    const int nvalid = FULL ? 8 : static_cast<int>(t_end) - static_cast<int>(t0c + 8 * j);
-    // two accumulator chains per M-block: hi and lo query parts accumulate
-    // into one; the QJL sign products into another
-    f32x4 sk[2], sz[2];
+    auto mm = [&](half8 x, half8 qf, f32x4 c) { return SWAP ? mfma16(qf, x, c) : mfma16(x, qf, c); };
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) sk[mb] = sz[mb] = f32x4{};
 #pragma unroll
@@ -921,7 +981,7 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
         }
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], frag_at(0, ks), sk[mb]);
+      for (int mb = 0; mb < 2; ++mb) sk[mb] = mm(a[mb], frag_at(0, ks), sk[mb]);
       if constexpr (QJL) {
         half8 z[2];
 #pragma unroll
@@ -930,16 +990,34 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
           z[mb] = as_half8(lutz[zv & 3], lutz[(zv >> 2) & 3], lutz[(zv >> 4) & 3], lutz[zv >> 6]);
         }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], frag_at(2, ks), sz[mb]);
+        for (int mb = 0; mb < 2; ++mb) sz[mb] = mm(z[mb], frag_at(2, ks), sz[mb]);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], frag_at(1, ks), sk[mb]);
+        for (int mb = 0; mb < 2; ++mb) sk[mb] = mm(a[mb], frag_at(1, ks), sk[mb]);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sz[mb] = mfma16(z[mb], frag_at(3, ks), sz[mb]);
+        for (int mb = 0; mb < 2; ++mb) sz[mb] = mm(z[mb], frag_at(3, ks), sz[mb]);
       } else {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sk[mb] = mfma16(a[mb], frag_at(1, ks), sk[mb]);
+        for (int mb = 0; mb < 2; ++mb) sk[mb] = mm(a[mb], frag_at(1, ks), sk[mb]);
       }
     }
+  };
+
+  // P V of one tile: pa is this lane's A operand (row n = head n, tokens
+  // 8 j .. 8 j + 7), the value sub-blocks through the LUT the B operands.
+  auto pv_tile = [&](const TRg& tr, half8 pa) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      half8 bv;
+      if constexpr (VLO == VHI) bv = dequant8<VLO>(tr.vw, nb, lut_vlo, lane4);
+      else bv = nb < 4 ? dequant8<VLO>(tr.vw, nb, lut_vlo, lane4) : dequant8<VHI>(tr.vw + 4, nb - 4, lut_vhi, lane4);
+      acc[nb] = mfma16(pa, bv, acc[nb]);
+    }
+  };
+
+  auto tile_step = [&]<bool FULL, bool VSKIP>(const TRg& tr, uint32_t t0c) __attribute__((always_inline)) {
+    const int nvalid = FULL ? 8 : static_cast<int>(t_end) - static_cast<int>(t0c + 8 * j);
+    f32x4 sk[2], sz[2];
+    score_tile.template operator()<false>(tr, sk, sz);
     float s[8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -989,16 +1067,98 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     }
     l_run += psum;
     // skip the value work of a tile whose weights all fell below v_skip
-    if (!VSKIP || __any(any && head_ok)) {
-      const half8 pa = as_half8(pw[0], pw[1], pw[2], pw[3]);
+    if (!VSKIP || __any(any && head_ok)) pv_tile(tr, as_half8(pw[0], pw[1], pw[2], pw[3]));
+  };
+
+  // ---- compact softmax (CG): the state of head i < 4 of the group sits in
+  // component i, the same value in every lane for the maximum (mc); the sums
+  // (lc) are per-lane partials, added up after the stream.
+  float mc[4], lc[4], qinvc[4], uinvc[4];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        half8 bv;
-        if constexpr (VLO == VHI) bv = dequant8<VLO>(tr.vw, nb, lut_vlo, lane4);
-        else bv = nb < 4 ? dequant8<VLO>(tr.vw, nb, lut_vlo, lane4) : dequant8<VHI>(tr.vw + 4, nb - 4, lut_vhi, lane4);
-        acc[nb] = mfma16(pa, bv, acc[nb]);
+  for (int i = 0; i < 4; ++i) {
+    mc[i] = -INFINITY;
+    lc[i] = 0.0f;
+    qinvc[i] = CG && i < G ? ldexpf(1.0f, -shx[i]) : 0.0f;
+    uinvc[i] = CG && QJL && i < G ? ldexpf(QJL_C, -shx[GMAX + i]) : 0.0f;
+  }
+  // per-wave P array: [tile of the pair][head row (16; rows >= G stay zero)][32 tokens + pad]
+  constexpr int PWROW = 40;
+  _Float16* pwl = reinterpret_cast<_Float16*>(smem + PRO_OFF + GMAX * D * 4) + wave * (2 * 16 * PWROW);
+  if constexpr (CG) {
+    static_assert(SW * 2 * 16 * PWROW * 2 <= 4 * GMAX * D * 4, "P arrays fit the prologue's partial-dot area");
+    // the prologue's partial dots are dead: zero this wave's P array
+    uint4* z4 = reinterpret_cast<uint4*>(pwl);
+    for (int c = lane; c < 2 * 16 * PWROW * 2 / 16; c += 64) z4[c] = uint4{};
+  }
+  // Two tiles (A at token t0a, B at t0b) through the compact softmax.  Lane
+  // (n, j) takes token lo.tokc of tile A (j < 2) or B (j >= 2), all heads.
+  auto pair_step = [&]<bool FULL, bool VSKIP>(const TRg& ta_, uint32_t t0a, const TRg& tb_, uint32_t t0b)
+                       __attribute__((always_inline)) {
+    f32x4 ska[2], sza[2], skb[2], szb[2];
+    score_tile.template operator()<true>(ta_, ska, sza);
+    score_tile.template operator()<true>(tb_, skb, szb);
+    const bool in_b = j >= 2;
+    const uint32_t t0 = in_b ? t0b : t0a;
+    const bool valid = FULL || t0 + lo.tokc < t_end;
+    auto nval = [&](float a, float bb) {
+      const float x = in_b ? bb : a;
+      if constexpr (NF16) return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(__float_as_uint(x))));
+      else return x;
+    };
+    const float kn = nval(ta_.kn[0].x, tb_.kn[0].x);
+    const float vn = valid ? nval(ta_.vn[0].x, tb_.vn[0].x) : 0.0f;
+    const float rn = QJL ? (in_b ? tb_.rn[0].x : ta_.rn[0].x) : 0.0f;
+    float sc[4];
+    bool up = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float dot = gather_rows0(ska[0][i], ska[1][i], skb[0][i], skb[1][i]) * qinvc[i];
+      if constexpr (QJL) dot = fmaf(rn * gather_rows0(sza[0][i], sza[1][i], szb[0][i], szb[1][i]), uinvc[i], dot);
+      sc[i] = valid && i < G ? kn * dot : -INFINITY;
+      up |= sc[i] > mc[i] + RESCALE_SLACK;
+    }
+    // rescale only when some head's maximum grew past the slack
+    if (__any(up)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mx = wave_max(sc[i]);
+        const float mn = mx > mc[i] + RESCALE_SLACK ? mx : mc[i];
+        const float al = mc[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc[i] - mn);
+        mc[i] = mn;
+        lc[i] *= al;
+        // acc row 4 j + i: head i in the first row, padding heads (zero) elsewhere
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k][i] *= al;
       }
     }
+    bool any = !VSKIP;
+    _Float16* prow = pwl + (in_b ? 16 * PWROW : 0) + lo.tokc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p = sc[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - mc[i]);
+      if constexpr (VSKIP) {
+        if (p < v_skip) p = 0.0f;
+        any |= p > 0.0f;
+      }
+      lc[i] += p;
+      if (i < G) prow[i * PWROW] = static_cast<_Float16>(p * vn);
+    }
+    bool any_a = true, any_b = true;
+    if constexpr (VSKIP) {
+      any_a = __any(any && !in_b);
+      any_b = __any(any && in_b);
+    }
+    // the P array is this wave's own: its writes precede its reads in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const half8 pa = *reinterpret_cast<const half8*>(pwl + n * PWROW + 8 * j);
+    const half8 pb = *reinterpret_cast<const half8*>(pwl + (16 + n) * PWROW + 8 * j);
+    if (any_a) pv_tile(ta_, pa);
+    if (any_b) pv_tile(tb_, pb);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
   // Two tiles in flight per wave in fixed registers: each buffer is refilled
@@ -1023,12 +1183,48 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
       tile_step.template operator()<false, VSKIP>(bufA, ta);
     }
   };
-  if (v_skip > 0.0f) stream_tiles.template operator()<true>();
-  else stream_tiles.template operator()<false>();
+  // CG: two pairs of tiles in flight (buffers A, B and C, D), each pair
+  // refilled with the pair after next once it has been consumed.
+  auto stream_pairs = [&]<bool VSKIP>() __attribute__((always_inline)) {
+    int k = 0;
+    for (; k + 4 <= nfull; k += 4) {
+      const uint32_t ta = first + STEP * k;
+      pair_step.template operator()<true, VSKIP>(bufA, ta, bufB, ta + STEP);
+      load_at(bufA, k + 4, ta + 4 * STEP);
+      load_at(bufB, k + 5, ta + 5 * STEP);
+      pair_step.template operator()<true, VSKIP>(bufC, ta + 2 * STEP, bufD, ta + 3 * STEP);
+      load_at(bufC, k + 6, ta + 6 * STEP);
+      load_at(bufD, k + 7, ta + 7 * STEP);
+    }
+    // at most three whole tiles and a partial one remain; tokens past the
+    // split's end (and tiles past the wave's last) are masked out
+    const uint32_t ta = first + STEP * k;
+    if (k < nt) pair_step.template operator()<false, VSKIP>(bufA, ta, bufB, ta + STEP);
+    if (k + 2 < nt) pair_step.template operator()<false, VSKIP>(bufC, ta + 2 * STEP, bufD, ta + 3 * STEP);
+  };
+  if constexpr (CG) {
+    if (v_skip > 0.0f) stream_pairs.template operator()<true>();
+    else stream_pairs.template operator()<false>();
+  } else {
+    if (v_skip > 0.0f) stream_tiles.template operator()<true>();
+    else stream_tiles.template operator()<false>();
+  }
 
-  // ---- merge the waves; l: sum over the 4 token lanes of a head.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  // ---- merge the waves; l: sum over the 4 token lanes of a head (CG: over
+  // all lanes, head i from component i).
+  if constexpr (CG) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lc[i] = wave_sum(lc[i]);
+      if (lane == i) {
+        m_run = mc[i];
+        l_run = lc[i];
+      }
+    }
+  } else {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+  }
   __syncthreads();  // LUTs are dead from here on: reuse their space
   float* mrg_m = reinterpret_cast<float*>(smem);           // [SW][16]
   float* mrg_l = mrg_m + SW * 16;                           // [SW][16]
@@ -1069,18 +1265,31 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
   finish();
 }
 
-template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED, bool NF16>
-hipError_t launch_split_as(const SplitArgs& f) {
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED, bool NF16, bool CG>
+hipError_t launch_split_cg(const SplitArgs& f) {
   const tq_attn& a = *f.a;
   const AttendPlan& plan = *f.plan;
   const tq_cache &kc = *f.kc, &vc = *f.vc;
   const dim3 grid(a.hkv, a.batch, plan.n_split);
-  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL, PAGED, NF16>), grid, dim3(ST), 0, f.st, f.ktab, kc.codes,
+  hipLaunchKernelGGL((split_kernel<KLO, KHI, VLO, VHI, QJL, PAGED, NF16, CG>), grid, dim3(ST), 0, f.st, f.ktab, kc.codes,
                      kc.norms, kc.qjl_signs, kc.qjl_rnorms, kc.cap, f.vtab, vc.codes, vc.norms, vc.cap, f.seq_lens,
                      f.q, f.sink_k, f.sink_v, f.parts, f.out, a.hq, a.hkv, a.sink, plan.n_split, plan.n_slot,
                      plan.chunk, a.v_skip, a.scale * LOG2E, f.block_table, PAGED ? f.max_pages : 0,
                      PAGED ? f.n_pages : 0, static_cast<int>(a.max_len));
   return hipGetLastError();
+}
+
+// Groups of at most 4 query heads take the compact softmax when every
+// stream is a single split (a batch of 256 or more streams): each wave then
+// streams its stream's whole length, and the compact step pays for its fixed
+// costs.  (With many short splits per stream it measured slower: the
+// gqa_decode shape 19.2 -> 21.7 us, long_context 40.7 -> 42.9 us; the
+// batched ragged workload 265 -> 253 us.)
+template <int KLO, int KHI, int VLO, int VHI, bool QJL, bool PAGED, bool NF16>
+hipError_t launch_split_as(const SplitArgs& f) {
+  return f.a->hq / f.a->hkv <= 4 && f.plan->n_split == 1
+             ? launch_split_cg<KLO, KHI, VLO, VHI, QJL, PAGED, NF16, true>(f)
+             : launch_split_cg<KLO, KHI, VLO, VHI, QJL, PAGED, NF16, false>(f);
 }
 
 template <int KLO, int KHI, int VLO, int VHI, bool QJL>

@@ -364,8 +364,8 @@ tq_status check_spec(const tq_spec* s, tq::Spec* out) {
   if (s->qjl_m != 0 && s->qjl_m != TQ_QJL_M) return fail(TQ_E_UNSUPPORTED, "qjl_m must be 0 or 128");
   if (s->qjl_m && s->layout != TQ_LAYOUT_RECORD)
     return fail(TQ_E_UNSUPPORTED, "the QJL sketch needs the record layout");
-  if (s->rotation != TQ_ROT_HAAR && s->rotation != TQ_ROT_HADAMARD)
-    return fail(TQ_E_ARG, "rotation must be TQ_ROT_HAAR or TQ_ROT_HADAMARD");
+  if (s->rotation != TQ_ROT_HAAR && s->rotation != TQ_ROT_HADAMARD && s->rotation != TQ_ROT_HADAMARD_FWHT)
+    return fail(TQ_E_ARG, "rotation must be TQ_ROT_HAAR, TQ_ROT_HADAMARD or TQ_ROT_HADAMARD_FWHT");
   if (s->norm_f16 != 0 && s->norm_f16 != 1) return fail(TQ_E_ARG, "norm_f16 must be 0 or 1");
   if (out) {
     out->bits_lo = bl;
@@ -374,6 +374,7 @@ tq_status check_spec(const tq_spec* s, tq::Spec* out) {
     out->layout = s->layout;
     out->code_bytes = 8 * (bl + bhi);
     out->norm16 = s->norm_f16;
+    out->rotation = s->rotation;
   }
   return TQ_OK;
 }
@@ -521,7 +522,7 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
         return fail(TQ_E_UNSUPPORTED, "codebook boundaries too close for the code cell table");
     }
     std::vector<double> m(tq::D * tq::D);
-    if (spec->rotation == TQ_ROT_HADAMARD) hadamard_rotation_build(tq::D, spec->rot_seed, m.data());
+    if (spec->rotation != TQ_ROT_HAAR) hadamard_rotation_build(tq::D, spec->rot_seed, m.data());
     else rotation_build(tq::D, spec->rot_seed, m.data());
     for (int i = 0; i < tq::D; ++i)
       for (int k = 0; k < tq::D; ++k) t->pit[k * tq::D + i] = static_cast<float>(m[i * tq::D + k]);

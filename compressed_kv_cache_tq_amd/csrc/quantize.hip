@@ -29,6 +29,7 @@
 // the xor of the masks j with 2^k | (j+1), done on the scalar unit; the sign
 // turns count into code.  Each code bit is appended to the packed word with
 // one v_addc (w = 2w + bit), most significant bit first.
+#include <atomic>
 #include <type_traits>
 #include <vector>
 
@@ -1211,16 +1212,16 @@ hipError_t launch_each(const Tables* tab, const void* x, const QSeq* seqs, int64
 }
 
 // Compute units of the current device (cached per device).
-int cu_count() {
-  static int cached[64] = {};
+int cu_count_cached() {
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // tiles [t_lo, t_lo + t_step, ...) (tiles of them) of every stream of a sequence
@@ -1242,7 +1243,7 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
     // A persistent launch (chunks of 6 tiles, each pair looping over its
     // chunks) once every resident pair gets at least 8 chunks; else one chunk
     // per pair: 8 tiles once that still fills every CU twice over, or 2.
-    const int64_t pairs = 4 * static_cast<int64_t>(cu_count());  // two resident workgroups of two pairs per CU
+    const int64_t pairs = 4 * static_cast<int64_t>(cu_count_cached());  // two resident workgroups of two pairs per CU
     const int K = MERGE ? 2 : raw >= 6 * 8 * pairs ? 6 : raw >= 8 * 1024 ? 8 : 2;
 
     RotqArgs a{};
@@ -1280,7 +1281,7 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
     if (K == 6) {
       // two resident workgroups per CU (the register budget of the kernel),
       // each pair looping over its chunks
-      const int64_t resident = 2 * static_cast<int64_t>(cu_count());
+      const int64_t resident = 2 * static_cast<int64_t>(cu_count_cached());
       if (blocks > resident) blocks = static_cast<unsigned>(resident);
       a.n_iter = static_cast<int32_t>((a.n_chunks + 2 * blocks - 1) / (2 * blocks));
     }
@@ -1378,9 +1379,16 @@ hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const v
 
 }  // namespace
 
+int cu_count() { return cu_count_cached(); }
+
 hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
                            int64_t n_seq, int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c,
                            const PageMap& pm, hipStream_t st) {
+  // the Hadamard rotation by butterflies where that kernel applies (and its
+  // 32-bit buffer offsets hold); otherwise the same matrix on the MFMA path
+  if (sp.rotation == TQ_ROT_HADAMARD_FWHT && fwht_supported(sp, dtype, pm.table != nullptr) &&
+      64 * xrs < (int64_t{1} << 30) && c.cap < (int64_t{1} << 24))
+    return launch_quantize_fwht(sp, tab, x, seqs, n_seq, hkv, xss, xrs, c, st);
   const int key = sp.bits_lo * 10 + sp.bits_hi;
   switch (key) {
     case 22: return dispatch_layout<2, 2>(sp, tab, dtype, x, seqs, n_seq, hkv, xss, xrs, c, pm, st);

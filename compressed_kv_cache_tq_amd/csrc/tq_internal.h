@@ -96,6 +96,7 @@ struct Spec {
   int layout;
   int code_bytes;  // per token
   int norm16;      // norms stored as fp16 (else fp32)
+  int rotation;    // tq_rotation
 };
 
 // One sequence of a quantize call: hkv streams whose rows start at element
@@ -117,6 +118,15 @@ struct PageMap {
   int64_t ld = 0;
   int64_t n_pages = 0;
 };
+
+// Compute units of the current device (cached per device).
+int cu_count();
+
+// The butterfly quantize (fwht.hip): keys in the record layout, bf16, uniform
+// 2-4 bit codes, no sketch, contiguous cache.
+bool fwht_supported(const Spec& sp, int dtype, bool paged);
+hipError_t launch_quantize_fwht(const Spec& sp, const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq,
+                                int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c, hipStream_t st);
 
 hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
                            int64_t n_seq, int64_t hkv, int64_t x_stream_stride, int64_t x_row_stride,

@@ -21,7 +21,7 @@ TILE = 32
 QJL_M = 128
 F32, BF16 = 0, 1
 LAYOUT_RECORD, LAYOUT_TILED = 0, 1
-ROT_HAAR, ROT_HADAMARD = 0, 1
+ROT_HAAR, ROT_HADAMARD, ROT_HADAMARD_FWHT = 0, 1, 2
 STATUS = {0: "TQ_OK", -1: "TQ_E_ARG", -2: "TQ_E_UNSUPPORTED", -3: "TQ_E_WORKSPACE", -4: "TQ_E_HIP"}
 
 EXPORTS = [

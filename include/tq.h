@@ -79,8 +79,14 @@ typedef enum {
  * span less than 2^30 bytes (else TQ_E_UNSUPPORTED). */
 /* How the rotation Pi is drawn from rot_seed. */
 typedef enum {
-  TQ_ROT_HAAR = 0,      /* Haar-distributed orthogonal matrix (tq_rotation_build) */
-  TQ_ROT_HADAMARD = 1   /* randomized Hadamard matrix (tq_hadamard_rotation_build) */
+  TQ_ROT_HAAR = 0,          /* Haar-distributed orthogonal matrix (tq_rotation_build) */
+  TQ_ROT_HADAMARD = 1,      /* randomized Hadamard matrix (tq_hadamard_rotation_build) */
+  TQ_ROT_HADAMARD_FWHT = 2  /* the same matrix, applied in the quantize by the O(d log d)
+                               butterfly transform where that kernel applies (bf16 keys in
+                               the record layout, uniform 2-4 bit codes, no sketch,
+                               contiguous cache), by the dense product elsewhere; the
+                               tables, the codes and the decode are those of
+                               TQ_ROT_HADAMARD */
 } tq_rotation;
 
 typedef struct {

@@ -27,7 +27,7 @@ def to_device(x_f32: np.ndarray, dtype: str):
 def ospec(s: tq.Spec) -> oqz.Spec:
     return oqz.Spec(bits_lo=s.bits_lo, bits_hi=s.bits_lo if s.bits_hi is None else s.bits_hi,
                     split=s.split, qjl_m=s.qjl_m, rot_seed=s.rot_seed, qjl_seed=s.qjl_seed,
-                    rotation="hadamard" if s.rotation == tq.ROT_HADAMARD else "haar", norm_f16=bool(s.norm_f16))
+                    rotation="haar" if s.rotation == tq.ROT_HAAR else "hadamard", norm_f16=bool(s.norm_f16))
 
 
 def read_codes(spec: tq.Spec, cache: tq.Cache, stream: int, n_tok: int, tok0: int = 0) -> np.ndarray:

@@ -65,7 +65,7 @@ int main() {
   for (const W& w : widths)
     for (int layout : {TQ_LAYOUT_RECORD, TQ_LAYOUT_TILED})
       for (int qjl : {0, TQ_QJL_M})
-        for (int rot : {TQ_ROT_HAAR, TQ_ROT_HADAMARD})
+        for (int rot : {TQ_ROT_HAAR, TQ_ROT_HADAMARD, TQ_ROT_HADAMARD_FWHT})
           for (int nf : {0, 1}) {
             tq_spec sp{TQ_DIM, w.lo, w.hi, w.split, qjl, layout, 0, 1, rot, nf};
             const tq_status st = tq_tables_build(&sp, tab, tb);
@@ -77,7 +77,7 @@ int main() {
               CHECK(std::strlen(tq_last_error()) > 0);
             }
           }
-  CHECK(n_ok >= 40);
+  CHECK(n_ok >= 60);
   tq_spec bad{TQ_DIM, 5, 5, 128, 0, 0, 0, 1, 0, 0};
   CHECK(tq_tables_build(&bad, tab, tb) != TQ_OK);
   CHECK(tq_tables_build(nullptr, tab, tb) != TQ_OK);

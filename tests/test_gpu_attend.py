@@ -48,14 +48,16 @@ def test_attend_small(name, ctx, batch):
     _check(Run(workloads.generate(name, ctx=ctx, batch=batch)), label=f"{name} small")
 
 
+@pytest.mark.parametrize("rot", [tq.ROT_HADAMARD, tq.ROT_HADAMARD_FWHT])
 @pytest.mark.parametrize("name,ctx,batch", [("gqa_decode", 1500, None), ("qjl", 1000, 2), ("batched_ragged", 900, 3)])
-def test_attend_hadamard_rotation(name, ctx, batch):
+def test_attend_hadamard_rotation(name, ctx, batch, rot):
     """Keys and values rotated by the randomized Hadamard matrix (QJL keys
-    included): the same kernels, the oracle with the Hadamard Pi."""
-    print(f"[attend] hadamard {name}", flush=True)
+    included), as a dense product or (TQ_ROT_HADAMARD_FWHT, the sketch-free
+    bf16 keys) by butterflies: the oracle with the Hadamard Pi."""
+    print(f"[attend] hadamard {name} rotation {rot}", flush=True)
     run = Run(workloads.generate(name, ctx=ctx, batch=batch))
-    run.kspec = dataclasses.replace(run.kspec, rotation=tq.ROT_HADAMARD)
-    run.vspec = dataclasses.replace(run.vspec, rotation=tq.ROT_HADAMARD)
+    run.kspec = dataclasses.replace(run.kspec, rotation=rot)
+    run.vspec = dataclasses.replace(run.vspec, rotation=rot)
     run.ktab, run.vtab = tq.device_tables(run.kspec), tq.device_tables(run.vspec)
     _check(run, label=f"{name} hadamard")
 

@@ -459,3 +459,48 @@ def test_quantize_fp16_norms_saturate(bits, layout, qjl, dtype):
     assert np.all(np.isfinite(norms.astype(np.float32))), "an fp16 norm overflowed to infinity"
     signs = read_signs(cache, 0, 96) if qjl else None
     check_quantized(spec, x[0], read_codes(spec, cache, 0, 96), norms, signs=signs, label=f"fp16 saturation {bits}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_hadamard_butterflies(bits):
+    """TQ_ROT_HADAMARD_FWHT: the randomized Hadamard matrix applied by the
+    butterfly kernel (bf16 keys, record layout).  Codes and norms pass the
+    oracle's rules for the Hadamard rotation, over a ragged call with
+    unaligned offsets, a partial last tile and zero vectors, with fp32 and
+    fp16 norms; the dense-product Hadamard path gives the same codes up to
+    band mismatches against the same oracle."""
+    print(f"[quantize] hadamard butterflies {bits}-bit", flush=True)
+    T = torch()
+    lens = [45, 0, 130, 77]
+    hkv, rows = 3, 140
+    x = np.random.default_rng(70 + bits).standard_normal((len(lens) * hkv, rows, 128), dtype=np.float32)
+    x[1, 3] = 0.0
+    x[7, 50] = 0.0
+    x = workloads.bf16_to_f32(workloads.bf16_bits(x))
+    tok0 = [5, 0, 33, 0]
+    for nf in (0, 1):
+        fw = tq.Spec(bits, layout=tq.LAYOUT_RECORD, rotation=tq.ROT_HADAMARD_FWHT, norm_f16=nf)
+        dense = tq.Spec(bits, layout=tq.LAYOUT_RECORD, rotation=tq.ROT_HADAMARD, norm_f16=nf)
+        got = {}
+        for spec in (fw, dense):
+            cache = tq.alloc_cache(spec, len(lens) * hkv, 192, fill=0x5A)
+            tq.quantize_kv_ragged(spec, tq.device_tables(spec), to_device(x, "bf16"), cache, hkv=hkv, n_tok=lens,
+                                  tok0=tok0)
+            T.cuda.synchronize()
+            got[spec.rotation] = cache
+        for b, n in enumerate(lens):
+            for h in range(hkv):
+                s = b * hkv + h
+                if n == 0:
+                    raw = got[tq.ROT_HADAMARD_FWHT].codes[s * 192 * 16 * bits:(s + 1) * 192 * 16 * bits]
+                    assert T.all(raw == 0x5A), "an empty sequence was written"
+                    continue
+                for rot, cache in got.items():
+                    check_quantized(fw if rot == tq.ROT_HADAMARD_FWHT else dense, x[s, :n],
+                                    read_codes(fw, cache, s, n, tok0[b]), read_norms(cache, s, n, tok0[b]),
+                                    label=f"rotation {rot} b{b} h{h} nf{nf}")
+                # positions outside the written range keep their fill
+                c = got[tq.ROT_HADAMARD_FWHT]
+                rb = 16 * bits
+                stream = c.codes[s * 192 * rb:(s + 1) * 192 * rb].view(192, rb)
+                assert T.all(stream[:tok0[b]] == 0x5A) and T.all(stream[tok0[b] + n:] == 0x5A)

@@ -63,14 +63,17 @@ def test_hadamard_rotation_errors_and_spec_fields():
         assert L.tq_hadamard_rotation_build(d, 0, m.ctypes.data) == -1
     assert L.tq_hadamard_rotation_build(4, 0, None) == -1
     buf = np.zeros(tq.tables_bytes(), dtype=np.uint8)
-    for rot, nf16 in ((2, 0), (-1, 0), (0, 2)):
+    for rot, nf16 in ((3, 0), (-1, 0), (0, 2)):
         cs = tq.Spec(4).c()
         cs.rotation, cs.norm_f16 = rot, nf16
         assert tq.lib().tq_tables_build(ctypes.byref(cs), buf.ctypes.data, buf.size) == -1
 
 
-def test_hadamard_tables():
-    spec = tq.Spec(3, layout=tq.LAYOUT_TILED, rot_seed=5, rotation=tq.ROT_HADAMARD)
+@pytest.mark.parametrize("rot", [1, 2])
+def test_hadamard_tables(rot):
+    """Both Hadamard options (dense product, butterflies) carry the same
+    matrix in the tables."""
+    spec = tq.Spec(3, layout=tq.LAYOUT_TILED, rot_seed=5, rotation=rot)
     ref = orot.hadamard_rotation(5, 128)
     hdr, pi, pi_hi, pi_lo, *_ = _tables_view(spec, ref)
     assert np.array_equal(pi, ref.astype(np.float32))
