@@ -76,22 +76,25 @@ STEP_SOURCES = {"quantize_k": KERNEL_SOURCES[0], "quantize_v": KERNEL_SOURCES[0]
 
 def step_kernels(wname: str) -> dict:
     """Kernels of one bench step of a workload (default options), by the name
-    rocprofv3 reports ('*' stands for the tiles-per-chunk argument the launch
-    picks by size): the traffic of a phase is the sum over its kernels."""
+    rocprofv3 reports ('*' stands for a template argument the launch picks:
+    the quantize's tiles per chunk, by size; the decode's softmax form, by
+    group size and splits): the traffic of a phase is the sum over its
+    kernels."""
     from compressed_kv_cache_tq_amd import workloads
     wl = workloads.WORKLOADS[wname]
     f32 = "true" if wl.dtype == "f32" else "false"
     k, v = wl.k, wl.v
     # (kernel, dispatches per call)
-    if k.qjl_m:  # the sketch kernel launches once per sequence
-        qk = [(f"quantize_kernel<{k.bits_lo}, {k.bits_hi}, {2 if wl.dtype == 'f32' else 1}, false, true>", wl.batch)]
+    if k.qjl_m:  # the sketch kernel launches once per 32 sequences
+        qk = [(f"quantize_kernel<{k.bits_lo}, {k.bits_hi}, {2 if wl.dtype == 'f32' else 1}, false, true>",
+               -(-wl.batch // 32))]
     else:
         qk = [(f"rotq_kernel<{k.bits_lo}, {k.bits_hi}, {f32}, false, *, false, false>", 1)]
     qv = [(f"rotq_kernel<{v.bits_lo}, {v.bits_hi}, {f32}, true, *, false, false>", 1)]
     if wl.lens_range:  # ragged lengths: the last, partly written value tile of each sequence
         qv.append((f"rotq_kernel<{v.bits_lo}, {v.bits_hi}, {f32}, true, 2, true, false>", 1))
     at = [(f"split_kernel<{k.bits_lo}, {k.bits_hi}, {v.bits_lo}, {v.bits_hi}, {'true' if k.qjl_m else 'false'}, "
-           f"false, false>", 1)]
+           f"false, false, *>", 1)]
     if not wl.lens_range:
         at.append(("combine_kernel", 1))
     return {"quantize_k": qk, "quantize_v": qv, "attend": at}
@@ -133,7 +136,7 @@ def traffic_summary(fetch_dir: str, write_dir: str, wname: str, command: str = "
         for key, names in STEP_KERNELS.items():
             tot, raw = 0.0, 0.0
             for kname, mult in names:
-                pat = re.compile(re.escape(kname).replace(r"\*", r"\d+"))
+                pat = re.compile(re.escape(kname).replace(r"\*", r"\w+"))
                 vals = [v for n, v in per.values() if pat.search(n.replace("(anonymous namespace)::", ""))]
                 if not vals:
                     raise SystemExit(f"{run_dir}: no dispatch of {kname}")

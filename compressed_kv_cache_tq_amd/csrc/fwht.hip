@@ -18,6 +18,7 @@
 // dense kernel, packed LSB first into the record's half of lane h.  Keys in
 // the record layout, bf16 input, uniform 2-, 3- or 4-bit codes, no sketch,
 // contiguous caches; one launch covers up to 64 sequences of a ragged batch.
+#include "cell.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -167,8 +168,7 @@ __global__ __launch_bounds__(FW_THREADS) void fwht_kernel(const FwArgs A) {
 #pragma unroll
       for (int p = 0; p < 32; ++p) {
         const float yy = y[32 * half + p] * inv;
-        const float f = __builtin_amdgcn_fmed3f(fmaf(yy, 64.0f, 64.0f), 0.0f, 128.0f);
-        const uint2 e = cell_s[static_cast<uint32_t>(f)];
+        const uint2 e = cell_entry(cell_s, yy);
         c[p] = e.y + (yy > __uint_as_float(e.x) ? 1u : 0u);
       }
       // 32 codes LSB first into B dwords

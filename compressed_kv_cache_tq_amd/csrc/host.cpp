@@ -395,20 +395,15 @@ tq_status hip_status(hipError_t e, const char* where) {
 }
 
 
-// Cell table of one codebook (fp32 boundaries, ascending).  Cell c covers
-// [c/64 - 1, (c+1)/64 - 1).  The kernel finds the cell as the fp32 round of
-// 64 y + 64 truncated, which can only move a value that lies just below an
-// edge up into the next cell; the code stays exact if no boundary lies in
-// that sliver below an edge.  Fails if a cell holds two boundaries or a
-// boundary sits within 1e-6 below an edge.
-// Cell c covers [c / scale - offset, (c + 1) / scale - offset); false when a
-// cell holds two boundaries or a boundary lies less than `margin` below a
-// cell edge (the kernels' fp32 cell index fma(y, scale, scale * offset) can
-// round such a y across the edge: by at most 2^-25 at both scales used).
-bool cell_table(const float* bnd, int nb, uint32_t (*cell)[2], int entries = tq::CELL_ENTRIES, double scale = 64.0,
-                double offset = 1.0, double margin = 1e-6) {
+// Cell tables of a codebook (fp32 boundaries, ascending): entry c = {bits of
+// the one boundary inside cell c (or of +inf), number of boundaries below the
+// cell}, so that the code of y in cell c is below + (y > boundary).  Cell c is
+// the half-open interval [lo(c), lo(c + 1)); false when a cell holds two
+// boundaries or a boundary lies less than `margin` below an upper edge.
+template <class Lo>
+bool cell_table(const float* bnd, int nb, uint32_t (*cell)[2], int entries, Lo lo_of, double margin) {
   for (int c = 0; c < entries; ++c) {
-    const double lo = c / scale - offset, hi = (c + 1) / scale - offset;
+    const double lo = lo_of(c), hi = lo_of(c + 1);
     uint32_t below = 0, inside = 0;
     float b_in = INFINITY;
     for (int j = 0; j < nb; ++j) {
@@ -427,6 +422,24 @@ bool cell_table(const float* bnd, int nb, uint32_t (*cell)[2], int entries = tq:
     cell[c][1] = below;
   }
   return true;
+}
+
+// 2- to 4-bit codebooks: the kernels take the cell of y from the fp32 fma
+// u = fl(512 y + 512 + 2^23), one rounding to nearest even, as bits 3..10 of
+// u's mantissa, i.e. c = RNE(512 y + 512) >> 3.  Ties go to even integers, so
+// cell c is exactly [(8c - 1/2) / 512 - 1, (8c + 15/2) / 512 - 1) for every
+// |y| <= 1 + 1/1024, and the code below + (y > boundary) is exact with no
+// margin.
+bool cell_table_u(const float* bnd, int nb, uint32_t (*cell)[2]) {
+  return cell_table(bnd, nb, cell, tq::CELL_ENTRIES, [](int c) { return (8.0 * c - 0.5) / 512.0 - 1.0; }, 0.0);
+}
+
+// 8-bit codebooks: cell c = [c / 1024 - 1/2, (c + 1) / 1024 - 1/2), found as
+// the truncated fp32 fma(y, 1024, 512) clamped to [0, 1024], which can move a
+// y lying just below an edge up into the next cell (by at most 2^-25): no
+// boundary may lie within 1e-7 below an edge.
+bool cell_table_8(const float* bnd, int nb, uint32_t (*cell)[2]) {
+  return cell_table(bnd, nb, cell, tq::CELL8_ENTRIES, [](int c) { return c / 1024.0 - 0.5; }, 1e-7);
 }
 
 }  // namespace
@@ -509,7 +522,7 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
           t->cen16_8[j] = to_half(c[j]);
         }
         if (!(bd[0] > -0.5 && bd[254] < 0.5) ||
-            !cell_table(t->bnd8, 255, t->cell8, tq::CELL8_ENTRIES, tq::CELLS8, 0.5, 1e-7))
+            !cell_table_8(t->bnd8, 255, t->cell8))
           return fail(TQ_E_UNSUPPORTED, "8-bit codebook boundaries too close for the code cell table");
         break;
       }
@@ -518,7 +531,7 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
         t->cen[h][j] = j < L ? static_cast<float>(c[j]) : 0.0f;
         t->cen16[h][j] = j < L ? to_half(c[j]) : 0;
       }
-      if (!cell_table(t->bnd[h], L - 1, t->cell[h]))
+      if (!cell_table_u(t->bnd[h], L - 1, t->cell[h]))
         return fail(TQ_E_UNSUPPORTED, "codebook boundaries too close for the code cell table");
     }
     std::vector<double> m(tq::D * tq::D);

@@ -33,6 +33,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "cell.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -187,8 +188,7 @@ __device__ __forceinline__ void store_record(uint8_t* dst, const uint32_t (&w)[8
 // Code of y (a rotated unit-vector coordinate) from the cell table: the
 // cell gives the number of boundaries below it and the one boundary inside.
 __device__ __forceinline__ uint32_t cell_code(float y, const uint2* cells) {
-  const float f = __builtin_amdgcn_fmed3f(fmaf(y, 64.0f, 64.0f), 0.0f, 128.0f);
-  const uint2 e = cells[static_cast<uint32_t>(f)];
+  const uint2 e = cell_entry(cells, y);
   return e.y + (y > __uint_as_float(e.x) ? 1u : 0u);
 }
 
@@ -282,12 +282,46 @@ __device__ __forceinline__ void store_tiled_chunk(uint8_t* dst, const uint32_t (
   }
 }
 
+// Sequences of one launch of the general kernel: the launch's tiles are the
+// sequences' tiles in order (each sequence's hkv streams, stream-major).
+constexpr int GEN_MAX_SEQ = 32;
+struct GenSeq {
+  int64_t x_off;     // element offset of the sequence's stream 0, row 0
+  int64_t tok0;      // cache position of row 0
+  int64_t n_tok;     // rows per stream
+  int64_t stream0;   // contiguous cache: cache stream of kv head 0 (paged: 0)
+  int64_t tiles;     // tiles per stream
+  int64_t tile0;     // tiled layout: first tile touched (record: 0)
+  int64_t start;     // first launch tile of the sequence
+  int64_t page_row;  // paged: the sequence's row of the block table
+};
+struct GenArgs {
+  const Tables* tab;
+  const void* x;
+  int64_t xss, xrs, cap, stream_code_bytes;
+  uint8_t* codes;
+  float* norms;
+  uint8_t* signs;
+  float* rnorms;
+  const int32_t* pages;  // paged: the block table (else nullptr)
+  int64_t page_ld, n_pages;
+  int64_t hkv;
+  int64_t total_tiles;
+  int32_t n_seq;
+  int32_t norm16;
+  GenSeq seq[GEN_MAX_SEQ];  // ascending start
+};
+
 template <int BLO, int BHI, int XM, bool TILED, bool QJL>
-__global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
-    const Tables* __restrict__ tab, const void* __restrict__ xv, int64_t n_tok, int64_t xss, int64_t xrs,
-    int64_t tok0, uint8_t* __restrict__ codes, float* __restrict__ norms, uint8_t* __restrict__ signs,
-    float* __restrict__ rnorms, int64_t cap, int64_t stream_code_bytes, int64_t tiles_per_stream, int64_t tile0,
-    int64_t total_tiles, const int32_t* __restrict__ pages, int64_t n_pages, int64_t page_streams, int norm16) {
+__global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
+  const Tables* __restrict__ tab = A.tab;
+  const int64_t xss = A.xss, xrs = A.xrs, cap = A.cap, stream_code_bytes = A.stream_code_bytes;
+  const int64_t total_tiles = A.total_tiles;
+  const int norm16 = A.norm16;
+  uint8_t* __restrict__ codes = A.codes;
+  float* __restrict__ norms = A.norms;
+  uint8_t* __restrict__ signs = A.signs;
+  float* __restrict__ rnorms = A.rnorms;
   constexpr bool F32IN = XM == X_F32;
   constexpr int NPART = XM == X_BF16 ? 3 : 2;
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
@@ -328,27 +362,47 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
     else norms[i] = v;
   };
 
-  // Row of x this lane loads for tile w (vector column n for the record
-  // layout, token slot tiled_slot(n) for the tiled layout).
-  auto locate = [&](int64_t w, int64_t& s, int64_t& T, int64_t& row, int64_t& pos) {
-    s = w / tiles_per_stream;
-    T = w - s * tiles_per_stream;
+  // Tile w of the launch: its sequence (the last one starting at or before
+  // it; wave-uniform), stream s of the sequence, tile T of the stream, and the
+  // row of x and the cache position this lane's vector takes (vector column
+  // n for the record layout, token slot tiled_slot(n) for the tiled layout).
+  struct Loc {
+    int64_t x_off, tok0, n_tok, stream0, tile0, page_row;
+    int64_t s, T, row, pos;
+  };
+  auto locate = [&](int64_t w) {
+    int sq = 0;
+#pragma unroll
+    for (int step = GEN_MAX_SEQ / 2; step > 0; step >>= 1)
+      if (sq + step < A.n_seq && A.seq[sq + step].start <= w) sq += step;
+    const GenSeq& Q = A.seq[sq];
+    Loc L;
+    L.x_off = Q.x_off;
+    L.tok0 = Q.tok0;
+    L.n_tok = Q.n_tok;
+    L.stream0 = Q.stream0;
+    L.tile0 = Q.tile0;
+    L.page_row = Q.page_row;
+    const int64_t local = w - Q.start;
+    L.s = local / Q.tiles;
+    L.T = local - L.s * Q.tiles;
     if constexpr (TILED) {
-      pos = 32 * (tile0 + T) + tiled_slot(n);
-      row = pos - tok0;
+      L.pos = 32 * (L.tile0 + L.T) + tiled_slot(n);
+      L.row = L.pos - L.tok0;
     } else {
-      row = 32 * T + n;
-      pos = tok0 + row;
+      L.row = 32 * L.T + n;
+      L.pos = L.tok0 + L.row;
     }
+    return L;
   };
   // this lane's 64 elements (its half of the vector) as raw words
   constexpr int NW = F32IN ? 16 : 8;
   auto load_x = [&](int64_t w, uint4 (&dst)[NW]) {
-    int64_t s, T, row, pos;
-    locate(w, s, T, row, pos);
-    if (w < total_tiles && row >= 0 && row < n_tok) {
-      const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(xv) +
-                                                       (s * xss + row * xrs + 64 * h) * (F32IN ? 4 : 2));
+    const Loc L = locate(w < total_tiles ? w : total_tiles - 1);
+    if (w < total_tiles && L.row >= 0 && L.row < L.n_tok) {
+      const uint4* xp = reinterpret_cast<const uint4*>(
+          static_cast<const uint8_t*>(A.x) +
+          ((L.x_off + L.s * xss + L.row * xrs) + 64 * h) * (F32IN ? 4 : 2));
 #pragma unroll
       for (int k = 0; k < NW; ++k) dst[k] = xp[k];
     } else {
@@ -361,20 +415,20 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(
   load_x(static_cast<int64_t>(blockIdx.x) * WAVES + wave, xr);
 
   for (int64_t w = static_cast<int64_t>(blockIdx.x) * WAVES + wave; w < total_tiles; w += stride) {
-    int64_t s, T, row, pos;
-    locate(w, s, T, row, pos);
-    bool valid = row >= 0 && row < n_tok;
+    const Loc L = locate(w);
+    const int64_t s = L.s, T = L.T, pos = L.pos, tok0 = L.tok0, n_tok = L.n_tok, tile0 = L.tile0;
+    bool valid = L.row >= 0 && L.row < n_tok;
     // destination stream ds and position dp of this lane's vector.  Paged
     // cache: the page of the position (tiled layout: of the tile, which lies
     // inside one page) from the sequence's block-table row; a page outside
     // the pool is not written.
-    int64_t ds = s, dp = pos, dt = tile0 + T;
+    int64_t ds = L.stream0 + s, dp = pos, dt = tile0 + T;
     bool page_ok = true;
-    if (pages != nullptr) {
+    if (A.pages != nullptr) {
       const int64_t lp = (TILED ? 32 * (tile0 + T) : pos) / TQ_PAGE_TOKENS;
-      const int pg = TILED || valid ? pages[lp] : -1;
-      page_ok = pg >= 0 && pg < n_pages;
-      ds = static_cast<int64_t>(page_ok ? pg : 0) * page_streams + s;
+      const int pg = TILED || valid ? A.pages[L.page_row * A.page_ld + lp] : -1;
+      page_ok = pg >= 0 && pg < A.n_pages;
+      ds = static_cast<int64_t>(page_ok ? pg : 0) * A.hkv + s;
       dp = pos % TQ_PAGE_TOKENS;
       dt = (tile0 + T) % (TQ_PAGE_TOKENS / 32);
       valid = valid && page_ok;
@@ -678,10 +732,7 @@ __device__ __forceinline__ void cell_codes(YF yof, int p0, const uint2* cells, u
 #pragma unroll
   for (int i = 0; i < N; ++i) y[i] = yof(p0 + i);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float f = __builtin_amdgcn_fmed3f(fmaf(y[i], 64.0f, 64.0f), 0.0f, 128.0f);
-    e[i] = cells[static_cast<uint32_t>(f)];
-  }
+  for (int i = 0; i < N; ++i) e[i] = cell_entry(cells, y[i]);
 #pragma unroll
   for (int i = 0; i < N; ++i) c[i] = e[i].y + (y[i] > __uint_as_float(e[i].x) ? 1u : 0u);
 }
@@ -1163,52 +1214,64 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   }
 }
 
+// The general kernel over a ragged batch: one launch per GEN_MAX_SEQ
+// sequences, each launch's workgroups walking all of its tiles (so every
+// workgroup stages the rotation and sketch fragments once per launch).
 template <int BLO, int BHI, int XM, bool TILED, bool QJL>
-hipError_t launch_one(const Tables* tab, const void* x, int64_t n_streams, int64_t n_tok, int64_t xss, int64_t xrs,
-                      int64_t tok0, const tq_cache& c, const int32_t* pages, int64_t n_pages, int norm16,
-                      hipStream_t st) {
+hipError_t launch_general(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv,
+                          int64_t xss, int64_t xrs, const tq_cache& c, const PageMap& pm, int norm16,
+                          hipStream_t st) {
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
-  int64_t tiles, tile0 = 0;
-  if (TILED) {
-    tile0 = tok0 / TILE;
-    tiles = (tok0 + n_tok + TILE - 1) / TILE - tile0;
-  } else {
-    tiles = (n_tok + TILE - 1) / TILE;
-  }
-  const int64_t stream_bytes = c.cap * CODE_BYTES;
-  const int64_t total = n_streams * tiles;
-  const int64_t blocks = std::min<int64_t>((total + WAVES - 1) / WAVES, 256);
-  hipLaunchKernelGGL((quantize_kernel<BLO, BHI, XM, TILED, QJL>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(THREADS), 0, st, tab, x, n_tok, xss, xrs, tok0, c.codes, c.norms, c.qjl_signs,
-                     c.qjl_rnorms, c.cap, stream_bytes, tiles, tile0, total, pages, n_pages, n_streams, norm16);
-  return hipGetLastError();
-}
-
-// cache arrays of the streams from s0 on
-tq_cache streams_from(const tq_cache& c, int64_t s0, int64_t code_bytes, int norm16) {
-  tq_cache o = c;
-  o.codes = c.codes + s0 * c.cap * code_bytes;
-  o.norms = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(c.norms) + s0 * c.cap * (norm16 ? 2 : 4));
-  if (c.qjl_signs) o.qjl_signs = c.qjl_signs + s0 * c.cap * (QJL_M / 8);
-  if (c.qjl_rnorms) o.qjl_rnorms = c.qjl_rnorms + s0 * c.cap;
-  return o;
-}
-
-// one general-kernel launch per sequence
-template <int BLO, int BHI, int XM, bool TILED, bool QJL>
-hipError_t launch_each(const Tables* tab, const void* x, const QSeq* seqs, int64_t n_seq, int64_t hkv, int64_t xss,
-                       int64_t xrs, const tq_cache& c, const PageMap& pm, int norm16, hipStream_t st) {
-  constexpr int64_t ES = XM == X_F32 ? 4 : 2;
+  GenArgs a{};
+  a.tab = tab;
+  a.x = x;
+  a.xss = xss;
+  a.xrs = xrs;
+  a.cap = c.cap;
+  a.stream_code_bytes = c.cap * CODE_BYTES;
+  a.codes = c.codes;
+  a.norms = c.norms;
+  a.signs = c.qjl_signs;
+  a.rnorms = c.qjl_rnorms;
+  a.pages = pm.table;
+  a.page_ld = pm.ld;
+  a.n_pages = pm.n_pages;
+  a.hkv = hkv;
+  a.norm16 = norm16;
+  auto flush = [&]() -> hipError_t {
+    if (a.n_seq == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((a.total_tiles + WAVES - 1) / WAVES, 256);
+    hipLaunchKernelGGL((quantize_kernel<BLO, BHI, XM, TILED, QJL>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(THREADS), 0, st, a);
+    a.n_seq = 0;
+    a.total_tiles = 0;
+    return hipGetLastError();
+  };
   for (int64_t i = 0; i < n_seq; ++i) {
     const QSeq& q = seqs[i];
-    const int32_t* pages = pm.table ? pm.table + q.page_row * pm.ld : nullptr;
-    const hipError_t e = launch_one<BLO, BHI, XM, TILED, QJL>(tab, static_cast<const uint8_t*>(x) + q.x_off * ES,
-                                                              hkv, q.n_tok, xss, xrs, q.tok0,
-                                                              streams_from(c, q.stream0, 8 * (BLO + BHI), norm16),
-                                                              pages, pm.n_pages, norm16, st);
-    if (e != hipSuccess) return e;
+    if (q.n_tok <= 0) continue;
+    GenSeq g{};
+    g.x_off = q.x_off;
+    g.tok0 = q.tok0;
+    g.n_tok = q.n_tok;
+    g.stream0 = pm.table ? 0 : q.stream0;
+    g.page_row = q.page_row;
+    if (TILED) {
+      g.tile0 = q.tok0 / TILE;
+      g.tiles = (q.tok0 + q.n_tok + TILE - 1) / TILE - g.tile0;
+    } else {
+      g.tile0 = 0;
+      g.tiles = (q.n_tok + TILE - 1) / TILE;
+    }
+    g.start = a.total_tiles;
+    a.seq[a.n_seq++] = g;
+    a.total_tiles += hkv * g.tiles;
+    if (a.n_seq == GEN_MAX_SEQ) {
+      const hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
   }
-  return hipSuccess;
+  return flush();
 }
 
 // Compute units of the current device (cached per device).
@@ -1345,7 +1408,7 @@ hipError_t launch_rotq(const Tables* tab, const void* x, const QSeq* seqs, int64
       streams >= (int64_t{1} << 31)) {
     // (8-bit codes have no general-kernel path)
     if constexpr (BLO == 8) return hipErrorNotSupported;
-    else return launch_each<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, norm16, st);
+    else return launch_general<BLO, BHI, XM, TILED, false>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, norm16, st);
   }
   auto run = [&](auto pg) {
     constexpr bool P = decltype(pg)::value;
@@ -1366,8 +1429,8 @@ hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const v
   const bool f32 = dtype == TQ_F32;
   if (sp.qjl_m) {
     const int nf = sp.norm16;
-    return f32 ? launch_each<BLO, BHI, X_F32, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, nf, st)
-               : launch_each<BLO, BHI, X_BF16_F16, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, nf, st);
+    return f32 ? launch_general<BLO, BHI, X_F32, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, nf, st)
+               : launch_general<BLO, BHI, X_BF16_F16, false, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, nf, st);
   }
   if (sp.layout == TQ_LAYOUT_TILED) {
     return f32 ? launch_rotq<BLO, BHI, true, true>(tab, x, seqs, n_seq, hkv, xss, xrs, c, pm, sp.norm16, st)
@@ -1379,7 +1442,6 @@ hipError_t dispatch_layout(const Spec& sp, const Tables* tab, int dtype, const v
 
 }  // namespace
 
-int cu_count() { return cu_count_cached(); }
 
 hipError_t launch_quantize(const Spec& sp, const Tables* tab, int dtype, const void* x, const QSeq* seqs,
                            int64_t n_seq, int64_t hkv, int64_t xss, int64_t xrs, const tq_cache& c,

@@ -15,7 +15,7 @@ constexpr int D = TQ_DIM;
 constexpr int TILE = TQ_TILE_TOKENS;
 constexpr int QJL_M = TQ_QJL_M;
 constexpr uint32_t TABLES_MAGIC = 0x31515454u;  // "TTQ1"
-constexpr int CELLS = 128;        // cells of the code table over [-1, 1]
+constexpr int CELLS = 128;        // cells of the code table over [-1, 1] (each 1/64 wide)
 constexpr int CELL_ENTRIES = 132; // CELLS + 1, padded
 constexpr int CELLS8 = 1024;        // cells of the 8-bit code table over [-1/2, 1/2]
 constexpr int CELL8_ENTRIES = 1028; // CELLS8 + 1, padded
@@ -56,9 +56,10 @@ struct alignas(256) Tables {
   float sit[D * D];
   uint16_t pi_b16[3][D * D];  // bf16 split of pi: hi + mid + lo keeps ~24 bits
   // Cell table of each half's codebook: y in [-1, 1] falls in cell
-  // floor(64 (y + 1)), c in [0, 128].  Entry c = {bits of the one boundary in
-  // [c/64 - 1, (c+1)/64 - 1) or of +inf, number of boundaries below c/64 - 1},
-  // so the code of y is code_low + (y > boundary).
+  // c = RNE(512 y + 512) >> 3 in [0, 128] (cell.h), the interval
+  // [(8c - 1/2) / 512 - 1, (8c + 15/2) / 512 - 1).  Entry c = {bits of the one
+  // boundary in the cell or of +inf, number of boundaries below the cell}, so
+  // the code of y is code_low + (y > boundary).
   uint32_t cell[2][CELL_ENTRIES][2];
   // pi_hi / pi_lo again, in the register order of the rotation kernel's MFMA
   // fragments so that every fragment load is one contiguous 1 KiB read:
@@ -118,9 +119,6 @@ struct PageMap {
   int64_t ld = 0;
   int64_t n_pages = 0;
 };
-
-// Compute units of the current device (cached per device).
-int cu_count();
 
 // The butterfly quantize (fwht.hip): keys in the record layout, bf16, uniform
 // 2-4 bit codes, no sketch, contiguous cache.

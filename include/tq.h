@@ -85,8 +85,12 @@ typedef enum {
                                butterfly transform where that kernel applies (bf16 keys in
                                the record layout, uniform 2-4 bit codes, no sketch,
                                contiguous cache), by the dense product elsewhere; the
-                               tables, the codes and the decode are those of
-                               TQ_ROT_HADAMARD */
+                               tables and the decode are those of TQ_ROT_HADAMARD, and
+                               so are the codes except where a rotated coordinate lies
+                               within rounding of a boundary.  On gfx950 the butterfly
+                               kernel is slower than the dense product (it loads the
+                               vector ALUs that the codes already use); it is kept as
+                               the transform the pages' port applies */
 } tq_rotation;
 
 typedef struct {

@@ -211,11 +211,19 @@ def test_quantize_ragged_many_sequences_and_packed_rows():
                                     label=f"packed/{layout}/stream {s}")
 
 
-def test_quantize_ragged_qjl():
-    """A spec with the sketch goes through one launch per sequence."""
-    print("[quantize] ragged qjl", flush=True)
+@pytest.mark.parametrize("n_seq", [3, 70])
+def test_quantize_ragged_qjl(n_seq):
+    """A spec with the sketch goes through the general kernel, one launch per
+    32 sequences (70: three launches, the last one partial), with empty
+    sequences skipped and every sequence's own offset and start position."""
+    print(f"[quantize] ragged qjl: {n_seq} sequences", flush=True)
     spec = tq.Spec(2, qjl_m=128)
-    lens, tok0s, hkv = [40, 0, 77], [0, 3, 9], 2
+    if n_seq == 3:
+        lens, tok0s, hkv = [40, 0, 77], [0, 3, 9], 2
+    else:
+        rng = np.random.default_rng(45)
+        lens, tok0s, hkv = rng.integers(0, 78, n_seq).tolist(), rng.integers(0, 19, n_seq).tolist(), 2
+        lens[5] = lens[40] = 0
     B = len(lens)
     x = _data(B * hkv * 77, seed=44, dtype="bf16").reshape(B * hkv, 77, 128)
     tab = tq.device_tables(spec)
@@ -265,8 +273,7 @@ def test_quantize_ragged_full_size_sampled():
 
 def test_quantize_wide_row_stride_general_kernel():
     """Rows 2^24 elements apart (32 MiB of bf16) exceed the rotation kernel's
-    32-bit buffer offsets, so the call goes to the general kernel, one launch
-    per sequence; records and tiles (with partly written tiles merged) must
+    32-bit buffer offsets, so the call goes to the general kernel; records and tiles (with partly written tiles merged) must
     still match the oracle, and the tiled neighbours must keep their codes."""
     print("[quantize] wide row stride: general kernel", flush=True)
     T = torch()

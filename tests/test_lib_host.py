@@ -181,11 +181,12 @@ def test_tables_content():
         assert np.all(np.isinf(bnd[h, L - 1:]))
         assert np.array_equal(cen[h, :L], cb.centroids.astype(np.float32))
         assert np.array_equal(cen16[h, :L], cb.centroids.astype(np.float16))
-        # cell table: cell c covers [c/64 - 1, (c+1)/64 - 1); boundaries below it
-        # and the one boundary inside it (or +inf), from the fp32 boundaries
+        # cell table: cell c covers [(8c - 1/2)/512 - 1, (8c + 15/2)/512 - 1);
+        # boundaries below it and the one boundary inside it (or +inf), from
+        # the fp32 boundaries
         b32 = cb.boundaries.astype(np.float32).astype(np.float64)
         for c in range(129):
-            lo, hi = c / 64 - 1, (c + 1) / 64 - 1
+            lo, hi = (8 * c - 0.5) / 512 - 1, (8 * c + 7.5) / 512 - 1
             inside = b32[(b32 >= lo) & (b32 < hi)]
             assert len(inside) <= 1
             want = np.float32(inside[0]) if len(inside) else np.float32(np.inf)
@@ -194,8 +195,9 @@ def test_tables_content():
 
 
 def test_cell_table_gives_the_codes():
-    """Codes from the cell rule (code_low + (y > boundary)) equal the count of
-    boundaries below y for random and boundary-adjacent fp32 values."""
+    """Codes from the cell rule (code_low + (y > boundary), cell from the
+    kernels' index) equal the count of boundaries below y for random and
+    boundary-adjacent fp32 values."""
     for bits in (2, 3, 4):
         spec = tq.Spec(bits)
         *_, bnd, cen, cen16, cells = _tables_view(spec)
@@ -205,11 +207,35 @@ def test_cell_table_gives_the_codes():
         y = np.concatenate([rng.normal(0, 0.09, 20000), rng.uniform(-1, 1, 2000), [-1.0, 1.0, 0.0]]).astype(np.float32)
         near = np.concatenate([np.nextafter(b32, np.float32(np.inf)), np.nextafter(b32, np.float32(-np.inf)), b32])
         y = np.concatenate([y, near.astype(np.float32)])
-        f = np.clip(np.float32(64) * y + np.float32(64), 0, 128).astype(np.float32)
-        c = f.astype(np.int64)
+        c = _cell_of(y)
         code = cells[0, c, 1].astype(np.int64) + (y > cells[0, c, 0].view(np.float32))
         want = np.searchsorted(b32, y, side="left")
         assert np.array_equal(code, want)
+
+
+def _cell_of(y):
+    """The kernels' cell index of fp32 y: bits 3..10 of the fp32 rounding
+    (nearest, ties to even) of 512 y + 512 + 2^23, which float64 holds exactly."""
+    u = (np.asarray(y, np.float32).astype(np.float64) * 512.0 + 8389120.0).astype(np.float32)
+    return ((u.view(np.uint32) & 0x7F8) >> 3).astype(np.int64)
+
+
+def test_cell_index_rounds_to_nearest_even():
+    """The cell index is RNE(512 y + 512) >> 3: values on either side of a
+    cell's edges, the ties exactly on them (to even: the lower edge belongs to
+    the cell, the upper to the next one), and the ends of [-1, 1]."""
+    for c in (0, 1, 63, 64, 65, 127, 128):
+        lo, hi = (8 * c - 0.5) / 512 - 1, (8 * c + 7.5) / 512 - 1
+        for y, want in ((lo, c), (hi, c + 1), ((lo + hi) / 2, c)):
+            if y < -1 - 1 / 2048:
+                continue  # outside the domain (|y| <= 1 up to rounding): 512 y + 512 + 2^23 < 2^23
+            y32 = np.float32(y)
+            assert float(y32) == y  # the edges are exact in fp32
+            assert _cell_of(y32) == want, (c, y)
+            assert _cell_of(np.nextafter(y32, np.float32(-2))) == want - (y == lo or y == hi), (c, y)
+    assert _cell_of(np.float32(-1.0)) == 0 and _cell_of(np.float32(1.0)) == 128
+    assert _cell_of(np.float32(-1 - 1 / 4096)) == 0 and _cell_of(np.float32(1 + 1 / 2048)) == 128
+    assert _cell_of(np.float32(0.0)) == 64
 
 
 def test_eight_bit_tables_and_cell_rule():
