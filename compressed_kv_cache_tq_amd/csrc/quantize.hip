@@ -104,12 +104,6 @@ struct Width {
   static constexpr int NPOS = HALF - 1;  // positive thresholds
 };
 
-template <int B>
-__device__ __forceinline__ void load_pos_thresholds(const Tables* tab, int half, float scale, float* tp) {
-#pragma unroll
-  for (int k = 0; k < Width<B>::NPOS; ++k) tp[k] = tab->bnd[half][Width<B>::HALF + k] * scale;
-}
-
 // Bit planes of the code of value v (same scale as the thresholds tp) as lane
 // masks: plane[k] = lanes whose code has bit k set.  code = #{t_j < v}; the
 // codebook is symmetric with a 0 threshold, v <= 0 counts on the negative side.
@@ -353,7 +347,10 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
         make_uint2(tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][0], tab->cell[c / CELL_ENTRIES][c % CELL_ENTRIES][1]);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (wave-uniform: the tile index, its sequence and every address derived
+  // from them live in scalar registers, and the sequence search reads the
+  // kernel arguments with scalar loads)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
   // norm i of the launch's streams: fp32, or fp16 rounded to nearest even
   // and saturated at the largest finite binary16 value
@@ -411,6 +408,14 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
     }
   };
   const int64_t stride = static_cast<int64_t>(gridDim.x) * WAVES;
+  // positive thresholds of each half's codebook (the sketch spec with two
+  // widths), read once: scaled per vector in the loop
+  float tpos[2][7];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    tpos[0][k] = k < Width<BLO>::NPOS ? tab->bnd[0][Width<BLO>::HALF + k] : 0.0f;
+    tpos[1][k] = k < Width<BHI>::NPOS ? tab->bnd[1][Width<BHI>::HALF + k] : 0.0f;
+  }
   uint4 xr[NW];
   load_x(static_cast<int64_t>(blockIdx.x) * WAVES + wave, xr);
 
@@ -521,29 +526,39 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
           pack_run<BLO>([&](int p) { return cell_code(acc[2 + (p >> 4)][p & 15] * inv, cell_s[0]); }, wds + BLO);
           if (valid) store_record<BLO>(rec + 8 * BLO * h, wds);
         } else if (h == 0) {
-          load_pos_thresholds<BLO>(tab, 0, sc, tp);
+#pragma unroll
+          for (int k = 0; k < Width<BLO>::NPOS; ++k) tp[k] = tpos[0][k] * sc;
           pack_record<BLO>(acc, tp, wds);
           if (valid) store_record<BLO>(rec, wds);
         } else {
-          load_pos_thresholds<BHI>(tab, 1, sc, tp);
+#pragma unroll
+          for (int k = 0; k < Width<BHI>::NPOS; ++k) tp[k] = tpos[1][k] * sc;
           pack_record<BHI>(acc, tp, wds);
           if (valid) store_record<BHI>(rec + 8 * BLO, wds);
         }
         if (valid && h == 0) put_norm(ds * cap + dp, normf);
       } else {
         uint32_t idx[64];
-        if (h == 0) {
-          load_pos_thresholds<BLO>(tab, 0, sc, tp);
+        if constexpr (BLO == BHI) {
+          // one width: cell-table codes for both halves of the vector at once
+          const float inv = sc > 0.0f ? 1.0f / sc : 0.0f;
+#pragma unroll
+          for (int c = 0; c < 64; ++c) idx[c] = cell_code(acc[c >> 4][c & 15] * inv, cell_s[0]);
+          pack_run<BLO>([&](int p) { return idx[p]; }, wds);
+          pack_run<BLO>([&](int p) { return idx[32 + p]; }, wds + BLO);
+          if (valid) store_record<BLO>(rec + 8 * BLO * h, wds);
+        } else if (h == 0) {
+#pragma unroll
+          for (int k = 0; k < Width<BLO>::NPOS; ++k) tp[k] = tpos[0][k] * sc;
           pack_record_scalar<BLO>(acc, tp, wds, idx);
+          if (valid) store_record<BLO>(rec, wds);
         } else {
-          load_pos_thresholds<BHI>(tab, 1, sc, tp);
+#pragma unroll
+          for (int k = 0; k < Width<BHI>::NPOS; ++k) tp[k] = tpos[1][k] * sc;
           pack_record_scalar<BHI>(acc, tp, wds, idx);
+          if (valid) store_record<BHI>(rec + 8 * BLO, wds);
         }
-        if (valid) {
-          if (h == 0) store_record<BLO>(rec, wds);
-          else store_record<BHI>(rec + 8 * BLO, wds);
-          if (h == 0) put_norm(ds * cap + dp, normf);
-        }
+        if (valid && h == 0) put_norm(ds * cap + dp, normf);
         // residual r = y - c[idx] in the rotated unit-norm domain, scaled by 2^8
         // and split into fp16 hi + lo for the sketch contraction S r.
         const float inv = sc > 0.0f ? 1.0f / sc : 0.0f;
@@ -585,14 +600,22 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
           for (int t = 0; t < 4; ++t) sa[t] = mfma(s_l[t], rh[ks], sa[t]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        uint32_t sb[2] = {0u, 0u};
+        // sign bits, bit j of word k for sketch row 32 k + j of this half: one
+        // funnel shift per row, from the last row down, moves the word up a
+        // place and takes the value's IEEE sign bit at the bottom; inverted,
+        // a bit is 1 for S r >= 0 (and 0 for a -0.0 sum, where either sign is
+        // as good)
+        uint32_t sb[2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int k = 0; k < 2; ++k) {
+          uint32_t wv = 0u;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = 16 * t + r;
-            sb[j >> 5] |= (sa[t][r] >= 0.0f ? 1u : 0u) << (j & 31);
+          for (int j = 31; j >= 0; --j) {
+            const int row = 32 * k + j;
+            wv = __builtin_amdgcn_alignbit(wv, __float_as_uint(sa[row >> 4][row & 15]), 31);
           }
+          sb[k] = ~wv;
+        }
         if (valid) {
           *reinterpret_cast<uint2*>(signs + (ds * cap + dp) * (QJL_M / 8) + 8 * h) = make_uint2(sb[0], sb[1]);
           if (h == 0) rnorms[ds * cap + dp] = sqrtf(g2);
@@ -626,11 +649,13 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
                                                       cell_s[0]); }, wds);
           store_tiled_chunk<BLO>(tbase + g * G + 8 * BLO * q + 4 * BLO * (j & 1), wds, vmask);
         } else if (j < 16) {
-          load_pos_thresholds<BLO>(tab, 0, 1.0f, tp);
+#pragma unroll
+          for (int k = 0; k < Width<BLO>::NPOS; ++k) tp[k] = tpos[0][k];
           pack_tiled<BLO>(acc, inv, tp, gg, wds);
           store_tiled_chunk<BLO>(tbase + g * G + 8 * BLO * q + 4 * BLO * (j & 1), wds, vmask);
         } else {
-          load_pos_thresholds<BHI>(tab, 1, 1.0f, tp);
+#pragma unroll
+          for (int k = 0; k < Width<BHI>::NPOS; ++k) tp[k] = tpos[1][k];
           pack_tiled<BHI>(acc, inv, tp, gg, wds);
           store_tiled_chunk<BHI>(tbase + g * G + 64 * BLO + 8 * BHI * (q - 8) + 4 * BHI * (j & 1), wds, vmask);
         }
