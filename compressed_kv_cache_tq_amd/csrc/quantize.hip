@@ -671,7 +671,9 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
 // Register-resident rotation kernel: every spec without the QJL stage (for
 // the tiled layout, the tiles that are written whole).
 //
-// A workgroup of 4 waves works on two 32-vector tiles at a time.  Waves 2p
+// A workgroup of 2 RQ_PAIRS waves (4) works on RQ_PAIRS 32-vector tiles at a
+// time, two workgroups per CU (the register budget allows two waves per
+// SIMD; one pair per workgroup and four workgroups measured no faster).  Waves 2p
 // and 2p + 1 form pair p and split the 128 rotated coordinates of the pair's
 // tile: wave w of the pair owns coordinates [64 w, 64 w + 64) and keeps the
 // rows of 256 Pi for them as fp16 hi + lo MFMA fragments in registers for the
@@ -708,8 +710,10 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
 // One launch covers up to RQ_MAX_SEQ sequences of a batch (ragged lengths
 // and offsets); each sequence's tiles start on a multiple of the tiles per
 // pair, so a pair finds its sequence once and all of its tiles lie in it.
-constexpr int RQ_WAVES = 4;
+constexpr int RQ_PAIRS = 2;  // pairs of waves per workgroup
+constexpr int RQ_WAVES = 2 * RQ_PAIRS;
 constexpr int RQ_THREADS = 64 * RQ_WAVES;
+constexpr int RQ_RESIDENT_PAIRS = 4;  // per CU: two waves per SIMD (the register budget)
 constexpr int RSRC_WORD3 = 0x00020000;
 constexpr int RQ_MAX_SEQ = 64;
 constexpr int RQ_OOB = 0x40000000;  // buffer offset beyond every extent used here
@@ -842,8 +846,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   constexpr int ES = F32IN ? 4 : 2;          // input element bytes
   constexpr int NQW = F32IN ? 8 : 4;         // 16-byte input words per staging thread
   constexpr int CODE_BYTES = 8 * (BLO + BHI);
-  __shared__ uint4 xbuf[2][2][XP][8 * 64];   // [pair][buffer][part][ks * 64 + lane]
-  __shared__ float inv_s[2][2][32];          // [pair][buffer][vector]: 1 / (norm 2^(sh+8))
+  __shared__ uint4 xbuf[RQ_PAIRS][2][XP][8 * 64];  // [pair][buffer][part][ks * 64 + lane]
+  __shared__ float inv_s[RQ_PAIRS][2][32];         // [pair][buffer][vector]: 1 / (norm 2^(sh+8))
   __shared__ uint2 cell_s[B8 ? 1 : 2][B8 ? CELL8_ENTRIES : CELL_ENTRIES];
   __shared__ uint4 pil1_s[2][8][64];         // low parts of the t = 1 fragments: [w][ks][lane]
 
@@ -857,7 +861,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   // (a store right here would hold back every later load behind this one)
   constexpr int NCE = B8 ? CELL8_ENTRIES : 2 * CELL_ENTRIES;  // cell entries
   constexpr int CPT = (NCE + RQ_THREADS - 1) / RQ_THREADS;      // per thread
-  static_assert(B8 || CPT == 2, "cell table fill");
+  static_assert(NCE <= CPT * RQ_THREADS && RQ_THREADS <= NCE, "cell table fill");
   const uint2* cell_g = reinterpret_cast<const uint2*>(B8 ? &tab->cell8[0][0] : &tab->cell[0][0][0]);
   uint2 cv[CPT];
   cv[0] = cell_g[tid];
@@ -881,12 +885,13 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   }
 
   // A chunk is K consecutive launch tiles, all in one sequence (each
-  // sequence's tiles start on a multiple of K).  PERSIST: pair p of workgroup
-  // g takes chunks 2 g + p + i * 2 gridDim.x for i < A.n_iter, the same count
-  // for every pair (a chunk past A.n_chunks is empty: its loads read zeros
-  // and its stores are dropped), and its pipeline runs on across chunk
-  // boundaries, so the rotation fragments and the pipeline's start are paid
-  // once per pair.  Otherwise the pair takes chunk 2 g + p alone.
+  // sequence's tiles start on a multiple of K).  With P = RQ_PAIRS pairs per
+  // workgroup, PERSIST: pair p of workgroup g takes chunks P g + p +
+  // i P gridDim.x for i < A.n_iter, the same count for every pair (a chunk
+  // past A.n_chunks is empty: its loads read zeros and its stores are
+  // dropped), and its pipeline runs on across chunk boundaries, so the
+  // rotation fragments and the pipeline's start are paid once per pair.
+  // Otherwise the pair takes chunk P g + p alone.
   constexpr bool PERSIST = K % 6 == 0;  // buffer roles repeat every 3 tiles, LDS buffers every 2
   const int64_t xss = A.xss, xrs = A.xrs, cap = A.cap;
   const int64_t stream_code_bytes = A.stream_code_bytes;
@@ -922,8 +927,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     v.page_row = Q.page_row;
     return v;
   };
-  const int64_t chunk0 = static_cast<int64_t>(blockIdx.x) * 2 + pair;
-  const int64_t chunk_step = static_cast<int64_t>(gridDim.x) * 2;
+  const int64_t chunk0 = static_cast<int64_t>(blockIdx.x) * RQ_PAIRS + pair;
+  const int64_t chunk_step = static_cast<int64_t>(gridDim.x) * RQ_PAIRS;
   SeqView cur = view_of(chunk0);
 
   // Tile tl of the sequence: stream s, tile T of the stream; its rows of x
@@ -1331,7 +1336,7 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
     // A persistent launch (chunks of 6 tiles, each pair looping over its
     // chunks) once every resident pair gets at least 8 chunks; else one chunk
     // per pair: 8 tiles once that still fills every CU twice over, or 2.
-    const int64_t pairs = 4 * static_cast<int64_t>(cu_count_cached());  // two resident workgroups of two pairs per CU
+    const int64_t pairs = RQ_RESIDENT_PAIRS * static_cast<int64_t>(cu_count_cached());
     const int K = MERGE ? 2 : raw >= 6 * 8 * pairs ? 6 : raw >= 8 * 1024 ? 8 : 2;
 
     RotqArgs a{};
@@ -1364,14 +1369,14 @@ hipError_t launch_rotq_list(const Tables* tab, const void* x, const std::vector<
       total += (hkv * p.tiles + K - 1) / K * K;
     }
     a.n_chunks = total / K;
-    unsigned blocks = static_cast<unsigned>((a.n_chunks + 1) / 2);
+    unsigned blocks = static_cast<unsigned>((a.n_chunks + RQ_PAIRS - 1) / RQ_PAIRS);
     a.n_iter = 1;
     if (K == 6) {
-      // two resident workgroups per CU (the register budget of the kernel),
-      // each pair looping over its chunks
-      const int64_t resident = 2 * static_cast<int64_t>(cu_count_cached());
+      // the resident workgroups only (two waves per SIMD, the register
+      // budget of the kernel), each pair looping over its chunks
+      const int64_t resident = RQ_RESIDENT_PAIRS / RQ_PAIRS * static_cast<int64_t>(cu_count_cached());
       if (blocks > resident) blocks = static_cast<unsigned>(resident);
-      a.n_iter = static_cast<int32_t>((a.n_chunks + 2 * blocks - 1) / (2 * blocks));
+      a.n_iter = static_cast<int32_t>((a.n_chunks + RQ_PAIRS * blocks - 1) / (RQ_PAIRS * blocks));
     }
     if constexpr (MERGE) {
       hipLaunchKernelGGL((rotq_kernel<BLO, BHI, F32IN, TILED, 2, true, PAGED>), dim3(blocks), dim3(RQ_THREADS), 0,
