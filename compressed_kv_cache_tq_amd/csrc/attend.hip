@@ -82,7 +82,8 @@ __global__ __launch_bounds__(CT) void combine_kernel(const Tables* __restrict__ 
     if (hs + 2 * u < n_split) a = fmaf(wsp[hs + 2 * u], pa[u], a);
 #pragma unroll 8
   for (int sp = hs + 2 * PA; sp < n_split; sp += 2) a = fmaf(wsp[sp], pp[static_cast<int64_t>(sp) * PART + 4 + c], a);
-  rs[hs][c] = a;
+  // (the value lookup tables hold centroids times the codebook's scale)
+  rs[hs][c] = a / vtab->cen16_scale[c < static_cast<int>(vtab->split) ? 0 : 1];
   __syncthreads();
   const float Ls = red[4] + red[5] + red[6] + red[7];
   // ---- slice of the inverse rotation (+ the sink values): thread (oi, cq)

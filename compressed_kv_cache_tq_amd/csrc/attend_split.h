@@ -66,8 +66,10 @@ __device__ __forceinline__ uint32_t row_bits(const uint32_t* w, int k) {
 // LDS layout of the replicated LUTs (bytes): widths 3 and 2 first, then 4
 // and 8, so every LUT base (at most 20 KiB) fits the immediate offset of the
 // LDS read and the lane-dependent part of the address is one AND-OR.  Widths
-// up to 4 map a code pair (one byte of 4-bit codes) to two fp16 centroids;
-// width 8 maps one code (one byte) to one fp16 centroid in the low half.
+// up to 4 map a code pair (one byte of 4-bit codes) to two fp16 centroids,
+// each times the width's centroid scale from the tables (divided out of the
+// query coordinates and the value accumulator); width 8 maps one code (one
+// byte) to one fp16 centroid in the low half (scale 1).
 template <int B>
 constexpr int lut_entries() { return B == 8 ? 256 : 1 << (2 * B); }
 template <int B>
@@ -448,12 +450,12 @@ __device__ __forceinline__ int rank_sequence(const int32_t* __restrict__ seq_len
   return order_s[r];
 }
 
-// Split kernel: one workgroup of 8 waves per (split, kv head, sequence).
 // Merge of one stream's partials, run by the stream's workgroup when it is
 // the stream's only split: for each of its G query heads, the log-sum-exp weights of
 // the n_split split partials (rotated value domain) and of the sink partial
 // (slot n_split, original domain, present when n_slot > n_split), the
-// weighted rotated sum, one inverse rotation Pi_V^T, the division by l.
+// weighted rotated sum (divided by the value codebook's centroid scale), one
+// inverse rotation Pi_V^T, the division by l.
 // pp: partials of the group's first head; og: its output rows.
 __device__ __forceinline__ void merge_stream(uint8_t* smem, const Tables* __restrict__ vtab,
                                              const float* __restrict__ pp, float* __restrict__ og, int G,
@@ -503,7 +505,8 @@ __device__ __forceinline__ void merge_stream(uint8_t* smem, const Tables* __rest
     float a = 0.0f;
 #pragma unroll 8
     for (int sl = 0; sl < n_split; ++sl) a = fmaf(wg[sl], ph[sl * PART], a);
-    rs[idx] = a;
+    // (the value lookup tables hold centroids times the codebook's scale)
+    rs[idx] = a / vtab->cen16_scale[c < static_cast<int>(vtab->split) ? 0 : 1];
   }
   if (tid < G) swt[tid] = n_slot > n_split ? wsm[tid * WROW + n_split] : 0.0f;
   __syncthreads();
@@ -865,7 +868,8 @@ __global__ __launch_bounds__(ST, 1) void split_kernel(
     if (idx < G * D) {
       const int g = idx >> 7, i = idx & (D - 1);
       const float x = reduce_part(g, i) * qscale;
-      store_split(0, g, i, x, shx[g]);
+      // the key lookup tables hold centroids times the codebook's scale
+      store_split(0, g, i, x / ktab->cen16_scale[i < static_cast<int>(ktab->split) ? 0 : 1], shx[g]);
       if constexpr (QJL) qrot[idx] = x;
     }
   }

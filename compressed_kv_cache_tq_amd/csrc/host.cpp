@@ -6,6 +6,7 @@
 // rotation, per-coordinate optimal scalar quantizer, 1-bit JL sketch of the
 // residual) and "Cosa aggiunge turboquant-mlx" (Lloyd-Max codebook).
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -310,6 +311,38 @@ uint16_t to_half(double v) {
   return sign | static_cast<uint16_t>(((ex + 15) << 10) | (static_cast<int>(m) - 1024));
 }
 
+// The value of a binary16 bit pattern (finite).
+double from_half(uint16_t h) {
+  const int ex = (h >> 10) & 31, m = h & 1023;
+  const double a = ex == 0 ? std::ldexp(static_cast<double>(m), -24) : std::ldexp(1024.0 + m, ex - 25);
+  return (h & 0x8000u) ? -a : a;
+}
+
+// Scale s in [1, 2) of a codebook's fp16 centroids: the kernels' lookup
+// tables hold fp16(c_j s), and s is divided out in fp32 on the other operand
+// (the query's coordinates before their hi + lo split, the value
+// accumulator before the inverse rotation).  s minimises the largest relative
+// rounding error over the centroids, searched over s = 1 + k / 2^16: for a
+// 4-bit codebook that is about 4 times below the 2^-12 bound of plain fp16,
+// more for fewer levels.  A pure function of the centroids.
+double centroid_scale(const double* c, int n) {
+  double best = INFINITY, best_s = 1.0;
+  for (int k = 0; k < (1 << 16); ++k) {
+    const double sc = 1.0 + k * 0x1.0p-16;
+    double worst = 0.0;
+    for (int j = 0; j < n && worst < best; ++j) {
+      if (c[j] == 0.0) continue;
+      const double v = c[j] * sc;
+      worst = std::max(worst, std::fabs(from_half(to_half(v)) - v) / std::fabs(v));
+    }
+    if (worst < best) {
+      best = worst;
+      best_s = sc;
+    }
+  }
+  return best_s;
+}
+
 // bfloat16 from a double, round to nearest even (one rounding step; finite
 // values below the overflow threshold).
 uint16_t to_bf16(double v) {
@@ -334,12 +367,6 @@ double from_bf16(uint16_t b) {
   float f;
   std::memcpy(&f, &u, 4);
   return f;
-}
-
-double from_half(uint16_t h) {
-  const int ex = (h >> 10) & 0x1F, man = h & 0x3FF;
-  double v = ex == 0 ? std::ldexp(man, -24) : std::ldexp(1024 + man, ex - 25);
-  return (h & 0x8000u) ? -v : v;
 }
 
 // ---------------------------------------------------------------------------
@@ -516,6 +543,7 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
       codebook_build(tq::D, b, c.data(), bd.data());
       if (b == 8) {
         if (h == 1) break;  // uniform width: one codebook
+        t->cen16_scale[0] = t->cen16_scale[1] = 1.0f;
         for (int j = 0; j < 256; ++j) {
           t->bnd8[j] = j < 255 ? static_cast<float>(bd[j]) : INFINITY;
           t->cen8[j] = static_cast<float>(c[j]);
@@ -526,10 +554,18 @@ tq_status tq_tables_build(const tq_spec* spec, void* host_buf, size_t bytes) {
           return fail(TQ_E_UNSUPPORTED, "8-bit codebook boundaries too close for the code cell table");
         break;
       }
+      // (the scale depends on the width alone: computed once per width)
+      static std::atomic<double> scale_of[9];
+      double sc = scale_of[b].load(std::memory_order_relaxed);
+      if (!(sc >= 1.0)) {
+        sc = centroid_scale(c.data(), L);
+        scale_of[b].store(sc, std::memory_order_relaxed);
+      }
+      t->cen16_scale[h] = static_cast<float>(sc);
       for (int j = 0; j < 16; ++j) {
         t->bnd[h][j] = j < L - 1 ? static_cast<float>(bd[j]) : INFINITY;
         t->cen[h][j] = j < L ? static_cast<float>(c[j]) : 0.0f;
-        t->cen16[h][j] = j < L ? to_half(c[j]) : 0;
+        t->cen16[h][j] = j < L ? to_half(c[j] * sc) : 0;
       }
       if (!cell_table_u(t->bnd[h], L - 1, t->cell[h]))
         return fail(TQ_E_UNSUPPORTED, "codebook boundaries too close for the code cell table");

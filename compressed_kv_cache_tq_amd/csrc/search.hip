@@ -77,7 +77,10 @@ __global__ __launch_bounds__(D) void ipq_prep_kernel(const Tables* __restrict__ 
   float a = 0.0f;
 #pragma unroll 8
   for (int k = 0; k < D; ++k) a = fmaf(tab->pit[k * D + i], qs[k], a);
-  const float qinv = split_row(a, nq, w->q[qi][0], w->q[qi][1], i);
+  // (the lookup tables hold centroids times the codebook's scale, s >= 1:
+  // the bound nq still holds for the divided coordinate)
+  const float qinv =
+      split_row(a / tab->cen16_scale[i < static_cast<int>(tab->split) ? 0 : 1], nq, w->q[qi][0], w->q[qi][1], i);
   if (i == 0) w->qinv[qi] = qinv;
   if (qjl) {
     qt[i] = a;

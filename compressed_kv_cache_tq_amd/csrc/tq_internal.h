@@ -44,8 +44,14 @@ struct alignas(256) Tables {
   uint32_t pad0;
   float bnd[2][16];
   float cen[2][16];
+  // fp16 centroids for the lookup tables of the decode and the search:
+  // cen16[h][j] = fp16(cen[h][j] * cen16_scale[h]), with the scale s in [1, 2)
+  // that minimises the largest relative rounding error of the codebook (a
+  // function of the width alone, 1 for 8-bit codes).  The kernels divide s
+  // out in fp32 on the other operand.
   uint16_t cen16[2][16];
-  uint8_t pad1[512 - 32 - 128 - 128 - 64];
+  float cen16_scale[2];
+  uint8_t pad1[512 - 32 - 128 - 128 - 64 - 8];
   float pi[D * D];
   uint16_t pi_hi[D * D];
   uint16_t pi_lo[D * D];

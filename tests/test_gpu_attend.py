@@ -73,6 +73,25 @@ def test_attend_sink_and_peaked_v_skip():
     _check(Run(inp), label="v-skip edge")
 
 
+@pytest.mark.parametrize("name,ctx,batch,qs", [
+    ("long_context", 3000, None, 16.0),
+    ("long_context", 3000, None, 32.0),
+    ("gqa_decode", 2000, None, 32.0),
+    ("batched_ragged", 1500, 4, 32.0),
+])
+def test_attend_peaked_scores(name, ctx, batch, qs):
+    """Queries scaled so the logits spread 16 or 32 times wider: softmaxes
+    close to one-hot, where a score error moves weight between the top
+    tokens.  The lookup tables' fp16 centroids carry a per-width scale that
+    cuts their rounding error (3.5x at 4 bits, 9x at 3), which keeps these
+    within the bar (with plain fp16 centroids long_context reached 3.7e-3 at
+    x32)."""
+    print(f"[attend] peaked scores {name} q x{qs:g}", flush=True)
+    inp = workloads.generate(name, ctx=ctx, batch=batch)
+    inp.q = inp.q * np.float32(qs)
+    _check(Run(inp), label=f"peaked {name} q x{qs:g}")
+
+
 def test_attend_gqa_g1_and_g16():
     for hq, hkv in ((8, 8), (16, 1)):
         print(f"[attend] hq={hq} hkv={hkv}", flush=True)
