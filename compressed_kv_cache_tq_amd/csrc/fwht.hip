@@ -19,6 +19,7 @@
 // the record layout, bf16 input, uniform 2-, 3- or 4-bit codes, no sketch,
 // contiguous caches; one launch covers up to 64 sequences of a ragged batch.
 #include "cell.h"
+#include "lanes.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(FW_THREADS) void fwht_kernel(const FwArgs A) {
       }
       ss += static_cast<double>(c);
     }
-    ss += __shfl_xor(ss, 32);
+    ss = add_half_swap(ss);
     const float normf = static_cast<float>(sqrt(ss));
     // ---- sign flips, then the transform on the lane's 64 coordinates
     float y[64];

@@ -34,6 +34,7 @@
 #include <vector>
 
 #include "cell.h"
+#include "lanes.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
         ss += static_cast<double>(c);
       }
     }
-    ss += __shfl_xor(ss, 32);
+    ss = add_half_swap(ss);
     const float normf = static_cast<float>(sqrt(ss));
     int ex;
     frexpf(normf, &ex);
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
           rr[c] = y - cen_s[h][idx[c]];
           g2 = fmaf(rr[c], rr[c], g2);
         }
-        g2 += __shfl_xor(g2, 32);
+        g2 = add_half_swap(g2);
         half8 rh[8], rl[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
@@ -1020,8 +1021,8 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
         ss += static_cast<double>(c);
       }
     }
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
+    ss = add_quad_xor<1>(ss);
+    ss = add_quad_xor<2>(ss);
     const float normf = static_cast<float>(sqrt(ss));
     int ex = 0;
     frexpf(normf, &ex);
