@@ -22,8 +22,11 @@
  * Conventions for every entry point
  *  - Ownership: the caller owns every host and device buffer, including the
  *    device copy of the tables and the attention workspace.  The library
- *    allocates no device memory and keeps no state except a thread-local
- *    error string.
+ *    allocates no device memory at run time; its one device array is the
+ *    static scratch of tq_attend_decode_noalloc, part of the loaded code
+ *    object.  Host state: a thread-local error string and process-wide
+ *    caches of derived constants (compute units and that scratch's address
+ *    per device, the codebook centroid scales), none of it caller data.
  *  - Errors: arguments are validated on the host before any launch.  A
  *    failed check returns a negative tq_status, launches nothing and sets
  *    tq_last_error().  A failed launch returns TQ_E_HIP with the HIP error
@@ -32,7 +35,9 @@
  *    codes and outputs; vectors whose squared norm overflows fp32 likewise.
  *  - Streams: `stream` is a hipStream_t (NULL = default stream).  Every
  *    device call is asynchronous on that stream; the library never
- *    synchronizes.
+ *    synchronizes.  A device call issues kernel launches only (no memset,
+ *    copy or allocation), so it can be captured in a HIP graph and replayed
+ *    (with the same arguments, pointing at the same buffers).
  *  - Device pointers must be 16-byte aligned unless stated otherwise.
  */
 #ifndef TQ_H_
