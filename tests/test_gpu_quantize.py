@@ -511,3 +511,32 @@ def test_quantize_hadamard_butterflies(bits):
                 rb = 16 * bits
                 stream = c.codes[s * 192 * rb:(s + 1) * 192 * rb].view(192, rb)
                 assert T.all(stream[:tok0[b]] == 0x5A) and T.all(stream[tok0[b] + n:] == 0x5A)
+
+
+def test_quantize_hadamard_butterflies_many_sequences():
+    """The butterfly kernel takes at most 64 sequences per launch: a ragged
+    call of 150 short sequences (three launches, empty ones among them) must
+    write every sequence's streams, held to the oracle's Hadamard rotation."""
+    print("[quantize] hadamard butterflies: 150 sequences", flush=True)
+    T = torch()
+    rng = np.random.default_rng(75)
+    n_seq, hkv, rows, cap = 150, 2, 40, 64
+    lens = rng.integers(0, rows + 1, n_seq).tolist()
+    lens[0] = lens[64] = lens[128] = 0
+    tok0 = rng.integers(0, cap - rows + 1, n_seq).tolist()
+    x = workloads.bf16_to_f32(workloads.bf16_bits(
+        rng.standard_normal((n_seq * hkv, rows, 128), dtype=np.float32)))
+    spec = tq.Spec(4, layout=tq.LAYOUT_RECORD, rotation=tq.ROT_HADAMARD_FWHT)
+    cache = tq.alloc_cache(spec, n_seq * hkv, cap, fill=0x5A)
+    tq.quantize_kv_ragged(spec, tq.device_tables(spec), to_device(x, "bf16"), cache, hkv=hkv, n_tok=lens, tok0=tok0)
+    T.cuda.synchronize()
+    rb = tq.code_bytes(spec)
+    streams = cache.codes[: n_seq * hkv * cap * rb].view(n_seq * hkv, cap, rb)
+    for b, n in enumerate(lens):
+        for h in range(hkv):
+            s = b * hkv + h
+            assert T.all(streams[s, :tok0[b]] == 0x5A) and T.all(streams[s, tok0[b] + n:] == 0x5A), \
+                f"sequence {b}: positions outside its range were written"
+            if n:
+                check_quantized(spec, x[s, :n], read_codes(spec, cache, s, n, tok0[b]),
+                                read_norms(cache, s, n, tok0[b]), label=f"butterflies seq {b} head {h}")
