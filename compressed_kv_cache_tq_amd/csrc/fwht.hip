@@ -20,6 +20,7 @@
 // contiguous caches; one launch covers up to 64 sequences of a ragged batch.
 #include "cell.h"
 #include "lanes.h"
+#include "norm.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -132,6 +133,15 @@ __global__ __launch_bounds__(FW_THREADS) void fwht_kernel(const FwArgs A) {
       ss += static_cast<double>(c);
     }
     ss = add_half_swap(ss);
+    // a sum outside the fp32 chains' exact range (rare): both lanes of such
+    // a vector redo theirs on scaled elements
+    const bool slow = !sumsq_fast_ok(ss);
+    const bool any_slow = __builtin_amdgcn_ballot_w64(slow) != 0;
+    if (any_slow) {
+      const float s = sumsq_rescale(ss);
+      const double s2 = add_half_swap(static_cast<double>(bf16_sumsq_scaled(xr, s)));
+      if (slow) ss = s2 / (static_cast<double>(s) * static_cast<double>(s));
+    }
     const float normf = static_cast<float>(sqrt(ss));
     // ---- sign flips, then the transform on the lane's 64 coordinates
     float y[64];
@@ -140,6 +150,19 @@ __global__ __launch_bounds__(FW_THREADS) void fwht_kernel(const FwArgs A) {
       const uint32_t w = fw_word(xr[k >> 2], k & 3) ^ flip[k];
       y[2 * k] = __uint_as_float(w << 16);
       y[2 * k + 1] = __uint_as_float(w & 0xFFFF0000u);
+    }
+    // Such vectors are scaled by a power of two to a norm in [1/2, 1) (exact in
+    // fp32, denormal inputs included), so that neither the butterfly sums
+    // nor 1 / norm leave fp32's range; the transform is linear.
+    float nrm_eff = normf;
+    if (any_slow) {
+      int ex = 0;
+      frexpf(normf, &ex);
+      const int e = min(-ex, 126);  // (a norm below 2^-126 ends in [2^-7, 1))
+      const float f = slow ? ldexpf(1.0f, e) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) y[i] *= f;
+      nrm_eff = slow ? ldexpf(normf, e) : normf;
     }
 #pragma unroll
     for (int len = 1; len < 64; len <<= 1)
@@ -161,7 +184,7 @@ __global__ __launch_bounds__(FW_THREADS) void fwht_kernel(const FwArgs A) {
       y[i] = fmaf(y[i], sgn, other);
     }
     // ---- codes from the cell table: y / (sqrt(d) ||x||) is the rotated unit vector
-    const float inv = normf > 0.0f ? INV_SQRT_D / normf : 0.0f;
+    const float inv = nrm_eff > 0.0f ? INV_SQRT_D / nrm_eff : 0.0f;
     uint32_t wd[2 * B];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {

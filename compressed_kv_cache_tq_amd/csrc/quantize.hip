@@ -35,6 +35,7 @@
 
 #include "cell.h"
 #include "lanes.h"
+#include "norm.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -464,10 +465,20 @@ __global__ __launch_bounds__(THREADS, 1) void quantize_kernel(const GenArgs A) {
       }
     }
     ss = add_half_swap(ss);
+    if constexpr (!F32IN) {
+      // a sum outside the fp32 chains' exact range (rare): both lanes of
+      // such a vector redo theirs on scaled elements
+      const bool slow = !sumsq_fast_ok(ss);
+      if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+        const float s = sumsq_rescale(ss);
+        const double s2 = add_half_swap(static_cast<double>(bf16_sumsq_scaled(xr, s)));
+        if (slow) ss = s2 / (static_cast<double>(s) * static_cast<double>(s));
+      }
+    }
     const float normf = static_cast<float>(sqrt(ss));
     int ex;
     frexpf(normf, &ex);
-    const int sh = 14 - ex;  // fp16 paths: |x * 2^sh| < 2^14
+    const int sh = min(14 - ex, 127);  // fp16 paths: |x * 2^sh| < 2^14 (2^sh finite)
 
     // ---- rotation on MFMA, one k-step at a time
     f32x16 acc[4];
@@ -851,6 +862,7 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   __shared__ float inv_s[RQ_PAIRS][2][32];         // [pair][buffer][vector]: 1 / (norm 2^(sh+8))
   __shared__ uint2 cell_s[B8 ? 1 : 2][B8 ? CELL8_ENTRIES : CELL_ENTRIES];
   __shared__ uint4 pil1_s[2][8][64];         // low parts of the t = 1 fragments: [w][ks][lane]
+  __shared__ int redo_s;                     // a vector needs the robust staging
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform: the pair's tiles, and so the buffer resources, live in SGPRs
@@ -998,8 +1010,14 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     for (int k = 0; k < NQW; ++k)
       dst[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0));
   };
-  // norm, scale, fp16 conversion into buffer b; the norm goes out here too
-  auto stage = [&](const SeqView& v, int64_t tl, const uint4 (&xin)[NQW], int b) {
+  // norm, scale, fp16 conversion into buffer b; the norm goes out here too.
+  // Returns whether one of the thread's vectors lies outside the range where
+  // the fp32 chains of squares are exact (elements below about 2^-63 or
+  // above 2^64); the ROBUST staging (a rare second pass over such a tile)
+  // redoes those sums on scaled elements.  The check stays out of the hot
+  // path, whose registers and scheduling a branch here would disturb.
+  auto stage = [&](auto robust, const SeqView& v, int64_t tl, const uint4 (&xin)[NQW], int b) {
+    constexpr bool ROBUST = decltype(robust)::value;
     double ss = 0.0;
     if constexpr (F32IN) {
 #pragma unroll
@@ -1023,10 +1041,23 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     }
     ss = add_quad_xor<1>(ss);
     ss = add_quad_xor<2>(ss);
+    // (fp32 inputs: squares in fp64, exact over the whole range; rows the
+    // tile does not write, such as the zero rows past a partial tile's end,
+    // do not count)
+    const TileAt a = tile_at(v, tl);
+    const bool slow = !F32IN && !sumsq_fast_ok(ss) && sv >= a.lo && sv < a.nv;
+    if constexpr (ROBUST && !F32IN) {
+      const float s = sumsq_rescale(ss);
+      double s2 = static_cast<double>(bf16_sumsq_scaled(xin, s));
+      s2 = add_quad_xor<1>(s2);
+      s2 = add_quad_xor<2>(s2);
+      if (slow) ss = s2 / (static_cast<double>(s) * static_cast<double>(s));
+    }
     const float normf = static_cast<float>(sqrt(ss));
     int ex = 0;
     frexpf(normf, &ex);
-    const int sh = 14 - ex;
+    // (2^sh stays finite for the smallest norms, where |x| 2^127 < 2^14)
+    const int sh = min(14 - ex, 127);
     const float up = ldexpf(1.0f, sh);
     const int arow = TILED ? tiled_row(sv) : sv;
 #pragma unroll
@@ -1060,7 +1091,6 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     }
     // the four threads of a vector write the same values
     inv_s[pair][b][sv] = normf > 0.0f ? 1.0f / ldexpf(normf, sh + 8) : 0.0f;
-    const TileAt a = tile_at(v, tl);
     const Dst d = dest_at(v, a);
     const __amdgpu_buffer_rsrc_t rn =
         rsrc(v.nrm + (d.s * cap + d.p) * nbytes, d.ok ? static_cast<int64_t>(a.nv) * nbytes : 0);
@@ -1070,28 +1100,41 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
                                             rn, noff, 0, 0);
     else
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(normf), rn, noff, 0, 0);
+    return slow;
   };
-
   // ---- pipeline, straight-line over each chunk's K tiles: three register
   // buffers with fixed roles (tile k+1 is staged from X[(k+1) % 3] while
   // tiles k+2, k+3 are still loading; the buffer is then refilled with tile
   // k+4), so the waits on in-flight loads are exact.  PERSIST: tiles k+1 and
   // k+4 past the chunk's end are the first tiles of the pair's next chunk.
+  //
+  // The loop runs once with the fast staging and collects whether any of
+  // its vectors lay outside the fast norm's range; if one did anywhere in
+  // the workgroup (never, for data of any ordinary scale), the workgroup
+  // runs it again with the robust staging, which rewrites every output of
+  // its tiles.  The hot loop itself then has no extra branch.
+  if (tid == 0) redo_s = 0;
+  auto pass = [&, pl1, cv](auto robust) __attribute__((always_inline)) -> bool {
+  constexpr bool R = decltype(robust)::value;
+  uint64_t need = 0;
+  cur = view_of(chunk0);
   uint4 X[3][NQW];
   load_x(cur, cur.first, X[0]);
   if (PERSIST || K > 1) load_x(cur, cur.first + 1, X[1]);
   if (PERSIST || K > 2) load_x(cur, cur.first + 2, X[2]);
   // (the fragment loads are older than the tile loads: this waits for them only)
-  if (pair == 0) {
+  if (!R && pair == 0) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) pil1_s[w][ks][lane] = pl1[ks];
   }
-  stage(cur, cur.first, X[0], 0);
+  need |= __builtin_amdgcn_ballot_w64(stage(robust, cur, cur.first, X[0], 0));
   if (PERSIST || K > 3) load_x(cur, cur.first + 3, X[0]);
-  reinterpret_cast<uint2*>(cell_s)[tid] = cv[0];
+  if constexpr (!R) {
+    reinterpret_cast<uint2*>(cell_s)[tid] = cv[0];
 #pragma unroll
-  for (int i = 1; i < CPT; ++i)
-    if (tid + i * RQ_THREADS < NCE) reinterpret_cast<uint2*>(cell_s)[tid + i * RQ_THREADS] = cv[i];
+    for (int i = 1; i < CPT; ++i)
+      if (tid + i * RQ_THREADS < NCE) reinterpret_cast<uint2*>(cell_s)[tid + i * RQ_THREADS] = cv[i];
+  }
   __syncthreads();
   const int n_iter = PERSIST ? A.n_iter : 1;
   for (int it = 0; it < n_iter; ++it) {
@@ -1131,11 +1174,11 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
     // stage the next tile into the other buffer while the products finish,
     // and refill its registers: they are free before the codes are made
     if (k + 1 < K) {
-      stage(cur, tl + 1, X[(k + 1) % 3], b ^ 1);
+      need |= __builtin_amdgcn_ballot_w64(stage(robust, cur, tl + 1, X[(k + 1) % 3], b ^ 1));
       if (k + 4 < K) load_x(cur, tl + 4, X[(k + 1) % 3]);
       else if (PERSIST) load_x(nxt, nxt.first + (k + 4 - K), X[(k + 1) % 3]);
     } else if (PERSIST) {
-      stage(nxt, nxt.first, X[(k + 1) % 3], b ^ 1);
+      need |= __builtin_amdgcn_ballot_w64(stage(robust, nxt, nxt.first, X[(k + 1) % 3], b ^ 1));
       load_x(nxt, nxt.first + 3, X[(k + 1) % 3]);
     }
     const TileAt a = tile_at(cur, tl);
@@ -1243,6 +1286,11 @@ __global__ __launch_bounds__(RQ_THREADS, 2) void rotq_kernel(const RotqArgs A) {
   }
   cur = nxt;
   }
+  return need != 0;
+  };
+  if (pass(std::false_type{})) redo_s = 1;
+  __syncthreads();
+  if (redo_s != 0) pass(std::true_type{});
 }
 
 // The general kernel over a ragged batch: one launch per GEN_MAX_SEQ

@@ -540,3 +540,60 @@ def test_quantize_hadamard_butterflies_many_sequences():
             if n:
                 check_quantized(spec, x[s, :n], read_codes(spec, cache, s, n, tok0[b]),
                                 read_norms(cache, s, n, tok0[b]), label=f"butterflies seq {b} head {h}")
+
+
+def _extreme_scale_vectors(dtype):
+    """Vectors whose elements span bf16's exponent range: groups of 24 N(0,1)
+    vectors scaled by 2^e for e from -120 to +120 (squares below or above the
+    fp32 range), then vectors that mix one element of 2^70 or 2^-70 with
+    unit-scale ones, and zero vectors."""
+    rng = np.random.default_rng(404)
+    exps = [-120, -100, -80, -66, -40, 0, 40, 66, 90, 120]
+    x = rng.standard_normal((len(exps) * 24 + 16, 128), dtype=np.float32)
+    for g, e in enumerate(exps):
+        x[24 * g:24 * (g + 1)] *= np.float32(2.0 ** e)
+    tail = x[len(exps) * 24:]
+    tail[0:4, 7] = np.float32(2.0 ** 70)
+    tail[4:8, 100] = np.float32(2.0 ** -70)
+    tail[4:8, :100] *= np.float32(2.0 ** -60)
+    tail[8:12] = 0.0
+    tail[12:16] *= np.float32(2.0 ** -124)
+    if dtype == "bf16":
+        x = workloads.bf16_to_f32(workloads.bf16_bits(x))
+    return x[None]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", [tq.LAYOUT_RECORD, tq.LAYOUT_TILED])
+def test_quantize_extreme_scales(layout, dtype):
+    """Norms from 2^-130 to 2^124: the stored norm is within 1 ulp of the
+    correctly rounded one and the codes follow the oracle's band rule, where
+    the squares of the elements fall below or above the fp32 range."""
+    print(f"[quantize] extreme scales layout={layout} dtype={dtype}", flush=True)
+    spec = tq.Spec(4, layout=layout)
+    x = _extreme_scale_vectors(dtype)
+    n = x.shape[1]
+    cache = _quantize(spec, x, dtype)
+    check_quantized(spec, x[0], read_codes(spec, cache, 0, n), read_norms(cache, 0, n), label=f"{layout}/{dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_extreme_scales_sketch(dtype):
+    """The same vectors through the kernel of the sketch spec."""
+    print(f"[quantize] extreme scales qjl dtype={dtype}", flush=True)
+    spec = tq.Spec(2, qjl_m=128)
+    x = _extreme_scale_vectors(dtype)
+    n = x.shape[1]
+    cache = _quantize(spec, x, dtype)
+    check_quantized(spec, x[0], read_codes(spec, cache, 0, n), read_norms(cache, 0, n),
+                    signs=read_signs(cache, 0, n), label=f"qjl/{dtype}")
+
+
+def test_quantize_extreme_scales_butterflies():
+    """The same vectors through the butterfly Hadamard kernel (bf16 records)."""
+    print("[quantize] extreme scales hadamard butterflies", flush=True)
+    spec = tq.Spec(4, layout=tq.LAYOUT_RECORD, rotation=tq.ROT_HADAMARD_FWHT)
+    x = _extreme_scale_vectors("bf16")
+    n = x.shape[1]
+    cache = _quantize(spec, x, "bf16")
+    check_quantized(spec, x[0], read_codes(spec, cache, 0, n), read_norms(cache, 0, n), label="fwht")
