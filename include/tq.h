@@ -32,7 +32,12 @@
  *    tq_last_error().  A failed launch returns TQ_E_HIP with the HIP error
  *    text.
  *  - Data: kernels never fail on data.  Non-finite inputs give unspecified
- *    codes and outputs; vectors whose squared norm overflows fp32 likewise.
+ *    codes and outputs, and so does a vector whose norm exceeds FLT_MAX.
+ *    Every other input vector, denormal elements included, is quantized to
+ *    the same rule (stored norm within 1 ulp, codes exact but for ties
+ *    within rounding of a boundary), except on the bf16 fallback for row
+ *    strides beyond 32-bit offsets, where norms below about 2^-100 may lose
+ *    accuracy.
  *  - Streams: `stream` is a hipStream_t (NULL = default stream).  Every
  *    device call is asynchronous on that stream; the library never
  *    synchronizes.  A device call issues kernel launches only (no memset,
